@@ -1,0 +1,333 @@
+"""CPU oracle for the ReplaySSM Gated DeltaNet decode path.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg import this package. The product library neither imports,
+links nor calls anything here, and nothing here imports the product.
+
+Parts:
+  O1  gdn_step          plain sequential fp64 recurrence (C, liboracle.so)
+  O2  ReplayModel       the checkpoint + ring + cursor state machine, run
+                        exactly on the integers and in fp64 on the values,
+                        producing outputs through the closed-form replay
+  O3  fold_f32          the pinned-rounding fp32 fold (C, liboracle.so)
+  O4  window_ref        a verify window evaluated token by token with O1
+
+Every function states the passage it follows. The pages cited are: SGLang
+PR #28451 (ReplaySSM decode port), the ReplaySSM blog on llm.rainlin.net,
+vLLM PR #49887 (GDN speculative decode), SGLang PR #36821 (KDA fused verify
+with a ring) and SGLang PR #42388 (lossless verify).
+
+Parity pins: every function here is checked in tests/test_oracle_pins.py
+against exact rational arithmetic, brute-force matrix products, the worked
+flush table, closed forms and special cases (none of which reuse this code).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        L.oracle_gdn_step_f64.argtypes = [i32] * 6 + [P] * 9
+        L.oracle_gdn_step_f64.restype = None
+        L.oracle_fold_f32.argtypes = [i32] * 7 + [P] * 6 + [i32]
+        L.oracle_fold_f32.restype = None
+        L.oracle_version.restype = i32
+        assert L.oracle_version() == 1
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------ O1
+
+def gdn_step(S: np.ndarray, slot: np.ndarray, q, k, v, g, beta,
+             want_u: bool = False):
+    """O1: one decode token of the gated delta rule, fp64, in place on S.
+
+    Follows the ReplaySSM blog (section 1): S~ = alpha S, u = beta (v - S~ k),
+    S_t = S~ + u k^T, y = S_t q, alpha = exp(g).
+    S [N,Hv,dv,dk] float64 (modified), slot [B], q,k [B,Hk,dk], v [B,Hv,dv],
+    g,beta [B,Hv]. Returns o [B,Hv,dv] (and u when want_u).
+    """
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    N, Hv, dv, dk = S.shape
+    B = slot.shape[0]
+    Hk = q.shape[1]
+    slot = _c(slot, np.int32)
+    q, k, v, g, beta = (_c(x, np.float64) for x in (q, k, v, g, beta))
+    assert q.shape == (B, Hk, dk) and k.shape == (B, Hk, dk)
+    assert v.shape == (B, Hv, dv) and g.shape == (B, Hv) and beta.shape == (B, Hv)
+    o = np.empty((B, Hv, dv), np.float64)
+    u = np.empty((B, Hv, dv), np.float64) if want_u else None
+    lib().oracle_gdn_step_f64(B, N, Hv, Hk, dk, dv, _p(slot), _p(S), _p(q), _p(k),
+                              _p(v), _p(g), _p(beta), _p(o), _p(u))
+    return (o, u) if want_u else o
+
+
+# ------------------------------------------------------------------ O3
+
+def fold_f32(ckpt: np.ndarray, slot: np.ndarray, write_pos: np.ndarray,
+             ring_d: np.ndarray, ring_k: np.ndarray, ring_g: np.ndarray,
+             order: int = 0) -> None:
+    """O3: fold each listed slot's valid ring entries into its fp32 checkpoint
+    with pinned rounding, x <- fma(d_j[v], k_j[k], RN(RN(exp(g_j)) * x)),
+    then reset the slot's write_pos to 0 (in place on ckpt and write_pos).
+
+    Follows SGLang PR #42388 ("The idea": a separately rounded decayed state,
+    then one FMA for the update) applied to the checkpoint fold of SGLang PR
+    #36821 ("Technical principle"). ring_d/ring_k are the ring values upcast
+    exactly to fp32. order=1 selects a deliberately different association and
+    exists only for the control test.
+    """
+    assert ckpt.dtype == np.float32 and ckpt.flags.c_contiguous
+    assert write_pos.dtype == np.int32 and write_pos.flags.c_contiguous
+    N, Hv, dv, dk = ckpt.shape
+    Hk, L = ring_k.shape[1], ring_k.shape[2]
+    slot = _c(slot, np.int32)
+    ring_d, ring_k, ring_g = (_c(x, np.float32) for x in (ring_d, ring_k, ring_g))
+    assert ring_d.shape == (N, Hv, L, dv) and ring_k.shape == (N, Hk, L, dk)
+    assert ring_g.shape == (N, Hv, L)
+    lib().oracle_fold_f32(slot.shape[0], N, Hv, Hk, dk, dv, L, _p(slot), _p(write_pos),
+                          _p(ckpt), _p(ring_d), _p(ring_k), _p(ring_g), order)
+
+
+# ------------------------------------------------------------------ O2
+
+def next_cursor(p: int, L: int, force: bool) -> Tuple[bool, int]:
+    """Flush decision and next cursor of one slot for a single-token step.
+
+    SGLang PR #28451, Design 3 and 5: a step flushes when write_pos == L-1 or
+    when force_flush is set; the cursor then becomes 0, otherwise write_pos+1.
+    """
+    flush = (p == L - 1) or bool(force)
+    return flush, (0 if flush else p + 1)
+
+
+class ReplayModel:
+    """O2: the ReplaySSM per-slot state machine, exact on the integers and fp64
+    on the values.
+
+    State per slot (ReplaySSM blog, section 2.2 cache layout): a checkpoint
+    [Hv, dv, dk], a ring of (u, k, g) entries with capacity L (u per v-head,
+    k per k-head, g per v-head) and write_pos, the number of valid entries.
+
+    Values are produced by the method's own route, not by the sequential
+    recurrence: the pre-token state is rebuilt with the closed-form replay of
+    the blog's section 2.1,
+        S_{c+h} = P_h S_c + sum_j w_{j,h} u_j k_j^T,
+        P_h = prod_{i=1..h} alpha_i,  w_{j,h} = prod_{i=j+1..h} alpha_i,
+    (empty products are 1), and the token is read out with the output-only
+    form of SGLang PR #28451 (Modifications):
+        d_cur = beta (v - alpha (S k)),  o = alpha (S q) + d_cur (k^T q).
+    A non-flush step appends (d_cur, k, g) at position write_pos; a flush step
+    writes alpha S + d_cur k^T into the checkpoint and leaves the ring bytes as
+    they are (blog section 3.3); only entries below write_pos are ever read
+    (SGLang PR #28451, Design 5).
+    """
+
+    def __init__(self, S0: np.ndarray, Hk: int, L: int):
+        assert L >= 1
+        self.N, self.Hv, self.dv, self.dk = S0.shape
+        self.Hk, self.L = Hk, L
+        self.G = self.Hv // Hk
+        self.ckpt = np.array(S0, dtype=np.float64, copy=True)
+        self.ring_u = np.zeros((self.N, self.Hv, L, self.dv))
+        self.ring_k = np.zeros((self.N, Hk, L, self.dk))
+        self.ring_g = np.zeros((self.N, self.Hv, L))
+        self.write_pos = np.zeros(self.N, dtype=np.int64)
+
+    # -- closed form -------------------------------------------------------
+    @staticmethod
+    def replay(S_c: np.ndarray, us, ks, gs) -> np.ndarray:
+        """Closed-form state after h entries (blog section 2.1) for one head.
+        S_c [dv,dk], us [h,dv], ks [h,dk], gs [h]."""
+        h = len(gs)
+        alpha = [float(np.exp(x)) for x in gs]
+        P = 1.0
+        for a in alpha:
+            P *= a
+        S = P * S_c
+        for j in range(h):
+            w = 1.0
+            for i in range(j + 1, h):
+                w *= alpha[i]
+            S = S + w * np.outer(us[j], ks[j])
+        return S
+
+    def head_state(self, s: int, h: int) -> np.ndarray:
+        p = int(self.write_pos[s])
+        hk = h // self.G
+        return self.replay(self.ckpt[s, h], self.ring_u[s, h, :p],
+                           self.ring_k[s, hk, :p], self.ring_g[s, h, :p])
+
+    def state(self, s: int) -> np.ndarray:
+        return np.stack([self.head_state(s, h) for h in range(self.Hv)])
+
+    # -- single-token decode ---------------------------------------------
+    def decode(self, slot, q, k, v, g, beta, force_flush=None):
+        """One single-token decode over a batch (T = 1). q,k [B,Hk,dk],
+        v [B,Hv,dv], g,beta [B,Hv] (float64). Returns (o [B,Hv,dv], flush [B]).
+        The cursors are not moved here; call advance() once per forward."""
+        B = len(slot)
+        o = np.zeros((B, self.Hv, self.dv))
+        flush = np.zeros(B, dtype=bool)
+        for b in range(B):
+            s = int(slot[b])
+            if s < 0:
+                continue
+            p = int(self.write_pos[s])
+            ff = bool(force_flush[b]) if force_flush is not None else False
+            flush[b], _ = next_cursor(p, self.L, ff)
+            for h in range(self.Hv):
+                hk = h // self.G
+                S = self.head_state(s, h)
+                alpha = float(np.exp(g[b, h]))
+                Sk = S @ k[b, hk]
+                Sq = S @ q[b, hk]
+                d = beta[b, h] * (v[b, h] - alpha * Sk)
+                o[b, h] = alpha * Sq + d * float(k[b, hk] @ q[b, hk])
+                if flush[b]:
+                    self.ckpt[s, h] = alpha * S + np.outer(d, k[b, hk])
+                else:
+                    self.ring_u[s, h, p] = d
+                    self.ring_g[s, h, p] = g[b, h]
+                    self.ring_k[s, hk, p] = k[b, hk]
+        return o, flush
+
+    def advance(self, slot, flush) -> None:
+        """Cursor advance, once per forward (SGLang PR #28451, Design 3)."""
+        for b in range(len(slot)):
+            s = int(slot[b])
+            if s < 0:
+                continue
+            self.write_pos[s] = 0 if flush[b] else self.write_pos[s] + 1
+
+    # -- verify window -------------------------------------------------------
+    def verify(self, slot, q, k, v, g, beta):
+        """A T-token verify window read from the checkpoint and ring (vLLM PR
+        #49887, Core concept): every window output comes from the same
+        checkpoint plus ring, token t sees tokens < t of the window; the
+        window's entries are written at positions p .. p+T-1 and the cursor
+        does not move. q,k [B,T,Hk,dk], v [B,T,Hv,dv], g,beta [B,T,Hv].
+        Returns o [B,T,Hv,dv]. Rows with p + T > L are invalid: they get zero
+        outputs and no writes."""
+        B, T = q.shape[0], q.shape[1]
+        o = np.zeros((B, T, self.Hv, self.dv))
+        for b in range(B):
+            s = int(slot[b])
+            if s < 0:
+                continue
+            p = int(self.write_pos[s])
+            if p + T > self.L:
+                continue
+            for h in range(self.Hv):
+                hk = h // self.G
+                us = list(self.ring_u[s, h, :p])
+                ks = list(self.ring_k[s, hk, :p])
+                gs = list(self.ring_g[s, h, :p])
+                for t in range(T):
+                    S = self.replay(self.ckpt[s, h], us, ks, gs)
+                    alpha = float(np.exp(g[b, t, h]))
+                    Sk = S @ k[b, t, hk]
+                    Sq = S @ q[b, t, hk]
+                    d = beta[b, t, h] * (v[b, t, h] - alpha * Sk)
+                    o[b, t, h] = alpha * Sq + d * float(k[b, t, hk] @ q[b, t, hk])
+                    us.append(d)
+                    ks.append(k[b, t, hk])
+                    gs.append(g[b, t, h])
+                    self.ring_u[s, h, p + t] = d
+                    self.ring_g[s, h, p + t] = g[b, t, h]
+                    self.ring_k[s, hk, p + t] = k[b, t, hk]
+        return o
+
+    def commit(self, slot, accepted) -> None:
+        """Keep the first `accepted` window entries: write_pos += a (vLLM PR
+        #49887: rollback is a cursor move)."""
+        for b in range(len(slot)):
+            s = int(slot[b])
+            if s < 0:
+                continue
+            self.write_pos[s] += int(accepted[b])
+
+    def fold(self, slot) -> None:
+        """Fold the valid entries into the checkpoint (fp64, sequential
+        S <- alpha S + u k^T per entry) and reset write_pos to 0."""
+        for b in range(len(slot)):
+            s = int(slot[b])
+            if s < 0:
+                continue
+            p = int(self.write_pos[s])
+            for h in range(self.Hv):
+                hk = h // self.G
+                X = self.ckpt[s, h]
+                for j in range(p):
+                    X = np.exp(self.ring_g[s, h, j]) * X + np.outer(
+                        self.ring_u[s, h, j], self.ring_k[s, hk, j])
+                self.ckpt[s, h] = X
+            self.write_pos[s] = 0
+
+
+# ------------------------------------------------------------------ O4
+
+def window_ref(S: np.ndarray, slot, q, k, v, g, beta, want_u: bool = False):
+    """O4: the outputs of a T-token window, computed by running O1 token by
+    token on a copy of the true state (vLLM PR #49887, Tests: the reference
+    is the packed decode run on a clone through the window). S is not changed.
+    q,k [B,T,Hk,dk], v [B,T,Hv,dv], g,beta [B,T,Hv]. Returns o [B,T,Hv,dv]
+    (and u [B,T,Hv,dv])."""
+    Sc = np.array(S, dtype=np.float64, copy=True)
+    T = q.shape[1]
+    outs, us = [], []
+    for t in range(T):
+        o, u = gdn_step(Sc, slot, q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], want_u=True)
+        outs.append(o)
+        us.append(u)
+    o = np.stack(outs, axis=1)
+    return (o, np.stack(us, axis=1)) if want_u else o
+
+
+def rel_err(x: np.ndarray, ref: np.ndarray) -> float:
+    """max |x - ref| / max |ref| (the tolerance measure used throughout)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(x - ref))) if ref.size else 0.0
+    if den == 0.0:
+        return num
+    return num / den

@@ -1,0 +1,158 @@
+/*
+ * gdn_oracle.c -- CPU oracle for the Gated DeltaNet decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY. This is a plain, slow, sequential reference that
+ * the parity tests, the smoke check and the benchmark's CPU-baseline leg call.
+ * The product (the HIP library) never links, loads or calls it, and it shares
+ * no code, header, table or helper with the HIP side.
+ *
+ * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -fPIC -shared -lm
+ * (no contraction, no flush-to-zero: every operation below rounds exactly as
+ * written, in IEEE round-to-nearest-even).
+ *
+ * Layouts (all row-major, contiguous):
+ *   S / ckpt   [N, Hv, dv, dk]   per value head a dv x dk matrix, dk fastest
+ *   q, k       [B, Hk, dk]       one token per row
+ *   v, o, u    [B, Hv, dv]
+ *   g, beta    [B, Hv]
+ *   ring_d     [N, Hv, L, dv]    ring_k [N, Hk, L, dk]    ring_g [N, Hv, L]
+ * Value head h reads key head h / (Hv / Hk) (contiguous GQA groups).
+ * A row whose slot index is negative is a padding row: its outputs are zero
+ * and no state is touched.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+/*
+ * O1 -- one decode token of the gated delta rule, in float64.
+ *
+ * Follows the recurrence as the ReplaySSM blog (llm.rainlin.net, section 1,
+ * "Decode state cost") defines it for one value head, with alpha = exp(g):
+ *     S~  = alpha * S_{t-1}
+ *     u   = beta * (v - S~ k)
+ *     S_t = S~ + u k^T
+ *     y   = S_t q
+ * The state is materialised first and the output read from the new state, so
+ * this function does not use the output-only factorisation of the decode
+ * kernels; the tests check that factorisation against it.
+ *
+ * u_out (nullable) receives u, the correction vector the ring stores.
+ */
+void oracle_gdn_step_f64(int32_t B, int32_t N, int32_t Hv, int32_t Hk,
+                         int32_t dk, int32_t dv, const int32_t *slot,
+                         double *S, const double *q, const double *k,
+                         const double *v, const double *g, const double *beta,
+                         double *o, double *u_out)
+{
+    const int32_t G = Hv / Hk;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t s = slot[b];
+        for (int32_t h = 0; h < Hv; ++h) {
+            double *ob = o + ((size_t)b * Hv + h) * dv;
+            double *ub = u_out ? u_out + ((size_t)b * Hv + h) * dv : NULL;
+            if (s < 0 || s >= N) {
+                for (int32_t i = 0; i < dv; ++i) {
+                    ob[i] = 0.0;
+                    if (ub) ub[i] = 0.0;
+                }
+                continue;
+            }
+            const int32_t hk = h / G;
+            double *Sh = S + ((size_t)s * Hv + h) * dv * dk;
+            const double *qb = q + ((size_t)b * Hk + hk) * dk;
+            const double *kb = k + ((size_t)b * Hk + hk) * dk;
+            const double *vb = v + ((size_t)b * Hv + h) * dv;
+            const double alpha = exp(g[(size_t)b * Hv + h]);
+            const double bt = beta[(size_t)b * Hv + h];
+
+            /* S~ = alpha * S */
+            for (size_t e = 0; e < (size_t)dv * dk; ++e) Sh[e] = alpha * Sh[e];
+            /* u = beta * (v - S~ k), then S = S~ + u k^T, row by row */
+            for (int32_t i = 0; i < dv; ++i) {
+                double *row = Sh + (size_t)i * dk;
+                double sk = 0.0;
+                for (int32_t j = 0; j < dk; ++j) sk += row[j] * kb[j];
+                const double u = bt * (vb[i] - sk);
+                if (ub) ub[i] = u;
+                for (int32_t j = 0; j < dk; ++j) row[j] = row[j] + u * kb[j];
+            }
+            /* y = S_t q */
+            for (int32_t i = 0; i < dv; ++i) {
+                const double *row = Sh + (size_t)i * dk;
+                double y = 0.0;
+                for (int32_t j = 0; j < dk; ++j) y += row[j] * qb[j];
+                ob[i] = y;
+            }
+        }
+    }
+}
+
+/*
+ * O3 -- fold of a slot's valid ring entries into its fp32 checkpoint, with the
+ * rounding pinned.
+ *
+ * Per element x of the checkpoint and per ring entry j = 0 .. p-1 in order:
+ *     a = RN_f32(exp_f64(g_j))         the entry's decay, rounded once to fp32
+ *     t = RN_f32(a * x)                the decayed state, a separately rounded multiply
+ *     x = fma_f32(d_j[v], k_j[k], t)   the rank-1 update, one fused multiply-add
+ * This is the recurrence S <- alpha*S + d k^T driven by the stored entries, in
+ * the two-instruction form SGLang PR #42388 ("The idea") prescribes for an exact
+ * replay: the decayed state is rounded on its own and the update is a single
+ * FMA. The fold is the checkpoint update of the SGLang PR #36821 commit ("the
+ * accepted prefix is folded back into the persistent checkpoint"), here for the
+ * GDN (d, k, g) ring. The ring values are taken as their exact fp32 upcasts.
+ *
+ * order = 0 is the pinned form above. order = 1 is a deliberately different
+ * association, x = fma_f32(a, x, RN_f32(d*k)), kept only so that a test can
+ * show the bitwise comparison detects a change of operation order.
+ *
+ * write_pos[s] is the number of valid entries p of slot s; after the fold the
+ * slot's write_pos is reset to 0. Rows with a negative or out-of-range slot,
+ * or with p outside [0, L], are skipped.
+ */
+void oracle_fold_f32(int32_t B, int32_t N, int32_t Hv, int32_t Hk, int32_t dk,
+                     int32_t dv, int32_t L, const int32_t *slot,
+                     int32_t *write_pos, float *ckpt, const float *ring_d,
+                     const float *ring_k, const float *ring_g, int32_t order)
+{
+    const int32_t G = Hv / Hk;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t s = slot[b];
+        if (s < 0 || s >= N) continue;
+        const int32_t p = write_pos[s];
+        if (p < 0 || p > L) continue;
+        for (int32_t h = 0; h < Hv; ++h) {
+            const int32_t hk = h / G;
+            float *X = ckpt + ((size_t)s * Hv + h) * dv * dk;
+            for (int32_t j = 0; j < p; ++j) {
+                const float a = (float)exp((double)ring_g[((size_t)s * Hv + h) * L + j]);
+                const float *dj = ring_d + (((size_t)s * Hv + h) * L + j) * dv;
+                const float *kj = ring_k + (((size_t)s * Hk + hk) * L + j) * dk;
+                for (int32_t i = 0; i < dv; ++i) {
+                    for (int32_t c = 0; c < dk; ++c) {
+                        float *x = X + (size_t)i * dk + c;
+                        if (order == 0) {
+                            const float t = a * (*x);
+                            *x = fmaf(dj[i], kj[c], t);
+                        } else {
+                            const float dk_ = dj[i] * kj[c];
+                            *x = fmaf(a, *x, dk_);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t s = slot[b];
+        if (s < 0 || s >= N) continue;
+        const int32_t p = write_pos[s];
+        if (p < 0 || p > L) continue;
+        write_pos[s] = 0;
+    }
+}
+
+/* ABI version of this oracle library, for the loader's sanity check. */
+int32_t oracle_version(void) { return 1; }
