@@ -90,6 +90,7 @@ class Workload:
     n_pad: int = 0      # rows whose slot index is -1
     permute: bool = False  # rows map to slots by a seeded injection into [0, N)
     stagger: bool = True   # one forced flush per slot during the first L steps
+    bf16_values: bool = False  # fp32 tensors carrying bf16-representable values
     seed: int = 0
 
     @property
@@ -112,6 +113,7 @@ def c4(L: int, ring: str = "f16") -> Workload:
     does not mask the fp32 reconstruction."""
     qkv = "f32" if ring == "f32" else "bf16"
     return replace(C2, name=f"c4_L{L}_{ring}", L=L, ring=ring, qkv=qkv,
+                   bf16_values=(ring == "f32"),
                    seed=400 + L + (1000 if ring == "f32" else 0))
 
 
@@ -194,6 +196,8 @@ def step_inputs(w: Workload, step: int, B: Optional[int] = None,
     v = r.standard_normal((B, T, w.Hv, w.dv), dtype=np.float32)
     g = _logsigmoid(r.normal(2.0, 1.0, (B, T, w.Hv))).astype(np.float32)
     beta = _sigmoid(r.standard_normal((B, T, w.Hv))).astype(np.float32)
+    if w.bf16_values:
+        q, k, v = (bf16_bits_to_f32(f32_to_bf16_bits(a)) for a in (q, k, v))
     return StepInputs(cast(q, w.qkv), cast(k, w.qkv), cast(v, w.qkv), g, beta, w.qkv)
 
 

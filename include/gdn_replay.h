@@ -1,0 +1,195 @@
+/*
+ * gdn_replay.h -- C ABI of the MI355X (gfx950) ReplaySSM Gated DeltaNet
+ * decode library (libgdn_replay.so).
+ *
+ * The method: a slot's recurrent state is kept as one fp32 checkpoint plus a
+ * ring of the last L steps' (d, k, g) entries. A decode step rebuilds the
+ * pre-token state from them, reads the output out of it, appends its own
+ * entry to the ring, and writes the full state back only on a flush
+ * (ReplaySSM blog, llm.rainlin.net, sections 2-3; SGLang PR #28451,
+ * Modifications and Design 1-5).
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are device (HBM) pointers; the `shape` struct
+ *     is a host pointer read during the call only. `stream` is a hipStream_t
+ *     (NULL = the null stream).
+ *   - Every call is asynchronous on `stream`: it validates its host-side
+ *     arguments, enqueues one or two kernels, and returns. It never
+ *     synchronises, never allocates and never frees. The caller owns every
+ *     buffer and must keep it alive until the stream has passed the call.
+ *   - On a host-side validation failure the call returns a non-zero status
+ *     and enqueues nothing. A failed launch returns GDN_ERR_HIP.
+ *   - Data errors that only the device can see (a slot index >= N, a cursor
+ *     out of range, a verify window that does not fit the ring, an accepted
+ *     count out of range) are reported by OR-ing GDN_EF_* bits into
+ *     *err_flags (device int32, nullable) without a sync; the affected row is
+ *     then handled as a padding row (zero output, no state or ring write).
+ *   - A negative slot index marks a padding row: its outputs are written as
+ *     zeros and nothing else is touched (ReplaySSM blog, section 3.1).
+ *   - Within one call, the non-negative slot indices must be distinct.
+ *   - Calls on one stream are ordered; calls on different streams that touch
+ *     the same slots race.
+ *
+ * Tensor layouts (all contiguous, row-major, base pointers 16-byte aligned):
+ *   q, k           [B, T, Hk, dk]   qkv_dtype; q/k already normalised, q scaled
+ *   v, o           [B, T, Hv, dv]   qkv_dtype (o is written in the same dtype)
+ *   g, beta        [B, T, Hv]       fp32; g is the log-decay, alpha = exp(g)
+ *   state / ckpt   [N, Hv, dv, dk]  fp32, dk fastest (ReplaySSM blog, 2.2)
+ *   ring_d         [N, Hv, L, dv]   ring_dtype  (the correction vectors d)
+ *   ring_k         [N, Hk, L, dk]   ring_dtype  (keys, one per k-head)
+ *   ring_g         [N, Hv, L]       fp32        (log-decays)
+ *   write_pos      [N]              int32, number of valid ring entries
+ *   slot_idx       [B]              int32, row -> slot, negative = padding
+ *   force_flush    [B]              uint8, nullable
+ *   accepted       [B]              int32
+ * Value head h uses key head h / (Hv / Hk).
+ *
+ * Supported sizes: dk in {32, 64, 128, 256}; dv a multiple of 16, 16..512;
+ * Hv % Hk == 0 with Hv / Hk <= 16; 1 <= L <= 64; 1 <= T <= 16; B >= 0.
+ * qkv_dtype in {GDN_F32, GDN_BF16}; ring_dtype in {GDN_F32, GDN_F16, GDN_BF16}.
+ */
+#ifndef GDN_REPLAY_H
+#define GDN_REPLAY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size or mode    */
+    GDN_ERR_UNSUPPORTED = 2, /* a size or dtype outside the compiled set        */
+    GDN_ERR_HIP = 3          /* the HIP runtime refused the launch              */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
+
+/* Device-side data error bits OR-ed into *err_flags. */
+enum {
+    GDN_EF_SLOT_RANGE = 1,   /* slot_idx[b] >= N                                */
+    GDN_EF_CURSOR_RANGE = 2, /* write_pos outside its valid range for the call  */
+    GDN_EF_WINDOW = 4,       /* verify window: write_pos + T > L                */
+    GDN_EF_ACCEPTED = 8      /* commit: accepted outside [0, T] or past L       */
+};
+
+typedef struct {
+    int32_t B;          /* rows in the call                                      */
+    int32_t T;          /* tokens per row (1 for decode; the window length)      */
+    int32_t N;          /* slots in the pool                                     */
+    int32_t Hv, Hk;     /* value / key heads                                     */
+    int32_t dk, dv;     /* key / value head dimensions                           */
+    int32_t L;          /* ring capacity (ignored by gdn_packed_decode)          */
+    int32_t qkv_dtype;  /* gdn_dtype of q, k, v and o                            */
+    int32_t ring_dtype; /* gdn_dtype of ring_d and ring_k                        */
+    int32_t window;     /* gdn_replay_decode: 0 = decode step, 1 = verify window */
+} gdn_shape;
+
+/*
+ * gdn_packed_decode -- the plain read-update-write decode step (T must be 1).
+ *
+ * Per row b with slot s = slot_idx[b] >= 0 and per value head h, with
+ * alpha = exp(g), following SGLang PR #28451 (Modifications, the GDN math):
+ *     Sq = S q,  Sk = S k                     (S = state[s, h], before the token)
+ *     d  = beta (v - alpha Sk)
+ *     o  = alpha Sq + d (k^T q)
+ *     state[s, h] <- alpha S + d k^T          (written every step)
+ * The state update is rounded in two steps, fma(d[v], k[c], RN(alpha*S[v,c])),
+ * the form SGLang PR #42388 ("The idea") names for an exactly reproducible
+ * replay. This is the baseline whose per-step state read+write the ReplaySSM
+ * path removes (SGLang PR #28451, Motivation).
+ *   state   (device) fp32 [N, Hv, dv, dk], read and written.
+ *   o       (device) [B, 1, Hv, dv], written for every row (zeros for padding).
+ */
+gdn_status gdn_packed_decode(const gdn_shape *shape, const void *q, const void *k,
+                             const void *v, const float *g, const float *beta,
+                             const int32_t *slot_idx, float *state, void *o,
+                             int32_t *err_flags, void *stream);
+
+/*
+ * gdn_replay_decode -- the ReplaySSM output-only decode step (window = 0,
+ * T = 1) or the verify window from one checkpoint (window = 1, T >= 1).
+ *
+ * Per row b with slot s and per value head h, with p = write_pos[s] valid ring
+ * entries (only positions < p are ever read, SGLang PR #28451 Design 5):
+ *   pre-token state (ReplaySSM blog, section 2.1, closed form):
+ *       S = A ckpt[s,h] + sum_{j<p} w_j d_j k_j^T,
+ *       A = exp(sum_{i<p} g_i),  w_j = exp(sum_{j<i<p} g_i)   (empty sum = 0)
+ *   readout (SGLang PR #28451, Modifications): as for gdn_packed_decode.
+ * Decode (window = 0, T = 1): the step flushes when p == L-1 or
+ * force_flush[b] != 0 (SGLang PR #28451, Design 4-5). A non-flush step appends
+ * (d, k, g) at ring position p (k once per key head); a flush step writes
+ * ckpt[s,h] <- fma(d[v], k[c], RN(alpha*S[v,c])) and leaves the ring bytes
+ * unchanged (ReplaySSM blog, section 3.3). write_pos is NOT changed: advance it
+ * once per forward with gdn_replay_advance, after every layer's decode call.
+ * Requires 0 <= p <= L-1, else GDN_EF_CURSOR_RANGE.
+ * Verify window (window = 1): tokens t = 0..T-1 of the row are read out in
+ * order from the same checkpoint + ring; token t sees window tokens < t
+ * through an on-chip update of S (vLLM PR #49887, Core concept). Entries are
+ * written at positions p..p+T-1; there is no flush and write_pos is NOT moved
+ * (commit with gdn_replay_commit). force_flush must be NULL. Requires
+ * p + T <= L, else GDN_EF_WINDOW.
+ *   ckpt           (device) fp32 [N, Hv, dv, dk]; written only on a flush.
+ *   ring_d/k/g     (device) read at positions < p, written as described.
+ *   write_pos      (device) int32 [N], read only.
+ *   force_flush    (device) uint8 [B] or NULL.
+ *   o              (device) [B, T, Hv, dv], written for every row.
+ */
+gdn_status gdn_replay_decode(const gdn_shape *shape, const void *q, const void *k,
+                             const void *v, const float *g, const float *beta,
+                             const int32_t *slot_idx, float *ckpt, void *ring_d,
+                             void *ring_k, float *ring_g, const int32_t *write_pos,
+                             const uint8_t *force_flush, void *o, int32_t *err_flags,
+                             void *stream);
+
+/*
+ * gdn_replay_advance -- the cursor advance that follows a forward's decode
+ * calls (SGLang PR #28451, Design 3): for each row with slot s >= 0,
+ *     write_pos[s] <- (write_pos[s] == L-1 || force_flush[b]) ? 0 : write_pos[s]+1.
+ * It must see the same force_flush as the forward's decode calls.
+ *   write_pos (device) int32 [N], read and written. force_flush nullable.
+ * A cursor outside [0, L-1] is left as is and sets GDN_EF_CURSOR_RANGE.
+ */
+gdn_status gdn_replay_advance(const gdn_shape *shape, const int32_t *slot_idx,
+                              int32_t *write_pos, const uint8_t *force_flush,
+                              int32_t *err_flags, void *stream);
+
+/*
+ * gdn_replay_commit -- keep the accepted prefix of a verify window: for each
+ * row with slot s >= 0, write_pos[s] <- write_pos[s] + accepted[b] (vLLM PR
+ * #49887: rollback of rejected drafts is only a cursor move). accepted[b]
+ * must lie in [0, T] and write_pos[s] + accepted[b] <= L, else the cursor is
+ * left as is and GDN_EF_ACCEPTED is set.
+ */
+gdn_status gdn_replay_commit(const gdn_shape *shape, const int32_t *slot_idx,
+                             const int32_t *accepted, int32_t *write_pos,
+                             int32_t *err_flags, void *stream);
+
+/*
+ * gdn_replay_fold -- fold each listed slot's p = write_pos[s] valid ring
+ * entries into its checkpoint, then set write_pos[s] = 0 (SGLang PR #36821,
+ * Technical principle: the accepted prefix is folded into the persistent
+ * checkpoint by a bit-clone of the recurrence). Per element, for j = 0..p-1:
+ *     a = RN_f32(exp_f64(g_j));  x <- fma(d_j[v], k_j[c], RN(a*x))
+ * with the two-instruction rounding of SGLang PR #42388 ("The idea"). The
+ * result is bit-identical to that sequential recurrence on the stored entries.
+ * Requires 0 <= p <= L, else GDN_EF_CURSOR_RANGE (the slot is not touched).
+ *   ckpt (device) read and written; ring_d/k/g (device) read at positions < p.
+ */
+gdn_status gdn_replay_fold(const gdn_shape *shape, const int32_t *slot_idx,
+                           float *ckpt, const void *ring_d, const void *ring_k,
+                           const float *ring_g, int32_t *write_pos,
+                           int32_t *err_flags, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *gdn_status_string(gdn_status status);
+
+/* Library ABI version (incremented on any signature change). */
+int32_t gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_REPLAY_H */

@@ -1,0 +1,224 @@
+"""Python binding of libgdn_replay.so (the MI355X ReplaySSM GDN decode library).
+
+Argument marshalling only: every function checks the tensors it is given,
+derives the sizes, and calls the C entry point of the same name on the
+current HIP stream. All arithmetic runs in the library's gfx950 kernels. There
+is no fallback: if the library is missing, importing this package raises.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn_replay.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gdn_replay.h")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
+GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
+EF_SLOT_RANGE, EF_CURSOR_RANGE, EF_WINDOW, EF_ACCEPTED = 1, 2, 4, 8
+
+_DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
+
+
+class gdn_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "T", "N", "Hv", "Hk", "dk", "dv", "L", "qkv_dtype", "ring_dtype", "window")]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {lib().gdn_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run __graft_entry__.build() "
+        "(or python linear_attention_ssm_amd/build.py) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_S = ctypes.POINTER(gdn_shape)
+_lib.gdn_packed_decode.argtypes = [_S] + [_P] * 10
+_lib.gdn_replay_decode.argtypes = [_S] + [_P] * 15
+_lib.gdn_replay_advance.argtypes = [_S] + [_P] * 5
+_lib.gdn_replay_commit.argtypes = [_S] + [_P] * 5
+_lib.gdn_replay_fold.argtypes = [_S] + [_P] * 8
+for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_advance",
+           "gdn_replay_commit", "gdn_replay_fold"):
+    getattr(_lib, _f).restype = ctypes.c_int
+_lib.gdn_status_string.argtypes = [ctypes.c_int]
+_lib.gdn_status_string.restype = ctypes.c_char_p
+_lib.gdn_abi_version.restype = ctypes.c_int32
+ABI_VERSION = 1
+if _lib.gdn_abi_version() != ABI_VERSION:
+    raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
+
+
+def lib():
+    return _lib
+
+
+def declared_symbols() -> list:
+    """Function names declared in include/gdn_replay.h."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\S[^;(]*?\b(gdn_\w+)\s*\(", text, flags=re.M)))
+
+
+# ------------------------------------------------------------------ helpers
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype=None, ndim=None, dev=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _raise(status: int, what: str):
+    if status != GDN_OK:
+        raise GdnError(status, what)
+
+
+def _io_shape(q, k, v, g, beta, slot_idx):
+    _check(q, "q", (torch.float32, torch.bfloat16), 4)
+    dev = q.device
+    _check(k, "k", q.dtype, 4, dev)
+    _check(v, "v", q.dtype, 4, dev)
+    _check(g, "g", torch.float32, 3, dev)
+    _check(beta, "beta", torch.float32, 3, dev)
+    _check(slot_idx, "slot_idx", torch.int32, 1, dev)
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv) \
+            or beta.shape != (B, T, Hv) or slot_idx.shape != (B,):
+        raise ValueError("inconsistent q/k/v/g/beta/slot_idx shapes")
+    return B, T, Hk, dk, Hv, dv, dev
+
+
+def _out(o, B, T, Hv, dv, dtype, dev):
+    if o is None:
+        return torch.empty((B, T, Hv, dv), dtype=dtype, device=dev)
+    _check(o, "o", dtype, 4, dev)
+    if tuple(o.shape) != (B, T, Hv, dv):
+        raise ValueError("o has the wrong shape")
+    return o
+
+
+# ------------------------------------------------------------------ entry points
+
+def gdn_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None, stream=None):
+    """Plain read-update-write decode step; see gdn_packed_decode in gdn_replay.h.
+    q,k [B,1,Hk,dk]; v [B,1,Hv,dv]; g,beta [B,1,Hv] fp32; slot_idx [B] int32;
+    state [N,Hv,dv,dk] fp32 (updated in place). Returns o [B,1,Hv,dv]."""
+    B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
+    _check(state, "state", torch.float32, 4, dev)
+    if tuple(state.shape[1:]) != (Hv, dv, dk):
+        raise ValueError("state must be [N, Hv, dv, dk]")
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, None, dev)
+    o = _out(o, B, T, Hv, dv, q.dtype, dev)
+    sh = gdn_shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0)
+    _raise(_lib.gdn_packed_decode(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(slot_idx), _ptr(state), _ptr(o), _ptr(err_flags),
+                                  _stream(stream)), "gdn_packed_decode")
+    return o
+
+
+def _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev):
+    _check(ckpt, "ckpt", torch.float32, 4, dev)
+    _check(ring_d, "ring_d", (torch.float32, torch.float16, torch.bfloat16), 4, dev)
+    _check(ring_k, "ring_k", ring_d.dtype, 4, dev)
+    _check(ring_g, "ring_g", torch.float32, 3, dev)
+    _check(write_pos, "write_pos", torch.int32, 1, dev)
+    N = ckpt.shape[0]
+    L = ring_d.shape[2]
+    if tuple(ckpt.shape) != (N, Hv, dv, dk) or tuple(ring_d.shape) != (N, Hv, L, dv) \
+            or tuple(ring_k.shape) != (N, Hk, L, dk) or tuple(ring_g.shape) != (N, Hv, L) \
+            or tuple(write_pos.shape) != (N,):
+        raise ValueError("inconsistent checkpoint / ring / write_pos shapes")
+    return N, L
+
+
+def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
+                      force_flush=None, o=None, err_flags=None, window=False, stream=None):
+    """ReplaySSM decode step (window=False, T=1) or verify window (window=True);
+    see gdn_replay_decode in gdn_replay.h. Returns o [B,T,Hv,dv]."""
+    B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
+    N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev)
+    if force_flush is not None:
+        _check(force_flush, "force_flush", torch.uint8, 1, dev)
+        if force_flush.shape != (B,):
+            raise ValueError("force_flush must be [B]")
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, None, dev)
+    o = _out(o, B, T, Hv, dv, q.dtype, dev)
+    sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)))
+    _raise(_lib.gdn_replay_decode(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d), _ptr(ring_k),
+                                  _ptr(ring_g), _ptr(write_pos), _ptr(force_flush), _ptr(o),
+                                  _ptr(err_flags), _stream(stream)), "gdn_replay_decode")
+    return o
+
+
+def gdn_replay_advance(slot_idx, write_pos, L, force_flush=None, err_flags=None, stream=None):
+    """Cursor advance once per forward; see gdn_replay_advance in gdn_replay.h."""
+    _check(slot_idx, "slot_idx", torch.int32, 1)
+    _check(write_pos, "write_pos", torch.int32, 1, slot_idx.device)
+    if force_flush is not None:
+        _check(force_flush, "force_flush", torch.uint8, 1, slot_idx.device)
+    sh = gdn_shape(slot_idx.shape[0], 1, write_pos.shape[0], 1, 1, 32, 16, int(L), 0, 0, 0)
+    _raise(_lib.gdn_replay_advance(ctypes.byref(sh), _ptr(slot_idx), _ptr(write_pos),
+                                   _ptr(force_flush), _ptr(err_flags), _stream(stream)),
+           "gdn_replay_advance")
+
+
+def gdn_replay_commit(slot_idx, accepted, write_pos, L, T, err_flags=None, stream=None):
+    """write_pos[slot] += accepted; see gdn_replay_commit in gdn_replay.h."""
+    _check(slot_idx, "slot_idx", torch.int32, 1)
+    _check(accepted, "accepted", torch.int32, 1, slot_idx.device)
+    _check(write_pos, "write_pos", torch.int32, 1, slot_idx.device)
+    sh = gdn_shape(slot_idx.shape[0], int(T), write_pos.shape[0], 1, 1, 32, 16, int(L), 0, 0, 0)
+    _raise(_lib.gdn_replay_commit(ctypes.byref(sh), _ptr(slot_idx), _ptr(accepted),
+                                  _ptr(write_pos), _ptr(err_flags), _stream(stream)),
+           "gdn_replay_commit")
+
+
+def gdn_replay_fold(slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags=None,
+                    stream=None):
+    """Exact fold of the valid ring entries into the checkpoint, then
+    write_pos = 0; see gdn_replay_fold in gdn_replay.h."""
+    _check(slot_idx, "slot_idx", torch.int32, 1)
+    dev = slot_idx.device
+    _check(ckpt, "ckpt", torch.float32, 4, dev)
+    N, Hv, dv, dk = ckpt.shape
+    Hk = ring_k.shape[1]
+    _, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev)
+    sh = gdn_shape(slot_idx.shape[0], 1, N, Hv, Hk, dk, dv, L, GDN_F32, _DT[ring_d.dtype], 0)
+    _raise(_lib.gdn_replay_fold(ctypes.byref(sh), _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d),
+                                _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(err_flags),
+                                _stream(stream)), "gdn_replay_fold")

@@ -1,0 +1,243 @@
+// gdn_api.hip -- the C ABI (include/gdn_replay.h): host-side validation,
+// launch geometry and dispatch to the typed kernel instances. No call here
+// synchronises, allocates or frees.
+#include <cstdlib>
+#include <cstring>
+
+#include "gdn_launch.h"
+#include "gdn_replay.h"
+
+using namespace gdn;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+size_t elem_size(int dt) { return dt == GDN_F32 ? 4 : 2; }
+
+bool dk_supported(int dk) { return dk == 32 || dk == 64 || dk == 128 || dk == 256; }
+
+// Waves per decode workgroup (a tuning knob; GDN_WAVES_PER_WG overrides the
+// default of 8 for experiments).
+int target_waves() {
+  static int w = [] {
+    const char* e = std::getenv("GDN_WAVES_PER_WG");
+    int v = e ? std::atoi(e) : 8;
+    if (v < 1) v = 1;
+    if (v > 16) v = 16;
+    return v;
+  }();
+  return w;
+}
+
+// Value rows per head per workgroup: the largest multiple of 16 dividing dv
+// with G * VB / 16 <= target waves (at least 16, so at most 16 waves).
+int pick_vb(int dv, int G) {
+  const int tw = target_waves();
+  int best = 16;
+  for (int vb = 16; vb <= dv; vb += 16)
+    if (dv % vb == 0 && G * (vb / 16) <= (tw > G ? tw : G)) best = vb;
+  return best;
+}
+
+gdn_status check_shape(const gdn_shape* s, bool need_ring) {
+  if (!s) return GDN_ERR_INVALID_ARG;
+  if (s->B < 0 || s->T < 1 || s->T > 16 || s->N < 1) return GDN_ERR_INVALID_ARG;
+  if (s->Hv < 1 || s->Hk < 1 || s->Hv % s->Hk != 0 || s->Hv / s->Hk > 16)
+    return GDN_ERR_INVALID_ARG;
+  if (!dk_supported(s->dk)) return GDN_ERR_UNSUPPORTED;
+  if (s->dv < 16 || s->dv > 512 || s->dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
+  if (s->qkv_dtype != GDN_F32 && s->qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (need_ring) {
+    if (s->L < 1 || s->L > 64) return GDN_ERR_INVALID_ARG;
+    if (s->ring_dtype != GDN_F32 && s->ring_dtype != GDN_F16 && s->ring_dtype != GDN_BF16)
+      return GDN_ERR_UNSUPPORTED;
+  }
+  return GDN_OK;
+}
+
+gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+hipError_t dispatch_packed(int dk, const DecodeArgs& a, int qkv, dim3 g, dim3 b, size_t sm,
+                           hipStream_t st) {
+  switch (dk) {
+    case 32: return launch_packed<32>(a, qkv, g, b, sm, st);
+    case 64: return launch_packed<64>(a, qkv, g, b, sm, st);
+    case 128: return launch_packed<128>(a, qkv, g, b, sm, st);
+    case 256: return launch_packed<256>(a, qkv, g, b, sm, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_replay(int dk, const DecodeArgs& a, int qkv, int ring, dim3 g, dim3 b,
+                           size_t sm, hipStream_t st) {
+  switch (dk) {
+    case 32: return launch_replay<32>(a, qkv, ring, g, b, sm, st);
+    case 64: return launch_replay<64>(a, qkv, ring, g, b, sm, st);
+    case 128: return launch_replay<128>(a, qkv, ring, g, b, sm, st);
+    case 256: return launch_replay<256>(a, qkv, ring, g, b, sm, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_fold(int dk, const FoldArgs& a, int ring, dim3 g, dim3 b, size_t sm,
+                         hipStream_t st) {
+  switch (dk) {
+    case 32: return launch_fold<32>(a, ring, g, b, sm, st);
+    case 64: return launch_fold<64>(a, ring, g, b, sm, st);
+    case 128: return launch_fold<128>(a, ring, g, b, sm, st);
+    case 256: return launch_fold<256>(a, ring, g, b, sm, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+void fill_decode_geometry(const gdn_shape* s, DecodeArgs& a, dim3& grid, dim3& block) {
+  a.B = s->B; a.T = s->T; a.N = s->N; a.Hv = s->Hv; a.Hk = s->Hk; a.dv = s->dv; a.L = s->L;
+  a.G = s->Hv / s->Hk;
+  a.VB = pick_vb(s->dv, a.G);
+  a.nvb = s->dv / a.VB;
+  grid = dim3(static_cast<unsigned>(s->B) * s->Hk * a.nvb);
+  block = dim3(64u * a.G * (a.VB / 16));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const int32_t* slot_idx,
+                             float* state, void* o, int32_t* err_flags, void* stream) {
+  const gdn_status st = check_shape(s, false);
+  if (st != GDN_OK) return st;
+  if (s->T != 1 || s->window != 0) return GDN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !g || !beta || !slot_idx || !state || !o) return GDN_ERR_INVALID_ARG;
+  const size_t es = elem_size(s->qkv_dtype);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state, 16) || !aligned(v, es) ||
+      !aligned(o, es) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(slot_idx, 4) ||
+      (err_flags && !aligned(err_flags, 4)))
+    return GDN_ERR_INVALID_ARG;
+  if (s->B == 0) return GDN_OK;
+  DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.slot = slot_idx; a.state = state;
+  a.o = o; a.err = err_flags;
+  dim3 grid, block;
+  fill_decode_geometry(s, a, grid, block);
+  a.L = 1;
+  const size_t smem = 2u * s->dk * sizeof(float);
+  return from_hip(dispatch_packed(s->dk, a, s->qkv_dtype, grid, block, smem,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const int32_t* slot_idx,
+                             float* ckpt, void* ring_d, void* ring_k, float* ring_g,
+                             const int32_t* write_pos, const uint8_t* force_flush, void* o,
+                             int32_t* err_flags, void* stream) {
+  const gdn_status st = check_shape(s, true);
+  if (st != GDN_OK) return st;
+  if (s->window != 0 && s->window != 1) return GDN_ERR_INVALID_ARG;
+  if (s->window == 0 && s->T != 1) return GDN_ERR_INVALID_ARG;
+  if (s->window == 1 && force_flush) return GDN_ERR_INVALID_ARG;
+  if (s->T > s->L) return GDN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !g || !beta || !slot_idx || !ckpt || !ring_d || !ring_k || !ring_g ||
+      !write_pos || !o)
+    return GDN_ERR_INVALID_ARG;
+  const size_t es = elem_size(s->qkv_dtype), rs = elem_size(s->ring_dtype);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(ckpt, 16) || !aligned(ring_k, 16) ||
+      !aligned(ring_d, rs) || !aligned(v, es) || !aligned(o, es) || !aligned(g, 4) ||
+      !aligned(beta, 4) || !aligned(ring_g, 4) || !aligned(write_pos, 4) ||
+      !aligned(slot_idx, 4) || (err_flags && !aligned(err_flags, 4)))
+    return GDN_ERR_INVALID_ARG;
+  if (s->B == 0) return GDN_OK;
+  DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.slot = slot_idx; a.state = ckpt;
+  a.ring_d = ring_d; a.ring_k = ring_k; a.ring_g = ring_g; a.write_pos = write_pos;
+  a.force_flush = force_flush; a.o = o; a.err = err_flags; a.window = s->window;
+  dim3 grid, block;
+  fill_decode_geometry(s, a, grid, block);
+  size_t kt_bytes;
+  if (s->ring_dtype == GDN_F32) {
+    kt_bytes = static_cast<size_t>((s->L + 3) / 4 * 4) * s->dk * sizeof(float);
+    a.kts = s->dk;
+  } else {
+    a.kts = (s->L + 15) / 16 * 16 + 4;
+    kt_bytes = static_cast<size_t>(s->dk) * a.kts * 2;
+  }
+  const size_t smem = static_cast<size_t>(s->T) * 2 * s->dk * sizeof(float) + kt_bytes;
+  return from_hip(dispatch_replay(s->dk, a, s->qkv_dtype, s->ring_dtype, grid, block, smem,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_replay_advance(const gdn_shape* s, const int32_t* slot_idx, int32_t* write_pos,
+                              const uint8_t* force_flush, int32_t* err_flags, void* stream) {
+  if (!s || s->B < 0 || s->N < 1 || s->L < 1 || s->L > 64) return GDN_ERR_INVALID_ARG;
+  if (!slot_idx || !write_pos) return GDN_ERR_INVALID_ARG;
+  if (!aligned(slot_idx, 4) || !aligned(write_pos, 4) || (err_flags && !aligned(err_flags, 4)))
+    return GDN_ERR_INVALID_ARG;
+  if (s->B == 0) return GDN_OK;
+  CursorArgs a{};
+  a.slot = slot_idx; a.force_flush = force_flush; a.write_pos = write_pos; a.err = err_flags;
+  a.B = s->B; a.N = s->N; a.L = s->L; a.T = s->T;
+  return from_hip(launch_advance(a, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_replay_commit(const gdn_shape* s, const int32_t* slot_idx, const int32_t* accepted,
+                             int32_t* write_pos, int32_t* err_flags, void* stream) {
+  if (!s || s->B < 0 || s->N < 1 || s->L < 1 || s->L > 64 || s->T < 1 || s->T > 16)
+    return GDN_ERR_INVALID_ARG;
+  if (!slot_idx || !accepted || !write_pos) return GDN_ERR_INVALID_ARG;
+  if (!aligned(slot_idx, 4) || !aligned(accepted, 4) || !aligned(write_pos, 4) ||
+      (err_flags && !aligned(err_flags, 4)))
+    return GDN_ERR_INVALID_ARG;
+  if (s->B == 0) return GDN_OK;
+  CursorArgs a{};
+  a.slot = slot_idx; a.accepted = accepted; a.write_pos = write_pos; a.err = err_flags;
+  a.B = s->B; a.N = s->N; a.L = s->L; a.T = s->T;
+  return from_hip(launch_commit(a, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, float* ckpt,
+                           const void* ring_d, const void* ring_k, const float* ring_g,
+                           int32_t* write_pos, int32_t* err_flags, void* stream) {
+  const gdn_status st = check_shape(s, true);
+  if (st != GDN_OK) return st;
+  if (!slot_idx || !ckpt || !ring_d || !ring_k || !ring_g || !write_pos)
+    return GDN_ERR_INVALID_ARG;
+  const size_t rs = elem_size(s->ring_dtype);
+  if (!aligned(ckpt, 16) || !aligned(ring_d, rs) || !aligned(ring_k, rs) ||
+      !aligned(ring_g, 4) || !aligned(write_pos, 4) || !aligned(slot_idx, 4) ||
+      (err_flags && !aligned(err_flags, 4)))
+    return GDN_ERR_INVALID_ARG;
+  if (s->B == 0) return GDN_OK;
+  FoldArgs a{};
+  a.slot = slot_idx; a.ckpt = ckpt; a.ring_d = ring_d; a.ring_k = ring_k; a.ring_g = ring_g;
+  a.write_pos = write_pos; a.err = err_flags;
+  a.B = s->B; a.N = s->N; a.Hv = s->Hv; a.Hk = s->Hk; a.dv = s->dv; a.L = s->L;
+  a.G = s->Hv / s->Hk;
+  const dim3 grid(static_cast<unsigned>(s->B) * s->Hv * (s->dv / 16));
+  const dim3 block(static_cast<unsigned>(16 * s->dk / 4));
+  const size_t smem = static_cast<size_t>(s->L) * (1 + 16 + s->dk) * sizeof(float);
+  hipError_t e = dispatch_fold(s->dk, a, s->ring_dtype, grid, block, smem,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  CursorArgs c{};
+  c.slot = slot_idx; c.write_pos = write_pos; c.err = err_flags;
+  c.B = s->B; c.N = s->N; c.L = s->L; c.T = s->T;
+  return from_hip(launch_fold_reset(c, static_cast<hipStream_t>(stream)));
+}
+
+const char* gdn_status_string(gdn_status status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_INVALID_ARG: return "invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "unsupported size or dtype";
+    case GDN_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int32_t gdn_abi_version(void) { return kAbiVersion; }
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// gdn_cursor.hip -- the per-slot cursor kernels (fold reset, advance, commit)
+// and their launchers. One thread per row; every kernel only touches
+// write_pos[slot_idx[b]] of its own row.
+#include "gdn_launch.h"
+
+namespace gdn {
+
+// ============================================================= cursors
+
+// write_pos[s] <- 0 for each folded slot (separate launch: every fold
+// workgroup of the slot has read the old value by then).
+__global__ static void fold_reset_kernel(CursorArgs a) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= a.B) return;
+  const int s = a.slot[b];
+  if (s < 0 || s >= a.N) return;
+  const int p = a.write_pos[s];
+  if (p < 0 || p > a.L) return;
+  a.write_pos[s] = 0;
+}
+
+// Advance after a forward's decode calls (SGLang PR #28451, Design 3).
+__global__ static void advance_kernel(CursorArgs a) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= a.B) return;
+  const int s = a.slot[b];
+  if (s < 0) return;
+  if (s >= a.N) {
+    if (a.err) atomicOr(a.err, EF_SLOT);
+    return;
+  }
+  const int p = a.write_pos[s];
+  if (p < 0 || p > a.L - 1) {
+    if (a.err) atomicOr(a.err, EF_CURSOR);
+    return;
+  }
+  const bool flush = (p == a.L - 1) || (a.force_flush != nullptr && a.force_flush[b] != 0);
+  a.write_pos[s] = flush ? 0 : p + 1;
+}
+
+// Commit of a verify window's accepted prefix (vLLM PR #49887).
+__global__ static void commit_kernel(CursorArgs a) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= a.B) return;
+  const int s = a.slot[b];
+  if (s < 0) return;
+  if (s >= a.N) {
+    if (a.err) atomicOr(a.err, EF_SLOT);
+    return;
+  }
+  const int p = a.write_pos[s];
+  const int acc = a.accepted[b];
+  if (p < 0 || acc < 0 || acc > a.T || p + acc > a.L) {
+    if (a.err) atomicOr(a.err, EF_ACCEPTED);
+    return;
+  }
+  a.write_pos[s] = p + acc;
+}
+
+
+static hipError_t launch_rows(void (*kernel)(CursorArgs), const CursorArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(kernel, dim3((a.B + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_reset(const CursorArgs& a, hipStream_t st) { return launch_rows(fold_reset_kernel, a, st); }
+hipError_t launch_advance(const CursorArgs& a, hipStream_t st) { return launch_rows(advance_kernel, a, st); }
+hipError_t launch_commit(const CursorArgs& a, hipStream_t st) { return launch_rows(commit_kernel, a, st); }
+
+}  // namespace gdn

@@ -1,0 +1,72 @@
+// gdn_launch_impl.h -- definitions of the typed launchers (included by the
+// per-key-dimension translation units only).
+#pragma once
+
+#include "gdn_kernels.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+template <typename K, typename A>
+static hipError_t launch(K kernel, const A& a, dim3 grid, dim3 block, size_t smem,
+                         hipStream_t stream) {
+  if (smem > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(smem));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kernel, grid, block, smem, stream, a);
+  return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_packed(const DecodeArgs& a, int qkv, dim3 grid, dim3 block, size_t smem,
+                         hipStream_t stream) {
+  switch (qkv) {
+    case DT_F32: return launch(packed_decode_kernel<DK, DT_F32>, a, grid, block, smem, stream);
+    case DT_BF16: return launch(packed_decode_kernel<DK, DT_BF16>, a, grid, block, smem, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DK, int QKV>
+static hipError_t launch_replay_q(const DecodeArgs& a, int ring, dim3 grid, dim3 block,
+                                  size_t smem, hipStream_t stream) {
+  switch (ring) {
+    case DT_F32: return launch(replay_decode_kernel<DK, QKV, DT_F32>, a, grid, block, smem, stream);
+    case DT_F16: return launch(replay_decode_kernel<DK, QKV, DT_F16>, a, grid, block, smem, stream);
+    case DT_BF16: return launch(replay_decode_kernel<DK, QKV, DT_BF16>, a, grid, block, smem, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DK>
+hipError_t launch_replay(const DecodeArgs& a, int qkv, int ring, dim3 grid, dim3 block,
+                         size_t smem, hipStream_t stream) {
+  switch (qkv) {
+    case DT_F32: return launch_replay_q<DK, DT_F32>(a, ring, grid, block, smem, stream);
+    case DT_BF16: return launch_replay_q<DK, DT_BF16>(a, ring, grid, block, smem, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DK>
+hipError_t launch_fold(const FoldArgs& a, int ring, dim3 grid, dim3 block, size_t smem,
+                       hipStream_t stream) {
+  switch (ring) {
+    case DT_F32: return launch(fold_kernel<DK, DT_F32>, a, grid, block, smem, stream);
+    case DT_F16: return launch(fold_kernel<DK, DT_F16>, a, grid, block, smem, stream);
+    case DT_BF16: return launch(fold_kernel<DK, DT_BF16>, a, grid, block, smem, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+#define GDN_INSTANTIATE(DK)                                                                 \
+  template hipError_t launch_packed<DK>(const DecodeArgs&, int, dim3, dim3, size_t,         \
+                                        hipStream_t);                                        \
+  template hipError_t launch_replay<DK>(const DecodeArgs&, int, int, dim3, dim3, size_t,    \
+                                        hipStream_t);                                        \
+  template hipError_t launch_fold<DK>(const FoldArgs&, int, dim3, dim3, size_t, hipStream_t);
+
+}  // namespace gdn

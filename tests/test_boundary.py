@@ -1,0 +1,122 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, and rejects invalid arguments on the host before any HIP
+call (no kernel is launched by these tests)."""
+import ctypes
+
+import pytest
+
+import linear_attention_ssm_amd as gdn
+from linear_attention_ssm_amd import gdn_shape
+
+EXPECTED = ["gdn_abi_version", "gdn_packed_decode", "gdn_replay_advance", "gdn_replay_commit",
+            "gdn_replay_decode", "gdn_replay_fold", "gdn_status_string"]
+
+# Fake, 256-byte aligned, non-null device addresses: never dereferenced, since
+# every call below must fail validation (or return early for B = 0) first.
+FAKE = [ctypes.c_void_p(0x100000 + 0x1000 * i) for i in range(16)]
+
+
+def shape(**kw):
+    d = dict(B=2, T=1, N=4, Hv=4, Hk=2, dk=128, dv=128, L=16, qkv_dtype=gdn.GDN_BF16,
+             ring_dtype=gdn.GDN_F16, window=0)
+    d.update(kw)
+    return gdn_shape(**d)
+
+
+def test_header_declares_exactly_the_exported_symbols():
+    assert gdn.declared_symbols() == EXPECTED
+    lib = gdn.lib()
+    for name in EXPECTED:
+        assert hasattr(lib, name), name
+    assert lib.gdn_abi_version() == 1
+    for st in range(4):
+        assert lib.gdn_status_string(st)
+    assert lib.gdn_status_string(99) == b"unknown status"
+
+
+def replay(sh, ptrs=None, ff=None):
+    p = list(ptrs or FAKE[:12])
+    # q k v g beta slot ckpt ring_d ring_k ring_g write_pos | force_flush o err stream
+    return gdn.lib().gdn_replay_decode(ctypes.byref(sh), *p[:11], ff, p[11], None, None)
+
+
+def packed(sh, ptrs=None):
+    p = list(ptrs or FAKE[:8])
+    return gdn.lib().gdn_packed_decode(ctypes.byref(sh), *p, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(L=65), gdn.GDN_ERR_INVALID_ARG),
+    (dict(Hv=3, Hk=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(Hv=34, Hk=2), gdn.GDN_ERR_INVALID_ARG),       # G = 17 > 16
+    (dict(dk=96), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dv=40), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(qkv_dtype=gdn.GDN_F16), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(ring_dtype=7), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(T=2), gdn.GDN_ERR_INVALID_ARG),               # decode mode needs T = 1
+    (dict(T=2, window=1, L=1), gdn.GDN_ERR_INVALID_ARG),  # window longer than the ring
+    (dict(window=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(B=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(N=0), gdn.GDN_ERR_INVALID_ARG),
+])
+def test_replay_decode_rejects_bad_shapes(kw, status):
+    assert replay(shape(**kw)) == status
+
+
+def test_replay_decode_rejects_bad_pointers():
+    assert gdn.lib().gdn_replay_decode(None, *FAKE[:11], None, FAKE[11], None, None) \
+        == gdn.GDN_ERR_INVALID_ARG
+    for i in range(12):
+        p = list(FAKE[:12])
+        p[i] = None
+        assert replay(shape(), p) == gdn.GDN_ERR_INVALID_ARG, i
+    p = list(FAKE[:12])
+    p[6] = ctypes.c_void_p(FAKE[6].value + 4)            # checkpoint not 16-byte aligned
+    assert replay(shape(), p) == gdn.GDN_ERR_INVALID_ARG
+    p = list(FAKE[:12])
+    p[0] = ctypes.c_void_p(FAKE[0].value + 2)            # q not 16-byte aligned
+    assert replay(shape(), p) == gdn.GDN_ERR_INVALID_ARG
+    # force_flush is not allowed with a verify window
+    assert replay(shape(T=2, window=1), ff=FAKE[13]) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op():
+    assert replay(shape(B=0)) == gdn.GDN_OK
+    assert packed(shape(B=0)) == gdn.GDN_OK
+    lib = gdn.lib()
+    sh = shape(B=0)
+    assert lib.gdn_replay_fold(ctypes.byref(sh), *FAKE[:6], None, None) == gdn.GDN_OK
+    assert lib.gdn_replay_advance(ctypes.byref(sh), FAKE[0], FAKE[1], None, None, None) == gdn.GDN_OK
+    assert lib.gdn_replay_commit(ctypes.byref(sh), FAKE[0], FAKE[1], FAKE[2], None, None) == gdn.GDN_OK
+
+
+def test_packed_and_cursor_entry_points_validate():
+    assert packed(shape(T=2)) == gdn.GDN_ERR_INVALID_ARG
+    assert packed(shape(dk=48)) == gdn.GDN_ERR_UNSUPPORTED
+    p = list(FAKE[:8])
+    p[6] = None
+    assert packed(shape(), p) == gdn.GDN_ERR_INVALID_ARG
+    lib = gdn.lib()
+    sh = shape(L=0)
+    assert lib.gdn_replay_advance(ctypes.byref(sh), FAKE[0], FAKE[1], None, None, None) \
+        == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_replay_advance(ctypes.byref(shape()), None, FAKE[1], None, None, None) \
+        == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_replay_commit(ctypes.byref(shape(T=0)), FAKE[0], FAKE[1], FAKE[2], None, None) \
+        == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_replay_commit(ctypes.byref(shape()), FAKE[0], None, FAKE[2], None, None) \
+        == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_replay_fold(ctypes.byref(shape(dv=8)), *FAKE[:6], None, None) \
+        == gdn.GDN_ERR_UNSUPPORTED
+    p = list(FAKE[:6])
+    p[1] = ctypes.c_void_p(FAKE[1].value + 8)            # checkpoint misaligned
+    assert lib.gdn_replay_fold(ctypes.byref(shape()), *p, None, None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_python_binding_checks_tensors_before_calling():
+    import torch
+    q = torch.zeros(2, 1, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gdn.gdn_packed_decode(q, q, q, torch.zeros(2, 1, 4), torch.zeros(2, 1, 4),
+                              torch.zeros(2, dtype=torch.int32), torch.zeros(4, 4, 128, 128))

@@ -1,0 +1,181 @@
+"""GPU parity of the single-token decode (packed and ReplaySSM) against the
+CPU oracle, at the five workloads' sizes, plus the edge cases: padding rows,
+forced mid-buffer flushes, the L = 1 degeneracy (bitwise against the packed
+decode), ragged shapes, a corrupted ring key, stale-entry garbage, and the
+device-side error flags."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+from gdn_harness import DEV, Pool, bits, dev_inputs, log, run_decode, to_dev, to_f64
+from oracle import gdn_step, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import linear_attention_ssm_amd as m
+    return m
+
+
+def test_c1_tiny_fp32_replay(gdn):
+    rep = run_decode(gi.C1, "replay", garbage=True, recon_every=1)
+    assert rep.flushes == 2 * 10          # 2 slots x flushes at steps 4, 8, ..., 40
+
+
+def test_c1_tiny_fp32_packed(gdn):
+    run_decode(gi.C1, "packed")
+
+
+def test_c2_standard_replay(gdn):
+    run_decode(gi.C2, "replay", n_sample=6, garbage=True, recon_every=16)
+
+
+def test_c2_standard_packed(gdn):
+    run_decode(gi.C2, "packed", n_sample=6)
+
+
+def test_c3_large_pool_with_padding(gdn):
+    run_decode(gi.C3, "replay", n_sample=6, check_untouched=True)
+
+
+@pytest.mark.parametrize("L", [1, 4, 16, 32])
+def test_c4_ring_depth(gdn, L):
+    run_decode(gi.c4(L), "replay", n_sample=4, recon_every=32 if L > 1 else 0)
+
+
+def test_c4_fp32_ring(gdn):
+    run_decode(gi.c4(16, "f32"), "replay", n_sample=4, recon_every=16)
+
+
+@pytest.mark.parametrize("ring", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("dims", [(64, 48, 6, 2), (32, 16, 3, 3), (256, 128, 4, 1)])
+def test_ragged_shapes(gdn, ring, dims):
+    """Several key tiles, value blocks that are not a power of two, GQA
+    groups of 1..3, a row count that fills no tile evenly."""
+    dk, dv, Hv, Hk = dims
+    qkv = "f32" if ring == "f32" else "bf16"
+    w = gi.Workload(f"ragged_{dk}_{dv}_{Hv}_{Hk}_{ring}", B=5, N=7, Hv=Hv, Hk=Hk, dk=dk, dv=dv,
+                    L=5, steps=13, qkv=qkv, ring=ring, n_pad=1, permute=True,
+                    bf16_values=(ring == "f32"), seed=900 + dk + dv + Hv)
+    run_decode(w, "replay", garbage=True, recon_every=4, check_untouched=True)
+    run_decode(w, "packed")
+
+
+def test_L1_replay_equals_packed_bitwise(gdn):
+    """At L = 1 the ring is always empty and every step flushes, so the replay
+    decode must reproduce the packed decode bit for bit (SGLang PR #28451,
+    Design 1: the L = 1 kernel reduces to the packed decode)."""
+    w = dataclasses.replace(gi.c4(1), steps=6, n_pad=2, permute=True, N=80)
+    S0 = gi.initial_state(w)
+    slots = gi.slot_map(w)
+    a = Pool(w, S0)
+    state = to_dev(S0)
+    slot_t = to_dev(slots)
+    for t in range(w.steps):
+        xi = dev_inputs(gi.step_inputs(w, t))
+        o1 = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, a.ckpt, a.ring_d,
+                                   a.ring_k, a.ring_g, a.write_pos, err_flags=a.err)
+        gdn.gdn_replay_advance(slot_t, a.write_pos, w.L, err_flags=a.err)
+        o2 = gdn.gdn_packed_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, state)
+        assert torch.equal(bits(o1), bits(o2)), f"step {t}: outputs differ"
+        assert torch.equal(bits(a.ckpt), bits(state)), f"step {t}: states differ"
+        assert int(a.write_pos.abs().sum().item()) == 0
+    assert int(a.err.item()) == 0
+
+
+def test_corrupted_ring_key_changes_output(gdn):
+    """Negative test (vLLM PR #49887, Tests): corrupting one valid cached key
+    must change the output of the heads that read it, and only those."""
+    w = gi.scaled(gi.C2, name="corrupt", B=4, N=4, L=8, steps=5, stagger=False, seed=31)
+    S0 = gi.initial_state(w)
+    slots = gi.slot_map(w)
+    pool = Pool(w, S0)
+    slot_t = to_dev(slots)
+    for t in range(w.steps):
+        xi = dev_inputs(gi.step_inputs(w, t))
+        gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, pool.ckpt, pool.ring_d,
+                              pool.ring_k, pool.ring_g, pool.write_pos)
+        gdn.gdn_replay_advance(slot_t, pool.write_pos, w.L)
+    assert pool.write_pos.cpu().tolist() == [5, 5, 5, 5]
+    xi = dev_inputs(gi.step_inputs(w, 99))
+    saved = [x.clone() for x in (pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g)]
+    o1 = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, *saved[:1],
+                               saved[1].clone(), saved[2].clone(), saved[3].clone(),
+                               pool.write_pos)
+    rk = saved[2].clone()
+    rk[slots[1], 3, 2] = -rk[slots[1], 3, 2]          # slot of row 1, k-head 3, entry 2
+    o2 = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, saved[0].clone(),
+                               saved[1].clone(), rk, saved[3].clone(), pool.write_pos)
+    G = w.Hv // w.Hk
+    diff = (bits(o1) != bits(o2)).any(dim=-1)[:, 0]    # [B, Hv]
+    expect = torch.zeros_like(diff)
+    expect[1, 3 * G:3 * G + G] = True
+    assert torch.equal(diff, expect)
+    e = rel_err(to_f64(o2[1, 0, 3 * G]), to_f64(o1[1, 0, 3 * G]))
+    assert e > 1e-2
+
+
+def test_forced_flush_mid_buffer_reads_only_valid_entries(gdn):
+    """A forced flush in the middle of the ring (SGLang PR #28451, Design 5)
+    folds only the entries below write_pos; garbage beyond them is never
+    read. Covered by the staggered workloads too; here every slot is forced
+    at a different depth and the rings start as a garbage template."""
+    w = gi.scaled(gi.C2, name="midflush", B=8, N=8, L=8, steps=20, seed=41)
+    run_decode(w, "replay", garbage=True, recon_every=5)
+
+
+def test_device_error_flags(gdn):
+    w = gi.scaled(gi.C2, name="errors", B=4, N=4, L=4, steps=1, stagger=False, seed=51)
+    S0 = gi.initial_state(w)
+    pool = Pool(w, S0)
+    xi = dev_inputs(gi.step_inputs(w, 0))
+    # slot index beyond the pool: EF_SLOT_RANGE, zero output, nothing written
+    slots = to_dev(np.array([0, 9, 2, -1], np.int32))
+    ck0 = pool.ckpt.clone()
+    o = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slots, pool.ckpt, pool.ring_d,
+                              pool.ring_k, pool.ring_g, pool.write_pos, err_flags=pool.err)
+    assert int(pool.err.item()) == gdn.EF_SLOT_RANGE
+    assert torch.count_nonzero(o[1]).item() == 0 and torch.count_nonzero(o[3]).item() == 0
+    assert torch.count_nonzero(o[0]).item() > 0
+    # cursor out of range: EF_CURSOR_RANGE, row treated as padding
+    pool.err.zero_()
+    pool.write_pos.copy_(to_dev(np.array([0, 4, 0, 0], np.int32)))
+    slots = to_dev(np.array([0, 1, 2, 3], np.int32))
+    o = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slots, pool.ckpt, pool.ring_d,
+                              pool.ring_k, pool.ring_g, pool.write_pos, err_flags=pool.err)
+    assert int(pool.err.item()) == gdn.EF_CURSOR_RANGE
+    assert torch.count_nonzero(o[1]).item() == 0
+    assert torch.equal(bits(pool.ckpt[1]), bits(ck0[1]))
+    gdn.gdn_replay_advance(slots, pool.write_pos, w.L, err_flags=pool.err)
+    assert pool.write_pos.cpu().tolist() == [1, 4, 1, 1]
+    # verify window that does not fit: EF_WINDOW
+    pool.err.zero_()
+    wv = gi.scaled(w, T=3)
+    xv = dev_inputs(gi.step_inputs(wv, 0))
+    o = gdn.gdn_replay_decode(xv.q, xv.k, xv.v, xv.g, xv.beta, slots, pool.ckpt, pool.ring_d,
+                              pool.ring_k, pool.ring_g, pool.write_pos, err_flags=pool.err,
+                              window=True)
+    assert int(pool.err.item()) == gdn.EF_WINDOW | gdn.EF_CURSOR_RANGE or \
+        int(pool.err.item()) == gdn.EF_WINDOW
+    assert torch.count_nonzero(o[1]).item() == 0 and torch.count_nonzero(o[0]).item() > 0
+    # commit beyond the window: EF_ACCEPTED, cursor unchanged
+    pool.err.zero_()
+    acc = to_dev(np.array([4, 0, 1, 2], np.int32))
+    gdn.gdn_replay_commit(slots, acc, pool.write_pos, w.L, 3, err_flags=pool.err)
+    assert int(pool.err.item()) == gdn.EF_ACCEPTED
+    assert pool.write_pos.cpu().tolist() == [1, 4, 2, 3]
+    # fold with a cursor beyond the ring: EF_CURSOR_RANGE, checkpoint untouched
+    pool.err.zero_()
+    pool.write_pos.copy_(to_dev(np.array([1, 5, 0, 3], np.int32)))
+    ck0 = pool.ckpt.clone()
+    gdn.gdn_replay_fold(slots, pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
+                        pool.write_pos, err_flags=pool.err)
+    assert int(pool.err.item()) == gdn.EF_CURSOR_RANGE
+    assert torch.equal(bits(pool.ckpt[1]), bits(ck0[1]))
+    assert torch.equal(bits(pool.ckpt[2]), bits(ck0[2]))      # p = 0: nothing to fold
+    assert pool.write_pos.cpu().tolist() == [0, 5, 0, 0]

@@ -1,0 +1,175 @@
+"""GPU parity of the verify window, the commit and the fold.
+
+The c5 protocol: a T = 1 history that never flushes, then rounds of
+verify (T = 5) -> accept a ~ U{0..5} -> commit -> fold when the ring cannot
+hold another window, then a final fold. Outputs, stored corrections and
+folded checkpoints are checked against the oracle's true recurrence within
+the 16-bit-ring tolerance; cursors bit for bit. The fold itself is checked
+bit for bit against the oracle's pinned-rounding fold on seeded rings.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+from gdn_harness import (DEV, TORCH_DT, Pool, bits, dev_inputs, log, to_dev, to_f64, tol_o,
+                         tol_state)
+from oracle import fold_f32, gdn_step, rel_err, window_ref
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import linear_attention_ssm_amd as m
+    return m
+
+
+def _advance_true(S, slots, x64, counts):
+    """Advance the oracle's true states by the first counts[b] tokens of each row."""
+    q, k, v, g, beta = x64
+    for b, s in enumerate(slots):
+        if s < 0:
+            continue
+        one = np.array([s], np.int32)
+        for t in range(int(counts[b])):
+            gdn_step(S, one, q[b:b + 1, t], k[b:b + 1, t], v[b:b + 1, t], g[b:b + 1, t],
+                     beta[b:b + 1, t])
+
+
+@pytest.mark.parametrize("ring", ["f16", "f32"])
+def test_c5_verify_commit_fold_protocol(gdn, ring):
+    w = gi.C5 if ring == "f16" else dataclasses.replace(gi.C5, name="c5_f32ring", ring="f32",
+                                                       qkv="f32", bf16_values=True)
+    T, L = w.T, w.L
+    S0 = gi.initial_state(w)
+    slots = gi.slot_map(w)
+    hist = gi.history_lengths(w)
+    pool = Pool(w, S0, garbage=True)
+    S_true = S0.astype(np.float64)
+    wp = np.zeros(w.N, dtype=np.int64)
+    tol_o_, tol_s_ = tol_o(w), tol_state(w)
+    errs = {"hist": [], "win": [], "d": [], "fold": []}
+    # -- history of single-token steps (never reaching a flush)
+    for i in range(int(hist.max())):
+        act = np.array([hist[s] > i for s in slots])
+        sl = np.where(act, slots, -1).astype(np.int32)
+        x = gi.step_inputs(w, 1000 + i, T=1)
+        xi = dev_inputs(x)
+        slt = to_dev(sl)
+        o = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slt, pool.ckpt, pool.ring_d,
+                                  pool.ring_k, pool.ring_g, pool.write_pos, err_flags=pool.err)
+        gdn.gdn_replay_advance(slt, pool.write_pos, L, err_flags=pool.err)
+        q, k, v, g, beta = (a[:, 0] for a in x.f64())
+        o_ref = gdn_step(S_true, sl, q, k, v, g, beta)
+        e = rel_err(to_f64(o[:, 0]), o_ref)
+        errs["hist"].append(e)
+        assert e <= tol_o_
+        wp[sl[sl >= 0]] += 1
+    assert np.array_equal(pool.write_pos.cpu().numpy(), wp)
+    assert np.array_equal(wp, hist)
+    slot_t = to_dev(slots)
+    for r in range(w.steps):
+        x = gi.step_inputs(w, 2000 + r)
+        xi = dev_inputs(x)
+        p_before = wp.copy()
+        assert np.all(p_before[slots] + T <= L)
+        o = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, pool.ckpt,
+                                  pool.ring_d, pool.ring_k, pool.ring_g, pool.write_pos,
+                                  err_flags=pool.err, window=True)
+        x64 = x.f64()
+        o_ref, u_ref = window_ref(S_true, slots, *x64, want_u=True)
+        e = rel_err(to_f64(o), o_ref)
+        errs["win"].append(e)
+        assert e <= tol_o_, f"round {r}: window output rel err {e:.3e}"
+        # the window's corrections were written at p .. p+T-1
+        rd = to_f64(pool.ring_d)
+        d_gpu = np.stack([rd[s, :, p_before[s]:p_before[s] + T].transpose(1, 0, 2)
+                          for s in slots])                              # [B, T, Hv, dv]
+        ed = rel_err(d_gpu, u_ref)
+        errs["d"].append(ed)
+        assert ed <= tol_s_, f"round {r}: stored corrections rel err {ed:.3e}"
+        assert np.array_equal(pool.write_pos.cpu().numpy(), wp), "verify moved a cursor"
+        acc = gi.accepted_counts(w, r)
+        gdn.gdn_replay_commit(slot_t, to_dev(acc), pool.write_pos, L, T, err_flags=pool.err)
+        _advance_true(S_true, slots, x64, acc)
+        wp[slots] += acc
+        assert np.array_equal(pool.write_pos.cpu().numpy(), wp)
+        need = wp[slots] + T > L
+        if need.any():
+            sl = np.where(need, slots, -1).astype(np.int32)
+            gdn.gdn_replay_fold(to_dev(sl), pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
+                                pool.write_pos, err_flags=pool.err)
+            wp[slots[need]] = 0
+            ef = rel_err(to_f64(pool.ckpt[to_dev(slots[need]).long()]), S_true[slots[need]])
+            errs["fold"].append(ef)
+            assert ef <= tol_s_, f"round {r}: folded checkpoint rel err {ef:.3e}"
+            assert np.array_equal(pool.write_pos.cpu().numpy(), wp)
+    gdn.gdn_replay_fold(slot_t, pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
+                        pool.write_pos, err_flags=pool.err)
+    ef = rel_err(to_f64(pool.ckpt), S_true)
+    errs["fold"].append(ef)
+    assert ef <= tol_s_
+    assert int(pool.write_pos.abs().sum().item()) == 0
+    assert int(pool.err.item()) == 0
+    log(f"[{w.name}] " + "  ".join(f"{k} {max(v):.2e}" for k, v in errs.items() if v))
+
+
+def test_window_equals_token_by_token_windows(gdn):
+    """A T-token window and T single-token windows (each committed with
+    accepted = 1) give the same outputs within tolerance, and both match the
+    oracle (vLLM PR #49887, Tests: window vs one token at a time)."""
+    w = gi.scaled(gi.C5, name="win_vs_tok", B=8, N=8, steps=1, seed=606)
+    S0 = gi.initial_state(w)
+    slots = gi.slot_map(w)
+    a, b = Pool(w, S0), Pool(w, S0)
+    slot_t = to_dev(slots)
+    x = gi.step_inputs(w, 0)
+    xi = dev_inputs(x)
+    oa = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, a.ckpt, a.ring_d,
+                               a.ring_k, a.ring_g, a.write_pos, window=True)
+    ob = []
+    one = torch.ones(w.B, dtype=torch.int32, device=DEV)
+    for t in range(w.T):
+        sl = lambda z: z[:, t:t + 1].contiguous()
+        ob.append(gdn.gdn_replay_decode(sl(xi.q), sl(xi.k), sl(xi.v), sl(xi.g), sl(xi.beta),
+                                        slot_t, b.ckpt, b.ring_d, b.ring_k, b.ring_g,
+                                        b.write_pos, window=True))
+        gdn.gdn_replay_commit(slot_t, one, b.write_pos, w.L, 1)
+    ob = torch.cat(ob, dim=1)
+    o_ref = window_ref(S0.astype(np.float64), slots, *x.f64())
+    assert rel_err(to_f64(oa), o_ref) <= tol_o(w)
+    assert rel_err(to_f64(ob), o_ref) <= tol_o(w)
+    assert rel_err(to_f64(oa), to_f64(ob)) <= tol_o(w)
+
+
+@pytest.mark.parametrize("ring", ["f16", "bf16", "f32"])
+def test_fold_bitwise_against_oracle(gdn, ring):
+    """gdn_replay_fold is bit-identical to the oracle's pinned-rounding fold
+    (every element of every slot, listed or not), and resets the cursors."""
+    w = dataclasses.replace(gi.C5, ring=ring, N=40, B=36, n_pad=3, permute=True)
+    rc = gi.random_ring(w, seed_tag={"f16": 1, "bf16": 2, "f32": 3}[ring])
+    slots = gi.slot_map(w)
+    wp = rc.write_pos.copy()
+    live = slots[slots >= 0]
+    wp[live[0]] = w.L          # a full ring
+    wp[live[1]] = 0            # an empty one
+    ckpt = to_dev(rc.ckpt)
+    rd, rk = to_dev(rc.d, ring), to_dev(rc.k, ring)
+    rg = to_dev(rc.g)
+    wpt = to_dev(wp.astype(np.int32))
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gdn.gdn_replay_fold(to_dev(slots), ckpt, rd, rk, rg, wpt, err_flags=err)
+    ref = rc.ckpt.copy()
+    wref = wp.astype(np.int32).copy()
+    fold_f32(ref, slots, wref, gi.as_f64(rc.d, ring).astype(np.float32),
+             gi.as_f64(rc.k, ring).astype(np.float32), rc.g)
+    got = ckpt.cpu().numpy()
+    mism = np.count_nonzero(got.view(np.uint32) != ref.view(np.uint32))
+    assert mism == 0, f"{mism} elements differ from the oracle's fold"
+    assert np.array_equal(wpt.cpu().numpy(), wref)
+    assert int(err.item()) == 0
+    log(f"[fold/{ring}] bit-exact over {got.size} elements, "
+        f"{int(wp[live].sum())} entries folded")
