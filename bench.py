@@ -1,0 +1,416 @@
+"""Benchmark of the ReplaySSM GDN decode step on one MI355X.
+
+One step = one decode forward of the standard workload (B = 64 rows, Hv = 32,
+Hk = 16, dk = dv = 128, ring L = 16, fp32 checkpoint, bf16 q/k/v/o, fp16 d/k
+ring, staggered cursors) through R = 8 GDN layers: one gdn_replay_decode call
+per layer, each on its own checkpoint + ring set, then one gdn_replay_advance
+(the cursor is shared by the layers and advances once per forward). The 8
+layer sets (~1.1 GiB) exceed the 256 MB Infinity Cache, so the checkpoint is
+streamed from HBM as in a real multi-layer model.
+
+Printed: one JSON line with head-steps/s (value), the HBM roofline of the
+replay decode kernel (per-launch HIP events on the launch stream), the packed
+read-update-write decode built alongside it on the same workload, the verify
+window + fold of the speculative workload, and the CPU oracle baseline.
+
+Modes for profiling runs (same kernels, fewer steps, no CPU baseline):
+  --profile-pass   warmup + a few timed steps of each kernel
+  --copy-probe     one plain 1 GiB device copy (counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gdn_inputs as gi  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "GDN decode head-steps/sec and achieved HBM GB/s (% of peak) at B=64, L=16"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["linear_attention_ssm_amd/csrc/gdn_kernels.h",
+                  "linear_attention_ssm_amd/csrc/gdn_device.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ byte model
+
+def bytes_decode_head_step(w: gi.Workload, p: int, flush: bool, kind: str) -> float:
+    """Algorithmic HBM bytes of one (row, value head) decode step.
+    State fp32; ring entries and I/O in the workload dtypes; the key side
+    (q, k and the key ring) is counted once per key head, i.e. 1/G per value
+    head."""
+    es = 2 if w.qkv != "f32" else 4
+    rs = 2 if w.ring != "f32" else 4
+    G = w.Hv // w.Hk
+    state = 4 * w.dv * w.dk
+    io = 2 * es * w.dk / G + 2 * es * w.dv + 8          # q, k (per k-head), v, o, g, beta
+    if kind == "packed":
+        return 2 * state + io
+    b = state + io
+    b += p * (rs * w.dv + rs * w.dk / G + 4)             # valid ring entries read
+    if flush:
+        b += state                                       # checkpoint written from registers
+    else:
+        b += rs * w.dv + rs * w.dk / G + 4               # ring append
+    return b
+
+
+def cursor_sequence(w: gi.Workload, slots: np.ndarray, steps: int):
+    """Per step: list of (p, flush) per live row, from the cursor rule
+    (flush when p == L-1 or forced; next = 0 on flush, else p+1)."""
+    wp = np.zeros(w.N, dtype=np.int64)
+    seq = []
+    for t in range(steps):
+        ff = gi.force_flush_schedule(w, t, slots)
+        cur = []
+        for b, s in enumerate(slots):
+            if s < 0:
+                continue
+            fl = (wp[s] == w.L - 1) or bool(ff[b])
+            cur.append((int(wp[s]), bool(fl)))
+            wp[s] = 0 if fl else wp[s] + 1
+        seq.append(cur)
+    return seq
+
+
+# ------------------------------------------------------------------ helpers
+
+def dev_tensor(x, dt, dev):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dt == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to(dev)
+
+
+class LayerSet:
+    def __init__(self, w, seed, dev, with_ring=True):
+        import torch
+        ws = dataclasses.replace(w, seed=seed)
+        self.state = dev_tensor(gi.initial_state(ws), None, dev)
+        if with_ring:
+            rdt = torch.float16 if w.ring == "f16" else (
+                torch.bfloat16 if w.ring == "bf16" else torch.float32)
+            self.ring_d = torch.zeros((w.N, w.Hv, w.L, w.dv), dtype=rdt, device=dev)
+            self.ring_k = torch.zeros((w.N, w.Hk, w.L, w.dk), dtype=rdt, device=dev)
+            self.ring_g = torch.zeros((w.N, w.Hv, w.L), dtype=torch.float32, device=dev)
+
+
+def input_sets(w, n, dev, T=None):
+    out = []
+    for i in range(n):
+        x = gi.step_inputs(w, 10_000 + i, T=T)
+        out.append(tuple(dev_tensor(a, x.dtype if j < 3 else None, dev)
+                         for j, a in enumerate((x.q, x.k, x.v, x.g, x.beta))))
+    return out
+
+
+def graph_of(fn):
+    """Capture fn's launches (all enqueued on torch's current stream, which is
+    the capture stream during capture) into a HIP graph."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                                   # one eager run on the capture stream first
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps):
+    """Mean milliseconds per replay, HIP events on the replay stream."""
+    import torch
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def load_traffic(name: str):
+    """HBM bytes per launch from a committed rocprofv3 summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"kernel_sources_sha256_16:\s*(\w+)", txt)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not t or m.group(1) != kernel_hash():
+        return None
+    return float(t.group(1))
+
+
+# ------------------------------------------------------------------ benches
+
+def bench_replay(w, R, steps, warmup, dev, log):
+    import torch
+    import linear_attention_ssm_amd as gdn
+    slots = gi.slot_map(w)
+    slot_t = dev_tensor(slots, None, dev)
+    layers = [LayerSet(w, w.seed + 17 * i, dev) for i in range(R)]
+    wp = torch.zeros(w.N, dtype=torch.int32, device=dev)
+    ins = input_sets(w, 4, dev)
+    ff_sched = [dev_tensor(gi.force_flush_schedule(w, t, slots), None, dev) for t in range(w.L)]
+    no_ff = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    o = torch.empty((w.B, 1, w.Hv, w.dv), dtype=torch.bfloat16, device=dev)
+
+    def decodes(ff):
+        for i, ls in enumerate(layers):
+            q, k, v, g, beta = ins[i % len(ins)]
+            gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
+                                  ls.ring_g, wp, force_flush=ff, o=o, err_flags=err)
+
+    def forward(ff):
+        decodes(ff)
+        gdn.gdn_replay_advance(slot_t, wp, w.L, force_flush=ff, err_flags=err)
+
+    # eager warm-up: the staggered forced flushes of the first L steps spread
+    # the slots' flush phases evenly over the ring cycle
+    warmup = max(warmup, w.L)
+    for t in range(warmup):
+        forward(ff_sched[t] if t < w.L else no_ff)
+    torch.cuda.synchronize()
+    n_fwd = warmup                                    # forwards applied so far
+    g_fwd = graph_of(lambda: forward(no_ff))          # runs one forward eagerly, then captures
+    n_fwd += 1
+    g_dec = graph_of(lambda: decodes(no_ff))          # one decode-only run, then captures
+    # pass 1: whole-job throughput (R decodes + the advance per step)
+    ms_step = time_graph(g_fwd, steps)
+    n_fwd += steps + 1                                # time_graph replays once before timing
+    # pass 2: the decode kernels alone, back to back (cursors frozen at this phase)
+    ms_dec = time_graph(g_dec, steps) / R
+    assert int(err.item()) == 0, f"device error flags {int(err.item())}"
+    seq = cursor_sequence(w, slots, n_fwd + 1)
+    cur = seq[n_fwd]                                   # the phase the frozen decodes see
+    bytes_launch = sum(bytes_decode_head_step(w, p, fl, "replay") for p, fl in cur) * w.Hv
+    live = int(np.count_nonzero(slots >= 0))
+    mean_p = float(np.mean([p for p, _ in cur]))
+    flush_frac = float(np.mean([fl for _, fl in cur]))
+    log(f"replay: {ms_step * 1e3:.1f} us/step ({R} layers + advance), decode kernel "
+        f"{ms_dec * 1e3:.2f} us, {bytes_launch / 1e6:.2f} MB/launch, mean p {mean_p:.2f}, "
+        f"flush frac {flush_frac:.4f}")
+    return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
+                kernel_ms=ms_dec, bytes_per_launch=bytes_launch,
+                head_steps_per_launch=live * w.Hv, mean_p=mean_p, flush_frac=flush_frac)
+
+
+def bench_packed(w, R, steps, dev, log):
+    import torch
+    import linear_attention_ssm_amd as gdn
+    slots = gi.slot_map(w)
+    slot_t = dev_tensor(slots, None, dev)
+    layers = [LayerSet(w, w.seed + 17 * i, dev, with_ring=False) for i in range(R)]
+    ins = input_sets(w, 4, dev)
+    o = torch.empty((w.B, 1, w.Hv, w.dv), dtype=torch.bfloat16, device=dev)
+
+    def forward():
+        for i, ls in enumerate(layers):
+            q, k, v, g, beta = ins[i % len(ins)]
+            gdn.gdn_packed_decode(q, k, v, g, beta, slot_t, ls.state, o=o)
+
+    g = graph_of(forward)
+    ms_step = time_graph(g, steps)
+    live = int(np.count_nonzero(slots >= 0))
+    bytes_launch = live * w.Hv * bytes_decode_head_step(w, 0, False, "packed")
+    log(f"packed: {ms_step * 1e3:.1f} us/step ({R} layers), kernel {ms_step / R * 1e3:.2f} us, "
+        f"{bytes_launch / 1e6:.2f} MB/launch")
+    return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
+                kernel_ms=ms_step / R, bytes_per_launch=bytes_launch)
+
+
+def bench_window_fold(w, R, steps, dev, log):
+    """Verify window (T tokens from checkpoint + ring with p0 = L - T - 1
+    valid entries) and the fold of a ring holding p0 + T entries, R layer
+    sets each."""
+    import torch
+    import linear_attention_ssm_amd as gdn
+    slots = gi.slot_map(w)
+    slot_t = dev_tensor(slots, None, dev)
+    layers = [LayerSet(w, w.seed + 17 * i, dev) for i in range(R)]
+    ins = input_sets(w, 2, dev)
+    p0 = w.L - w.T - 1
+    pf = p0 + w.T
+    wps = [torch.full((w.N,), p0, dtype=torch.int32, device=dev) for _ in range(R)]
+    wpf = [torch.full((w.N,), pf, dtype=torch.int32, device=dev) for _ in range(R)]
+    o = torch.empty((w.B, w.T, w.Hv, w.dv), dtype=torch.bfloat16, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def verify():
+        for i, ls in enumerate(layers):
+            q, k, v, g, beta = ins[i % 2]
+            gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
+                                  ls.ring_g, wps[i], o=o, err_flags=err, window=True)
+
+    def fold():
+        for i, ls in enumerate(layers):
+            wpf[i].fill_(pf)
+            gdn.gdn_replay_fold(slot_t, ls.state, ls.ring_d, ls.ring_k, ls.ring_g, wpf[i],
+                                err_flags=err)
+
+    mv = time_graph(graph_of(verify), steps) / R
+    mf = time_graph(graph_of(fold), steps) / R
+    assert int(err.item()) == 0
+    G = w.Hv // w.Hk
+    live = int(np.count_nonzero(slots >= 0))
+    rs, es = 2, 2
+    ent = rs * w.dv + rs * w.dk / G + 4
+    vb = live * w.Hv * (4 * w.dv * w.dk + p0 * ent + w.T * ent
+                        + w.T * (2 * es * w.dk / G + 2 * es * w.dv + 8))
+    fb = live * w.Hv * (8 * w.dv * w.dk + pf * ent)
+    log(f"verify T={w.T}: {mv * 1e3:.2f} us/launch ({vb / mv / 1e6:.0f} GB/s); "
+        f"fold p={pf}: {mf * 1e3:.2f} us/call incl. cursor fill+reset ({fb / mf / 1e6:.0f} GB/s)")
+    return dict(verify_kernel_us=mv * 1e3, verify_gbs=vb / mv / 1e6,
+                verify_head_tokens_per_s=live * w.Hv * w.T / (mv / 1e3),
+                fold_call_us=mf * 1e3, fold_gbs=fb / mf / 1e6, window_p=p0, fold_p=pf)
+
+
+def cpu_baseline(w, budget_s, log):
+    """The CPU oracle (sequential fp64 recurrence, single thread) on a bounded
+    sample of the same workload: the c2 batch for as many steps as fit in
+    the time budget."""
+    import oracle
+    S = gi.initial_state(w).astype(np.float64)
+    slots = gi.slot_map(w)
+    live = int(np.count_nonzero(slots >= 0))
+    xs = [gi.step_inputs(w, i) for i in range(4)]
+    x64 = [tuple(a[:, 0] for a in x.f64()) for x in xs]
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gdn_step(S, slots, *x64[n % 4])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    hs = live * w.Hv * n / el
+    log(f"cpu oracle: {n} steps of {live}x{w.Hv} head-steps in {el:.1f} s -> {hs:.0f} head-steps/s")
+    return dict(value=hs, unit="head-steps/s", cores=1, kind="oracle",
+                sample=f"{n} decode steps of the B={live} x Hv={w.Hv} (dk=dv={w.dk}) batch "
+                       f"through the fp64 sequential recurrence, single thread, {el:.1f} s")
+
+
+def copy_probe(dev, log):
+    import torch
+    n = 1 << 28                                     # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 copies of {n * 4} bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs on a single MI355X and has "
+              "no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    import linear_attention_ssm_amd  # noqa: F401  (fails loudly if the library is missing)
+    if args.copy_probe:
+        copy_probe(dev, log)
+        return
+    w = gi.C2
+    R = args.layers
+    steps, warmup = args.steps, args.warmup
+    if args.profile_pass:
+        steps, warmup = 4, 16
+    rep = bench_replay(w, R, steps, warmup, dev, log)
+    pk = bench_packed(w, R, steps, dev, log)
+    wf = bench_window_fold(gi.C5, R, max(4, steps // 8), dev, log)
+    if args.profile_pass:
+        return
+    achieved = rep["bytes_per_launch"] / (rep["kernel_ms"] / 1e3) / 1e9
+    traffic = load_traffic("replay_decode_c2_hbm_traffic.txt")
+    out = {
+        "metric": METRIC,
+        "value": rep["head_steps_per_s"],
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": rep["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"ReplaySSM GDN single-token decode, B={w.B} rows, Hv={w.Hv}, Hk={w.Hk}, "
+                         f"dk=dv={w.dk}, ring L={w.L}, fp32 checkpoint, bf16 q/k/v/o, fp16 d/k "
+                         f"ring (fp16 MFMA operands), staggered cursors; one step = {R} layers "
+                         f"x gdn_replay_decode + 1 gdn_replay_advance"),
+            "global_batch": w.B, "layers_per_step": R, "ring_L": w.L,
+            "head_steps_per_launch": rep["head_steps_per_launch"],
+            "mean_valid_entries": round(rep["mean_p"], 3),
+            "flush_fraction": round(rep["flush_frac"], 4),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "kernel": "replay_decode_kernel<128, bf16, f16>",
+            "kernel_us": rep["kernel_ms"] * 1e3,
+            "algorithmic_bytes_per_launch": rep["bytes_per_launch"],
+        },
+        "packed_baseline": {
+            "head_steps_per_s": pk["head_steps_per_s"], "ms_per_step": pk["ms_per_step"],
+            "kernel_us": pk["kernel_ms"] * 1e3,
+            "achieved_gbs": pk["bytes_per_launch"] / (pk["kernel_ms"] / 1e3) / 1e9,
+            "frac": pk["bytes_per_launch"] / (pk["kernel_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_launch": pk["bytes_per_launch"],
+        },
+        "replay_vs_packed": rep["head_steps_per_s"] / pk["head_steps_per_s"],
+        "verify_window_c5": wf,
+        "cpu_baseline": None,
+        "kernel_sources_sha256_16": kernel_hash(),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, log)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

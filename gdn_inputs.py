@@ -202,10 +202,10 @@ def step_inputs(w: Workload, step: int, B: Optional[int] = None,
 
 
 def force_flush_schedule(w: Workload, step: int, slots: np.ndarray) -> np.ndarray:
-    """[B] uint8. With stagger on, slot s is forced to flush at step s mod L
+    """[B] int32 flags. With stagger on, slot s is forced to flush at step s mod L
     during the first L steps, which spreads the flush phases of the slots
     evenly over the ring cycle; afterwards no row is forced."""
-    ff = np.zeros(slots.shape[0], dtype=np.uint8)
+    ff = np.zeros(slots.shape[0], dtype=np.int32)
     if w.stagger and step < w.L:
         ff[(slots >= 0) & ((slots % w.L) == step)] = 1
     return ff

@@ -40,7 +40,7 @@
  *   ring_g         [N, Hv, L]       fp32        (log-decays)
  *   write_pos      [N]              int32, number of valid ring entries
  *   slot_idx       [B]              int32, row -> slot, negative = padding
- *   force_flush    [B]              uint8, nullable
+ *   force_flush    [B]              int32, nullable (nonzero = force a flush)
  *   accepted       [B]              int32
  * Value head h uses key head h / (Hv / Hk).
  *
@@ -133,14 +133,14 @@ gdn_status gdn_packed_decode(const gdn_shape *shape, const void *q, const void *
  *   ckpt           (device) fp32 [N, Hv, dv, dk]; written only on a flush.
  *   ring_d/k/g     (device) read at positions < p, written as described.
  *   write_pos      (device) int32 [N], read only.
- *   force_flush    (device) uint8 [B] or NULL.
+ *   force_flush    (device) int32 [B] or NULL; nonzero forces a flush.
  *   o              (device) [B, T, Hv, dv], written for every row.
  */
 gdn_status gdn_replay_decode(const gdn_shape *shape, const void *q, const void *k,
                              const void *v, const float *g, const float *beta,
                              const int32_t *slot_idx, float *ckpt, void *ring_d,
                              void *ring_k, float *ring_g, const int32_t *write_pos,
-                             const uint8_t *force_flush, void *o, int32_t *err_flags,
+                             const int32_t *force_flush, void *o, int32_t *err_flags,
                              void *stream);
 
 /*
@@ -152,7 +152,7 @@ gdn_status gdn_replay_decode(const gdn_shape *shape, const void *q, const void *
  * A cursor outside [0, L-1] is left as is and sets GDN_EF_CURSOR_RANGE.
  */
 gdn_status gdn_replay_advance(const gdn_shape *shape, const int32_t *slot_idx,
-                              int32_t *write_pos, const uint8_t *force_flush,
+                              int32_t *write_pos, const int32_t *force_flush,
                               int32_t *err_flags, void *stream);
 
 /*

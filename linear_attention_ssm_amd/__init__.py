@@ -171,7 +171,7 @@ def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, 
     B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
     N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev)
     if force_flush is not None:
-        _check(force_flush, "force_flush", torch.uint8, 1, dev)
+        _check(force_flush, "force_flush", torch.int32, 1, dev)
         if force_flush.shape != (B,):
             raise ValueError("force_flush must be [B]")
     if err_flags is not None:
@@ -190,7 +190,7 @@ def gdn_replay_advance(slot_idx, write_pos, L, force_flush=None, err_flags=None,
     _check(slot_idx, "slot_idx", torch.int32, 1)
     _check(write_pos, "write_pos", torch.int32, 1, slot_idx.device)
     if force_flush is not None:
-        _check(force_flush, "force_flush", torch.uint8, 1, slot_idx.device)
+        _check(force_flush, "force_flush", torch.int32, 1, slot_idx.device)
     sh = gdn_shape(slot_idx.shape[0], 1, write_pos.shape[0], 1, 1, 32, 16, int(L), 0, 0, 0)
     _raise(_lib.gdn_replay_advance(ctypes.byref(sh), _ptr(slot_idx), _ptr(write_pos),
                                    _ptr(force_flush), _ptr(err_flags), _stream(stream)),

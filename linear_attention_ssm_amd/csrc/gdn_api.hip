@@ -96,10 +96,37 @@ hipError_t dispatch_fold(int dk, const FoldArgs& a, int ring, dim3 g, dim3 b, si
 void fill_decode_geometry(const gdn_shape* s, DecodeArgs& a, dim3& grid, dim3& block) {
   a.B = s->B; a.T = s->T; a.N = s->N; a.Hv = s->Hv; a.Hk = s->Hk; a.dv = s->dv; a.L = s->L;
   a.G = s->Hv / s->Hk;
+  a.GH = a.G;
+  a.nhc = 1;
   a.VB = pick_vb(s->dv, a.G);
   a.nvb = s->dv / a.VB;
   grid = dim3(static_cast<unsigned>(s->B) * s->Hk * a.nvb);
   block = dim3(64u * a.G * (a.VB / 16));
+}
+
+// Work-item geometry of the persistent replay kernel: GH value heads (a
+// divisor of G) times VB value rows per item, one wavefront per 16 rows of
+// one head, at most 8 wavefronts (GDN_REPLAY_WAVES, default 4).
+void fill_replay_geometry(const gdn_shape* s, DecodeArgs& a, dim3& block, int& n_items) {
+  static const int tw = [] {
+    const char* e = std::getenv("GDN_REPLAY_WAVES");
+    int v = e ? std::atoi(e) : 4;
+    return v < 1 ? 1 : (v > 8 ? 8 : v);
+  }();
+  a.B = s->B; a.T = s->T; a.N = s->N; a.Hv = s->Hv; a.Hk = s->Hk; a.dv = s->dv; a.L = s->L;
+  a.G = s->Hv / s->Hk;
+  int gh = 1;
+  for (int d = 1; d <= a.G; ++d)
+    if (a.G % d == 0 && d <= tw) gh = d;
+  a.GH = gh;
+  a.nhc = a.G / gh;
+  int vb = 16;
+  for (int v = 16; v <= s->dv; v += 16)
+    if (s->dv % v == 0 && gh * (v / 16) <= tw) vb = v;
+  a.VB = vb;
+  a.nvb = s->dv / vb;
+  block = dim3(64u * gh * (vb / 16));
+  n_items = s->B * s->Hk * a.nhc * a.nvb;
 }
 
 }  // namespace
@@ -125,7 +152,8 @@ gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, c
   dim3 grid, block;
   fill_decode_geometry(s, a, grid, block);
   a.L = 1;
-  const size_t smem = 2u * s->dk * sizeof(float);
+  a.dump_off = static_cast<int32_t>(2u * s->dk * sizeof(float));
+  const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
   return from_hip(dispatch_packed(s->dk, a, s->qkv_dtype, grid, block, smem,
                                   static_cast<hipStream_t>(stream)));
 }
@@ -133,7 +161,7 @@ gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, c
 gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
                              const float* g, const float* beta, const int32_t* slot_idx,
                              float* ckpt, void* ring_d, void* ring_k, float* ring_g,
-                             const int32_t* write_pos, const uint8_t* force_flush, void* o,
+                             const int32_t* write_pos, const int32_t* force_flush, void* o,
                              int32_t* err_flags, void* stream) {
   const gdn_status st = check_shape(s, true);
   if (st != GDN_OK) return st;
@@ -148,15 +176,21 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(ckpt, 16) || !aligned(ring_k, 16) ||
       !aligned(ring_d, rs) || !aligned(v, es) || !aligned(o, es) || !aligned(g, 4) ||
       !aligned(beta, 4) || !aligned(ring_g, 4) || !aligned(write_pos, 4) ||
-      !aligned(slot_idx, 4) || (err_flags && !aligned(err_flags, 4)))
+      !aligned(slot_idx, 4) || (err_flags && !aligned(err_flags, 4)) ||
+      (force_flush && !aligned(force_flush, 4)))
     return GDN_ERR_INVALID_ARG;
   if (s->B == 0) return GDN_OK;
   DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.slot = slot_idx; a.state = ckpt;
   a.ring_d = ring_d; a.ring_k = ring_k; a.ring_g = ring_g; a.write_pos = write_pos;
   a.force_flush = force_flush; a.o = o; a.err = err_flags; a.window = s->window;
-  dim3 grid, block;
-  fill_decode_geometry(s, a, grid, block);
+  // the kernel reads one flag per row unconditionally; without
+  // force_flush it reads the slot array and ignores the value
+  a.ff_on = force_flush != nullptr;
+  a.ff_flags = force_flush ? force_flush : slot_idx;
+  dim3 block;
+  int n_items = 0;
+  fill_replay_geometry(s, a, block, n_items);
   size_t kt_bytes;
   if (s->ring_dtype == GDN_F32) {
     kt_bytes = static_cast<size_t>((s->L + 3) / 4 * 4) * s->dk * sizeof(float);
@@ -165,13 +199,16 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
     a.kts = (s->L + 15) / 16 * 16 + 4;
     kt_bytes = static_cast<size_t>(s->dk) * a.kts * 2;
   }
-  const size_t smem = static_cast<size_t>(s->T) * 2 * s->dk * sizeof(float) + kt_bytes;
-  return from_hip(dispatch_replay(s->dk, a, s->qkv_dtype, s->ring_dtype, grid, block, smem,
-                                  static_cast<hipStream_t>(stream)));
+  const size_t qk_bytes = static_cast<size_t>(s->T) * 2 * s->dk * sizeof(float);
+  a.lds_buf = static_cast<int32_t>((qk_bytes + kt_bytes + 15) / 16 * 16);
+  a.dump_off = a.lds_buf;
+  const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
+  return from_hip(dispatch_replay(s->dk, a, s->qkv_dtype, s->ring_dtype, dim3(n_items), block,
+                                  smem, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_replay_advance(const gdn_shape* s, const int32_t* slot_idx, int32_t* write_pos,
-                              const uint8_t* force_flush, int32_t* err_flags, void* stream) {
+                              const int32_t* force_flush, int32_t* err_flags, void* stream) {
   if (!s || s->B < 0 || s->N < 1 || s->L < 1 || s->L > 64) return GDN_ERR_INVALID_ARG;
   if (!slot_idx || !write_pos) return GDN_ERR_INVALID_ARG;
   if (!aligned(slot_idx, 4) || !aligned(write_pos, 4) || (err_flags && !aligned(err_flags, 4)))

@@ -62,6 +62,14 @@ __device__ __forceinline__ typename Elem<DT>::T from_f32(float x) {
   else return static_cast<_Float16>(x);
 }
 
+// A 16-bit element's bits as its storage type. The element arrives as a
+// scalar parameter: applying __builtin_bit_cast to a vector element
+// expression (v.y) directly reads element 0 with this compiler.
+template <int DT>
+__device__ __forceinline__ typename Elem<DT>::T from_bits(uint16_t e) {
+  return __builtin_bit_cast(typename Elem<DT>::T, e);
+}
+
 // Four consecutive elements starting at element `idx` (a multiple of 4) of a
 // 16-byte aligned array, widened to fp32.
 template <int DT>
@@ -71,17 +79,45 @@ __device__ __forceinline__ f4 load4(const void* base, size_t idx) {
   } else {
     const u16x4 r = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(base) + idx);
     f4 out;
-    if constexpr (DT == DT_BF16) {
-      out.x = bf16_to_f32(r.x); out.y = bf16_to_f32(r.y);
-      out.z = bf16_to_f32(r.z); out.w = bf16_to_f32(r.w);
-    } else {
-      out.x = static_cast<float>(__builtin_bit_cast(_Float16, r.x));
-      out.y = static_cast<float>(__builtin_bit_cast(_Float16, r.y));
-      out.z = static_cast<float>(__builtin_bit_cast(_Float16, r.z));
-      out.w = static_cast<float>(__builtin_bit_cast(_Float16, r.w));
-    }
+    out.x = to_f32<DT>(from_bits<DT>(r[0]));
+    out.y = to_f32<DT>(from_bits<DT>(r[1]));
+    out.z = to_f32<DT>(from_bits<DT>(r[2]));
+    out.w = to_f32<DT>(from_bits<DT>(r[3]));
     return out;
   }
+}
+
+// Raw (undecoded) loads: issue the memory access now, decode later, so the
+// wait for the data lands at the first use rather than at the load.
+template <int DT> struct Raw4 { using T = u16x4; };
+template <> struct Raw4<DT_F32> { using T = f4; };
+
+template <int DT>
+__device__ __forceinline__ typename Raw4<DT>::T load4_raw(const void* base, size_t idx) {
+  using R = typename Raw4<DT>::T;
+  if constexpr (DT == DT_F32)
+    return *reinterpret_cast<const R*>(static_cast<const float*>(base) + idx);
+  else
+    return *reinterpret_cast<const R*>(static_cast<const uint16_t*>(base) + idx);
+}
+
+template <int DT>
+__device__ __forceinline__ f4 decode4(typename Raw4<DT>::T r) {
+  if constexpr (DT == DT_F32) {
+    return r;
+  } else {
+    f4 out;
+    out.x = to_f32<DT>(from_bits<DT>(r[0]));
+    out.y = to_f32<DT>(from_bits<DT>(r[1]));
+    out.z = to_f32<DT>(from_bits<DT>(r[2]));
+    out.w = to_f32<DT>(from_bits<DT>(r[3]));
+    return out;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ typename Elem<DT>::T load1_raw(const void* base, size_t idx) {
+  return static_cast<const typename Elem<DT>::T*>(base)[idx];
 }
 
 template <int DT>
@@ -109,36 +145,89 @@ __device__ __forceinline__ void store4(void* base, size_t idx, f4 x) {
   }
 }
 
+// Load of a wave-uniform value that no kernel writes while it runs (slot
+// indices, cursors, flags, per-head gates): through the constant address
+// space it becomes a scalar-cache load, counted on lgkmcnt, so waiting for
+// it never waits for the vector loads (the state stream) issued before it.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p, size_t i) {
+  return ((const __attribute__((address_space(4))) T*)(p))[i];
+}
+
 // ------------------------------------------------------------- launch mapping
 
-// Workgroups are handed to the 8 XCDs round-robin by workgroup id. Remap the
-// id so that each XCD receives one contiguous range of logical blocks: the
-// blocks that share a row's key ring and q/k then meet in the same L2.
-__device__ __forceinline__ int xcd_remap(int i, int n) {
+// Workgroups are handed to the 8 XCDs round-robin by workgroup id. The work
+// items come in groups of gsz consecutive items that share a row's key side
+// (q, k and the key ring of one key head). Map workgroup ids so that all items
+// of a group run on one XCD (they meet in its L2) and consecutive groups go to
+// different XCDs: the groups of one row, and with them the checkpoint writes
+// of a flushing row, spread over all eight XCDs instead of piling up on one.
+// The last n_groups % 8 groups keep the identity mapping.
+__device__ __forceinline__ int item_of_block(int i, int n_items, int gsz) {
   constexpr int X = 8;
-  const int xcd = i % X, local = i / X, per = n / X, rem = n % X;
-  return xcd < rem ? xcd * (per + 1) + local
-                   : rem * (per + 1) + (xcd - rem) * per + local;
+  const int full = (n_items / gsz) / X * X;
+  if (i >= full * gsz) return i;
+  const int x = i % X, k = i / X;
+  return ((k / gsz) * X + x) * gsz + (k % gsz);
 }
 
 // ------------------------------------------------------------- wave reductions
 
-// Sum over the four column groups (lanes l, l^16, l^32, l^48). Every lane of
-// the quartet ends with the same bits (IEEE addition commutes exactly).
+// Sum over the four column groups (lanes l, l^16, l^32, l^48) with the
+// gfx950 row-swap instructions: v_permlane16_swap hands each lane the lower
+// and the upper row of its row pair, v_permlane32_swap the lower and upper
+// half of the wave. Both partners add the two in the same order, so every
+// lane of a quartet ends with identical bits.
 __device__ __forceinline__ float quad_sum(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-// Inclusive suffix sum over the 64 lanes: lane j receives sum_{i >= j} x_i.
-__device__ __forceinline__ float wave_suffix_sum(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_down(x, off, 64);
-    if (lane + off < 64) x += y;
+// x from lane l + n of the same 16-lane row (0 past the row end), by DPP.
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xf, 0xf,
+                                                    false));
+}
+
+// Inclusive suffix sum over the 64 lanes (lane j receives sum_{i >= j} x_i)
+// and the exclusive one (lane j receives sum_{i > j} x_i). Within a 16-lane
+// row: four DPP row shifts; across rows (only when entries live in more than
+// one row, i.e. more than 16 of them): the row totals through scalar reads.
+__device__ __forceinline__ void wave_suffix_sums(float x, int lane, bool multi_row, float& incl,
+                                                 float& excl) {
+  x += row_shl<1>(x);
+  x += row_shl<2>(x);
+  x += row_shl<4>(x);
+  x += row_shl<8>(x);
+  if (multi_row) {
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    const int row = lane >> 4;
+    const float after = row == 0 ? r1 + (r2 + r3) : row == 1 ? r2 + r3 : row == 2 ? r3 : 0.f;
+    x += after;
+    // the first lane of the next row now holds the sum of everything after
+    // this row: the exclusive sum of a row's last lane
+    const float n1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float n2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float n3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    const float nxt = row == 0 ? n1 : row == 1 ? n2 : row == 2 ? n3 : 0.f;
+    incl = x;
+    // one DPP move, all lanes active: lane l takes lane l+1 of its row; the
+    // last lane of a row has no source in the row and keeps `nxt` (bound_ctrl
+    // off). A select here could turn into a divergent branch, and a DPP read
+    // from a lane switched off in EXEC does not see that lane's value.
+    excl = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(nxt), __float_as_int(x),
+                                                      0x101, 0xf, 0xf, false));
+  } else {
+    incl = x;
+    excl = row_shl<1>(x);
   }
-  return x;
 }
 
 // ------------------------------------------------------------- readout
@@ -173,9 +262,13 @@ __device__ __forceinline__ void slab_dots(const f4 (&S)[NT], const float* q_l,
   kq = quad_sum(pkq);
 }
 
-// alpha = exp(g) evaluated in double and rounded once to fp32: the same value
-// the checkpoint fold uses for a ring entry's decay.
-__device__ __forceinline__ float decay_of(float g) {
+// alpha = exp(g) of the current token (single precision hardware exp; the
+// decode results are held to a tolerance, the fold pins its own decay).
+__device__ __forceinline__ float decay_of(float g) { return __expf(g); }
+
+// alpha = exp(g) of a ring entry in the fold: evaluated in double and rounded
+// once to fp32, so that the fold is bit-reproducible against a reference.
+__device__ __forceinline__ float fold_decay_of(float g) {
   return static_cast<float>(exp(static_cast<double>(g)));
 }
 
@@ -223,20 +316,26 @@ struct DecodeArgs {
   void* ring_k;
   float* ring_g;
   const int32_t* write_pos;
-  const uint8_t* force_flush;
+  const int32_t* force_flush;
+  const int32_t* ff_flags;  // force_flush, or any readable [B] int32 when ff_on == 0
+  int32_t ff_on;
   void* o;
   int32_t* err;
   int32_t B, T, N, Hv, Hk, dv, L;
   int32_t G;               // Hv / Hk
-  int32_t VB;              // value rows per head per workgroup (multiple of 16)
+  int32_t GH;              // value heads per work item (divides G)
+  int32_t nhc;             // G / GH head chunks per key head
+  int32_t VB;              // value rows per head per work item (multiple of 16)
   int32_t nvb;             // dv / VB
   int32_t window;          // 1: verify window (no flush, entries at p..p+T-1)
   int32_t kts;             // LDS row stride (elements) of the transposed key ring
+  int32_t dump_off;        // LDS byte offset of the [64][8] fp32 write sink
+  int32_t lds_buf;         // bytes of one LDS staging buffer (replay: two, by item parity)
 };
 
 struct CursorArgs {
   const int32_t* slot;
-  const uint8_t* force_flush;
+  const int32_t* force_flush;
   const int32_t* accepted;
   int32_t* write_pos;
   int32_t* err;

@@ -9,6 +9,8 @@
 // the key entries).
 #pragma once
 
+#include <type_traits>
+
 #include "gdn_device.h"
 
 namespace gdn {
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4, col = lane & 15;
-  int blk = xcd_remap(blockIdx.x, gridDim.x);
+  int blk = item_of_block(blockIdx.x, gridDim.x, a.nvb);
   const int vb = blk % a.nvb;
   blk /= a.nvb;
   const int hk = blk % a.Hk;
@@ -63,23 +65,41 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   const int h = hk * a.G + wave / wph;
   const int vcol = vb * a.VB + (wave % wph) * 16 + col;
 
-  const int s = a.slot[b];
+  const int s = ld_uniform(a.slot, b);
   if (s < 0 || s >= a.N) {
     if (s >= a.N && threadIdx.x == 0 && a.err) atomicOr(a.err, EF_SLOT);
     zero_rows<QKV>(a, b, h, vcol, grp);
     return;
   }
 
+  // small loads first (raw, unconditional), then the state stream; the
+  // q/k decode and LDS staging then overlap the state loads in flight
+  constexpr int C4 = DK / 4;
+  const int tid = threadIdx.x;
+  const int cq = tid < C4 ? tid : C4 - 1;
+  const size_t qsrc = (static_cast<size_t>(b) * a.Hk + hk) * DK + cq * 4;
+  const auto q_raw = load4_raw<QKV>(a.q, qsrc);
+  const auto k_raw = load4_raw<QKV>(a.k, qsrc);
+  const size_t ih = static_cast<size_t>(b) * a.Hv + h;
+  const auto v_raw = load1_raw<QKV>(a.v, ih * a.dv + vcol);
+  const float gv = ld_uniform(a.g, ih), bt = ld_uniform(a.beta, ih);
+
   float* st = a.state + ((static_cast<size_t>(s) * a.Hv + h) * a.dv + vcol) * DK + 4 * grp;
   f4 S[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) S[t] = *reinterpret_cast<const f4*>(st + 16 * t);
 
-  const size_t ih = static_cast<size_t>(b) * a.Hv + h;
-  const float vv = load1<QKV>(a.v, ih * a.dv + vcol);
-  const float gv = a.g[ih], bt = a.beta[ih];
-  stage_qk<DK, QKV>(a, qk, b, hk);
+  {
+    // unconditional writes (surplus threads into the dump area) keep the
+    // early q/k loads ahead of the state loads
+    float* dump = reinterpret_cast<float*>(smem + a.dump_off);
+    float* qdst = tid < C4 ? qk + 4 * tid : dump + lane * 8;
+    float* kdst = tid < C4 ? qk + DK + 4 * tid : dump + lane * 8 + 4;
+    *reinterpret_cast<f4*>(qdst) = decode4<QKV>(q_raw);
+    *reinterpret_cast<f4*>(kdst) = decode4<QKV>(k_raw);
+  }
   __syncthreads();
+  const float vv = to_f32<QKV>(v_raw);
 
   float sq, sk, kq, d, o;
   slab_dots<NT>(S, qk, qk + DK, grp, sq, sk, kq);
@@ -96,19 +116,22 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
 // ReplaySSM output-only decode (window == 0, T == 1) and verify window
 // (window == 1). See gdn_replay.h for the contract.
 //
-// Steps per workgroup:
-//   1. resolve the row: slot, p = write_pos[slot], flush flag;
-//   2. load the checkpoint slab into registers (16-byte loads, issued early);
-//   3. stage q/k of the T tokens and the key ring (positions < p, zero beyond)
-//      into LDS, the key ring transposed to [key][entry] for the MFMA A operand;
-//   4. per wavefront: suffix-sum the ring's log-decays with a wave scan,
-//      A = exp(sum g), w_j = exp(sum_{i>j} g_i); build the B operand
-//      w_j * d_j[v] in the ring dtype;
-//   5. S = A * S0 (in registers), then S += K^T (w o D) on the MFMA units,
-//      one 16x16 tile per 16 keys, accumulated in place;
-//   6. per token: Sq, Sk, k^T q -> d, o; store o; append the ring entry
-//      (non-flush) or update the slab on chip (window tokens, flush);
-//   7. on a flush, write the updated slab to the checkpoint.
+// One workgroup per work item (row, key head, head chunk, value block); one
+// wavefront per 16 value rows of one head. Per item:
+//   fetch:   the cursor, the flush flag and the gates (scalar loads), q/k, one
+//            key-ring chunk per thread, the wave's ring d entries and g, v (all
+//            unconditional, clamped into their buffers), then the 16-row
+//            checkpoint slab in 16-byte loads straight into accumulator layout;
+//   process: stage q/k and the key ring (transposed to [key][entry] for the
+//            MFMA A operand) in LDS; suffix-
+//            sum the ring's log-decays with a wave scan, A = exp(sum g),
+//            w_j = exp(sum_{i>j} g_i); S = A*S0 + K^T (w o D) on the MFMA units;
+//            per token Sq, Sk, k^T q -> d, o; append the ring entry (non-flush)
+//            or update the slab on chip (window tokens, flush) and write it to
+//            the checkpoint on a flush.
+// The small operands are requested before the slab: vector loads retire in
+// issue order, so the staging and the MFMA operand build can proceed while
+// the slab is still in flight.
 template <int RING> struct RingMfma;
 
 template <> struct RingMfma<DT_F16> {
@@ -133,151 +156,260 @@ template <> struct RingMfma<DT_F32> {
   }
 };
 
+// Where a work item sits, and which head / value row this lane holds in it.
+struct ItemGeo {
+  int b, hk, hc, vb, h, vcol;
+};
+
+__device__ __forceinline__ ItemGeo item_geo(const DecodeArgs& a, int item, int wave, int col) {
+  ItemGeo g;
+  g.vb = item % a.nvb;
+  int r = item / a.nvb;
+  g.hc = r % a.nhc;
+  r /= a.nhc;
+  g.hk = r % a.Hk;
+  g.b = r / a.Hk;
+  const int wph = a.VB / 16;                    // wavefronts per head
+  g.h = g.hk * a.G + g.hc * a.GH + wave / wph;
+  g.vcol = g.vb * a.VB + (wave % wph) * 16 + col;
+  return g;
+}
+
+// The small operands of one item, as raw (undecoded) registers.
 template <int DK, int QKV, int RING>
-__global__ __launch_bounds__(1024) void replay_decode_kernel(DecodeArgs a) {
+struct Small {
+  using RT = typename Elem<RING>::T;
+  using KC = f4;                                   // 16 bytes of the key ring
+  static constexpr int KV = 16 / sizeof(RT);        // ring elements per chunk
+  int p_raw, ff_raw;
+  float g_pre, b_pre;
+  typename Raw4<QKV>::T q_raw, k_raw;
+  KC kr_raw[2];                                    // chunks tid and tid + blockDim
+  float g_raw;
+  RT d_raw[4];
+  typename Elem<QKV>::T v_raw;
+};
+
+// Request an item's small operands: the cursor, the flush flag and the gates
+// (scalar loads), q/k, one key-ring chunk per thread, the lane's ring d
+// entries and g, v. Every load is unconditional, from an address clamped into
+// its buffer; an invalid slot (padding / out of range) is masked in process().
+template <int DK, int QKV, int RING>
+__device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const DecodeArgs& a,
+                                            const ItemGeo& g, int s, int tid, int lane,
+                                            int grp) {
+  constexpr int C4 = DK / 4;
+  constexpr bool RF32 = (RING == DT_F32);
+  using RT = typename Elem<RING>::T;
+  using KC = typename Small<DK, QKV, RING>::KC;
+  const int sc = (s >= 0 && s < a.N) ? s : 0;
+  const size_t hs = static_cast<size_t>(sc) * a.Hv + g.h;
+  const size_t ks = static_cast<size_t>(sc) * a.Hk + g.hk;
+  f.p_raw = ld_uniform(a.write_pos, sc);
+  f.ff_raw = ld_uniform(a.ff_flags, g.b);
+  const size_t ih0 = static_cast<size_t>(g.b) * a.T * a.Hv + g.h;   // token 0
+  f.g_pre = ld_uniform(a.g, ih0);
+  f.b_pre = ld_uniform(a.beta, ih0);
+  const int nqk = a.T * C4;
+  const int cq = tid < nqk ? tid : nqk - 1;
+  const size_t qsrc = ((static_cast<size_t>(g.b) * a.T + cq / C4) * a.Hk + g.hk) * DK + (cq % C4) * 4;
+  f.q_raw = load4_raw<QKV>(a.q, qsrc);
+  f.k_raw = load4_raw<QKV>(a.k, qsrc);
+  constexpr int KV = Small<DK, QKV, RING>::KV;
+  const RT* ksrc = static_cast<const RT*>(a.ring_k) + ks * a.L * DK;
+  const int nkc = a.L * (DK / KV);                  // 16-byte chunks in a full ring
+  const int c0 = tid < nkc ? tid : nkc - 1;
+  const int c1 = tid + static_cast<int>(blockDim.x) < nkc ? tid + static_cast<int>(blockDim.x) : nkc - 1;
+  f.kr_raw[0] = *reinterpret_cast<const KC*>(ksrc + c0 * KV);
+  f.kr_raw[1] = *reinterpret_cast<const KC*>(ksrc + c1 * KV);
+  const int Lm1 = a.L - 1;
+  f.g_raw = a.ring_g[hs * a.L + (lane < a.L ? lane : Lm1)];
+  // this lane's ring d entries 0..15: 16-bit rings j = 4*grp + i (one
+  // 16x16x16 k-step), fp32 rings j = 4*i + grp (four 16x16x4 k-steps)
+  const RT* dsrc = static_cast<const RT*>(a.ring_d) + hs * a.L * a.dv + g.vcol;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = RF32 ? (4 * i + grp) : (4 * grp + i);
+    f.d_raw[i] = dsrc[static_cast<size_t>(j < a.L ? j : Lm1) * a.dv];
+  }
+  f.v_raw = load1_raw<QKV>(a.v, ih0 * a.dv + g.vcol);
+}
+
+// Request an item's 16-row checkpoint slab: 16-byte loads straight into the
+// accumulator layout.
+template <int DK>
+__device__ __forceinline__ void fetch_slab(f4 (&S)[DK / 16], const DecodeArgs& a,
+                                           const ItemGeo& g, int s, int grp) {
+  const int sc = (s >= 0 && s < a.N) ? s : 0;
+  const size_t hs = static_cast<size_t>(sc) * a.Hv + g.h;
+  const float* ck = a.state + (hs * a.dv + g.vcol) * DK + 4 * grp;
+#pragma unroll
+  for (int t = 0; t < DK / 16; ++t) S[t] = *reinterpret_cast<const f4*>(ck + 16 * t);
+}
+
+template <int DK, int QKV, int RING>
+__device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, int s,
+                                        const Small<DK, QKV, RING>& f, f4 (&S)[DK / 16],
+                                        unsigned char* buf, float* dump, int tid, int lane,
+                                        int grp, int col, int wave) {
   constexpr int NT = DK / 16;
   constexpr int C4 = DK / 4;
   using RT = typename Elem<RING>::T;
   using MM = RingMfma<RING>;
+  using KC = typename Small<DK, QKV, RING>::KC;
   constexpr int CH = MM::CH;
   constexpr bool RF32 = (RING == DT_F32);
+  const int nthr = blockDim.x;
+  float* qk = reinterpret_cast<float*>(buf);
+  RT* kt = reinterpret_cast<RT*>(buf + static_cast<size_t>(a.T) * 2 * DK * sizeof(float));
 
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* qk = reinterpret_cast<float*>(smem);
-  RT* kt = reinterpret_cast<RT*>(smem + static_cast<size_t>(a.T) * 2 * DK * sizeof(float));
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = lane >> 4, col = lane & 15;
-  int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int vb = blk % a.nvb;
-  blk /= a.nvb;
-  const int hk = blk % a.Hk;
-  const int b = blk / a.Hk;
-  const int wph = a.VB / 16;
-  const int h = hk * a.G + wave / wph;
-  const int vcol = vb * a.VB + (wave % wph) * 16 + col;
-
-  // ---- 1. row resolve
-  const int s = a.slot[b];
-  if (s < 0 || s >= a.N) {
-    if (s >= a.N && threadIdx.x == 0 && a.err) atomicOr(a.err, EF_SLOT);
-    zero_rows<QKV>(a, b, h, vcol, grp);
-    return;
-  }
-  const int p = a.write_pos[s];
-  const int ef = a.window ? ((p < 0 || p + a.T > a.L) ? EF_WINDOW : 0)
-                          : ((p < 0 || p > a.L - 1) ? EF_CURSOR : 0);
-  if (ef) {
-    if (threadIdx.x == 0 && a.err) atomicOr(a.err, ef);
-    zero_rows<QKV>(a, b, h, vcol, grp);
-    return;
-  }
-  const bool flush = !a.window &&
-                     (p == a.L - 1 || (a.force_flush != nullptr && a.force_flush[b] != 0));
+  // ---- row resolve: a padding row (negative slot), a slot beyond the pool
+  // or a cursor out of range runs masked with an empty ring: zero output,
+  // no state or ring write
+  const bool slot_ok = (s >= 0 && s < a.N);
+  int ef = (s >= a.N) ? EF_SLOT : 0;
+  if (slot_ok)
+    ef = a.window ? ((f.p_raw < 0 || f.p_raw + a.T > a.L) ? EF_WINDOW : 0)
+                  : ((f.p_raw < 0 || f.p_raw > a.L - 1) ? EF_CURSOR : 0);
+  const bool row_ok = slot_ok && ef == 0;
+  if (ef && tid == 0 && a.err) atomicOr(a.err, ef);
+  const int p = row_ok ? f.p_raw : 0;
   const int nch = (p + CH - 1) / CH;   // MFMA k-steps over the valid entries
   const int lp = nch * CH;             // entries covered, zero-padded beyond p
+  const int nqk = a.T * C4;
+  const int sc = slot_ok ? s : 0;
+  const size_t hs = static_cast<size_t>(sc) * a.Hv + g.h;
+  const size_t ks = static_cast<size_t>(sc) * a.Hk + g.hk;
 
-  const size_t hs = static_cast<size_t>(s) * a.Hv + h;            // (slot, head)
-  const size_t ks = static_cast<size_t>(s) * a.Hk + hk;           // (slot, k-head)
-
-  // ---- per-lane ring decay input (lane j < p holds g_j)
-  const float gj = (lane < p) ? a.ring_g[hs * a.L + lane] : 0.f;
-
-  // ---- 2. checkpoint slab
-  const float* ck = a.state + (hs * a.dv + vcol) * DK + 4 * grp;
-  f4 S[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) S[t] = *reinterpret_cast<const f4*>(ck + 16 * t);
-
-  // ---- 3. LDS staging: q/k of the window, the key ring
-  stage_qk<DK, QKV>(a, qk, b, hk);
+  // ---- LDS staging. Every thread writes (threads past the last chunk into a
+  // per-lane dump area) so the early loads have unconditional uses.
   {
-    const int total = p * C4;
-    const RT* src = static_cast<const RT*>(a.ring_k) + ks * a.L * DK;
-    for (int c = threadIdx.x; c < total; c += blockDim.x) {
-      const int j = c / C4, e4 = (c % C4) * 4;
-      if constexpr (RF32) {
-        *reinterpret_cast<f4*>(kt + j * DK + e4) =
-            *reinterpret_cast<const f4*>(src + static_cast<size_t>(j) * DK + e4);
-      } else {
-        const u16x4 r = *reinterpret_cast<const u16x4*>(src + static_cast<size_t>(j) * DK + e4);
-        uint16_t* kt16 = reinterpret_cast<uint16_t*>(kt);
-        kt16[(e4 + 0) * a.kts + j] = r.x;
-        kt16[(e4 + 1) * a.kts + j] = r.y;
-        kt16[(e4 + 2) * a.kts + j] = r.z;
-        kt16[(e4 + 3) * a.kts + j] = r.w;
+    const f4 qv = decode4<QKV>(f.q_raw), kv = decode4<QKV>(f.k_raw);
+    float* qdst = tid < nqk ? qk + ((tid / C4) * 2) * DK + (tid % C4) * 4 : dump + lane * 8;
+    float* kdst = tid < nqk ? qdst + DK : dump + lane * 8 + 4;
+    *reinterpret_cast<f4*>(qdst) = qv;
+    *reinterpret_cast<f4*>(kdst) = kv;
+  }
+  for (int c = tid + nthr; c < nqk; c += nthr) {        // long windows only
+    const int tau = c / C4, e4 = (c % C4) * 4;
+    const size_t src = ((static_cast<size_t>(g.b) * a.T + tau) * a.Hk + g.hk) * DK + e4;
+    *reinterpret_cast<f4*>(qk + (tau * 2 + 0) * DK + e4) = load4<QKV>(a.q, src);
+    *reinterpret_cast<f4*>(qk + (tau * 2 + 1) * DK + e4) = load4<QKV>(a.k, src);
+  }
+  const RT* ksrc = static_cast<const RT*>(a.ring_k) + ks * a.L * DK;
+  constexpr int KV = Small<DK, QKV, RING>::KV;      // ring elements per 16-byte chunk
+  constexpr int CPR = DK / KV;                      // chunks per ring entry
+  const int nkr = p * CPR;                          // chunks holding valid entries
+  // chunk c = entry j's keys e .. e+KV-1; 16-bit rings are stored transposed
+  auto put_kr = [&](int c, KC r, bool in) {
+    const int j = c / CPR, e = (c % CPR) * KV;
+    if constexpr (RF32) {
+      *reinterpret_cast<f4*>(in ? kt + j * DK + e : dump + lane * 8) = r;
+    } else {
+      const u16x4 lo = __builtin_bit_cast(u16x4, __builtin_shufflevector(r, r, 0, 1));
+      const u16x4 hi = __builtin_bit_cast(u16x4, __builtin_shufflevector(r, r, 2, 3));
+      uint16_t* kt16 = reinterpret_cast<uint16_t*>(kt);
+      uint16_t* d16 = reinterpret_cast<uint16_t*>(dump + lane * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *(in ? kt16 + (e + i) * a.kts + j : d16 + i) = lo[i];
+        *(in ? kt16 + (e + 4 + i) * a.kts + j : d16 + 4 + i) = hi[i];
       }
     }
-    const int pad = lp - p;   // zero the entries between p and the k-step edge
-    for (int c = threadIdx.x; c < pad * DK; c += blockDim.x) {
-      const int j = p + c / DK, key = c % DK;
-      if constexpr (RF32) kt[j * DK + key] = 0.f;
-      else reinterpret_cast<uint16_t*>(kt)[key * a.kts + j] = 0;
-    }
+  };
+  put_kr(tid, f.kr_raw[0], tid < nkr);
+  put_kr(tid + nthr, f.kr_raw[1], tid + nthr < nkr);
+  for (int c = tid + 2 * nthr; c < nkr; c += nthr)      // deep rings / small workgroups
+    put_kr(c, *reinterpret_cast<const KC*>(ksrc + c * KV), true);
+  for (int c = tid; c < (lp - p) * DK; c += nthr) {
+    const int j = p + c / DK, key = c % DK;
+    if constexpr (RF32) kt[j * DK + key] = 0.f;
+    else reinterpret_cast<uint16_t*>(kt)[key * a.kts + j] = 0;
   }
   __syncthreads();
 
-  // ---- 4./5. reconstruction S = A S0 + sum_j w_j d_j k_j^T
+  // ---- reconstruction S = A S0 + sum_j w_j d_j k_j^T
   if (p > 0) {
-    // Lanes >= p hold g = 0, so W_p = 0 exactly and lane p-1 reads
-    // W_{j+1} = 0 from its neighbour (p <= 63, so lane 63 never needs it).
-    const float W = wave_suffix_sum(gj, lane);          // W_j = sum_{i>=j} g_i
-    const float Wn = __shfl_down(W, 1, 64);             // W_{j+1}
-    const float wj = (lane < p) ? expf(Wn) : 0.f;       // w_j = exp(W_{j+1})
-    const float A = expf(__shfl(W, 0, 64));             // A = exp(W_0)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) S[t] *= A;
-    const RT* dsrc = static_cast<const RT*>(a.ring_d) + hs * a.L * a.dv + vcol;
-    for (int c = 0; c < nch; ++c) {
+    const float gj = lane < p ? f.g_raw : 0.f;          // lane j < p holds g_j
+    // Lanes >= p hold g = 0, so the exclusive sum of lane p-1 is exactly 0
+    // (empty product = 1).
+    float W, Wn;                                        // W_j = sum_{i>=j} g_i, W_{j+1}
+    wave_suffix_sums(gj, lane, p > 16, W, Wn);
+    const float wj = (lane < p) ? __expf(Wn) : 0.f;     // w_j = exp(W_{j+1})
+    const float A = __expf(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(W))));
+    const RT* dsrc = static_cast<const RT*>(a.ring_d) + hs * a.L * a.dv + g.vcol;
+    auto kstep = [&](int c, const float (&dval)[4]) {
       typename MM::op_t bop;
       if constexpr (RF32) {
         const int j = c * CH + grp;
-        const float w = __shfl(wj, j, 64);
-        bop = (j < p) ? w * dsrc[static_cast<size_t>(j) * a.dv] : 0.f;
+        bop = (j < p) ? __shfl(wj, j & 63, 64) * dval[0] : 0.f;
       } else {
         u16x4 bb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = c * CH + 4 * grp + i;
           const float w = __shfl(wj, j & 63, 64);
-          const float x = (j < p) ? w * to_f32<RING>(dsrc[static_cast<size_t>(j) * a.dv]) : 0.f;
-          bb[i] = __builtin_bit_cast(uint16_t, from_f32<RING>(x));
+          bb[i] = __builtin_bit_cast(uint16_t, from_f32<RING>((j < p) ? w * dval[i] : 0.f));
         }
         bop = __builtin_bit_cast(typename MM::op_t, bb);
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         typename MM::op_t aop;
-        if constexpr (RF32) {
-          aop = kt[(c * CH + grp) * DK + 16 * t + col];
-        } else {
-          aop = *reinterpret_cast<const typename MM::op_t*>(
-              kt + (16 * t + col) * a.kts + c * CH + 4 * grp);
-        }
+        if constexpr (RF32) aop = kt[(c * CH + grp) * DK + 16 * t + col];
+        else aop = *reinterpret_cast<const typename MM::op_t*>(kt + (16 * t + col) * a.kts +
+                                                              c * CH + 4 * grp);
         S[t] = MM::mma(aop, bop, S[t]);
       }
+    };
+#pragma unroll
+    for (int t = 0; t < NT; ++t) S[t] *= A;
+    constexpr int NPRE = RF32 ? 4 : 1;                  // k-steps covered by the fetch
+#pragma unroll
+    for (int c = 0; c < NPRE; ++c) {
+      if (c < nch) {
+        float dv1[4];
+        if constexpr (RF32) {
+          dv1[0] = (4 * c + grp < p) ? f.d_raw[c] : 0.f;
+          dv1[1] = dv1[2] = dv1[3] = 0.f;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dv1[i] = (4 * grp + i < p) ? to_f32<RING>(f.d_raw[i]) : 0.f;
+        }
+        kstep(c, dv1);
+      }
+    }
+    for (int c = NPRE; c < nch; ++c) {                  // rings deeper than 16 entries
+      float dv1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = RF32 ? (c * CH + grp) : (c * CH + 4 * grp + i);
+        dv1[i] = (j < p && (!RF32 || i == 0)) ? to_f32<RING>(dsrc[static_cast<size_t>(j) * a.dv]) : 0.f;
+      }
+      kstep(c, dv1);
     }
   }
 
-  // ---- 6. tokens
-  const bool kwriter = (vb == 0) && (wave == 0);        // one key-ring writer per k-head
-  const bool gwriter = (vb == 0) && (wave % wph == 0) && lane == 0;
+  // ---- tokens
+  const bool flush = row_ok && !a.window && (p == a.L - 1 || (a.ff_on && f.ff_raw != 0));
+  const int wph = a.VB / 16;
+  const bool kwriter = (g.vb == 0) && (g.hc == 0) && (wave == 0);   // one key-ring writer per k-head
+  const bool gwriter = (g.vb == 0) && (wave % wph == 0) && lane == 0;
   for (int tau = 0; tau < a.T; ++tau) {
     const float* ql = qk + tau * 2 * DK;
     const float* kl = ql + DK;
-    const size_t ih = (static_cast<size_t>(b) * a.T + tau) * a.Hv + h;
-    const float vv = load1<QKV>(a.v, ih * a.dv + vcol);
-    const float gv = a.g[ih], bt = a.beta[ih];
+    const size_t ih = (static_cast<size_t>(g.b) * a.T + tau) * a.Hv + g.h;
+    const float vv = tau == 0 ? to_f32<QKV>(f.v_raw) : load1<QKV>(a.v, ih * a.dv + g.vcol);
+    const float gv = tau == 0 ? f.g_pre : ld_uniform(a.g, ih);
+    const float bt = tau == 0 ? f.b_pre : ld_uniform(a.beta, ih);
     float sq, sk, kq, d, o;
     slab_dots<NT>(S, ql, kl, grp, sq, sk, kq);
     const float alpha = decay_of(gv);
     token_out(sq, sk, kq, alpha, bt, vv, d, o);
-    if (grp == 0) store1<QKV>(a.o, ih * a.dv + vcol, o);
-    if (!flush) {
+    if (grp == 0) store1<QKV>(a.o, ih * a.dv + g.vcol, row_ok ? o : 0.f);
+    if (row_ok && !flush) {
       const int pos = p + tau;
-      if (grp == 0)
-        store1<RING>(a.ring_d, (hs * a.L + pos) * a.dv + vcol, d);
+      if (grp == 0) store1<RING>(a.ring_d, (hs * a.L + pos) * a.dv + g.vcol, d);
       if (gwriter) a.ring_g[hs * a.L + pos] = gv;
       if (kwriter && lane < C4) {
         const f4 kv = *reinterpret_cast<const f4*>(kl + 4 * lane);
@@ -286,13 +418,30 @@ __global__ __launch_bounds__(1024) void replay_decode_kernel(DecodeArgs a) {
     }
     if (flush || (a.window && tau + 1 < a.T)) slab_update<NT>(S, kl, grp, alpha, d);
   }
-
-  // ---- 7. flush: the updated slab becomes the checkpoint
   if (flush) {
-    float* cw = a.state + (hs * a.dv + vcol) * DK + 4 * grp;
+    float* cw = a.state + (hs * a.dv + g.vcol) * DK + 4 * grp;
 #pragma unroll
     for (int t = 0; t < NT; ++t) *reinterpret_cast<f4*>(cw + 16 * t) = S[t];
   }
+}
+
+template <int DK, int QKV, int RING>
+__global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* dump = reinterpret_cast<float*>(smem + a.lds_buf);   // [64][8] write sink
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4, col = lane & 15;
+  const int item = item_of_block(blockIdx.x, gridDim.x, a.nhc * a.nvb);
+  const ItemGeo g = item_geo(a, item, wave, col);
+  const int s = ld_uniform(a.slot, g.b);
+  Small<DK, QKV, RING> sm;
+  f4 S[DK / 16];
+  fetch_small(sm, a, g, s, tid, lane, grp);
+  __builtin_amdgcn_sched_barrier(0);
+  fetch_slab<DK>(S, a, g, s, grp);
+  process(a, g, s, sm, S, smem, dump, tid, lane, grp, col, wave);
 }
 
 // ============================================================= fold
@@ -311,7 +460,7 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   float* al = dl + a.L * FV;                          // [L]      decays
 
   const int nvb = a.dv / FV;
-  int blk = xcd_remap(blockIdx.x, gridDim.x);
+  int blk = item_of_block(blockIdx.x, gridDim.x, nvb * a.G);
   const int vb = blk % nvb;
   blk /= nvb;
   const int h = blk % a.Hv;
@@ -338,7 +487,7 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   float* xp = a.ckpt + (hs * a.dv + v) * DK + e4;
   f4 x = *reinterpret_cast<const f4*>(xp);
 
-  if (tid < p) al[tid] = decay_of(a.ring_g[hs * a.L + tid]);
+  if (tid < p) al[tid] = fold_decay_of(a.ring_g[hs * a.L + tid]);
   for (int c = tid; c < p * FV; c += blockDim.x) {
     const int j = c / FV, r = c % FV;
     dl[c] = to_f32<RING>(static_cast<const RT*>(a.ring_d)[(hs * a.L + j) * a.dv + vb * FV + r]);
