@@ -222,3 +222,53 @@ def gdn_replay_fold(slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags
     _raise(_lib.gdn_replay_fold(ctypes.byref(sh), _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d),
                                 _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(err_flags),
                                 _stream(stream)), "gdn_replay_fold")
+
+
+# ------------------------------------------------------------------ prepared calls
+
+class Prepared:
+    """A library call with its arguments checked and marshalled once, for
+    loops that issue the same call many times (a decode step per layer).
+    Calling it enqueues the kernels again on the stream it was prepared for;
+    the tensors must stay alive and keep their shapes."""
+
+    __slots__ = ("_fn", "_args", "_keep", "_name")
+
+    def __init__(self, fn, args, keep, name):
+        self._fn, self._args, self._keep, self._name = fn, args, keep, name
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != GDN_OK:
+            raise GdnError(st, self._name)
+
+
+def prepare_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
+                          force_flush=None, o=None, err_flags=None, window=False, stream=None):
+    """gdn_replay_decode with the same arguments, prepared for repeated calls.
+    Returns (call, o)."""
+    B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
+    N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev)
+    if force_flush is not None:
+        _check(force_flush, "force_flush", torch.int32, 1, dev)
+    o = _out(o, B, T, Hv, dv, q.dtype, dev)
+    sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)))
+    args = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
+            _ptr(ckpt), _ptr(ring_d), _ptr(ring_k), _ptr(ring_g), _ptr(write_pos),
+            _ptr(force_flush), _ptr(o), _ptr(err_flags), _stream(stream))
+    keep = (sh, q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
+            force_flush, o, err_flags)
+    return Prepared(_lib.gdn_replay_decode, args, keep, "gdn_replay_decode"), o
+
+
+def prepare_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None,
+                          stream=None):
+    """gdn_packed_decode prepared for repeated calls. Returns (call, o)."""
+    B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
+    _check(state, "state", torch.float32, 4, dev)
+    o = _out(o, B, T, Hv, dv, q.dtype, dev)
+    sh = gdn_shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0)
+    args = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
+            _ptr(state), _ptr(o), _ptr(err_flags), _stream(stream))
+    keep = (sh, q, k, v, g, beta, slot_idx, state, o, err_flags)
+    return Prepared(_lib.gdn_packed_decode, args, keep, "gdn_packed_decode"), o

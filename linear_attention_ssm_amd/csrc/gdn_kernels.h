@@ -191,9 +191,10 @@ struct Small {
 };
 
 // Request an item's small operands: the cursor, the flush flag and the gates
-// (scalar loads), q/k, one key-ring chunk per thread, the lane's ring d
-// entries and g, v. Every load is unconditional, from an address clamped into
-// its buffer; an invalid slot (padding / out of range) is masked in process().
+// (scalar loads), q/k, two 16-byte key-ring chunks per thread, the lane's
+// ring d entries and g, v. Every vector load is unconditional, from an
+// address clamped into its buffer (ring reads to the valid entries); an
+// invalid slot or cursor is masked in process().
 template <int DK, int QKV, int RING>
 __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const DecodeArgs& a,
                                             const ItemGeo& g, int s, int tid, int lane,
@@ -217,20 +218,23 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
   f.k_raw = load4_raw<QKV>(a.k, qsrc);
   constexpr int KV = Small<DK, QKV, RING>::KV;
   const RT* ksrc = static_cast<const RT*>(a.ring_k) + ks * a.L * DK;
-  const int nkc = a.L * (DK / KV);                  // 16-byte chunks in a full ring
+  // the cursor arrives through the scalar cache: waiting for it here does not
+  // wait for any vector load, and it bounds the ring reads to the valid
+  // entries (a cursor out of range is handled in process(); clamp meanwhile)
+  const int pc = (f.p_raw >= 1 && f.p_raw <= a.L) ? f.p_raw : 1;
+  const int nkc = pc * (DK / KV);                   // 16-byte chunks holding valid entries
   const int c0 = tid < nkc ? tid : nkc - 1;
   const int c1 = tid + static_cast<int>(blockDim.x) < nkc ? tid + static_cast<int>(blockDim.x) : nkc - 1;
   f.kr_raw[0] = *reinterpret_cast<const KC*>(ksrc + c0 * KV);
   f.kr_raw[1] = *reinterpret_cast<const KC*>(ksrc + c1 * KV);
-  const int Lm1 = a.L - 1;
-  f.g_raw = a.ring_g[hs * a.L + (lane < a.L ? lane : Lm1)];
+  f.g_raw = a.ring_g[hs * a.L + (lane < pc ? lane : pc - 1)];
   // this lane's ring d entries 0..15: 16-bit rings j = 4*grp + i (one
   // 16x16x16 k-step), fp32 rings j = 4*i + grp (four 16x16x4 k-steps)
   const RT* dsrc = static_cast<const RT*>(a.ring_d) + hs * a.L * a.dv + g.vcol;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int j = RF32 ? (4 * i + grp) : (4 * grp + i);
-    f.d_raw[i] = dsrc[static_cast<size_t>(j < a.L ? j : Lm1) * a.dv];
+    f.d_raw[i] = dsrc[static_cast<size_t>(j < pc ? j : pc - 1) * a.dv];
   }
   f.v_raw = load1_raw<QKV>(a.v, ih0 * a.dv + g.vcol);
 }
