@@ -302,6 +302,36 @@ __device__ __forceinline__ void slab_update(f4 (&S)[NT], const float* k_l, int g
   }
 }
 
+// Lane i of each 16-lane row receives lane i^8's value (DPP row_ror:8).
+__device__ __forceinline__ f4 row_swap8(f4 x) {
+  f4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[i]), 0x128, 0xf, 0xf, false));
+  return r;
+}
+
+// Store a wavefront's 16-row slab (accumulator layout: lane (row col, group
+// grp) holds keys 16t+4grp..+3 of tile t) so that every store instruction
+// writes whole 128-byte lines: rows col and col^8 trade halves of each tile
+// pair, then one instruction writes rows 0-7 and the next rows 8-15 of keys
+// 32u..32u+31. `row` points at this lane's row + 4*grp; rows are DK apart.
+// Needs all 64 lanes active.
+template <int NT>
+__device__ __forceinline__ void store_slab(float* row, const f4 (&S)[NT], int col) {
+  constexpr int DK = NT * 16;
+  const bool lo = col < 8;
+#pragma unroll
+  for (int u = 0; u < NT / 2; ++u) {
+    const f4 x0 = S[2 * u], x1 = S[2 * u + 1];
+    const f4 z = row_swap8(lo ? x1 : x0);
+    float* pa = lo ? row + 32 * u : row - 8 * DK + 32 * u + 16;
+    float* pb = lo ? row + 8 * DK + 32 * u : row + 32 * u + 16;
+    *reinterpret_cast<f4*>(pa) = lo ? x0 : z;
+    *reinterpret_cast<f4*>(pb) = lo ? z : x1;
+  }
+}
+
 // ------------------------------------------------------------- kernel args
 
 struct DecodeArgs {

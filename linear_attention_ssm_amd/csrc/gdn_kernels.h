@@ -107,8 +107,7 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   token_out(sq, sk, kq, alpha, bt, vv, d, o);
   if (grp == 0) store1<QKV>(a.o, ih * a.dv + vcol, o);
   slab_update<NT>(S, qk + DK, grp, alpha, d);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) *reinterpret_cast<f4*>(st + 16 * t) = S[t];
+  store_slab<NT>(st, S, col);
 }
 
 // ============================================================= replay decode
@@ -422,11 +421,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
     }
     if (flush || (a.window && tau + 1 < a.T)) slab_update<NT>(S, kl, grp, alpha, d);
   }
-  if (flush) {
-    float* cw = a.state + (hs * a.dv + g.vcol) * DK + 4 * grp;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) *reinterpret_cast<f4*>(cw + 16 * t) = S[t];
-  }
+  if (flush) store_slab<NT>(a.state + (hs * a.dv + g.vcol) * DK + 4 * grp, S, col);
 }
 
 template <int DK, int QKV, int RING>
