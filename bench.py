@@ -263,7 +263,7 @@ def bench_window_fold(w, R, steps, dev, log):
     p0 = w.L - w.T - 1
     pf = p0 + w.T
     wps = [torch.full((w.N,), p0, dtype=torch.int32, device=dev) for _ in range(R)]
-    wpf = [torch.full((w.N,), pf, dtype=torch.int32, device=dev) for _ in range(R)]
+    wpf = torch.full((w.N,), pf, dtype=torch.int32, device=dev)    # shared by the layers
     o = torch.empty((w.B, w.T, w.Hv, w.dv), dtype=torch.bfloat16, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
 
@@ -274,9 +274,8 @@ def bench_window_fold(w, R, steps, dev, log):
                                   ls.ring_g, wps[i], o=o, err_flags=err, window=True)
 
     def fold():
-        for i, ls in enumerate(layers):
-            wpf[i].fill_(pf)
-            gdn.gdn_replay_fold(slot_t, ls.state, ls.ring_d, ls.ring_k, ls.ring_g, wpf[i],
+        for ls in layers:
+            gdn.gdn_replay_fold(slot_t, ls.state, ls.ring_d, ls.ring_k, ls.ring_g, wpf,
                                 err_flags=err)
 
     mv = time_graph(graph_of(verify), steps) / R
@@ -290,10 +289,69 @@ def bench_window_fold(w, R, steps, dev, log):
                         + w.T * (2 * es * w.dk / G + 2 * es * w.dv + 8))
     fb = live * w.Hv * (8 * w.dv * w.dk + pf * ent)
     log(f"verify T={w.T}: {mv * 1e3:.2f} us/launch ({vb / mv / 1e6:.0f} GB/s); "
-        f"fold p={pf}: {mf * 1e3:.2f} us/call incl. cursor fill+reset ({fb / mf / 1e6:.0f} GB/s)")
+        f"fold p={pf}: {mf * 1e3:.2f} us/launch ({fb / mf / 1e6:.0f} GB/s)")
     return dict(verify_kernel_us=mv * 1e3, verify_gbs=vb / mv / 1e6,
                 verify_head_tokens_per_s=live * w.Hv * w.T / (mv / 1e3),
-                fold_call_us=mf * 1e3, fold_gbs=fb / mf / 1e6, window_p=p0, fold_p=pf)
+                fold_kernel_us=mf * 1e3, fold_gbs=fb / mf / 1e6, window_p=p0, fold_p=pf)
+
+
+def bench_lossless(w, R, steps, dev, log):
+    """Lossless verify rounds (SGLang PR #42388): per round, every layer
+    verifies a T-token window from its exact checkpoint (empty ring, fp32
+    tuples), the accepted prefix is committed once, every layer folds it, and
+    the cursors are reset once. Seeded accepted counts a ~ U{0..T}."""
+    import torch
+    import linear_attention_ssm_amd as gdn
+    slots = gi.slot_map(w)
+    slot_t = dev_tensor(slots, None, dev)
+    layers = [LayerSet(w, w.seed + 17 * i, dev) for i in range(R)]
+    ins = input_sets(w, 2, dev)
+    acc_np = gi.accepted_counts(w, 0)
+    acc = dev_tensor(acc_np, None, dev)
+    wp = torch.zeros((w.N,), dtype=torch.int32, device=dev)
+    o = torch.empty((w.B, w.T, w.Hv, w.dv), dtype=torch.bfloat16, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def verify():
+        for i, ls in enumerate(layers):
+            q, k, v, g, beta = ins[i % 2]
+            gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
+                                  ls.ring_g, wp, o=o, err_flags=err, window=True)
+
+    def fold():
+        for ls in layers:
+            gdn.gdn_replay_fold(slot_t, ls.state, ls.ring_d, ls.ring_k, ls.ring_g, wp,
+                                err_flags=err)
+
+    def round_():
+        verify()
+        gdn.gdn_replay_commit(slot_t, acc, wp, w.L, w.T, err_flags=err)
+        fold()
+        gdn.gdn_replay_reset(slot_t, wp, err_flags=err)
+
+    m_round = time_graph(graph_of(round_), steps)
+    m_verify = time_graph(graph_of(verify), steps) / R
+    wpn = np.zeros(w.N, np.int32)                    # the cursors a commit leaves
+    wpn[slots[slots >= 0]] = acc_np[slots >= 0]
+    wp.copy_(dev_tensor(wpn, None, dev))
+    m_fold = time_graph(graph_of(fold), steps) / R
+    assert int(err.item()) == 0
+    G = w.Hv // w.Hk
+    live = slots >= 0
+    nh = int(np.count_nonzero(live)) * w.Hv
+    ent = 4 * w.dv + 4 * w.dk / G + 4
+    es = 2
+    vb = nh * (4 * w.dv * w.dk + w.T * ent + w.T * (2 * es * w.dk / G + 2 * es * w.dv + 8))
+    a_sum = float(acc_np[live].sum()) * w.Hv
+    fb = nh * 8 * w.dv * w.dk + a_sum * ent
+    log(f"lossless verify T={w.T}: round {m_round * 1e3:.1f} us ({R} layers: verify, commit, "
+        f"fold, reset); verify {m_verify * 1e3:.2f} us/launch ({vb / m_verify / 1e6:.0f} GB/s), "
+        f"fold {m_fold * 1e3:.2f} us/launch ({fb / m_fold / 1e6:.0f} GB/s)")
+    return dict(round_us=m_round * 1e3, layers=R,
+                accepted_tokens_per_s=float(acc_np[live].sum()) / (m_round / 1e3),
+                verify_kernel_us=m_verify * 1e3, verify_gbs=vb / m_verify / 1e6,
+                fold_kernel_us=m_fold * 1e3, fold_gbs=fb / m_fold / 1e6,
+                mean_accepted=float(acc_np[live].mean()))
 
 
 def cpu_baseline(w, budget_s, log):
@@ -365,6 +423,7 @@ def main():
     rep = bench_replay(w, R, steps, warmup, dev, log)
     pk = bench_packed(w, R, steps, dev, log)
     wf = bench_window_fold(gi.C5, R, max(4, steps // 8), dev, log)
+    ll = bench_lossless(gi.C6, R, max(4, steps // 8), dev, log)
     if args.profile_pass:
         return
     achieved = rep["bytes_per_launch"] / (rep["kernel_ms"] / 1e3) / 1e9
@@ -409,6 +468,7 @@ def main():
         "replay_vs_packed": rep["head_steps_per_s"] / pk["head_steps_per_s"],
         "replay_vs_packed_kernel": pk["kernel_ms"] / rep["kernel_ms"],
         "verify_window_c5": wf,
+        "lossless_verify_c6": ll,
         "cpu_baseline": None,
         "kernel_sources_sha256_16": kernel_hash(),
     }

@@ -120,8 +120,15 @@ def c4(L: int, ring: str = "f16") -> Workload:
 C5 = Workload("c5_verify_window", B=32, N=32, Hv=32, Hk=16, dk=128, dv=128,
               L=16, steps=8, T=5, stagger=False, seed=505)
 
+# Lossless verify: every round starts from an exact checkpoint (empty ring),
+# stores fp32 tuples for a T-token window, commits the accepted prefix and
+# folds it (SGLang PR #42388: MTP-style drafts of 4 plus the verified token).
+C6 = Workload("c6_lossless_verify", B=32, N=40, Hv=32, Hk=16, dk=128, dv=128,
+              L=8, steps=8, ring="f32", T=5, n_pad=2, permute=True, stagger=False,
+              seed=707)
+
 WORKLOADS = {w.name: w for w in (C1, C2, C3, c4(1), c4(4), c4(16), c4(32),
-                                 c4(16, "f32"), C5)}
+                                 c4(16, "f32"), C5, C6)}
 
 
 def scaled(w: Workload, **kw) -> Workload:

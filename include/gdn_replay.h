@@ -33,7 +33,9 @@
  * Tensor layouts (all contiguous, row-major, base pointers 16-byte aligned):
  *   q, k           [B, T, Hk, dk]   qkv_dtype; q/k already normalised, q scaled
  *   v, o           [B, T, Hv, dv]   qkv_dtype (o is written in the same dtype)
- *   g, beta        [B, T, Hv]       fp32; g is the log-decay, alpha = exp(g)
+ *   g, beta        [B, T, Hv]       fp32; g is the log-decay. Every kernel applies
+ *                                  the decay alpha = RN_f32(exp_f64(g)), one value per
+ *                                  step, so that stored steps replay exactly
  *   state / ckpt   [N, Hv, dv, dk]  fp32, dk fastest (ReplaySSM blog, 2.2)
  *   ring_d         [N, Hv, L, dv]   ring_dtype  (the correction vectors d)
  *   ring_k         [N, Hk, L, dk]   ring_dtype  (keys, one per k-head)
@@ -168,19 +170,36 @@ gdn_status gdn_replay_commit(const gdn_shape *shape, const int32_t *slot_idx,
 
 /*
  * gdn_replay_fold -- fold each listed slot's p = write_pos[s] valid ring
- * entries into its checkpoint, then set write_pos[s] = 0 (SGLang PR #36821,
+ * entries of one layer into that layer's checkpoint (SGLang PR #36821,
  * Technical principle: the accepted prefix is folded into the persistent
  * checkpoint by a bit-clone of the recurrence). Per element, for j = 0..p-1:
  *     a = RN_f32(exp_f64(g_j));  x <- fma(d_j[v], k_j[c], RN(a*x))
  * with the two-instruction rounding of SGLang PR #42388 ("The idea"). The
  * result is bit-identical to that sequential recurrence on the stored entries.
+ * The decays are the same values every decode and verify kernel applies, so a
+ * verify window started from an exact checkpoint (write_pos = 0) with an fp32
+ * ring, committed and folded, equals decoding the accepted tokens one at a
+ * time with gdn_packed_decode, bit for bit (the lossless verify of SGLang PR
+ * #42388).
+ * write_pos is only read: the cursors are shared by every layer, so fold all
+ * layers, then clear the cursors once with gdn_replay_reset.
  * Requires 0 <= p <= L, else GDN_EF_CURSOR_RANGE (the slot is not touched).
  *   ckpt (device) read and written; ring_d/k/g (device) read at positions < p.
  */
 gdn_status gdn_replay_fold(const gdn_shape *shape, const int32_t *slot_idx,
                            float *ckpt, const void *ring_d, const void *ring_k,
-                           const float *ring_g, int32_t *write_pos,
+                           const float *ring_g, const int32_t *write_pos,
                            int32_t *err_flags, void *stream);
+
+/*
+ * gdn_replay_reset -- write_pos[s] <- 0 for each row with slot s >= 0: the
+ * ring is empty again once every layer has folded it (SGLang PR #36821: after
+ * the fold the checkpoint holds the committed state). A slot >= N sets
+ * GDN_EF_SLOT_RANGE.
+ *   write_pos (device) int32 [N], written.
+ */
+gdn_status gdn_replay_reset(const gdn_shape *shape, const int32_t *slot_idx,
+                            int32_t *write_pos, int32_t *err_flags, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *gdn_status_string(gdn_status status);

@@ -51,13 +51,14 @@ _lib.gdn_replay_decode.argtypes = [_S] + [_P] * 15
 _lib.gdn_replay_advance.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_commit.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_fold.argtypes = [_S] + [_P] * 8
+_lib.gdn_replay_reset.argtypes = [_S] + [_P] * 4
 for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_advance",
-           "gdn_replay_commit", "gdn_replay_fold"):
+           "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_reset"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 1
+ABI_VERSION = 2
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -210,8 +211,8 @@ def gdn_replay_commit(slot_idx, accepted, write_pos, L, T, err_flags=None, strea
 
 def gdn_replay_fold(slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags=None,
                     stream=None):
-    """Exact fold of the valid ring entries into the checkpoint, then
-    write_pos = 0; see gdn_replay_fold in gdn_replay.h."""
+    """Exact fold of one layer's valid ring entries into its checkpoint
+    (write_pos is only read); see gdn_replay_fold in gdn_replay.h."""
     _check(slot_idx, "slot_idx", torch.int32, 1)
     dev = slot_idx.device
     _check(ckpt, "ckpt", torch.float32, 4, dev)
@@ -222,6 +223,16 @@ def gdn_replay_fold(slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags
     _raise(_lib.gdn_replay_fold(ctypes.byref(sh), _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d),
                                 _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(err_flags),
                                 _stream(stream)), "gdn_replay_fold")
+
+
+def gdn_replay_reset(slot_idx, write_pos, err_flags=None, stream=None):
+    """write_pos[slot] = 0 after every layer has folded; see gdn_replay_reset
+    in gdn_replay.h."""
+    _check(slot_idx, "slot_idx", torch.int32, 1)
+    _check(write_pos, "write_pos", torch.int32, 1, slot_idx.device)
+    sh = gdn_shape(slot_idx.shape[0], 1, write_pos.shape[0], 1, 1, 32, 16, 1, 0, 0, 0)
+    _raise(_lib.gdn_replay_reset(ctypes.byref(sh), _ptr(slot_idx), _ptr(write_pos),
+                                 _ptr(err_flags), _stream(stream)), "gdn_replay_reset")
 
 
 # ------------------------------------------------------------------ prepared calls

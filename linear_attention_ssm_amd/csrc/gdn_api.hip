@@ -11,7 +11,7 @@ using namespace gdn;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -237,7 +237,7 @@ gdn_status gdn_replay_commit(const gdn_shape* s, const int32_t* slot_idx, const 
 
 gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, float* ckpt,
                            const void* ring_d, const void* ring_k, const float* ring_g,
-                           int32_t* write_pos, int32_t* err_flags, void* stream) {
+                           const int32_t* write_pos, int32_t* err_flags, void* stream) {
   const gdn_status st = check_shape(s, true);
   if (st != GDN_OK) return st;
   if (!slot_idx || !ckpt || !ring_d || !ring_k || !ring_g || !write_pos)
@@ -256,13 +256,21 @@ gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, float* c
   const dim3 grid(static_cast<unsigned>(s->B) * s->Hv * (s->dv / 16));
   const dim3 block(static_cast<unsigned>(16 * s->dk / 4));
   const size_t smem = static_cast<size_t>(s->L) * (1 + 16 + s->dk) * sizeof(float);
-  hipError_t e = dispatch_fold(s->dk, a, s->ring_dtype, grid, block, smem,
-                               static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return GDN_ERR_HIP;
+  return from_hip(dispatch_fold(s->dk, a, s->ring_dtype, grid, block, smem,
+                                static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_replay_reset(const gdn_shape* s, const int32_t* slot_idx, int32_t* write_pos,
+                            int32_t* err_flags, void* stream) {
+  if (!s || s->B < 0 || s->N < 1) return GDN_ERR_INVALID_ARG;
+  if (!slot_idx || !write_pos) return GDN_ERR_INVALID_ARG;
+  if (!aligned(slot_idx, 4) || !aligned(write_pos, 4) || (err_flags && !aligned(err_flags, 4)))
+    return GDN_ERR_INVALID_ARG;
+  if (s->B == 0) return GDN_OK;
   CursorArgs c{};
   c.slot = slot_idx; c.write_pos = write_pos; c.err = err_flags;
   c.B = s->B; c.N = s->N; c.L = s->L; c.T = s->T;
-  return from_hip(launch_fold_reset(c, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_reset(c, static_cast<hipStream_t>(stream)));
 }
 
 const char* gdn_status_string(gdn_status status) {

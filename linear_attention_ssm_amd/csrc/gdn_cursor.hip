@@ -1,4 +1,4 @@
-// gdn_cursor.hip -- the per-slot cursor kernels (fold reset, advance, commit)
+// gdn_cursor.hip -- the per-slot cursor kernels (reset, advance, commit)
 // and their launchers. One thread per row; every kernel only touches
 // write_pos[slot_idx[b]] of its own row.
 #include "gdn_launch.h"
@@ -7,15 +7,17 @@ namespace gdn {
 
 // ============================================================= cursors
 
-// write_pos[s] <- 0 for each folded slot (separate launch: every fold
-// workgroup of the slot has read the old value by then).
-__global__ static void fold_reset_kernel(CursorArgs a) {
+// write_pos[s] <- 0 once every layer has folded the slot's ring (its own
+// launch, stream-ordered after the folds that read the old value).
+__global__ static void reset_kernel(CursorArgs a) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= a.B) return;
   const int s = a.slot[b];
-  if (s < 0 || s >= a.N) return;
-  const int p = a.write_pos[s];
-  if (p < 0 || p > a.L) return;
+  if (s < 0) return;
+  if (s >= a.N) {
+    if (a.err) atomicOr(a.err, EF_SLOT);
+    return;
+  }
   a.write_pos[s] = 0;
 }
 
@@ -63,7 +65,7 @@ static hipError_t launch_rows(void (*kernel)(CursorArgs), const CursorArgs& a, h
   return hipGetLastError();
 }
 
-hipError_t launch_fold_reset(const CursorArgs& a, hipStream_t st) { return launch_rows(fold_reset_kernel, a, st); }
+hipError_t launch_reset(const CursorArgs& a, hipStream_t st) { return launch_rows(reset_kernel, a, st); }
 hipError_t launch_advance(const CursorArgs& a, hipStream_t st) { return launch_rows(advance_kernel, a, st); }
 hipError_t launch_commit(const CursorArgs& a, hipStream_t st) { return launch_rows(commit_kernel, a, st); }
 

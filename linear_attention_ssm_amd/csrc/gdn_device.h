@@ -262,13 +262,13 @@ __device__ __forceinline__ void slab_dots(const f4 (&S)[NT], const float* q_l,
   kq = quad_sum(pkq);
 }
 
-// alpha = exp(g) of the current token (single precision hardware exp; the
-// decode results are held to a tolerance, the fold pins its own decay).
-__device__ __forceinline__ float decay_of(float g) { return __expf(g); }
-
-// alpha = exp(g) of a ring entry in the fold: evaluated in double and rounded
-// once to fp32, so that the fold is bit-reproducible against a reference.
-__device__ __forceinline__ float fold_decay_of(float g) {
+// alpha = exp(g) of one step, evaluated in double and rounded once to fp32.
+// Every kernel that applies a step's decay to a state (packed decode, the
+// replay readout and flush, the verify window, the fold) uses this one value,
+// so that replaying stored (d, k, g) entries with the two-instruction update
+// reproduces a sequential decode bit for bit (SGLang PR #42388, "The idea":
+// the rebuild must round exactly as the verify kernel does).
+__device__ __forceinline__ float decay_of(float g) {
   return static_cast<float>(exp(static_cast<double>(g)));
 }
 
@@ -300,6 +300,11 @@ __device__ __forceinline__ void slab_update(f4 (&S)[NT], const float* k_l, int g
     S[t].z = __builtin_fmaf(d, kv.z, az);
     S[t].w = __builtin_fmaf(d, kv.w, aw);
   }
+}
+
+// The value lane `i` (wave-uniform) holds, in every lane.
+__device__ __forceinline__ float lane_value(float x, int i) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i));
 }
 
 // Lane i of each 16-lane row receives lane i^8's value (DPP row_ror:8).

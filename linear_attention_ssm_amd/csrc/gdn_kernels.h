@@ -98,12 +98,12 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
     *reinterpret_cast<f4*>(qdst) = decode4<QKV>(q_raw);
     *reinterpret_cast<f4*>(kdst) = decode4<QKV>(k_raw);
   }
+  const float alpha = decay_of(gv);   // while the state is in flight
   __syncthreads();
   const float vv = to_f32<QKV>(v_raw);
 
   float sq, sk, kq, d, o;
   slab_dots<NT>(S, qk, qk + DK, grp, sq, sk, kq);
-  const float alpha = decay_of(gv);
   token_out(sq, sk, kq, alpha, bt, vv, d, o);
   if (grp == 0) store1<QKV>(a.o, ih * a.dv + vcol, o);
   slab_update<NT>(S, qk + DK, grp, alpha, d);
@@ -181,7 +181,7 @@ struct Small {
   using KC = f4;                                   // 16 bytes of the key ring
   static constexpr int KV = 16 / sizeof(RT);        // ring elements per chunk
   int p_raw, ff_raw;
-  float g_pre, b_pre;
+  float g_tok, b_tok;                              // lane t < T: token t's g and beta
   typename Raw4<QKV>::T q_raw, k_raw;
   KC kr_raw[2];                                    // chunks tid and tid + blockDim
   float g_raw;
@@ -208,8 +208,9 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
   f.p_raw = ld_uniform(a.write_pos, sc);
   f.ff_raw = ld_uniform(a.ff_flags, g.b);
   const size_t ih0 = static_cast<size_t>(g.b) * a.T * a.Hv + g.h;   // token 0
-  f.g_pre = ld_uniform(a.g, ih0);
-  f.b_pre = ld_uniform(a.beta, ih0);
+  const size_t iht = ih0 + static_cast<size_t>(lane < a.T ? lane : 0) * a.Hv;
+  f.g_tok = a.g[iht];
+  f.b_tok = a.beta[iht];
   const int nqk = a.T * C4;
   const int cq = tid < nqk ? tid : nqk - 1;
   const size_t qsrc = ((static_cast<size_t>(g.b) * a.T + cq / C4) * a.Hk + g.hk) * DK + (cq % C4) * 4;
@@ -329,6 +330,8 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
     if constexpr (RF32) kt[j * DK + key] = 0.f;
     else reinterpret_cast<uint16_t*>(kt)[key * a.kts + j] = 0;
   }
+  // every token's decay at once (lane t: token t), while the slab is in flight
+  const float al_tok = decay_of(f.g_tok);
   __syncthreads();
 
   // ---- reconstruction S = A S0 + sum_j w_j d_j k_j^T
@@ -398,16 +401,18 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
   const int wph = a.VB / 16;
   const bool kwriter = (g.vb == 0) && (g.hc == 0) && (wave == 0);   // one key-ring writer per k-head
   const bool gwriter = (g.vb == 0) && (wave % wph == 0) && lane == 0;
+  float vv = to_f32<QKV>(f.v_raw);
   for (int tau = 0; tau < a.T; ++tau) {
     const float* ql = qk + tau * 2 * DK;
     const float* kl = ql + DK;
     const size_t ih = (static_cast<size_t>(g.b) * a.T + tau) * a.Hv + g.h;
-    const float vv = tau == 0 ? to_f32<QKV>(f.v_raw) : load1<QKV>(a.v, ih * a.dv + g.vcol);
-    const float gv = tau == 0 ? f.g_pre : ld_uniform(a.g, ih);
-    const float bt = tau == 0 ? f.b_pre : ld_uniform(a.beta, ih);
+    // the next window token's v is requested before this token's readout
+    const float v_next = tau + 1 < a.T ? load1<QKV>(a.v, (ih + a.Hv) * a.dv + g.vcol) : 0.f;
+    const float gv = lane_value(f.g_tok, tau);
+    const float bt = lane_value(f.b_tok, tau);
+    const float alpha = lane_value(al_tok, tau);
     float sq, sk, kq, d, o;
     slab_dots<NT>(S, ql, kl, grp, sq, sk, kq);
-    const float alpha = decay_of(gv);
     token_out(sq, sk, kq, alpha, bt, vv, d, o);
     if (grp == 0) store1<QKV>(a.o, ih * a.dv + g.vcol, row_ok ? o : 0.f);
     if (row_ok && !flush) {
@@ -420,6 +425,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
       }
     }
     if (flush || (a.window && tau + 1 < a.T)) slab_update<NT>(S, kl, grp, alpha, d);
+    vv = v_next;
   }
   if (flush) store_slab<NT>(a.state + (hs * a.dv + g.vcol) * DK + 4 * grp, S, col);
 }
@@ -486,7 +492,7 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   float* xp = a.ckpt + (hs * a.dv + v) * DK + e4;
   f4 x = *reinterpret_cast<const f4*>(xp);
 
-  if (tid < p) al[tid] = fold_decay_of(a.ring_g[hs * a.L + tid]);
+  if (tid < p) al[tid] = decay_of(a.ring_g[hs * a.L + tid]);
   for (int c = tid; c < p * FV; c += blockDim.x) {
     const int j = c / FV, r = c % FV;
     dl[c] = to_f32<RING>(static_cast<const RT*>(a.ring_d)[(hs * a.L + j) * a.dv + vb * FV + r]);

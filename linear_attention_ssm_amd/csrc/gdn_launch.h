@@ -16,7 +16,7 @@ template <int DK>
 hipError_t launch_fold(const FoldArgs& a, int ring, dim3 grid, dim3 block, size_t smem,
                        hipStream_t stream);
 
-hipError_t launch_fold_reset(const CursorArgs& a, hipStream_t stream);
+hipError_t launch_reset(const CursorArgs& a, hipStream_t stream);
 hipError_t launch_advance(const CursorArgs& a, hipStream_t stream);
 hipError_t launch_commit(const CursorArgs& a, hipStream_t stream);
 

@@ -9,7 +9,7 @@ import linear_attention_ssm_amd as gdn
 from linear_attention_ssm_amd import gdn_shape
 
 EXPECTED = ["gdn_abi_version", "gdn_packed_decode", "gdn_replay_advance", "gdn_replay_commit",
-            "gdn_replay_decode", "gdn_replay_fold", "gdn_status_string"]
+            "gdn_replay_decode", "gdn_replay_fold", "gdn_replay_reset", "gdn_status_string"]
 
 # Fake, 256-byte aligned, non-null device addresses: never dereferenced, since
 # every call below must fail validation (or return early for B = 0) first.
@@ -28,7 +28,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
     for st in range(4):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -89,6 +89,7 @@ def test_empty_batch_is_a_no_op():
     assert lib.gdn_replay_fold(ctypes.byref(sh), *FAKE[:6], None, None) == gdn.GDN_OK
     assert lib.gdn_replay_advance(ctypes.byref(sh), FAKE[0], FAKE[1], None, None, None) == gdn.GDN_OK
     assert lib.gdn_replay_commit(ctypes.byref(sh), FAKE[0], FAKE[1], FAKE[2], None, None) == gdn.GDN_OK
+    assert lib.gdn_replay_reset(ctypes.byref(sh), FAKE[0], FAKE[1], None, None) == gdn.GDN_OK
 
 
 def test_packed_and_cursor_entry_points_validate():
@@ -112,6 +113,10 @@ def test_packed_and_cursor_entry_points_validate():
     p = list(FAKE[:6])
     p[1] = ctypes.c_void_p(FAKE[1].value + 8)            # checkpoint misaligned
     assert lib.gdn_replay_fold(ctypes.byref(shape()), *p, None, None) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_replay_reset(ctypes.byref(shape()), None, FAKE[1], None, None) \
+        == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_replay_reset(ctypes.byref(shape(N=0)), FAKE[0], FAKE[1], None, None) \
+        == gdn.GDN_ERR_INVALID_ARG
 
 
 def test_python_binding_checks_tensors_before_calling():

@@ -178,4 +178,10 @@ def test_device_error_flags(gdn):
     assert int(pool.err.item()) == gdn.EF_CURSOR_RANGE
     assert torch.equal(bits(pool.ckpt[1]), bits(ck0[1]))
     assert torch.equal(bits(pool.ckpt[2]), bits(ck0[2]))      # p = 0: nothing to fold
-    assert pool.write_pos.cpu().tolist() == [0, 5, 0, 0]
+    assert pool.write_pos.cpu().tolist() == [1, 5, 0, 3]      # the fold only reads cursors
+    # reset: every listed slot, out of range or not; a slot beyond the pool is flagged
+    pool.err.zero_()
+    gdn.gdn_replay_reset(to_dev(np.array([0, -1, 9, 1], np.int32)), pool.write_pos,
+                         err_flags=pool.err)
+    assert int(pool.err.item()) == gdn.EF_SLOT_RANGE
+    assert pool.write_pos.cpu().tolist() == [0, 0, 0, 3]

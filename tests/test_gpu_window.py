@@ -102,6 +102,8 @@ def test_c5_verify_commit_fold_protocol(gdn, ring):
             sl = np.where(need, slots, -1).astype(np.int32)
             gdn.gdn_replay_fold(to_dev(sl), pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
                                 pool.write_pos, err_flags=pool.err)
+            assert np.array_equal(pool.write_pos.cpu().numpy(), wp), "the fold moved a cursor"
+            gdn.gdn_replay_reset(to_dev(sl), pool.write_pos, err_flags=pool.err)
             wp[slots[need]] = 0
             ef = rel_err(to_f64(pool.ckpt[to_dev(slots[need]).long()]), S_true[slots[need]])
             errs["fold"].append(ef)
@@ -109,6 +111,7 @@ def test_c5_verify_commit_fold_protocol(gdn, ring):
             assert np.array_equal(pool.write_pos.cpu().numpy(), wp)
     gdn.gdn_replay_fold(slot_t, pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
                         pool.write_pos, err_flags=pool.err)
+    gdn.gdn_replay_reset(slot_t, pool.write_pos, err_flags=pool.err)
     ef = rel_err(to_f64(pool.ckpt), S_true)
     errs["fold"].append(ef)
     assert ef <= tol_s_
@@ -148,7 +151,8 @@ def test_window_equals_token_by_token_windows(gdn):
 @pytest.mark.parametrize("ring", ["f16", "bf16", "f32"])
 def test_fold_bitwise_against_oracle(gdn, ring):
     """gdn_replay_fold is bit-identical to the oracle's pinned-rounding fold
-    (every element of every slot, listed or not), and resets the cursors."""
+    (every element of every slot, listed or not) and leaves the cursors alone;
+    gdn_replay_reset then clears the listed ones."""
     w = dataclasses.replace(gi.C5, ring=ring, N=40, B=36, n_pad=3, permute=True)
     rc = gi.random_ring(w, seed_tag={"f16": 1, "bf16": 2, "f32": 3}[ring])
     slots = gi.slot_map(w)
@@ -162,6 +166,8 @@ def test_fold_bitwise_against_oracle(gdn, ring):
     wpt = to_dev(wp.astype(np.int32))
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     gdn.gdn_replay_fold(to_dev(slots), ckpt, rd, rk, rg, wpt, err_flags=err)
+    assert np.array_equal(wpt.cpu().numpy(), wp.astype(np.int32))
+    gdn.gdn_replay_reset(to_dev(slots), wpt, err_flags=err)
     ref = rc.ckpt.copy()
     wref = wp.astype(np.int32).copy()
     fold_f32(ref, slots, wref, gi.as_f64(rc.d, ring).astype(np.float32),
