@@ -11,6 +11,8 @@ Parts:
                         producing outputs through the closed-form replay
   O3  fold_f32          the pinned-rounding fp32 fold (C, liboracle.so)
   O4  window_ref        a verify window evaluated token by token with O1
+  O5  quantize          exact rounding to a 16-bit state format (binary16 or
+                        bfloat16), for the 16-bit checkpoint variant
 
 Every function states the passage it follows. The pages cited are: SGLang
 PR #28451 (ReplaySSM decode port), the ReplaySSM blog on llm.rainlin.net,
@@ -74,16 +76,49 @@ def _c(a, dtype) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=dtype)
 
 
+# ------------------------------------------------------------------ O5
+
+# (significant bits, exponent of the smallest normal, largest finite value)
+_FORMATS = {"f16": (11, -14, 65504.0),
+            "bf16": (8, -126, float(np.ldexp(2.0 - 2.0 ** -7, 127)))}
+
+
+def quantize(x, fmt: str) -> np.ndarray:
+    """O5: round float64 values to the nearest value of a storage format,
+    ties to even, returned as float64.
+
+    The pages note that the decode code also handles fp16 and bf16 state
+    (vLLM PR #49887, Out of scope: low-precision state); a 16-bit checkpoint
+    holds values of these formats. 'f16' is IEEE binary16: 11 significant
+    bits, smallest normal 2^-14, subnormal spacing 2^-24, largest finite 65504.
+    'bf16' is bfloat16: 8 significant bits and the exponent range of binary32
+    (smallest normal 2^-126, subnormal spacing 2^-133). 'f32' rounds to
+    binary32. Values beyond the largest finite one round to infinity.
+    """
+    x = np.asarray(x, np.float64)
+    if fmt == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    p, emin, vmax = _FORMATS[fmt]
+    _, e = np.frexp(x)                       # |x| in [2^(e-1), 2^e)
+    qexp = np.maximum(e - p, emin - p + 1)   # exponent of the spacing at x
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = np.ldexp(np.rint(np.ldexp(x, -qexp)), qexp)
+        y = np.where(np.abs(y) > vmax, np.copysign(np.inf, x), y)
+    return np.where(np.isfinite(x), y, x)
+
+
 # ------------------------------------------------------------------ O1
 
 def gdn_step(S: np.ndarray, slot: np.ndarray, q, k, v, g, beta,
-             want_u: bool = False):
+             want_u: bool = False, state_fmt: Optional[str] = None):
     """O1: one decode token of the gated delta rule, fp64, in place on S.
 
     Follows the ReplaySSM blog (section 1): S~ = alpha S, u = beta (v - S~ k),
     S_t = S~ + u k^T, y = S_t q, alpha = exp(g).
     S [N,Hv,dv,dk] float64 (modified), slot [B], q,k [B,Hk,dk], v [B,Hv,dv],
     g,beta [B,Hv]. Returns o [B,Hv,dv] (and u when want_u).
+    state_fmt ('f16' / 'bf16'): the state is stored in that format after every
+    token (O5), as a read-update-write decode with a 16-bit state does.
     """
     assert S.dtype == np.float64 and S.flags.c_contiguous
     N, Hv, dv, dk = S.shape
@@ -97,6 +132,10 @@ def gdn_step(S: np.ndarray, slot: np.ndarray, q, k, v, g, beta,
     u = np.empty((B, Hv, dv), np.float64) if want_u else None
     lib().oracle_gdn_step_f64(B, N, Hv, Hk, dk, dv, _p(slot), _p(S), _p(q), _p(k),
                               _p(v), _p(g), _p(beta), _p(o), _p(u))
+    if state_fmt is not None:
+        for s in slot:
+            if 0 <= s < N:
+                S[s] = quantize(S[s], state_fmt)
     return (o, u) if want_u else o
 
 
@@ -159,18 +198,30 @@ class ReplayModel:
     writes alpha S + d_cur k^T into the checkpoint and leaves the ring bytes as
     they are (blog section 3.3); only entries below write_pos are ever read
     (SGLang PR #28451, Design 5).
+
+    state_fmt ('f16' / 'bf16'): the checkpoint is stored in that format. It is
+    rounded (O5) only when it is written, at a flush and at the end of a fold;
+    between writes the state lives in the ring and the replay.
     """
 
-    def __init__(self, S0: np.ndarray, Hk: int, L: int):
+    def __init__(self, S0: np.ndarray, Hk: int, L: int, state_fmt: Optional[str] = None):
         assert L >= 1
+        self.state_fmt = state_fmt
         self.N, self.Hv, self.dv, self.dk = S0.shape
         self.Hk, self.L = Hk, L
         self.G = self.Hv // Hk
         self.ckpt = np.array(S0, dtype=np.float64, copy=True)
+        if state_fmt is not None:
+            assert np.array_equal(quantize(self.ckpt, state_fmt), self.ckpt), \
+                "the initial checkpoint must hold values of the state format"
         self.ring_u = np.zeros((self.N, self.Hv, L, self.dv))
         self.ring_k = np.zeros((self.N, Hk, L, self.dk))
         self.ring_g = np.zeros((self.N, self.Hv, L))
         self.write_pos = np.zeros(self.N, dtype=np.int64)
+
+    def _store(self, X: np.ndarray) -> np.ndarray:
+        """A checkpoint write: rounded to the state format, if any."""
+        return X if self.state_fmt is None else quantize(X, self.state_fmt)
 
     # -- closed form -------------------------------------------------------
     @staticmethod
@@ -223,7 +274,7 @@ class ReplayModel:
                 d = beta[b, h] * (v[b, h] - alpha * Sk)
                 o[b, h] = alpha * Sq + d * float(k[b, hk] @ q[b, hk])
                 if flush[b]:
-                    self.ckpt[s, h] = alpha * S + np.outer(d, k[b, hk])
+                    self.ckpt[s, h] = self._store(alpha * S + np.outer(d, k[b, hk]))
                 else:
                     self.ring_u[s, h, p] = d
                     self.ring_g[s, h, p] = g[b, h]
@@ -299,7 +350,7 @@ class ReplayModel:
                 for j in range(p):
                     X = np.exp(self.ring_g[s, h, j]) * X + np.outer(
                         self.ring_u[s, h, j], self.ring_k[s, hk, j])
-                self.ckpt[s, h] = X
+                self.ckpt[s, h] = self._store(X)
             self.write_pos[s] = 0
 
 

@@ -486,3 +486,133 @@ def test_rn32_model_is_correct_rounding():
     assert rn32(one + ulp + ulp / 2) == float(np.float32(1 + 2 * 2.0 ** -23))
     # subnormal
     assert rn32(Fr(3, 2 ** 150)) == float(np.float32(2.0 ** -148))
+
+
+# ----------------------------------------------------------------- O5
+
+def _f16_grid_samples(rng):
+    """Values around binary16: random magnitudes (normal and subnormal range),
+    exact midpoints between neighbours, points just off the midpoints, and the
+    overflow threshold."""
+    mags = np.ldexp(rng.uniform(0.5, 1.0, 4000), rng.integers(-30, 17, 4000))
+    a = rng.standard_normal(2000).astype(np.float16)
+    a = a[np.isfinite(a)]
+    b = np.nextafter(a, np.float16(np.inf))
+    mid = (a.astype(np.float64) + b.astype(np.float64)) / 2       # exact in float64
+    off = np.concatenate([np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf)])
+    sub = np.ldexp(rng.integers(0, 2048, 500).astype(np.float64) + 0.5, -24)   # subnormal ties
+    edge = np.array([65504.0, 65519.99, 65520.0, 65536.0, 2.0 ** -24, 2.0 ** -25,
+                     1.5 * 2.0 ** -25, 2.0 ** -26, 0.0, -0.0, np.inf, -np.inf])
+    x = np.concatenate([mags, -mags, mid, off, sub, -sub, edge])
+    return x
+
+
+def test_quantize_f16_matches_numpy_binary16():
+    """O5 'f16' equals numpy's float64 -> float16 conversion (round to
+    nearest, ties to even, with subnormals and overflow to infinity)."""
+    x = _f16_grid_samples(np.random.default_rng(501))
+    got = oracle.quantize(x, "f16")
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).astype(np.float64)
+    assert np.array_equal(got, ref, equal_nan=True)
+
+
+def _bf16_bits(y: float) -> int:
+    return int(np.array([y], np.float32).view(np.uint32)[0])
+
+
+def _from_bits(u: int) -> float:
+    return float(np.array([u], np.uint32).view(np.float32)[0])
+
+
+def test_quantize_bf16_is_nearest_even():
+    """O5 'bf16' against the definition of round-to-nearest-even on the
+    bfloat16 grid, in exact rational arithmetic: the result is a bfloat16 value
+    (a binary32 value whose low 16 bits are zero), no neighbouring bfloat16
+    value is nearer, and a tie goes to the even significand."""
+    rng = np.random.default_rng(502)
+    mags = np.ldexp(rng.uniform(0.5, 1.0, 1500), rng.integers(-140, 60, 1500))
+    grid = rng.integers(1, 0x7F7F, 600, dtype=np.int64) << 16      # bfloat16 bit patterns
+    lo = np.array(grid, np.uint32).view(np.float32).astype(np.float64)
+    hi = np.array(grid + 0x10000, np.uint32).view(np.float32).astype(np.float64)
+    ties = (lo + hi) / 2
+    x = np.concatenate([mags, ties, np.nextafter(ties, np.inf), np.nextafter(ties, -np.inf),
+                        [0.0, 2.0 ** -133, 1.5 * 2.0 ** -133, 2.0 ** -134]])
+    y = oracle.quantize(x, "bf16")
+    assert np.array_equal(oracle.quantize(-x, "bf16"), -y)
+    n_ties = 0
+    for xi, yi in zip(x, y):
+        u = _bf16_bits(yi)
+        assert float(np.float32(yi)) == yi and (u & 0xFFFF) == 0
+        X, Y = Fr(xi), Fr(yi)
+        for nb in (u + 0x10000, u - 0x10000 if u >= 0x10000 else None):
+            if nb is None or nb >= 0x7F800000:
+                continue
+            d_nb, d_y = abs(X - Fr(_from_bits(nb))), abs(X - Y)
+            assert d_y <= d_nb, (xi, yi)
+            if d_y == d_nb:
+                n_ties += 1
+                assert (u >> 16) & 1 == 0, (xi, yi)
+    assert n_ties > 300
+
+
+def test_quantize_bf16_matches_torch_on_binary32_inputs():
+    """On binary32 inputs O5 'bf16' equals torch's float32 -> bfloat16
+    conversion (an independent implementation)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(503)
+    x32 = (rng.standard_normal(20000) * np.ldexp(1.0, rng.integers(-40, 40, 20000))).astype(np.float32)
+    u = x32.view(np.uint32)
+    x32 = np.concatenate([x32, ((u & 0xFFFF0000) | 0x8000).view(np.float32)])   # exact ties
+    ref = torch.from_numpy(x32).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(oracle.quantize(x32.astype(np.float64), "bf16"), ref)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_replay_model_16bit_state_at_L1_equals_quantized_recurrence(fmt):
+    """With a ring of one entry every step flushes, so the 16-bit checkpoint
+    is written (and rounded) after every token: the replay machine must match
+    the sequential recurrence that stores its state in the same format after
+    every token, outputs and states."""
+    rng = np.random.default_rng(510)
+    S0, slot, toks = random_problem(rng, B=3, N=4, steps=9)
+    S0 = oracle.quantize(S0, fmt)
+    slot = np.array([3, -1, 1], np.int32)
+    S = S0.copy()
+    model = ReplayModel(S0, Hk=2, L=1, state_fmt=fmt)
+    for q, k, v, g, beta in toks:
+        o_ref = gdn_step(S, slot, q, k, v, g, beta, state_fmt=fmt)
+        o, flush = model.decode(slot, q, k, v, g, beta)
+        model.advance(slot, flush)
+        assert flush[[0, 2]].all()
+        assert rel_err(o, o_ref) <= 1e-9
+        assert np.array_equal(model.ckpt, S)
+    # the rounding is really applied: the unrounded run drifts away
+    S_plain = S0.copy()
+    for q, k, v, g, beta in toks:
+        gdn_step(S_plain, slot, q, k, v, g, beta)
+    assert rel_err(S, S_plain) > 1e-5
+
+
+def test_replay_model_16bit_rounds_only_when_writing():
+    """At L = 4 the 16-bit checkpoint changes only at flushes and folds, always
+    holds values of the format, and the model stays within the format's
+    rounding of the exact recurrence."""
+    rng = np.random.default_rng(511)
+    S0, slot, toks = random_problem(rng, B=2, N=3, steps=11)
+    S0 = oracle.quantize(S0, "bf16")
+    S = S0.copy()
+    model = ReplayModel(S0, Hk=2, L=4, state_fmt="bf16")
+    for q, k, v, g, beta in toks:
+        before = model.ckpt.copy()
+        o_ref = gdn_step(S, slot, q, k, v, g, beta)
+        o, flush = model.decode(slot, q, k, v, g, beta)
+        model.advance(slot, flush)
+        for b, s in enumerate(slot):
+            if not flush[b]:
+                assert np.array_equal(model.ckpt[s], before[s])
+        assert np.array_equal(oracle.quantize(model.ckpt, "bf16"), model.ckpt)
+        assert rel_err(o, o_ref) <= 2e-2
+    model.fold(slot)
+    assert np.array_equal(oracle.quantize(model.ckpt, "bf16"), model.ckpt)
+    assert rel_err(model.ckpt[slot], S[slot]) <= 2e-2
