@@ -107,7 +107,7 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   token_out(sq, sk, kq, alpha, bt, vv, d, o);
   if (grp == 0) store1<QKV>(a.o, ih * a.dv + vcol, o);
   slab_update<NT>(S, qk + DK, grp, alpha, d);
-  store_slab<NT>(st, S, col);
+  store_slab<NT>(st - col * DK - 4 * grp, S, col, grp);
 }
 
 // ============================================================= replay decode
@@ -427,7 +427,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
     if (flush || (a.window && tau + 1 < a.T)) slab_update<NT>(S, kl, grp, alpha, d);
     vv = v_next;
   }
-  if (flush) store_slab<NT>(a.state + (hs * a.dv + g.vcol) * DK + 4 * grp, S, col);
+  if (flush) store_slab<NT>(a.state + (hs * a.dv + g.vcol - col) * DK, S, col, grp);
 }
 
 template <int DK, int QKV, int RING>
