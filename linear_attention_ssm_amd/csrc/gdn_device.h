@@ -317,34 +317,36 @@ __device__ __forceinline__ f4 row_swap8(f4 x) {
   return r;
 }
 
+// One 16-byte store with the device-scope, non-temporal cache policy (sc1 nt)
+// through a buffer resource over `nbytes` bytes at the wave-uniform `base`.
+// A checkpoint line written this way goes on to memory at once instead of
+// staying dirty in L2 until the state stream evicts it at some later point,
+// between other reads; nothing reads it again in the same launch.
+__device__ __forceinline__ void store16_nt(float* base, int nbytes, int byte_off, f4 x) {
+  constexpr int SC1_NT = 16 | 2;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), rs, byte_off, 0, SC1_NT);
+}
+
 // Store a wavefront's 16-row slab (accumulator layout: lane (row col, group
 // grp) holds keys 16t+4grp..+3 of tile t) so that every store instruction
 // writes whole 128-byte lines: rows col and col^8 trade halves of each tile
 // pair, then one instruction writes rows 0-7 and the next rows 8-15 of keys
 // 32u..32u+31. `slab` is the wave-uniform address of row 0, key 0; rows are
-// DK apart. The stores carry the device-scope, non-temporal cache policy
-// (sc1 nt): each line goes on to memory at once, in one burst with the rest
-// of the slab, instead of staying dirty in L2 until the state stream evicts it
-// at some later point, between other reads. Nothing reads the slab again in
-// the same launch. Needs all 64 lanes active.
+// DK apart. The stores use store16_nt: a slab goes to memory in one burst.
+// Needs all 64 lanes active.
 template <int NT>
 __device__ __forceinline__ void store_slab(float* slab, const f4 (&S)[NT], int col, int grp) {
   constexpr int DK = NT * 16;
-  constexpr int SC1_NT = 16 | 2;
   const bool lo = col < 8;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(slab, 0, 16 * DK * 4, 0x00020000);
   const int r = col & 7;
   const int k0 = (lo ? 0 : 16) + 4 * grp;
 #pragma unroll
   for (int u = 0; u < NT / 2; ++u) {
     const f4 x0 = S[2 * u], x1 = S[2 * u + 1];
     const f4 z = row_swap8(lo ? x1 : x0);
-    const f4 va = lo ? x0 : z, vb = lo ? z : x1;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, va), rs,
-                                          (r * DK + 32 * u + k0) * 4, 0, SC1_NT);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, vb), rs,
-                                          ((r + 8) * DK + 32 * u + k0) * 4, 0, SC1_NT);
+    store16_nt(slab, 16 * DK * 4, (r * DK + 32 * u + k0) * 4, lo ? x0 : z);
+    store16_nt(slab, 16 * DK * 4, ((r + 8) * DK + 32 * u + k0) * 4, lo ? z : x1);
   }
 }
 

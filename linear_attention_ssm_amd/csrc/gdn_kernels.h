@@ -520,7 +520,7 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
       x.w = __builtin_fmaf(dj, kv.w, tw);
     }
   }
-  *reinterpret_cast<f4*>(xp) = x;
+  store16_nt(a.ckpt + (hs * a.dv + vb * FV) * DK, FV * DK * 4, (row * DK + e4) * 4, x);
 }
 
 }  // namespace gdn
