@@ -91,6 +91,7 @@ class Workload:
     permute: bool = False  # rows map to slots by a seeded injection into [0, N)
     stagger: bool = True   # one forced flush per slot during the first L steps
     bf16_values: bool = False  # fp32 tensors carrying bf16-representable values
+    state: str = "f32"  # storage dtype of the checkpoint / packed state
     seed: int = 0
 
     @property
@@ -160,6 +161,12 @@ def initial_state(w: Workload) -> np.ndarray:
     """fp32 checkpoint pool [N, Hv, dv, dk], S0 ~ N(0, 0.1^2)."""
     r = _rng(w.seed, 0)
     return (0.1 * r.standard_normal((w.N, w.Hv, w.dv, w.dk), dtype=np.float32)).astype(np.float32)
+
+
+def stored_state(w: Workload) -> np.ndarray:
+    """The initial state pool in the workload's state storage dtype (S0 as
+    drawn, rounded to nearest even for a 16-bit format; bf16 as uint16 bits)."""
+    return cast(initial_state(w), w.state)
 
 
 def slot_map(w: Workload) -> np.ndarray:

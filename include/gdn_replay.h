@@ -2,10 +2,11 @@
  * gdn_replay.h -- C ABI of the MI355X (gfx950) ReplaySSM Gated DeltaNet
  * decode library (libgdn_replay.so).
  *
- * The method: a slot's recurrent state is kept as one fp32 checkpoint plus a
- * ring of the last L steps' (d, k, g) entries. A decode step rebuilds the
- * pre-token state from them, reads the output out of it, appends its own
- * entry to the ring, and writes the full state back only on a flush
+ * The method: a slot's recurrent state is kept as one checkpoint (fp32, or a
+ * 16-bit format) plus a ring of the last L steps' (d, k, g) entries. A decode
+ * step rebuilds the pre-token state from them, reads the output out of it,
+ * appends its own entry to the ring, and writes the full state back only on a
+ * flush
  * (ReplaySSM blog, llm.rainlin.net, sections 2-3; SGLang PR #28451,
  * Modifications and Design 1-5).
  *
@@ -36,7 +37,7 @@
  *   g, beta        [B, T, Hv]       fp32; g is the log-decay. Every kernel applies
  *                                  the decay alpha = RN_f32(exp_f64(g)), one value per
  *                                  step, so that stored steps replay exactly
- *   state / ckpt   [N, Hv, dv, dk]  fp32, dk fastest (ReplaySSM blog, 2.2)
+ *   state / ckpt   [N, Hv, dv, dk]  state_dtype, dk fastest (ReplaySSM blog, 2.2)
  *   ring_d         [N, Hv, L, dv]   ring_dtype  (the correction vectors d)
  *   ring_k         [N, Hk, L, dk]   ring_dtype  (keys, one per k-head)
  *   ring_g         [N, Hv, L]       fp32        (log-decays)
@@ -48,7 +49,21 @@
  *
  * Supported sizes: dk in {32, 64, 128, 256}; dv a multiple of 16, 16..512;
  * Hv % Hk == 0 with Hv / Hk <= 16; 1 <= L <= 64; 1 <= T <= 16; B >= 0.
- * qkv_dtype in {GDN_F32, GDN_BF16}; ring_dtype in {GDN_F32, GDN_F16, GDN_BF16}.
+ * qkv_dtype in {GDN_F32, GDN_BF16}; ring_dtype in {GDN_F32, GDN_F16, GDN_BF16};
+ * state_dtype in {GDN_F32, GDN_BF16, GDN_F16}.
+ *
+ * 16-bit state (state_dtype GDN_BF16 or GDN_F16). vLLM PR #49887 (Out of
+ * scope) notes that the decode code handles fp16 and bf16 state; its review
+ * thread contrasts a decode that stores the state in 16 bits after every
+ * token with ReplaySSM, which keeps the state in fp32 between checkpoint
+ * writes and rounds only when the buffer is full. The library follows that
+ * reading. All arithmetic is fp32; a 16-bit value is widened exactly on load,
+ * and a state written to memory is rounded once, to nearest even:
+ *   gdn_packed_decode  rounds the updated state every step;
+ *   gdn_replay_decode  rounds the checkpoint only on a flush;
+ *   gdn_replay_fold    folds in fp32 and rounds the result once.
+ * At L = 1 replay and packed decode therefore still agree bit for bit. The
+ * bit-exact lossless-verify property (gdn_replay_fold) needs an fp32 state.
  */
 #ifndef GDN_REPLAY_H
 #define GDN_REPLAY_H
@@ -86,6 +101,7 @@ typedef struct {
     int32_t qkv_dtype;  /* gdn_dtype of q, k, v and o                            */
     int32_t ring_dtype; /* gdn_dtype of ring_d and ring_k                        */
     int32_t window;     /* gdn_replay_decode: 0 = decode step, 1 = verify window */
+    int32_t state_dtype;/* gdn_dtype of the state / checkpoint (0 = GDN_F32)     */
 } gdn_shape;
 
 /*
@@ -101,12 +117,13 @@ typedef struct {
  * the form SGLang PR #42388 ("The idea") names for an exactly reproducible
  * replay. This is the baseline whose per-step state read+write the ReplaySSM
  * path removes (SGLang PR #28451, Motivation).
- *   state   (device) fp32 [N, Hv, dv, dk], read and written.
+ *   state   (device) state_dtype [N, Hv, dv, dk], read and written (a 16-bit
+ *           state is rounded to its format after every step).
  *   o       (device) [B, 1, Hv, dv], written for every row (zeros for padding).
  */
 gdn_status gdn_packed_decode(const gdn_shape *shape, const void *q, const void *k,
                              const void *v, const float *g, const float *beta,
-                             const int32_t *slot_idx, float *state, void *o,
+                             const int32_t *slot_idx, void *state, void *o,
                              int32_t *err_flags, void *stream);
 
 /*
@@ -132,7 +149,8 @@ gdn_status gdn_packed_decode(const gdn_shape *shape, const void *q, const void *
  * written at positions p..p+T-1; there is no flush and write_pos is NOT moved
  * (commit with gdn_replay_commit). force_flush must be NULL. Requires
  * p + T <= L, else GDN_EF_WINDOW.
- *   ckpt           (device) fp32 [N, Hv, dv, dk]; written only on a flush.
+ *   ckpt           (device) state_dtype [N, Hv, dv, dk]; written only on a
+ *                  flush (rounded to a 16-bit state format there).
  *   ring_d/k/g     (device) read at positions < p, written as described.
  *   write_pos      (device) int32 [N], read only.
  *   force_flush    (device) int32 [B] or NULL; nonzero forces a flush.
@@ -140,7 +158,7 @@ gdn_status gdn_packed_decode(const gdn_shape *shape, const void *q, const void *
  */
 gdn_status gdn_replay_decode(const gdn_shape *shape, const void *q, const void *k,
                              const void *v, const float *g, const float *beta,
-                             const int32_t *slot_idx, float *ckpt, void *ring_d,
+                             const int32_t *slot_idx, void *ckpt, void *ring_d,
                              void *ring_k, float *ring_g, const int32_t *write_pos,
                              const int32_t *force_flush, void *o, int32_t *err_flags,
                              void *stream);
@@ -184,10 +202,12 @@ gdn_status gdn_replay_commit(const gdn_shape *shape, const int32_t *slot_idx,
  * write_pos is only read: the cursors are shared by every layer, so fold all
  * layers, then clear the cursors once with gdn_replay_reset.
  * Requires 0 <= p <= L, else GDN_EF_CURSOR_RANGE (the slot is not touched).
+ * With a 16-bit state the fold runs in fp32 from the widened checkpoint and the
+ * result is rounded once to the state format.
  *   ckpt (device) read and written; ring_d/k/g (device) read at positions < p.
  */
 gdn_status gdn_replay_fold(const gdn_shape *shape, const int32_t *slot_idx,
-                           float *ckpt, const void *ring_d, const void *ring_k,
+                           void *ckpt, const void *ring_d, const void *ring_k,
                            const float *ring_g, const int32_t *write_pos,
                            int32_t *err_flags, void *stream);
 

@@ -25,11 +25,13 @@ GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
 EF_SLOT_RANGE, EF_CURSOR_RANGE, EF_WINDOW, EF_ACCEPTED = 1, 2, 4, 8
 
 _DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
+STATE_DTYPES = (torch.float32, torch.bfloat16, torch.float16)
 
 
 class gdn_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("B", "T", "N", "Hv", "Hk", "dk", "dv", "L", "qkv_dtype", "ring_dtype", "window")]
+                ("B", "T", "N", "Hv", "Hk", "dk", "dv", "L", "qkv_dtype", "ring_dtype", "window",
+                 "state_dtype")]
 
 
 class GdnError(RuntimeError):
@@ -58,7 +60,7 @@ for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_advance",
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 2
+ABI_VERSION = 3
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -135,15 +137,16 @@ def _out(o, B, T, Hv, dv, dtype, dev):
 def gdn_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None, stream=None):
     """Plain read-update-write decode step; see gdn_packed_decode in gdn_replay.h.
     q,k [B,1,Hk,dk]; v [B,1,Hv,dv]; g,beta [B,1,Hv] fp32; slot_idx [B] int32;
-    state [N,Hv,dv,dk] fp32 (updated in place). Returns o [B,1,Hv,dv]."""
+    state [N,Hv,dv,dk] fp32, bf16 or fp16 (updated in place). Returns o [B,1,Hv,dv]."""
     B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
-    _check(state, "state", torch.float32, 4, dev)
+    _check(state, "state", STATE_DTYPES, 4, dev)
     if tuple(state.shape[1:]) != (Hv, dv, dk):
         raise ValueError("state must be [N, Hv, dv, dk]")
     if err_flags is not None:
         _check(err_flags, "err_flags", torch.int32, None, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
-    sh = gdn_shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0)
+    sh = gdn_shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0,
+                   _DT[state.dtype])
     _raise(_lib.gdn_packed_decode(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(slot_idx), _ptr(state), _ptr(o), _ptr(err_flags),
                                   _stream(stream)), "gdn_packed_decode")
@@ -151,7 +154,7 @@ def gdn_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None,
 
 
 def _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev):
-    _check(ckpt, "ckpt", torch.float32, 4, dev)
+    _check(ckpt, "ckpt", STATE_DTYPES, 4, dev)
     _check(ring_d, "ring_d", (torch.float32, torch.float16, torch.bfloat16), 4, dev)
     _check(ring_k, "ring_k", ring_d.dtype, 4, dev)
     _check(ring_g, "ring_g", torch.float32, 3, dev)
@@ -178,7 +181,8 @@ def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, 
     if err_flags is not None:
         _check(err_flags, "err_flags", torch.int32, None, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
-    sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)))
+    sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)),
+                   _DT[ckpt.dtype])
     _raise(_lib.gdn_replay_decode(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d), _ptr(ring_k),
                                   _ptr(ring_g), _ptr(write_pos), _ptr(force_flush), _ptr(o),
@@ -192,7 +196,7 @@ def gdn_replay_advance(slot_idx, write_pos, L, force_flush=None, err_flags=None,
     _check(write_pos, "write_pos", torch.int32, 1, slot_idx.device)
     if force_flush is not None:
         _check(force_flush, "force_flush", torch.int32, 1, slot_idx.device)
-    sh = gdn_shape(slot_idx.shape[0], 1, write_pos.shape[0], 1, 1, 32, 16, int(L), 0, 0, 0)
+    sh = gdn_shape(slot_idx.shape[0], 1, write_pos.shape[0], 1, 1, 32, 16, int(L), 0, 0, 0, 0)
     _raise(_lib.gdn_replay_advance(ctypes.byref(sh), _ptr(slot_idx), _ptr(write_pos),
                                    _ptr(force_flush), _ptr(err_flags), _stream(stream)),
            "gdn_replay_advance")
@@ -203,7 +207,8 @@ def gdn_replay_commit(slot_idx, accepted, write_pos, L, T, err_flags=None, strea
     _check(slot_idx, "slot_idx", torch.int32, 1)
     _check(accepted, "accepted", torch.int32, 1, slot_idx.device)
     _check(write_pos, "write_pos", torch.int32, 1, slot_idx.device)
-    sh = gdn_shape(slot_idx.shape[0], int(T), write_pos.shape[0], 1, 1, 32, 16, int(L), 0, 0, 0)
+    sh = gdn_shape(slot_idx.shape[0], int(T), write_pos.shape[0], 1, 1, 32, 16, int(L), 0, 0, 0,
+                   0)
     _raise(_lib.gdn_replay_commit(ctypes.byref(sh), _ptr(slot_idx), _ptr(accepted),
                                   _ptr(write_pos), _ptr(err_flags), _stream(stream)),
            "gdn_replay_commit")
@@ -215,11 +220,12 @@ def gdn_replay_fold(slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags
     (write_pos is only read); see gdn_replay_fold in gdn_replay.h."""
     _check(slot_idx, "slot_idx", torch.int32, 1)
     dev = slot_idx.device
-    _check(ckpt, "ckpt", torch.float32, 4, dev)
+    _check(ckpt, "ckpt", STATE_DTYPES, 4, dev)
     N, Hv, dv, dk = ckpt.shape
     Hk = ring_k.shape[1]
     _, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev)
-    sh = gdn_shape(slot_idx.shape[0], 1, N, Hv, Hk, dk, dv, L, GDN_F32, _DT[ring_d.dtype], 0)
+    sh = gdn_shape(slot_idx.shape[0], 1, N, Hv, Hk, dk, dv, L, GDN_F32, _DT[ring_d.dtype], 0,
+                   _DT[ckpt.dtype])
     _raise(_lib.gdn_replay_fold(ctypes.byref(sh), _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d),
                                 _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(err_flags),
                                 _stream(stream)), "gdn_replay_fold")
@@ -230,7 +236,7 @@ def gdn_replay_reset(slot_idx, write_pos, err_flags=None, stream=None):
     in gdn_replay.h."""
     _check(slot_idx, "slot_idx", torch.int32, 1)
     _check(write_pos, "write_pos", torch.int32, 1, slot_idx.device)
-    sh = gdn_shape(slot_idx.shape[0], 1, write_pos.shape[0], 1, 1, 32, 16, 1, 0, 0, 0)
+    sh = gdn_shape(slot_idx.shape[0], 1, write_pos.shape[0], 1, 1, 32, 16, 1, 0, 0, 0, 0)
     _raise(_lib.gdn_replay_reset(ctypes.byref(sh), _ptr(slot_idx), _ptr(write_pos),
                                  _ptr(err_flags), _stream(stream)), "gdn_replay_reset")
 
@@ -263,7 +269,8 @@ def prepare_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring
     if force_flush is not None:
         _check(force_flush, "force_flush", torch.int32, 1, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
-    sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)))
+    sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)),
+                   _DT[ckpt.dtype])
     args = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
             _ptr(ckpt), _ptr(ring_d), _ptr(ring_k), _ptr(ring_g), _ptr(write_pos),
             _ptr(force_flush), _ptr(o), _ptr(err_flags), _stream(stream))
@@ -276,9 +283,10 @@ def prepare_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=N
                           stream=None):
     """gdn_packed_decode prepared for repeated calls. Returns (call, o)."""
     B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
-    _check(state, "state", torch.float32, 4, dev)
+    _check(state, "state", STATE_DTYPES, 4, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
-    sh = gdn_shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0)
+    sh = gdn_shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0,
+                   _DT[state.dtype])
     args = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
             _ptr(state), _ptr(o), _ptr(err_flags), _stream(stream))
     keep = (sh, q, k, v, g, beta, slot_idx, state, o, err_flags)

@@ -11,7 +11,7 @@ using namespace gdn;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -50,6 +50,8 @@ gdn_status check_shape(const gdn_shape* s, bool need_ring) {
   if (!dk_supported(s->dk)) return GDN_ERR_UNSUPPORTED;
   if (s->dv < 16 || s->dv > 512 || s->dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
   if (s->qkv_dtype != GDN_F32 && s->qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (s->state_dtype != GDN_F32 && s->state_dtype != GDN_BF16 && s->state_dtype != GDN_F16)
+    return GDN_ERR_UNSUPPORTED;
   if (need_ring) {
     if (s->L < 1 || s->L > 64) return GDN_ERR_INVALID_ARG;
     if (s->ring_dtype != GDN_F32 && s->ring_dtype != GDN_F16 && s->ring_dtype != GDN_BF16)
@@ -60,35 +62,35 @@ gdn_status check_shape(const gdn_shape* s, bool need_ring) {
 
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
-hipError_t dispatch_packed(int dk, const DecodeArgs& a, int qkv, dim3 g, dim3 b, size_t sm,
-                           hipStream_t st) {
-  switch (dk) {
-    case 32: return launch_packed<32>(a, qkv, g, b, sm, st);
-    case 64: return launch_packed<64>(a, qkv, g, b, sm, st);
-    case 128: return launch_packed<128>(a, qkv, g, b, sm, st);
-    case 256: return launch_packed<256>(a, qkv, g, b, sm, st);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t dispatch_replay(int dk, const DecodeArgs& a, int qkv, int ring, dim3 g, dim3 b,
+hipError_t dispatch_packed(int dk, const DecodeArgs& a, int qkv, int sd, dim3 g, dim3 b,
                            size_t sm, hipStream_t st) {
   switch (dk) {
-    case 32: return launch_replay<32>(a, qkv, ring, g, b, sm, st);
-    case 64: return launch_replay<64>(a, qkv, ring, g, b, sm, st);
-    case 128: return launch_replay<128>(a, qkv, ring, g, b, sm, st);
-    case 256: return launch_replay<256>(a, qkv, ring, g, b, sm, st);
+    case 32: return launch_packed<32>(a, qkv, sd, g, b, sm, st);
+    case 64: return launch_packed<64>(a, qkv, sd, g, b, sm, st);
+    case 128: return launch_packed<128>(a, qkv, sd, g, b, sm, st);
+    case 256: return launch_packed<256>(a, qkv, sd, g, b, sm, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t dispatch_fold(int dk, const FoldArgs& a, int ring, dim3 g, dim3 b, size_t sm,
-                         hipStream_t st) {
+hipError_t dispatch_replay(int dk, const DecodeArgs& a, int qkv, int ring, int sd, dim3 g,
+                           dim3 b, size_t sm, hipStream_t st) {
   switch (dk) {
-    case 32: return launch_fold<32>(a, ring, g, b, sm, st);
-    case 64: return launch_fold<64>(a, ring, g, b, sm, st);
-    case 128: return launch_fold<128>(a, ring, g, b, sm, st);
-    case 256: return launch_fold<256>(a, ring, g, b, sm, st);
+    case 32: return launch_replay<32>(a, qkv, ring, sd, g, b, sm, st);
+    case 64: return launch_replay<64>(a, qkv, ring, sd, g, b, sm, st);
+    case 128: return launch_replay<128>(a, qkv, ring, sd, g, b, sm, st);
+    case 256: return launch_replay<256>(a, qkv, ring, sd, g, b, sm, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_fold(int dk, const FoldArgs& a, int ring, int sd, dim3 g, dim3 b,
+                         size_t sm, hipStream_t st) {
+  switch (dk) {
+    case 32: return launch_fold<32>(a, ring, sd, g, b, sm, st);
+    case 64: return launch_fold<64>(a, ring, sd, g, b, sm, st);
+    case 128: return launch_fold<128>(a, ring, sd, g, b, sm, st);
+    case 256: return launch_fold<256>(a, ring, sd, g, b, sm, st);
   }
   return hipErrorInvalidValue;
 }
@@ -135,7 +137,7 @@ extern "C" {
 
 gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
                              const float* g, const float* beta, const int32_t* slot_idx,
-                             float* state, void* o, int32_t* err_flags, void* stream) {
+                             void* state, void* o, int32_t* err_flags, void* stream) {
   const gdn_status st = check_shape(s, false);
   if (st != GDN_OK) return st;
   if (s->T != 1 || s->window != 0) return GDN_ERR_INVALID_ARG;
@@ -154,13 +156,13 @@ gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, c
   a.L = 1;
   a.dump_off = static_cast<int32_t>(2u * s->dk * sizeof(float));
   const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
-  return from_hip(dispatch_packed(s->dk, a, s->qkv_dtype, grid, block, smem,
+  return from_hip(dispatch_packed(s->dk, a, s->qkv_dtype, s->state_dtype, grid, block, smem,
                                   static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
                              const float* g, const float* beta, const int32_t* slot_idx,
-                             float* ckpt, void* ring_d, void* ring_k, float* ring_g,
+                             void* ckpt, void* ring_d, void* ring_k, float* ring_g,
                              const int32_t* write_pos, const int32_t* force_flush, void* o,
                              int32_t* err_flags, void* stream) {
   const gdn_status st = check_shape(s, true);
@@ -203,7 +205,8 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
   a.lds_buf = static_cast<int32_t>((qk_bytes + kt_bytes + 15) / 16 * 16);
   a.dump_off = a.lds_buf;
   const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
-  return from_hip(dispatch_replay(s->dk, a, s->qkv_dtype, s->ring_dtype, dim3(n_items), block,
+  return from_hip(dispatch_replay(s->dk, a, s->qkv_dtype, s->ring_dtype, s->state_dtype,
+                                  dim3(n_items), block,
                                   smem, static_cast<hipStream_t>(stream)));
 }
 
@@ -235,7 +238,7 @@ gdn_status gdn_replay_commit(const gdn_shape* s, const int32_t* slot_idx, const 
   return from_hip(launch_commit(a, static_cast<hipStream_t>(stream)));
 }
 
-gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, float* ckpt,
+gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, void* ckpt,
                            const void* ring_d, const void* ring_k, const float* ring_g,
                            const int32_t* write_pos, int32_t* err_flags, void* stream) {
   const gdn_status st = check_shape(s, true);
@@ -256,7 +259,7 @@ gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, float* c
   const dim3 grid(static_cast<unsigned>(s->B) * s->Hv * (s->dv / 16));
   const dim3 block(static_cast<unsigned>(16 * s->dk / 4));
   const size_t smem = static_cast<size_t>(s->L) * (1 + 16 + s->dk) * sizeof(float);
-  return from_hip(dispatch_fold(s->dk, a, s->ring_dtype, grid, block, smem,
+  return from_hip(dispatch_fold(s->dk, a, s->ring_dtype, s->state_dtype, grid, block, smem,
                                 static_cast<hipStream_t>(stream)));
 }
 

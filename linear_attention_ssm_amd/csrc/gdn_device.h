@@ -3,11 +3,17 @@
 // Tile layout used by every decode kernel. A wavefront owns 16 consecutive
 // value rows v0..v0+15 of one value head and all dk key columns. Lane l holds
 // column group g = l / 16 and value row v = v0 + l % 16, and for every key
-// tile t (16 keys) the four consecutive keys 16t + 4g .. 16t + 4g + 3:
-//     S[t] = state[v][16t + 4g .. 16t + 4g + 3]          (one 16-byte load)
-// This is exactly the accumulator layout of the 16x16 MFMA when the product is
-// computed transposed (rows = keys, columns = value rows), so the checkpoint
-// tile is loaded straight into the accumulator registers.
+// tile t the four consecutive keys key_base(t, g) .. key_base(t, g) + 3 in the
+// fp32 register S[t]. This is the accumulator layout of the 16x16 MFMA when
+// the product is computed transposed (rows = keys, columns = value rows): row
+// m of tile t stands for key key_base(t, m / 4) + m % 4, so the MFMA's key
+// operand is read in that order and the state tile lands in the accumulator.
+// The key order depends on the storage format of the state:
+//   fp32 state:    key_base(t, g) = 16t + 4g       S[t] is one 16-byte load
+//   16-bit state:  key_base(t, g) = 32(t/2) + 8g + 4(t%2)
+//                  S[2u], S[2u+1] are the 8 consecutive keys 32u + 8g .. +7,
+//                  one 16-byte load of eight 16-bit values
+// so that every lane reads its part of a value row in 16-byte pieces.
 //
 // The readout (Sq, Sk, k^T q, the correction d and the output o) and the
 // two-instruction state update live here so that the packed decode and the
@@ -29,6 +35,7 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------- conversions
 
@@ -61,6 +68,16 @@ __device__ __forceinline__ typename Elem<DT>::T from_f32(float x) {
   if constexpr (DT == DT_F32) return x;
   else if constexpr (DT == DT_BF16) return f32_to_bf16(x);
   else return static_cast<_Float16>(x);
+}
+
+// A state value rounded to its storage format, from the fp32 value as
+// computed. The empty asm keeps the compiler from folding an fp32 FMA and this
+// conversion into one mixed-precision FMA that rounds straight to fp16, which
+// would round the exact product-sum instead of its fp32 value.
+template <int DT>
+__device__ __forceinline__ typename Elem<DT>::T state_round(float x) {
+  if constexpr (DT == DT_F16) asm("" : "+v"(x));
+  return from_f32<DT>(x);
 }
 
 // A 16-bit element's bits as its storage type. The element arrives as a
@@ -231,20 +248,79 @@ __device__ __forceinline__ void wave_suffix_sums(float x, int lane, bool multi_r
   }
 }
 
+// ------------------------------------------------------------- state slab
+
+// First of the four keys lane group `grp` holds in tile t (layout above).
+template <int SD>
+__device__ __forceinline__ int key_base(int t, int grp) {
+  if constexpr (SD == DT_F32) return 16 * t + 4 * grp;
+  else return 32 * (t >> 1) + 8 * grp + 4 * (t & 1);
+}
+
+// The key of MFMA tile row m (0..15) in tile t.
+template <int SD>
+__device__ __forceinline__ int key_of_row(int t, int m) {
+  return key_base<SD>(t, m >> 2) + (m & 3);
+}
+
+// A wavefront's 16-row slab as loaded, before widening: NT 16-byte pieces of
+// fp32 state, or NT/2 pieces of eight 16-bit values.
+template <int SD, int DK> struct SlabRaw {
+  static constexpr int NP = SD == DT_F32 ? DK / 16 : DK / 32;
+  v4u r[NP];
+};
+
+// Request this lane's part of the slab whose row 0 starts at `slab` (rows DK
+// elements apart): row col, 16-byte pieces in the key order of key_base.
+template <int SD, int DK>
+__device__ __forceinline__ void slab_load(SlabRaw<SD, DK>& R, const void* slab, int col, int grp) {
+  if constexpr (SD == DT_F32) {
+    const float* row = static_cast<const float*>(slab) + col * DK + 4 * grp;
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t) R.r[t] = *reinterpret_cast<const v4u*>(row + 16 * t);
+  } else {
+    const uint16_t* row = static_cast<const uint16_t*>(slab) + col * DK + 8 * grp;
+#pragma unroll
+    for (int u = 0; u < DK / 32; ++u) R.r[u] = *reinterpret_cast<const v4u*>(row + 32 * u);
+  }
+}
+
+// Widen a loaded slab to the fp32 tile registers (exact for 16-bit formats).
+template <int SD, int DK>
+__device__ __forceinline__ void slab_decode(f4 (&S)[DK / 16], const SlabRaw<SD, DK>& R) {
+  if constexpr (SD == DT_F32) {
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t) S[t] = __builtin_bit_cast(f4, R.r[t]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < DK / 32; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = R.r[u][i];   // keys 2i, 2i+1 of the piece
+        const float lo = to_f32<SD>(from_bits<SD>(static_cast<uint16_t>(w & 0xffffu)));
+        const float hi = to_f32<SD>(from_bits<SD>(static_cast<uint16_t>(w >> 16)));
+        f4& dst = S[2 * u + (i >> 1)];
+        dst[2 * (i & 1)] = lo;
+        dst[2 * (i & 1) + 1] = hi;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------- readout
 
 // Per-lane partial dot products of the 16-row slab with q and k, and of k
 // with q, reduced over the four column groups. q_l / k_l point at fp32 copies
 // of the token's q and k in LDS.
-template <int NT>
+template <int SD, int NT>
 __device__ __forceinline__ void slab_dots(const f4 (&S)[NT], const float* q_l,
                                           const float* k_l, int grp, float& sq,
                                           float& sk, float& kq) {
   float pq = 0.f, pk = 0.f, pkq = 0.f;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const f4 qv = *reinterpret_cast<const f4*>(q_l + 16 * t + 4 * grp);
-    const f4 kv = *reinterpret_cast<const f4*>(k_l + 16 * t + 4 * grp);
+    const f4 qv = *reinterpret_cast<const f4*>(q_l + key_base<SD>(t, grp));
+    const f4 kv = *reinterpret_cast<const f4*>(k_l + key_base<SD>(t, grp));
     pq = __builtin_fmaf(S[t].x, qv.x, pq);
     pq = __builtin_fmaf(S[t].y, qv.y, pq);
     pq = __builtin_fmaf(S[t].z, qv.z, pq);
@@ -287,13 +363,13 @@ __device__ __forceinline__ void token_out(float sq, float sk, float kq,
 
 // State update S <- alpha S + d k^T with the two-instruction rounding
 // fma(d, k, RN(alpha * S)) (SGLang PR #42388, "The idea").
-template <int NT>
+template <int SD, int NT>
 __device__ __forceinline__ void slab_update(f4 (&S)[NT], const float* k_l, int grp,
                                             float alpha, float d) {
 #pragma clang fp contract(off)
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const f4 kv = *reinterpret_cast<const f4*>(k_l + 16 * t + 4 * grp);
+    const f4 kv = *reinterpret_cast<const f4*>(k_l + key_base<SD>(t, grp));
     const float ax = alpha * S[t].x, ay = alpha * S[t].y;
     const float az = alpha * S[t].z, aw = alpha * S[t].w;
     S[t].x = __builtin_fmaf(d, kv.x, ax);
@@ -328,25 +404,62 @@ __device__ __forceinline__ void store16_nt(float* base, int nbytes, int byte_off
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), rs, byte_off, 0, SC1_NT);
 }
 
-// Store a wavefront's 16-row slab (accumulator layout: lane (row col, group
-// grp) holds keys 16t+4grp..+3 of tile t) so that every store instruction
-// writes whole 128-byte lines: rows col and col^8 trade halves of each tile
-// pair, then one instruction writes rows 0-7 and the next rows 8-15 of keys
-// 32u..32u+31. `slab` is the wave-uniform address of row 0, key 0; rows are
-// DK apart. The stores use store16_nt: a slab goes to memory in one burst.
-// Needs all 64 lanes active.
-template <int NT>
-__device__ __forceinline__ void store_slab(float* slab, const f4 (&S)[NT], int col, int grp) {
-  constexpr int DK = NT * 16;
-  const bool lo = col < 8;
-  const int r = col & 7;
-  const int k0 = (lo ? 0 : 16) + 4 * grp;
+// The 8-byte form of store16_nt.
+__device__ __forceinline__ void store8_nt(float* base, int nbytes, int byte_off, u16x4 x) {
+  constexpr int SC1_NT = 16 | 2;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, x), rs, byte_off, 0, SC1_NT);
+}
+
+// Store a wavefront's 16-row slab, rounded to the state format (round to
+// nearest even), so that every store instruction writes whole 128-byte lines.
+// Each lane holds NP 16-byte pieces of its row (fp32: tile t = keys 16t+4g..;
+// 16-bit: piece u = keys 32u+8g..). Rows col and col^8 trade the odd pieces of
+// each pair (DPP row_ror:8): one instruction then writes rows 0-7 and the next
+// rows 8-15, each covering the pair's 2 x 64 bytes of all eight rows. A slab
+// with one piece per lane (16-bit, dk = 32) is written piece by piece.
+// `slab` is the wave-uniform address of row 0; rows are DK elements apart.
+// The stores use store16_nt: a slab goes to memory in one burst. Needs all 64
+// lanes active.
+template <int SD, int DK>
+__device__ __forceinline__ void store_slab(void* slab, const f4 (&S)[DK / 16], int col, int grp) {
+  constexpr int ES = SD == DT_F32 ? 4 : 2;          // bytes per element
+  constexpr int NP = SlabRaw<SD, DK>::NP;
+  constexpr int KP = SD == DT_F32 ? 16 : 32;        // keys between pieces of a lane
+  constexpr int KG = SD == DT_F32 ? 4 : 8;          // keys between lane groups
+  constexpr int NB = 16 * DK * ES;
+  float* base = static_cast<float*>(slab);
+  f4 X[NP];
+  if constexpr (SD == DT_F32) {
 #pragma unroll
-  for (int u = 0; u < NT / 2; ++u) {
-    const f4 x0 = S[2 * u], x1 = S[2 * u + 1];
-    const f4 z = row_swap8(lo ? x1 : x0);
-    store16_nt(slab, 16 * DK * 4, (r * DK + 32 * u + k0) * 4, lo ? x0 : z);
-    store16_nt(slab, 16 * DK * 4, ((r + 8) * DK + 32 * u + k0) * 4, lo ? z : x1);
+    for (int t = 0; t < NP; ++t) X[t] = S[t];
+  } else {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      v4u w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f4& src = S[2 * u + (i >> 1)];
+        const uint32_t lo = __builtin_bit_cast(uint16_t, state_round<SD>(src[2 * (i & 1)]));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, state_round<SD>(src[2 * (i & 1) + 1]));
+        w[i] = lo | (hi << 16);
+      }
+      X[u] = __builtin_bit_cast(f4, w);
+    }
+  }
+  if constexpr (NP == 1) {
+    store16_nt(base, NB, (col * DK + KG * grp) * ES, X[0]);
+  } else {
+    const bool lo = col < 8;
+    const int r = col & 7;
+    const int k0 = (lo ? 0 : KP) + KG * grp;
+#pragma unroll
+    for (int u = 0; u < NP / 2; ++u) {
+      const f4 x0 = X[2 * u], x1 = X[2 * u + 1];
+      const f4 z = row_swap8(lo ? x1 : x0);
+      store16_nt(base, NB, (r * DK + 2 * KP * u + k0) * ES, lo ? x0 : z);
+      store16_nt(base, NB, ((r + 8) * DK + 2 * KP * u + k0) * ES, lo ? z : x1);
+    }
   }
 }
 
@@ -359,7 +472,7 @@ struct DecodeArgs {
   const float* g;
   const float* beta;
   const int32_t* slot;
-  float* state;            // packed: the state; replay: the checkpoint
+  void* state;             // packed: the state; replay: the checkpoint (state dtype)
   void* ring_d;
   void* ring_k;
   float* ring_g;
@@ -392,7 +505,7 @@ struct CursorArgs {
 
 struct FoldArgs {
   const int32_t* slot;
-  float* ckpt;
+  void* ckpt;
   const void* ring_d;
   const void* ring_k;
   const float* ring_g;

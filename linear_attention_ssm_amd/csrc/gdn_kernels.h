@@ -47,7 +47,7 @@ __device__ __forceinline__ void stage_qk(const DecodeArgs& a, float* lds, int b,
 //
 // The plain read-update-write step (SGLang PR #28451: the packed decode that
 // reads the state, updates it and writes it back every step).
-template <int DK, int QKV>
+template <int DK, int QKV, int SD>
 __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   constexpr int NT = DK / 16;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -84,10 +84,10 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   const auto v_raw = load1_raw<QKV>(a.v, ih * a.dv + vcol);
   const float gv = ld_uniform(a.g, ih), bt = ld_uniform(a.beta, ih);
 
-  float* st = a.state + ((static_cast<size_t>(s) * a.Hv + h) * a.dv + vcol) * DK + 4 * grp;
-  f4 S[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) S[t] = *reinterpret_cast<const f4*>(st + 16 * t);
+  using SE = typename Elem<SD>::T;
+  SE* st = static_cast<SE*>(a.state) + ((static_cast<size_t>(s) * a.Hv + h) * a.dv + vcol - col) * DK;
+  SlabRaw<SD, DK> R;
+  slab_load<SD, DK>(R, st, col, grp);
 
   {
     // unconditional writes (surplus threads into the dump area) keep the
@@ -102,12 +102,14 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   __syncthreads();
   const float vv = to_f32<QKV>(v_raw);
 
+  f4 S[NT];
+  slab_decode<SD, DK>(S, R);
   float sq, sk, kq, d, o;
-  slab_dots<NT>(S, qk, qk + DK, grp, sq, sk, kq);
+  slab_dots<SD>(S, qk, qk + DK, grp, sq, sk, kq);
   token_out(sq, sk, kq, alpha, bt, vv, d, o);
   if (grp == 0) store1<QKV>(a.o, ih * a.dv + vcol, o);
-  slab_update<NT>(S, qk + DK, grp, alpha, d);
-  store_slab<NT>(st - col * DK - 4 * grp, S, col, grp);
+  slab_update<SD>(S, qk + DK, grp, alpha, d);
+  store_slab<SD, DK>(st, S, col, grp);
 }
 
 // ============================================================= replay decode
@@ -239,21 +241,20 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
   f.v_raw = load1_raw<QKV>(a.v, ih0 * a.dv + g.vcol);
 }
 
-// Request an item's 16-row checkpoint slab: 16-byte loads straight into the
-// accumulator layout.
-template <int DK>
-__device__ __forceinline__ void fetch_slab(f4 (&S)[DK / 16], const DecodeArgs& a,
-                                           const ItemGeo& g, int s, int grp) {
+// Request an item's 16-row checkpoint slab: 16-byte loads in the lane order
+// of the accumulator layout (widened to fp32 in process()).
+template <int SD, int DK>
+__device__ __forceinline__ void fetch_slab(SlabRaw<SD, DK>& R, const DecodeArgs& a,
+                                           const ItemGeo& g, int s, int col, int grp) {
   const int sc = (s >= 0 && s < a.N) ? s : 0;
   const size_t hs = static_cast<size_t>(sc) * a.Hv + g.h;
-  const float* ck = a.state + (hs * a.dv + g.vcol) * DK + 4 * grp;
-#pragma unroll
-  for (int t = 0; t < DK / 16; ++t) S[t] = *reinterpret_cast<const f4*>(ck + 16 * t);
+  using SE = typename Elem<SD>::T;
+  slab_load<SD, DK>(R, static_cast<const SE*>(a.state) + (hs * a.dv + g.vcol - col) * DK, col, grp);
 }
 
-template <int DK, int QKV, int RING>
+template <int DK, int QKV, int RING, int SD>
 __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, int s,
-                                        const Small<DK, QKV, RING>& f, f4 (&S)[DK / 16],
+                                        const Small<DK, QKV, RING>& f, const SlabRaw<SD, DK>& R,
                                         unsigned char* buf, float* dump, int tid, int lane,
                                         int grp, int col, int wave) {
   constexpr int NT = DK / 16;
@@ -335,6 +336,8 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
   __syncthreads();
 
   // ---- reconstruction S = A S0 + sum_j w_j d_j k_j^T
+  f4 S[NT];
+  slab_decode<SD, DK>(S, R);
   if (p > 0) {
     const float gj = lane < p ? f.g_raw : 0.f;          // lane j < p holds g_j
     // Lanes >= p hold g = 0, so the exclusive sum of lane p-1 is exactly 0
@@ -362,9 +365,9 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         typename MM::op_t aop;
-        if constexpr (RF32) aop = kt[(c * CH + grp) * DK + 16 * t + col];
-        else aop = *reinterpret_cast<const typename MM::op_t*>(kt + (16 * t + col) * a.kts +
-                                                              c * CH + 4 * grp);
+        const int key = key_of_row<SD>(t, col);
+        if constexpr (RF32) aop = kt[(c * CH + grp) * DK + key];
+        else aop = *reinterpret_cast<const typename MM::op_t*>(kt + key * a.kts + c * CH + 4 * grp);
         S[t] = MM::mma(aop, bop, S[t]);
       }
     };
@@ -412,7 +415,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
     const float bt = lane_value(f.b_tok, tau);
     const float alpha = lane_value(al_tok, tau);
     float sq, sk, kq, d, o;
-    slab_dots<NT>(S, ql, kl, grp, sq, sk, kq);
+    slab_dots<SD>(S, ql, kl, grp, sq, sk, kq);
     token_out(sq, sk, kq, alpha, bt, vv, d, o);
     if (grp == 0) store1<QKV>(a.o, ih * a.dv + g.vcol, row_ok ? o : 0.f);
     if (row_ok && !flush) {
@@ -424,13 +427,16 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
         store4<RING>(a.ring_k, (ks * a.L + pos) * DK + 4 * lane, kv);
       }
     }
-    if (flush || (a.window && tau + 1 < a.T)) slab_update<NT>(S, kl, grp, alpha, d);
+    if (flush || (a.window && tau + 1 < a.T)) slab_update<SD>(S, kl, grp, alpha, d);
     vv = v_next;
   }
-  if (flush) store_slab<NT>(a.state + (hs * a.dv + g.vcol - col) * DK, S, col, grp);
+  if (flush) {
+    using SE = typename Elem<SD>::T;
+    store_slab<SD, DK>(static_cast<SE*>(a.state) + (hs * a.dv + g.vcol - col) * DK, S, col, grp);
+  }
 }
 
-template <int DK, int QKV, int RING>
+template <int DK, int QKV, int RING, int SD>
 __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* dump = reinterpret_cast<float*>(smem + a.lds_buf);   // [64][8] write sink
@@ -442,11 +448,11 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   const ItemGeo g = item_geo(a, item, wave, col);
   const int s = ld_uniform(a.slot, g.b);
   Small<DK, QKV, RING> sm;
-  f4 S[DK / 16];
+  SlabRaw<SD, DK> R;
   fetch_small(sm, a, g, s, tid, lane, grp);
   __builtin_amdgcn_sched_barrier(0);
-  fetch_slab<DK>(S, a, g, s, grp);
-  process(a, g, s, sm, S, smem, dump, tid, lane, grp, col, wave);
+  fetch_slab<SD, DK>(R, a, g, s, col, grp);
+  process(a, g, s, sm, R, smem, dump, tid, lane, grp, col, wave);
 }
 
 // ============================================================= fold
@@ -454,7 +460,7 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
 // Fold the valid ring entries into the checkpoint with the pinned two-step
 // rounding (SGLang PR #42388 "The idea"; SGLang PR #36821 fold). Workgroup =
 // (row, value head, 16 value rows); thread = one 16-byte group of 4 keys.
-template <int DK, int RING>
+template <int DK, int RING, int SD>
 __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   constexpr int C4 = DK / 4;
   constexpr int FV = 16;
@@ -489,8 +495,9 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   const int row = tid / C4, e4 = (tid % C4) * 4;
   const int v = vb * FV + row;
 
-  float* xp = a.ckpt + (hs * a.dv + v) * DK + e4;
-  f4 x = *reinterpret_cast<const f4*>(xp);
+  using SE = typename Elem<SD>::T;
+  SE* xbase = static_cast<SE*>(a.ckpt) + (hs * a.dv + vb * FV) * DK;   // the block's 16 rows
+  f4 x = load4<SD>(xbase, row * DK + e4);
 
   if (tid < p) al[tid] = decay_of(a.ring_g[hs * a.L + tid]);
   for (int c = tid; c < p * FV; c += blockDim.x) {
@@ -520,7 +527,17 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
       x.w = __builtin_fmaf(dj, kv.w, tw);
     }
   }
-  store16_nt(a.ckpt + (hs * a.dv + vb * FV) * DK, FV * DK * 4, (row * DK + e4) * 4, x);
+  // fp32 result of the exact fold, rounded once to the state format
+  if constexpr (SD == DT_F32) {
+    store16_nt(reinterpret_cast<float*>(xbase), FV * DK * 4, (row * DK + e4) * 4, x);
+  } else {
+    u16x4 r;
+    r.x = __builtin_bit_cast(uint16_t, state_round<SD>(x.x));
+    r.y = __builtin_bit_cast(uint16_t, state_round<SD>(x.y));
+    r.z = __builtin_bit_cast(uint16_t, state_round<SD>(x.z));
+    r.w = __builtin_bit_cast(uint16_t, state_round<SD>(x.w));
+    store8_nt(reinterpret_cast<float*>(xbase), FV * DK * 2, (row * DK + e4) * 2, r);
+  }
 }
 
 }  // namespace gdn

@@ -7,13 +7,13 @@
 namespace gdn {
 
 template <int DK>
-hipError_t launch_packed(const DecodeArgs& a, int qkv, dim3 grid, dim3 block, size_t smem,
-                         hipStream_t stream);
-template <int DK>
-hipError_t launch_replay(const DecodeArgs& a, int qkv, int ring, dim3 grid, dim3 block,
+hipError_t launch_packed(const DecodeArgs& a, int qkv, int sd, dim3 grid, dim3 block,
                          size_t smem, hipStream_t stream);
 template <int DK>
-hipError_t launch_fold(const FoldArgs& a, int ring, dim3 grid, dim3 block, size_t smem,
+hipError_t launch_replay(const DecodeArgs& a, int qkv, int ring, int sd, dim3 grid, dim3 block,
+                         size_t smem, hipStream_t stream);
+template <int DK>
+hipError_t launch_fold(const FoldArgs& a, int ring, int sd, dim3 grid, dim3 block, size_t smem,
                        hipStream_t stream);
 
 hipError_t launch_reset(const CursorArgs& a, hipStream_t stream);

@@ -20,53 +20,87 @@ static hipError_t launch(K kernel, const A& a, dim3 grid, dim3 block, size_t sme
   return hipGetLastError();
 }
 
+template <int DK, int QKV>
+static hipError_t launch_packed_q(const DecodeArgs& a, int sd, dim3 grid, dim3 block, size_t smem,
+                                  hipStream_t stream) {
+  switch (sd) {
+    case DT_F32: return launch(packed_decode_kernel<DK, QKV, DT_F32>, a, grid, block, smem, stream);
+    case DT_BF16: return launch(packed_decode_kernel<DK, QKV, DT_BF16>, a, grid, block, smem, stream);
+    case DT_F16: return launch(packed_decode_kernel<DK, QKV, DT_F16>, a, grid, block, smem, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int DK>
-hipError_t launch_packed(const DecodeArgs& a, int qkv, dim3 grid, dim3 block, size_t smem,
+hipError_t launch_packed(const DecodeArgs& a, int qkv, int sd, dim3 grid, dim3 block, size_t smem,
                          hipStream_t stream) {
   switch (qkv) {
-    case DT_F32: return launch(packed_decode_kernel<DK, DT_F32>, a, grid, block, smem, stream);
-    case DT_BF16: return launch(packed_decode_kernel<DK, DT_BF16>, a, grid, block, smem, stream);
+    case DT_F32: return launch_packed_q<DK, DT_F32>(a, sd, grid, block, smem, stream);
+    case DT_BF16: return launch_packed_q<DK, DT_BF16>(a, sd, grid, block, smem, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DK, int QKV, int RING>
+static hipError_t launch_replay_r(const DecodeArgs& a, int sd, dim3 grid, dim3 block, size_t smem,
+                                  hipStream_t stream) {
+  switch (sd) {
+    case DT_F32: return launch(replay_decode_kernel<DK, QKV, RING, DT_F32>, a, grid, block, smem, stream);
+    case DT_BF16: return launch(replay_decode_kernel<DK, QKV, RING, DT_BF16>, a, grid, block, smem, stream);
+    case DT_F16: return launch(replay_decode_kernel<DK, QKV, RING, DT_F16>, a, grid, block, smem, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DK, int QKV>
-static hipError_t launch_replay_q(const DecodeArgs& a, int ring, dim3 grid, dim3 block,
+static hipError_t launch_replay_q(const DecodeArgs& a, int ring, int sd, dim3 grid, dim3 block,
                                   size_t smem, hipStream_t stream) {
   switch (ring) {
-    case DT_F32: return launch(replay_decode_kernel<DK, QKV, DT_F32>, a, grid, block, smem, stream);
-    case DT_F16: return launch(replay_decode_kernel<DK, QKV, DT_F16>, a, grid, block, smem, stream);
-    case DT_BF16: return launch(replay_decode_kernel<DK, QKV, DT_BF16>, a, grid, block, smem, stream);
+    case DT_F32: return launch_replay_r<DK, QKV, DT_F32>(a, sd, grid, block, smem, stream);
+    case DT_F16: return launch_replay_r<DK, QKV, DT_F16>(a, sd, grid, block, smem, stream);
+    case DT_BF16: return launch_replay_r<DK, QKV, DT_BF16>(a, sd, grid, block, smem, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DK>
-hipError_t launch_replay(const DecodeArgs& a, int qkv, int ring, dim3 grid, dim3 block,
+hipError_t launch_replay(const DecodeArgs& a, int qkv, int ring, int sd, dim3 grid, dim3 block,
                          size_t smem, hipStream_t stream) {
   switch (qkv) {
-    case DT_F32: return launch_replay_q<DK, DT_F32>(a, ring, grid, block, smem, stream);
-    case DT_BF16: return launch_replay_q<DK, DT_BF16>(a, ring, grid, block, smem, stream);
+    case DT_F32: return launch_replay_q<DK, DT_F32>(a, ring, sd, grid, block, smem, stream);
+    case DT_BF16: return launch_replay_q<DK, DT_BF16>(a, ring, sd, grid, block, smem, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DK, int RING>
+static hipError_t launch_fold_r(const FoldArgs& a, int sd, dim3 grid, dim3 block, size_t smem,
+                                hipStream_t stream) {
+  switch (sd) {
+    case DT_F32: return launch(fold_kernel<DK, RING, DT_F32>, a, grid, block, smem, stream);
+    case DT_BF16: return launch(fold_kernel<DK, RING, DT_BF16>, a, grid, block, smem, stream);
+    case DT_F16: return launch(fold_kernel<DK, RING, DT_F16>, a, grid, block, smem, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DK>
-hipError_t launch_fold(const FoldArgs& a, int ring, dim3 grid, dim3 block, size_t smem,
+hipError_t launch_fold(const FoldArgs& a, int ring, int sd, dim3 grid, dim3 block, size_t smem,
                        hipStream_t stream) {
   switch (ring) {
-    case DT_F32: return launch(fold_kernel<DK, DT_F32>, a, grid, block, smem, stream);
-    case DT_F16: return launch(fold_kernel<DK, DT_F16>, a, grid, block, smem, stream);
-    case DT_BF16: return launch(fold_kernel<DK, DT_BF16>, a, grid, block, smem, stream);
+    case DT_F32: return launch_fold_r<DK, DT_F32>(a, sd, grid, block, smem, stream);
+    case DT_F16: return launch_fold_r<DK, DT_F16>(a, sd, grid, block, smem, stream);
+    case DT_BF16: return launch_fold_r<DK, DT_BF16>(a, sd, grid, block, smem, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 #define GDN_INSTANTIATE(DK)                                                                 \
-  template hipError_t launch_packed<DK>(const DecodeArgs&, int, dim3, dim3, size_t,         \
+  template hipError_t launch_packed<DK>(const DecodeArgs&, int, int, dim3, dim3, size_t,    \
                                         hipStream_t);                                        \
-  template hipError_t launch_replay<DK>(const DecodeArgs&, int, int, dim3, dim3, size_t,    \
+  template hipError_t launch_replay<DK>(const DecodeArgs&, int, int, int, dim3, dim3, size_t, \
                                         hipStream_t);                                        \
-  template hipError_t launch_fold<DK>(const FoldArgs&, int, dim3, dim3, size_t, hipStream_t);
+  template hipError_t launch_fold<DK>(const FoldArgs&, int, int, dim3, dim3, size_t,        \
+                                      hipStream_t);
 
 }  // namespace gdn

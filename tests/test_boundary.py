@@ -28,7 +28,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
     for st in range(4):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -54,6 +54,8 @@ def packed(sh, ptrs=None):
     (dict(dv=40), gdn.GDN_ERR_UNSUPPORTED),
     (dict(qkv_dtype=gdn.GDN_F16), gdn.GDN_ERR_UNSUPPORTED),
     (dict(ring_dtype=7), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(state_dtype=3), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(state_dtype=-1), gdn.GDN_ERR_UNSUPPORTED),
     (dict(T=2), gdn.GDN_ERR_INVALID_ARG),               # decode mode needs T = 1
     (dict(T=2, window=1, L=1), gdn.GDN_ERR_INVALID_ARG),  # window longer than the ring
     (dict(window=2), gdn.GDN_ERR_INVALID_ARG),
@@ -95,6 +97,9 @@ def test_empty_batch_is_a_no_op():
 def test_packed_and_cursor_entry_points_validate():
     assert packed(shape(T=2)) == gdn.GDN_ERR_INVALID_ARG
     assert packed(shape(dk=48)) == gdn.GDN_ERR_UNSUPPORTED
+    assert packed(shape(state_dtype=5)) == gdn.GDN_ERR_UNSUPPORTED
+    assert gdn.lib().gdn_replay_fold(ctypes.byref(shape(state_dtype=5)), *FAKE[:6], None, None) \
+        == gdn.GDN_ERR_UNSUPPORTED
     p = list(FAKE[:8])
     p[6] = None
     assert packed(shape(), p) == gdn.GDN_ERR_INVALID_ARG
