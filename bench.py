@@ -58,8 +58,9 @@ def bytes_decode_head_step(w: gi.Workload, p: int, flush: bool, kind: str) -> fl
     head."""
     es = 2 if w.qkv != "f32" else 4
     rs = 2 if w.ring != "f32" else 4
+    ss = 2 if w.state != "f32" else 4
     G = w.Hv // w.Hk
-    state = 4 * w.dv * w.dk
+    state = ss * w.dv * w.dk
     io = 2 * es * w.dk / G + 2 * es * w.dv + 8          # q, k (per k-head), v, o, g, beta
     if kind == "packed":
         return 2 * state + io
@@ -104,7 +105,7 @@ class LayerSet:
     def __init__(self, w, seed, dev, with_ring=True):
         import torch
         ws = dataclasses.replace(w, seed=seed)
-        self.state = dev_tensor(gi.initial_state(ws), None, dev)
+        self.state = dev_tensor(gi.stored_state(ws), ws.state, dev)
         if with_ring:
             rdt = torch.float16 if w.ring == "f16" else (
                 torch.bfloat16 if w.ring == "bf16" else torch.float32)
@@ -217,7 +218,7 @@ def bench_replay(w, R, steps, warmup, dev, log):
     live = int(np.count_nonzero(slots >= 0))
     mean_p = float(np.mean([p for p, _ in cur]))
     flush_frac = float(np.mean([fl for _, fl in cur]))
-    log(f"replay: {ms_step * 1e3:.1f} us/step ({R} layers + advance), decode kernel "
+    log(f"replay [{w.state} state]: {ms_step * 1e3:.1f} us/step ({R} layers + advance), decode kernel "
         f"{ms_dec * 1e3:.2f} us, {bytes_launch / 1e6:.2f} MB/launch, "
         f"mean p {mean_p:.2f}, flush frac {flush_frac:.4f}")
     return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
@@ -244,7 +245,7 @@ def bench_packed(w, R, steps, dev, log):
     ms_k = ms_step / R
     live = int(np.count_nonzero(slots >= 0))
     bytes_launch = live * w.Hv * bytes_decode_head_step(w, 0, False, "packed")
-    log(f"packed: {ms_step * 1e3:.1f} us/step ({R} layers), kernel {ms_k * 1e3:.2f} us, "
+    log(f"packed [{w.state} state]: {ms_step * 1e3:.1f} us/step ({R} layers), kernel {ms_k * 1e3:.2f} us, "
         f"{bytes_launch / 1e6:.2f} MB/launch")
     return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
                 kernel_ms=ms_k, bytes_per_launch=bytes_launch)
@@ -422,6 +423,9 @@ def main():
         steps, warmup = 4, 16
     rep = bench_replay(w, R, steps, warmup, dev, log)
     pk = bench_packed(w, R, steps, dev, log)
+    w16 = dataclasses.replace(w, state="bf16")
+    rep16 = bench_replay(w16, R, steps, warmup, dev, log)
+    pk16 = bench_packed(w16, R, steps, dev, log)
     wf = bench_window_fold(gi.C5, R, max(4, steps // 8), dev, log)
     ll = bench_lossless(gi.C6, R, max(4, steps // 8), dev, log)
     if args.profile_pass:
@@ -454,7 +458,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": "replay_decode_kernel<128, bf16, f16>",
+            "kernel": "replay_decode_kernel<128, bf16, f16, f32>",
             "kernel_us": rep["kernel_ms"] * 1e3,
             "algorithmic_bytes_per_launch": rep["bytes_per_launch"],
         },
@@ -467,6 +471,20 @@ def main():
         },
         "replay_vs_packed": rep["head_steps_per_s"] / pk["head_steps_per_s"],
         "replay_vs_packed_kernel": pk["kernel_ms"] / rep["kernel_ms"],
+        "state_bf16": {
+            "note": "the standard workload with a bf16 checkpoint / packed state (fp32 math)",
+            "replay_head_steps_per_s": rep16["head_steps_per_s"],
+            "replay_kernel_us": rep16["kernel_ms"] * 1e3,
+            "replay_gbs": rep16["bytes_per_launch"] / (rep16["kernel_ms"] / 1e3) / 1e9,
+            "replay_frac": rep16["bytes_per_launch"] / (rep16["kernel_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "replay_bytes_per_launch": rep16["bytes_per_launch"],
+            "packed_head_steps_per_s": pk16["head_steps_per_s"],
+            "packed_kernel_us": pk16["kernel_ms"] * 1e3,
+            "packed_gbs": pk16["bytes_per_launch"] / (pk16["kernel_ms"] / 1e3) / 1e9,
+            "packed_bytes_per_launch": pk16["bytes_per_launch"],
+            "replay_vs_packed_kernel": pk16["kernel_ms"] / rep16["kernel_ms"],
+            "replay_vs_fp32_replay": rep["kernel_ms"] / rep16["kernel_ms"],
+        },
         "verify_window_c5": wf,
         "lossless_verify_c6": ll,
         "cpu_baseline": None,

@@ -1,6 +1,7 @@
 // gdn_api.hip -- the C ABI (include/gdn_replay.h): host-side validation,
 // launch geometry and dispatch to the typed kernel instances. No call here
 // synchronises, allocates or frees.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -61,6 +62,11 @@ gdn_status check_shape(const gdn_shape* s, bool need_ring) {
 }
 
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+// ceil(2^32 / d) for the device's udiv (0 encodes d = 1).
+uint32_t recip(int d) {
+  return d <= 1 ? 0u : static_cast<uint32_t>(((1ull << 32) + static_cast<uint64_t>(d) - 1) / d);
+}
 
 hipError_t dispatch_packed(int dk, const DecodeArgs& a, int qkv, int sd, dim3 g, dim3 b,
                            size_t sm, hipStream_t st) {
@@ -129,6 +135,13 @@ void fill_replay_geometry(const gdn_shape* s, DecodeArgs& a, dim3& block, int& n
   a.nvb = s->dv / vb;
   block = dim3(64u * gh * (vb / 16));
   n_items = s->B * s->Hk * a.nhc * a.nvb;
+  a.gsz = a.nhc * a.nvb;
+  const int n_groups = n_items / a.gsz;
+  a.full_blocks = (n_groups / 8 * 8) * a.gsz;
+  a.m_gsz = recip(a.gsz);
+  a.m_hk = recip(s->Hk);
+  a.m_nvb = recip(a.nvb);
+  a.m_wph = recip(vb / 16);
 }
 
 }  // namespace
@@ -192,7 +205,14 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
   a.ff_flags = force_flush ? force_flush : slot_idx;
   dim3 block;
   int n_items = 0;
+  if (static_cast<uint64_t>(s->B) * s->Hv * (s->dv / 16) >= (1ull << 31))
+    return GDN_ERR_UNSUPPORTED;
   fill_replay_geometry(s, a, block, n_items);
+  {
+    // udiv() needs every numerator below 2^32 / divisor
+    const uint64_t dmax = std::max({a.gsz, s->Hk, a.nvb, 16});
+    if (static_cast<uint64_t>(n_items) * dmax >= (1ull << 32)) return GDN_ERR_UNSUPPORTED;
+  }
   size_t kt_bytes;
   if (s->ring_dtype == GDN_F32) {
     kt_bytes = static_cast<size_t>((s->L + 3) / 4 * 4) * s->dk * sizeof(float);

@@ -174,6 +174,14 @@ __device__ __forceinline__ T ld_uniform(const T* p, size_t i) {
 
 // ------------------------------------------------------------- launch mapping
 
+// n / d for a wave-uniform n < 2^32 / d, given m = ceil(2^32 / d) (m = 0 for
+// d = 1): with e = m d - 2^32 < d, n m / 2^32 = n / d + n e / (d 2^32) and the
+// excess stays below 1/d, so the floor is exact (Granlund and Montgomery's
+// division by invariant integers, in its round-up form).
+__device__ __forceinline__ uint32_t udiv(uint32_t n, uint32_t m) {
+  return m ? __umulhi(n, m) : n;
+}
+
 // Workgroups are handed to the 8 XCDs round-robin by workgroup id. The work
 // items come in groups of gsz consecutive items that share a row's key side
 // (q, k and the key ring of one key head). Map workgroup ids so that all items
@@ -492,6 +500,11 @@ struct DecodeArgs {
   int32_t kts;             // LDS row stride (elements) of the transposed key ring
   int32_t dump_off;        // LDS byte offset of the [64][8] fp32 write sink
   int32_t lds_buf;         // bytes of one LDS staging buffer (replay: two, by item parity)
+  // work-item mapping of the replay kernel without runtime divisions: the
+  // divisors (items per key-side group, Hk, value blocks, waves per head) come
+  // with their reciprocals m = ceil(2^32 / d) (0 for d = 1), see udiv()
+  int32_t gsz, full_blocks;
+  uint32_t m_gsz, m_hk, m_nvb, m_wph;
 };
 
 struct CursorArgs {

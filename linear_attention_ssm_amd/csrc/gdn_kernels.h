@@ -162,17 +162,28 @@ struct ItemGeo {
   int b, hk, hc, vb, h, vcol;
 };
 
-__device__ __forceinline__ ItemGeo item_geo(const DecodeArgs& a, int item, int wave, int col) {
+__device__ __forceinline__ ItemGeo item_geo(const DecodeArgs& a, int wave, int col) {
+  // block -> (key-side group, item within the group): the blocks of a group
+  // run on one XCD, consecutive groups on different XCDs (item_of_block)
+  const uint32_t i = blockIdx.x;
+  uint32_t grp_i, w;
+  if (static_cast<int>(i) < a.full_blocks) {
+    const uint32_t kk = i >> 3, q = udiv(kk, a.m_gsz);
+    w = kk - q * a.gsz;
+    grp_i = q * 8 + (i & 7);
+  } else {
+    grp_i = udiv(i, a.m_gsz);
+    w = i - grp_i * a.gsz;
+  }
   ItemGeo g;
-  g.vb = item % a.nvb;
-  int r = item / a.nvb;
-  g.hc = r % a.nhc;
-  r /= a.nhc;
-  g.hk = r % a.Hk;
-  g.b = r / a.Hk;
+  g.b = static_cast<int>(udiv(grp_i, a.m_hk));
+  g.hk = static_cast<int>(grp_i) - g.b * a.Hk;
+  g.hc = static_cast<int>(udiv(w, a.m_nvb));
+  g.vb = static_cast<int>(w) - g.hc * a.nvb;
   const int wph = a.VB / 16;                    // wavefronts per head
-  g.h = g.hk * a.G + g.hc * a.GH + wave / wph;
-  g.vcol = g.vb * a.VB + (wave % wph) * 16 + col;
+  const int wh = static_cast<int>(udiv(static_cast<uint32_t>(wave), a.m_wph));
+  g.h = g.hk * a.G + g.hc * a.GH + wh;
+  g.vcol = g.vb * a.VB + (wave - wh * wph) * 16 + col;
   return g;
 }
 
@@ -185,7 +196,8 @@ struct Small {
   int p_raw, ff_raw;
   float g_tok, b_tok;                              // lane t < T: token t's g and beta
   typename Raw4<QKV>::T q_raw, k_raw;
-  KC kr_raw[2];                                    // chunks tid and tid + blockDim
+  KC kr_raw;                                       // fp32 ring: chunk tid; 16-bit ring:
+                                                   // keys 2s, 2s+1 of four entries (ktile)
   float g_raw;
   RT d_raw[4];
   typename Elem<QKV>::T v_raw;
@@ -225,10 +237,20 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
   // entries (a cursor out of range is handled in process(); clamp meanwhile)
   const int pc = (f.p_raw >= 1 && f.p_raw <= a.L) ? f.p_raw : 1;
   const int nkc = pc * (DK / KV);                   // 16-byte chunks holding valid entries
-  const int c0 = tid < nkc ? tid : nkc - 1;
-  const int c1 = tid + static_cast<int>(blockDim.x) < nkc ? tid + static_cast<int>(blockDim.x) : nkc - 1;
-  f.kr_raw[0] = *reinterpret_cast<const KC*>(ksrc + c0 * KV);
-  f.kr_raw[1] = *reinterpret_cast<const KC*>(ksrc + c1 * KV);
+  if constexpr (RF32) {
+    const int c0 = tid < nkc ? tid : nkc - 1;
+    f.kr_raw = *reinterpret_cast<const KC*>(ksrc + c0 * KV);
+  } else {
+    // thread tid stages keys 8kg + 2sub, +1 of entries 4eg .. 4eg+3
+    const int pr = tid >> 2, sub = tid & 3;
+    const int eg = pr / (DK / 8), kg = pr % (DK / 8);
+    const uint32_t* k32 = reinterpret_cast<const uint32_t*>(ksrc + kg * 8 + 2 * sub);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * eg + i;
+      f.kr_raw[i] = __uint_as_float(k32[static_cast<size_t>(e < pc ? e : pc - 1) * (DK / 2)]);
+    }
+  }
   f.g_raw = a.ring_g[hs * a.L + (lane < pc ? lane : pc - 1)];
   // this lane's ring d entries 0..15: 16-bit rings j = 4*grp + i (one
   // 16x16x16 k-step), fp32 rings j = 4*i + grp (four 16x16x4 k-steps)
@@ -305,63 +327,114 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
   constexpr int KV = Small<DK, QKV, RING>::KV;      // ring elements per 16-byte chunk
   constexpr int CPR = DK / KV;                      // chunks per ring entry
   const int nkr = p * CPR;                          // chunks holding valid entries
-  // chunk c = entry j's keys e .. e+KV-1; 16-bit rings are stored transposed
-  auto put_kr = [&](int c, KC r, bool in) {
-    const int j = c / CPR, e = (c % CPR) * KV;
-    if constexpr (RF32) {
+  const int nkz = lp * CPR;                         // ... and the zero padding up to lp
+  if constexpr (RF32) {
+    // chunk c = entry j's keys e .. e+3; chunks of entries p..lp-1 are written
+    // as zeros (the MFMA reads them), the other threads write the dump area
+    auto put_kr = [&](int c, KC r) {
+      const bool in = c < nkz;
+      if (c >= nkr) r = KC{0.f, 0.f, 0.f, 0.f};
+      const int j = c / CPR, e = (c % CPR) * KV;
       *reinterpret_cast<f4*>(in ? kt + j * DK + e : dump + lane * 8) = r;
-    } else {
-      const u16x4 lo = __builtin_bit_cast(u16x4, __builtin_shufflevector(r, r, 0, 1));
-      const u16x4 hi = __builtin_bit_cast(u16x4, __builtin_shufflevector(r, r, 2, 3));
+    };
+    put_kr(tid, f.kr_raw);
+    for (int c = tid + nthr; c < nkz; c += nthr)
+      put_kr(c, c < nkr ? *reinterpret_cast<const KC*>(ksrc + c * KV) : KC{0.f, 0.f, 0.f, 0.f});
+  } else {
+    // transposed [key][entry] (row stride kts): a thread writes two keys x four
+    // entries as two 8-byte pieces; entries p..lp-1 are zeros
+    constexpr int NKG = DK / 8;
+    auto put_kt = [&](int pr, int sub, const uint32_t (&v)[4]) {
+      const int eg = pr / NKG, kg = pr % NKG;
+      const bool in = 4 * eg < lp;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (4 * eg + i < p) ? v[i] : 0u;
+      uint2 a0, a1;
+      a0.x = (w[0] & 0xffffu) | (w[1] << 16);
+      a0.y = (w[2] & 0xffffu) | (w[3] << 16);
+      a1.x = (w[0] >> 16) | (w[1] & 0xffff0000u);
+      a1.y = (w[2] >> 16) | (w[3] & 0xffff0000u);
       uint16_t* kt16 = reinterpret_cast<uint16_t*>(kt);
-      uint16_t* d16 = reinterpret_cast<uint16_t*>(dump + lane * 8);
+      const int key = kg * 8 + 2 * sub;
+      *reinterpret_cast<uint2*>(in ? kt16 + key * a.kts + 4 * eg : reinterpret_cast<uint16_t*>(dump + lane * 8)) = a0;
+      *reinterpret_cast<uint2*>(in ? kt16 + (key + 1) * a.kts + 4 * eg : reinterpret_cast<uint16_t*>(dump + lane * 8 + 2)) = a1;
+    };
+    {
+      uint32_t v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f.kr_raw[i]);
+      put_kt(tid >> 2, tid & 3, v);
+    }
+    const int npr = (lp / 4) * NKG;                    // (entry group, key group) pairs
+    for (int t2 = tid + nthr; t2 < 4 * npr; t2 += nthr) {   // deep rings / small workgroups
+      const int pr = t2 >> 2, sub = t2 & 3;
+      const int eg = pr / NKG, kg = pr % NKG;
+      const uint32_t* k32 = reinterpret_cast<const uint32_t*>(ksrc + kg * 8 + 2 * sub);
+      uint32_t v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        *(in ? kt16 + (e + i) * a.kts + j : d16 + i) = lo[i];
-        *(in ? kt16 + (e + 4 + i) * a.kts + j : d16 + 4 + i) = hi[i];
+        const int e = 4 * eg + i;
+        v[i] = e < p ? k32[static_cast<size_t>(e) * (DK / 2)] : 0u;
       }
+      put_kt(pr, sub, v);
     }
-  };
-  put_kr(tid, f.kr_raw[0], tid < nkr);
-  put_kr(tid + nthr, f.kr_raw[1], tid + nthr < nkr);
-  for (int c = tid + 2 * nthr; c < nkr; c += nthr)      // deep rings / small workgroups
-    put_kr(c, *reinterpret_cast<const KC*>(ksrc + c * KV), true);
-  for (int c = tid; c < (lp - p) * DK; c += nthr) {
-    const int j = p + c / DK, key = c % DK;
-    if constexpr (RF32) kt[j * DK + key] = 0.f;
-    else reinterpret_cast<uint16_t*>(kt)[key * a.kts + j] = 0;
   }
   // every token's decay at once (lane t: token t), while the slab is in flight
   const float al_tok = decay_of(f.g_tok);
-  __syncthreads();
 
-  // ---- reconstruction S = A S0 + sum_j w_j d_j k_j^T
-  f4 S[NT];
-  slab_decode<SD, DK>(S, R);
+  // ---- reconstruction weights, before the barrier: the suffix sums of the
+  // log-decays W_j = sum_{i>=j} g_i, A = exp(W_0), w_j = exp(W_{j+1}), and the
+  // MFMA operand w o D of the first k-steps (from the entries fetched early)
+  constexpr int NPRE = RF32 ? 4 : 1;                  // k-steps covered by the fetch
+  float A = 1.f, wj = 0.f;
+  typename MM::op_t bops[NPRE];
+  auto bop_of = [&](int c, const float (&dval)[4]) {
+    typename MM::op_t bop;
+    if constexpr (RF32) {
+      const int j = c * CH + grp;
+      bop = (j < p) ? __shfl(wj, j & 63, 64) * dval[0] : 0.f;
+    } else {
+      u16x4 bb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = c * CH + 4 * grp + i;
+        const float w = __shfl(wj, j & 63, 64);
+        bb[i] = __builtin_bit_cast(uint16_t, from_f32<RING>((j < p) ? w * dval[i] : 0.f));
+      }
+      bop = __builtin_bit_cast(typename MM::op_t, bb);
+    }
+    return bop;
+  };
   if (p > 0) {
     const float gj = lane < p ? f.g_raw : 0.f;          // lane j < p holds g_j
     // Lanes >= p hold g = 0, so the exclusive sum of lane p-1 is exactly 0
     // (empty product = 1).
     float W, Wn;                                        // W_j = sum_{i>=j} g_i, W_{j+1}
     wave_suffix_sums(gj, lane, p > 16, W, Wn);
-    const float wj = (lane < p) ? __expf(Wn) : 0.f;     // w_j = exp(W_{j+1})
-    const float A = __expf(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(W))));
-    const RT* dsrc = static_cast<const RT*>(a.ring_d) + hs * a.L * a.dv + g.vcol;
-    auto kstep = [&](int c, const float (&dval)[4]) {
-      typename MM::op_t bop;
-      if constexpr (RF32) {
-        const int j = c * CH + grp;
-        bop = (j < p) ? __shfl(wj, j & 63, 64) * dval[0] : 0.f;
-      } else {
-        u16x4 bb;
+    wj = (lane < p) ? __expf(Wn) : 0.f;                 // w_j = exp(W_{j+1})
+    A = __expf(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(W))));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = c * CH + 4 * grp + i;
-          const float w = __shfl(wj, j & 63, 64);
-          bb[i] = __builtin_bit_cast(uint16_t, from_f32<RING>((j < p) ? w * dval[i] : 0.f));
-        }
-        bop = __builtin_bit_cast(typename MM::op_t, bb);
+    for (int c = 0; c < NPRE; ++c) {
+      float dv1[4];
+      if constexpr (RF32) {
+        dv1[0] = (4 * c + grp < p) ? f.d_raw[c] : 0.f;
+        dv1[1] = dv1[2] = dv1[3] = 0.f;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dv1[i] = (4 * grp + i < p) ? to_f32<RING>(f.d_raw[i]) : 0.f;
       }
+      bops[c] = bop_of(c, dv1);
+    }
+  }
+  __syncthreads();
+
+  // ---- reconstruction S = A S0 + sum_j w_j d_j k_j^T
+  f4 S[NT];
+  slab_decode<SD, DK>(S, R);
+  if (p > 0) {
+    const RT* dsrc = static_cast<const RT*>(a.ring_d) + hs * a.L * a.dv + g.vcol;
+    auto kstep = [&](int c, typename MM::op_t bop) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         typename MM::op_t aop;
@@ -373,21 +446,9 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
     };
 #pragma unroll
     for (int t = 0; t < NT; ++t) S[t] *= A;
-    constexpr int NPRE = RF32 ? 4 : 1;                  // k-steps covered by the fetch
 #pragma unroll
-    for (int c = 0; c < NPRE; ++c) {
-      if (c < nch) {
-        float dv1[4];
-        if constexpr (RF32) {
-          dv1[0] = (4 * c + grp < p) ? f.d_raw[c] : 0.f;
-          dv1[1] = dv1[2] = dv1[3] = 0.f;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dv1[i] = (4 * grp + i < p) ? to_f32<RING>(f.d_raw[i]) : 0.f;
-        }
-        kstep(c, dv1);
-      }
-    }
+    for (int c = 0; c < NPRE; ++c)
+      if (c < nch) kstep(c, bops[c]);
     for (int c = NPRE; c < nch; ++c) {                  // rings deeper than 16 entries
       float dv1[4];
 #pragma unroll
@@ -395,7 +456,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
         const int j = RF32 ? (c * CH + grp) : (c * CH + 4 * grp + i);
         dv1[i] = (j < p && (!RF32 || i == 0)) ? to_f32<RING>(dsrc[static_cast<size_t>(j) * a.dv]) : 0.f;
       }
-      kstep(c, dv1);
+      kstep(c, bop_of(c, dv1));
     }
   }
 
@@ -444,8 +505,7 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4, col = lane & 15;
-  const int item = item_of_block(blockIdx.x, gridDim.x, a.nhc * a.nvb);
-  const ItemGeo g = item_geo(a, item, wave, col);
+  const ItemGeo g = item_geo(a, wave, col);
   const int s = ld_uniform(a.slot, g.b);
   Small<DK, QKV, RING> sm;
   SlabRaw<SD, DK> R;
