@@ -167,7 +167,7 @@ gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, c
   dim3 grid, block;
   fill_decode_geometry(s, a, grid, block);
   a.L = 1;
-  a.dump_off = static_cast<int32_t>(2u * s->dk * sizeof(float));
+  a.dump_off = static_cast<int32_t>((2u * s->dk + 4) * sizeof(float));   // q, k, k^T q
   const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
   return from_hip(dispatch_packed(s->dk, a, s->qkv_dtype, s->state_dtype, grid, block, smem,
                                   static_cast<hipStream_t>(stream)));
@@ -221,9 +221,15 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
     a.kts = (s->L + 15) / 16 * 16 + 4;
     kt_bytes = static_cast<size_t>(s->dk) * a.kts * 2;
   }
+  // LDS: q and k of every token (fp32), k^T q per token, the gates of the
+  // workgroup's heads, the staged key ring, a [64][8] fp32 write sink
+  auto up16 = [](size_t x) { return (x + 15) / 16 * 16; };
   const size_t qk_bytes = static_cast<size_t>(s->T) * 2 * s->dk * sizeof(float);
-  a.lds_buf = static_cast<int32_t>((qk_bytes + kt_bytes + 15) / 16 * 16);
-  a.dump_off = a.lds_buf;
+  a.kq_off = static_cast<int32_t>(qk_bytes);
+  a.gate_off = static_cast<int32_t>(qk_bytes + 16 * sizeof(float));
+  a.kt_off = static_cast<int32_t>(up16(a.gate_off + static_cast<size_t>(a.GH) * s->T * 3 * sizeof(float)));
+  a.dump_off = static_cast<int32_t>(up16(a.kt_off + kt_bytes));
+  a.lds_buf = a.dump_off;
   const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
   return from_hip(dispatch_replay(s->dk, a, s->qkv_dtype, s->ring_dtype, s->state_dtype,
                                   dim3(n_items), block,

@@ -213,6 +213,24 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Sum over aligned groups of C lanes (C a power of two, at most 64) by a
+// butterfly: after each step a lane and its partner hold the same two
+// operands, so every lane of the group ends with identical bits.
+template <int C>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < C; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// A buffer resource over `nbytes` bytes at the wave-uniform `base`. Loads
+// through it at offsets past nbytes return zero without touching memory
+// (raw buffer bounds check), which is how reads are limited to the valid
+// ring entries and how a masked row reads nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, 0x00020000);
+}
+
 // x from lane l + n of the same 16-lane row (0 past the row end), by DPP.
 template <int N>
 __device__ __forceinline__ float row_shl(float x) {
@@ -322,9 +340,8 @@ __device__ __forceinline__ void slab_decode(f4 (&S)[DK / 16], const SlabRaw<SD, 
 // of the token's q and k in LDS.
 template <int SD, int NT>
 __device__ __forceinline__ void slab_dots(const f4 (&S)[NT], const float* q_l,
-                                          const float* k_l, int grp, float& sq,
-                                          float& sk, float& kq) {
-  float pq = 0.f, pk = 0.f, pkq = 0.f;
+                                          const float* k_l, int grp, float& sq, float& sk) {
+  float pq = 0.f, pk = 0.f;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const f4 qv = *reinterpret_cast<const f4*>(q_l + key_base<SD>(t, grp));
@@ -337,14 +354,22 @@ __device__ __forceinline__ void slab_dots(const f4 (&S)[NT], const float* q_l,
     pk = __builtin_fmaf(S[t].y, kv.y, pk);
     pk = __builtin_fmaf(S[t].z, kv.z, pk);
     pk = __builtin_fmaf(S[t].w, kv.w, pk);
-    pkq = __builtin_fmaf(kv.x, qv.x, pkq);
-    pkq = __builtin_fmaf(kv.y, qv.y, pkq);
-    pkq = __builtin_fmaf(kv.z, qv.z, pkq);
-    pkq = __builtin_fmaf(kv.w, qv.w, pkq);
   }
   sq = quad_sum(pq);
   sk = quad_sum(pk);
-  kq = quad_sum(pkq);
+}
+
+// k^T q of one token, from the staging threads' four-key pieces: each of the
+// DK/4 threads that stage the token's q and k forms its partial product, and
+// the group of DK/4 lanes sums them. Every kernel that reads a token out uses
+// this one order, so the packed and the replay decode agree bit for bit.
+template <int DK>
+__device__ __forceinline__ float token_kq(f4 qv, f4 kv) {
+  float x = qv.x * kv.x;
+  x = __builtin_fmaf(qv.y, kv.y, x);
+  x = __builtin_fmaf(qv.z, kv.z, x);
+  x = __builtin_fmaf(qv.w, kv.w, x);
+  return group_sum<DK / 4>(x);
 }
 
 // alpha = exp(g) of one step, evaluated in double and rounded once to fp32.
@@ -505,6 +530,9 @@ struct DecodeArgs {
   // with their reciprocals m = ceil(2^32 / d) (0 for d = 1), see udiv()
   int32_t gsz, full_blocks;
   uint32_t m_gsz, m_hk, m_nvb, m_wph;
+  // LDS byte offsets: per-token k^T q, per (head, token) gates (alpha, beta,
+  // g), the staged key ring
+  int32_t kq_off, gate_off, kt_off;
 };
 
 struct CursorArgs {

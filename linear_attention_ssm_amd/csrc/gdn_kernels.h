@@ -93,10 +93,15 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
     // unconditional writes (surplus threads into the dump area) keep the
     // early q/k loads ahead of the state loads
     float* dump = reinterpret_cast<float*>(smem + a.dump_off);
+    const f4 qv = decode4<QKV>(q_raw), kv = decode4<QKV>(k_raw);
     float* qdst = tid < C4 ? qk + 4 * tid : dump + lane * 8;
     float* kdst = tid < C4 ? qk + DK + 4 * tid : dump + lane * 8 + 4;
-    *reinterpret_cast<f4*>(qdst) = decode4<QKV>(q_raw);
-    *reinterpret_cast<f4*>(kdst) = decode4<QKV>(k_raw);
+    *reinterpret_cast<f4*>(qdst) = qv;
+    *reinterpret_cast<f4*>(kdst) = kv;
+    if (wave == 0) {
+      const float kq0 = token_kq<DK>(qv, kv);
+      if (lane == 0) qk[2 * DK] = kq0;
+    }
   }
   const float alpha = decay_of(gv);   // while the state is in flight
   __syncthreads();
@@ -104,8 +109,9 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
 
   f4 S[NT];
   slab_decode<SD, DK>(S, R);
-  float sq, sk, kq, d, o;
-  slab_dots<SD>(S, qk, qk + DK, grp, sq, sk, kq);
+  float sq, sk, d, o;
+  const float kq = qk[2 * DK];
+  slab_dots<SD>(S, qk, qk + DK, grp, sq, sk);
   token_out(sq, sk, kq, alpha, bt, vv, d, o);
   if (grp == 0) store1<QKV>(a.o, ih * a.dv + vcol, o);
   slab_update<SD>(S, qk + DK, grp, alpha, d);
@@ -190,198 +196,212 @@ __device__ __forceinline__ ItemGeo item_geo(const DecodeArgs& a, int wave, int c
 // The small operands of one item, as raw (undecoded) registers.
 template <int DK, int QKV, int RING>
 struct Small {
-  using RT = typename Elem<RING>::T;
-  using KC = f4;                                   // 16 bytes of the key ring
-  static constexpr int KV = 16 / sizeof(RT);        // ring elements per chunk
-  int p_raw, ff_raw;
-  float g_tok, b_tok;                              // lane t < T: token t's g and beta
-  typename Raw4<QKV>::T q_raw, k_raw;
-  KC kr_raw;                                       // fp32 ring: chunk tid; 16-bit ring:
-                                                   // keys 2s, 2s+1 of four entries (ktile)
-  float g_raw;
-  RT d_raw[4];
+  typename Raw4<QKV>::T q_raw, k_raw;   // staging threads: four keys of q and k
+  v4u kr;                               // key-ring piece of this thread (see fetch_small)
+  uint32_t g_raw;                       // ring g of entry `lane` (0 past the valid entries)
+  uint32_t d_raw[4];                    // this lane's ring d entries (raw bits)
+  float gate_g, gate_b;                 // wave 0, lane hh*T+t: g and beta of head hh, token t
   typename Elem<QKV>::T v_raw;
 };
 
-// Request an item's small operands: the cursor, the flush flag and the gates
-// (scalar loads), q/k, two 16-byte key-ring chunks per thread, the lane's
-// ring d entries and g, v. Every vector load is unconditional, from an
-// address clamped into its buffer (ring reads to the valid entries); an
-// invalid slot or cursor is masked in process().
-template <int DK, int QKV, int RING>
+// Where a row stands: its slot, its valid ring entries and whether it flushes.
+// A padding row (negative slot), a slot beyond the pool and a cursor out of
+// range all run masked: p = 0, zero output, no state or ring write.
+struct RowState {
+  int s, sc;          // slot, and the slot clamped into the pool
+  int p;              // valid ring entries read (0 for a masked row)
+  int ef;             // error bits of the row
+  bool slot_ok, ok, flush;
+};
+
+__device__ __forceinline__ RowState row_state(const DecodeArgs& a, int b, int T) {
+  RowState r;
+  r.s = ld_uniform(a.slot, b);
+  r.slot_ok = r.s >= 0 && r.s < a.N;
+  r.sc = r.slot_ok ? r.s : 0;
+  const int p_raw = ld_uniform(a.write_pos, r.sc);
+  const int ff = ld_uniform(a.ff_flags, b);
+  r.ef = r.s >= a.N ? EF_SLOT : 0;
+  if (r.slot_ok)
+    r.ef = a.window ? ((p_raw < 0 || p_raw + T > a.L) ? EF_WINDOW : 0)
+                    : ((p_raw < 0 || p_raw > a.L - 1) ? EF_CURSOR : 0);
+  r.ok = r.slot_ok && r.ef == 0;
+  r.p = r.ok ? p_raw : 0;
+  r.flush = r.ok && !a.window && (p_raw == a.L - 1 || (a.ff_on && ff != 0));
+  return r;
+}
+
+// Request an item's small operands. The ring reads go through buffer
+// resources sized to the valid entries, so that entries at or past p read as
+// zero without a memory access (they are also the MFMA's zero padding). All
+// loads are unconditional (surplus lanes read a clamped address) so that they
+// issue before the slab.
+template <int DK, int QKV, int RING, int TT>
 __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const DecodeArgs& a,
-                                            const ItemGeo& g, int s, int tid, int lane,
-                                            int grp) {
+                                            const ItemGeo& g, const RowState& r, int T,
+                                            int tid, int lane, int grp, int wave) {
   constexpr int C4 = DK / 4;
   constexpr bool RF32 = (RING == DT_F32);
-  using RT = typename Elem<RING>::T;
-  using KC = typename Small<DK, QKV, RING>::KC;
-  const int sc = (s >= 0 && s < a.N) ? s : 0;
-  const size_t hs = static_cast<size_t>(sc) * a.Hv + g.h;
-  const size_t ks = static_cast<size_t>(sc) * a.Hk + g.hk;
-  f.p_raw = ld_uniform(a.write_pos, sc);
-  f.ff_raw = ld_uniform(a.ff_flags, g.b);
-  const size_t ih0 = static_cast<size_t>(g.b) * a.T * a.Hv + g.h;   // token 0
-  const size_t iht = ih0 + static_cast<size_t>(lane < a.T ? lane : 0) * a.Hv;
-  f.g_tok = a.g[iht];
-  f.b_tok = a.beta[iht];
-  const int nqk = a.T * C4;
+  constexpr int RS = RF32 ? 4 : 2;
+  // wave 0: the gates of the workgroup's GH heads, lane hh*T + t
+  if (wave == 0) {
+    const int ng = a.GH * T;
+    const int l = lane < ng ? lane : 0;
+    const int hh = TT ? l : l / T, t = TT ? 0 : l - hh * T;
+    const size_t gi = (static_cast<size_t>(g.b) * T + t) * a.Hv + g.hk * a.G + g.hc * a.GH + hh;
+    f.gate_g = a.g[gi];
+    f.gate_b = a.beta[gi];
+  }
+  // staging threads: four keys of q and k of token c / C4
+  const int nqk = T * C4;
   const int cq = tid < nqk ? tid : nqk - 1;
-  const size_t qsrc = ((static_cast<size_t>(g.b) * a.T + cq / C4) * a.Hk + g.hk) * DK + (cq % C4) * 4;
+  const int tq = TT ? 0 : cq / C4;
+  const size_t qsrc = ((static_cast<size_t>(g.b) * T + tq) * a.Hk + g.hk) * DK + (cq - tq * C4) * 4;
   f.q_raw = load4_raw<QKV>(a.q, qsrc);
   f.k_raw = load4_raw<QKV>(a.k, qsrc);
-  constexpr int KV = Small<DK, QKV, RING>::KV;
-  const RT* ksrc = static_cast<const RT*>(a.ring_k) + ks * a.L * DK;
-  // the cursor arrives through the scalar cache: waiting for it here does not
-  // wait for any vector load, and it bounds the ring reads to the valid
-  // entries (a cursor out of range is handled in process(); clamp meanwhile)
-  const int pc = (f.p_raw >= 1 && f.p_raw <= a.L) ? f.p_raw : 1;
-  const int nkc = pc * (DK / KV);                   // 16-byte chunks holding valid entries
+  // the key ring of (slot, key head), the valid entries only
+  const char* kbase = static_cast<const char*>(a.ring_k) +
+                      (static_cast<size_t>(r.sc) * a.Hk + g.hk) * a.L * DK * RS;
+  const __amdgpu_buffer_rsrc_t rk = brsrc(kbase, static_cast<uint32_t>(r.p) * DK * RS);
   if constexpr (RF32) {
-    const int c0 = tid < nkc ? tid : nkc - 1;
-    f.kr_raw = *reinterpret_cast<const KC*>(ksrc + c0 * KV);
+    f.kr = __builtin_amdgcn_raw_buffer_load_b128(rk, tid * 16, 0, 0);   // chunk tid
   } else {
-    // thread tid stages keys 8kg + 2sub, +1 of entries 4eg .. 4eg+3
+    // keys 8kg + 2sub, +1 of entries 4eg .. 4eg+3
     const int pr = tid >> 2, sub = tid & 3;
     const int eg = pr / (DK / 8), kg = pr % (DK / 8);
-    const uint32_t* k32 = reinterpret_cast<const uint32_t*>(ksrc + kg * 8 + 2 * sub);
+    const int off = (4 * eg * DK + kg * 8 + 2 * sub) * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * eg + i;
-      f.kr_raw[i] = __uint_as_float(k32[static_cast<size_t>(e < pc ? e : pc - 1) * (DK / 2)]);
-    }
+    for (int i = 0; i < 4; ++i) f.kr[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + i * DK * 2, 0, 0);
   }
-  f.g_raw = a.ring_g[hs * a.L + (lane < pc ? lane : pc - 1)];
-  // this lane's ring d entries 0..15: 16-bit rings j = 4*grp + i (one
-  // 16x16x16 k-step), fp32 rings j = 4*i + grp (four 16x16x4 k-steps)
-  const RT* dsrc = static_cast<const RT*>(a.ring_d) + hs * a.L * a.dv + g.vcol;
+  const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
+  const __amdgpu_buffer_rsrc_t rg = brsrc(a.ring_g + hs * a.L, static_cast<uint32_t>(r.p) * 4);
+  f.g_raw = __builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0);
+  // this lane's ring d entries: 16-bit rings j = 4*grp + i (one 16x16x16
+  // k-step), fp32 rings j = 4*i + grp (four 16x16x4 k-steps)
+  const char* dbase = static_cast<const char*>(a.ring_d) + hs * a.L * a.dv * RS;
+  const __amdgpu_buffer_rsrc_t rd = brsrc(dbase, static_cast<uint32_t>(r.p) * a.dv * RS);
+  if constexpr (RF32) {
+    const int off = (grp * a.dv + g.vcol) * 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = RF32 ? (4 * i + grp) : (4 * grp + i);
-    f.d_raw[i] = dsrc[static_cast<size_t>(j < pc ? j : pc - 1) * a.dv];
+    for (int i = 0; i < 4; ++i) f.d_raw[i] = __builtin_amdgcn_raw_buffer_load_b32(rd, off, 16 * i * a.dv, 0);
+  } else {
+    const int off = (4 * grp * a.dv + g.vcol) * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.d_raw[i] = __builtin_amdgcn_raw_buffer_load_b16(rd, off, 2 * i * a.dv, 0);
   }
-  f.v_raw = load1_raw<QKV>(a.v, ih0 * a.dv + g.vcol);
+  f.v_raw = load1_raw<QKV>(a.v, (static_cast<size_t>(g.b) * T * a.Hv + g.h) * a.dv + g.vcol);
 }
 
 // Request an item's 16-row checkpoint slab: 16-byte loads in the lane order
-// of the accumulator layout (widened to fp32 in process()).
+// of the accumulator layout (widened to fp32 in process()). A masked row
+// reads nothing (zeros).
 template <int SD, int DK>
 __device__ __forceinline__ void fetch_slab(SlabRaw<SD, DK>& R, const DecodeArgs& a,
-                                           const ItemGeo& g, int s, int col, int grp) {
-  const int sc = (s >= 0 && s < a.N) ? s : 0;
-  const size_t hs = static_cast<size_t>(sc) * a.Hv + g.h;
-  using SE = typename Elem<SD>::T;
-  slab_load<SD, DK>(R, static_cast<const SE*>(a.state) + (hs * a.dv + g.vcol - col) * DK, col, grp);
+                                           const ItemGeo& g, const RowState& r, int col, int grp) {
+  constexpr int ES = SD == DT_F32 ? 4 : 2;
+  const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
+  const char* base = static_cast<const char*>(a.state) + (hs * a.dv + g.vcol - col) * DK * ES;
+  const __amdgpu_buffer_rsrc_t rs = brsrc(base, r.ok ? 16 * DK * ES : 0);
+  const int off = (col * DK + (SD == DT_F32 ? 4 : 8) * grp) * ES;
+#pragma unroll
+  for (int t = 0; t < SlabRaw<SD, DK>::NP; ++t)
+    R.r[t] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * t, 0, 0);
 }
 
-template <int DK, int QKV, int RING, int SD>
-__device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, int s,
-                                        const Small<DK, QKV, RING>& f, const SlabRaw<SD, DK>& R,
-                                        unsigned char* buf, float* dump, int tid, int lane,
-                                        int grp, int col, int wave) {
+template <int DK, int QKV, int RING, int SD, int TT>
+__device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, const RowState& r,
+                                        int T, const Small<DK, QKV, RING>& f,
+                                        const SlabRaw<SD, DK>& R, unsigned char* buf, float* dump,
+                                        int tid, int lane, int grp, int col, int wave) {
   constexpr int NT = DK / 16;
   constexpr int C4 = DK / 4;
   using RT = typename Elem<RING>::T;
   using MM = RingMfma<RING>;
-  using KC = typename Small<DK, QKV, RING>::KC;
   constexpr int CH = MM::CH;
   constexpr bool RF32 = (RING == DT_F32);
+  constexpr int RS = RF32 ? 4 : 2;
   const int nthr = blockDim.x;
-  float* qk = reinterpret_cast<float*>(buf);
-  RT* kt = reinterpret_cast<RT*>(buf + static_cast<size_t>(a.T) * 2 * DK * sizeof(float));
-
-  // ---- row resolve: a padding row (negative slot), a slot beyond the pool
-  // or a cursor out of range runs masked with an empty ring: zero output,
-  // no state or ring write
-  const bool slot_ok = (s >= 0 && s < a.N);
-  int ef = (s >= a.N) ? EF_SLOT : 0;
-  if (slot_ok)
-    ef = a.window ? ((f.p_raw < 0 || f.p_raw + a.T > a.L) ? EF_WINDOW : 0)
-                  : ((f.p_raw < 0 || f.p_raw > a.L - 1) ? EF_CURSOR : 0);
-  const bool row_ok = slot_ok && ef == 0;
-  if (ef && tid == 0 && a.err) atomicOr(a.err, ef);
-  const int p = row_ok ? f.p_raw : 0;
+  float* qk = reinterpret_cast<float*>(buf);                      // [T][2][DK]
+  float* kq_l = reinterpret_cast<float*>(buf + a.kq_off);         // [T]
+  float* gates = reinterpret_cast<float*>(buf + a.gate_off);      // [GH*T][alpha, beta, g]
+  RT* kt = reinterpret_cast<RT*>(buf + a.kt_off);                 // staged key ring
+  if (r.ef && tid == 0 && a.err) atomicOr(a.err, r.ef);
+  const int p = r.p;
   const int nch = (p + CH - 1) / CH;   // MFMA k-steps over the valid entries
   const int lp = nch * CH;             // entries covered, zero-padded beyond p
-  const int nqk = a.T * C4;
-  const int sc = slot_ok ? s : 0;
-  const size_t hs = static_cast<size_t>(sc) * a.Hv + g.h;
-  const size_t ks = static_cast<size_t>(sc) * a.Hk + g.hk;
+  const int nqk = T * C4;
 
-  // ---- LDS staging. Every thread writes (threads past the last chunk into a
+  // ---- LDS staging. Every thread writes (threads past the last piece into a
   // per-lane dump area) so the early loads have unconditional uses.
   {
     const f4 qv = decode4<QKV>(f.q_raw), kv = decode4<QKV>(f.k_raw);
-    float* qdst = tid < nqk ? qk + ((tid / C4) * 2) * DK + (tid % C4) * 4 : dump + lane * 8;
+    const int tq = TT ? 0 : tid / C4;
+    float* qdst = tid < nqk ? qk + tq * 2 * DK + (tid - tq * C4) * 4 : dump + lane * 8;
     float* kdst = tid < nqk ? qdst + DK : dump + lane * 8 + 4;
     *reinterpret_cast<f4*>(qdst) = qv;
     *reinterpret_cast<f4*>(kdst) = kv;
+    if (64 * wave < nqk) {                       // waves holding staging threads
+      const float kq0 = token_kq<DK>(qv, kv);
+      if (tid < nqk && tid - tq * C4 == 0) kq_l[tq] = kq0;
+    }
   }
   for (int c = tid + nthr; c < nqk; c += nthr) {        // long windows only
     const int tau = c / C4, e4 = (c % C4) * 4;
-    const size_t src = ((static_cast<size_t>(g.b) * a.T + tau) * a.Hk + g.hk) * DK + e4;
-    *reinterpret_cast<f4*>(qk + (tau * 2 + 0) * DK + e4) = load4<QKV>(a.q, src);
-    *reinterpret_cast<f4*>(qk + (tau * 2 + 1) * DK + e4) = load4<QKV>(a.k, src);
+    const size_t src = ((static_cast<size_t>(g.b) * T + tau) * a.Hk + g.hk) * DK + e4;
+    const f4 qv = load4<QKV>(a.q, src), kv = load4<QKV>(a.k, src);
+    *reinterpret_cast<f4*>(qk + (tau * 2 + 0) * DK + e4) = qv;
+    *reinterpret_cast<f4*>(qk + (tau * 2 + 1) * DK + e4) = kv;
+    const float kq0 = token_kq<DK>(qv, kv);   // groups of C4 lanes stay aligned
+    if (e4 == 0) kq_l[tau] = kq0;
   }
-  const RT* ksrc = static_cast<const RT*>(a.ring_k) + ks * a.L * DK;
-  constexpr int KV = Small<DK, QKV, RING>::KV;      // ring elements per 16-byte chunk
-  constexpr int CPR = DK / KV;                      // chunks per ring entry
-  const int nkr = p * CPR;                          // chunks holding valid entries
-  const int nkz = lp * CPR;                         // ... and the zero padding up to lp
+  // gates of the workgroup's heads (wave 0): alpha = RN_f32(exp_f64(g))
+  if (wave == 0) {
+    const float al = decay_of(f.gate_g);
+    if (lane < a.GH * T) {
+      gates[3 * lane + 0] = al;
+      gates[3 * lane + 1] = f.gate_b;
+      gates[3 * lane + 2] = f.gate_g;
+    }
+  }
+  // the key ring, entries p..lp-1 as zeros (the bounded loads read them so)
+  const char* kbase = static_cast<const char*>(a.ring_k) +
+                      (static_cast<size_t>(r.sc) * a.Hk + g.hk) * a.L * DK * RS;
+  const __amdgpu_buffer_rsrc_t rk = brsrc(kbase, static_cast<uint32_t>(p) * DK * RS);
   if constexpr (RF32) {
-    // chunk c = entry j's keys e .. e+3; chunks of entries p..lp-1 are written
-    // as zeros (the MFMA reads them), the other threads write the dump area
-    auto put_kr = [&](int c, KC r) {
-      const bool in = c < nkz;
-      if (c >= nkr) r = KC{0.f, 0.f, 0.f, 0.f};
-      const int j = c / CPR, e = (c % CPR) * KV;
-      *reinterpret_cast<f4*>(in ? kt + j * DK + e : dump + lane * 8) = r;
-    };
-    put_kr(tid, f.kr_raw);
+    const int nkz = lp * (DK / 4);               // 16-byte chunks up to lp
+    *reinterpret_cast<v4u*>(tid < nkz ? kt + tid * 4 : reinterpret_cast<RT*>(dump + lane * 8)) = f.kr;
     for (int c = tid + nthr; c < nkz; c += nthr)
-      put_kr(c, c < nkr ? *reinterpret_cast<const KC*>(ksrc + c * KV) : KC{0.f, 0.f, 0.f, 0.f});
+      *reinterpret_cast<v4u*>(kt + c * 4) = __builtin_amdgcn_raw_buffer_load_b128(rk, c * 16, 0, 0);
   } else {
     // transposed [key][entry] (row stride kts): a thread writes two keys x four
-    // entries as two 8-byte pieces; entries p..lp-1 are zeros
+    // entries as two 8-byte pieces
     constexpr int NKG = DK / 8;
-    auto put_kt = [&](int pr, int sub, const uint32_t (&v)[4]) {
+    auto put_kt = [&](int pr, int sub, const v4u& v) {
       const int eg = pr / NKG, kg = pr % NKG;
       const bool in = 4 * eg < lp;
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (4 * eg + i < p) ? v[i] : 0u;
       uint2 a0, a1;
-      a0.x = (w[0] & 0xffffu) | (w[1] << 16);
-      a0.y = (w[2] & 0xffffu) | (w[3] << 16);
-      a1.x = (w[0] >> 16) | (w[1] & 0xffff0000u);
-      a1.y = (w[2] >> 16) | (w[3] & 0xffff0000u);
+      a0.x = (v[0] & 0xffffu) | (v[1] << 16);
+      a0.y = (v[2] & 0xffffu) | (v[3] << 16);
+      a1.x = (v[0] >> 16) | (v[1] & 0xffff0000u);
+      a1.y = (v[2] >> 16) | (v[3] & 0xffff0000u);
       uint16_t* kt16 = reinterpret_cast<uint16_t*>(kt);
       const int key = kg * 8 + 2 * sub;
-      *reinterpret_cast<uint2*>(in ? kt16 + key * a.kts + 4 * eg : reinterpret_cast<uint16_t*>(dump + lane * 8)) = a0;
-      *reinterpret_cast<uint2*>(in ? kt16 + (key + 1) * a.kts + 4 * eg : reinterpret_cast<uint16_t*>(dump + lane * 8 + 2)) = a1;
+      uint16_t* d16 = reinterpret_cast<uint16_t*>(dump + lane * 8);
+      *reinterpret_cast<uint2*>(in ? kt16 + key * a.kts + 4 * eg : d16) = a0;
+      *reinterpret_cast<uint2*>(in ? kt16 + (key + 1) * a.kts + 4 * eg : d16 + 4) = a1;
     };
-    {
-      uint32_t v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f.kr_raw[i]);
-      put_kt(tid >> 2, tid & 3, v);
-    }
+    put_kt(tid >> 2, tid & 3, f.kr);
     const int npr = (lp / 4) * NKG;                    // (entry group, key group) pairs
     for (int t2 = tid + nthr; t2 < 4 * npr; t2 += nthr) {   // deep rings / small workgroups
       const int pr = t2 >> 2, sub = t2 & 3;
       const int eg = pr / NKG, kg = pr % NKG;
-      const uint32_t* k32 = reinterpret_cast<const uint32_t*>(ksrc + kg * 8 + 2 * sub);
-      uint32_t v[4];
+      const int off = (4 * eg * DK + kg * 8 + 2 * sub) * 2;
+      v4u v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * eg + i;
-        v[i] = e < p ? k32[static_cast<size_t>(e) * (DK / 2)] : 0u;
-      }
+      for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + i * DK * 2, 0, 0);
       put_kt(pr, sub, v);
     }
   }
-  // every token's decay at once (lane t: token t), while the slab is in flight
-  const float al_tok = decay_of(f.g_tok);
 
   // ---- reconstruction weights, before the barrier: the suffix sums of the
   // log-decays W_j = sum_{i>=j} g_i, A = exp(W_0), w_j = exp(W_{j+1}), and the
@@ -392,37 +412,38 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
   auto bop_of = [&](int c, const float (&dval)[4]) {
     typename MM::op_t bop;
     if constexpr (RF32) {
-      const int j = c * CH + grp;
-      bop = (j < p) ? __shfl(wj, j & 63, 64) * dval[0] : 0.f;
+      bop = __shfl(wj, (c * CH + grp) & 63, 64) * dval[0];
     } else {
       u16x4 bb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = c * CH + 4 * grp + i;
-        const float w = __shfl(wj, j & 63, 64);
-        bb[i] = __builtin_bit_cast(uint16_t, from_f32<RING>((j < p) ? w * dval[i] : 0.f));
+        const float w = __shfl(wj, (c * CH + 4 * grp + i) & 63, 64);
+        bb[i] = __builtin_bit_cast(uint16_t, from_f32<RING>(w * dval[i]));
       }
       bop = __builtin_bit_cast(typename MM::op_t, bb);
     }
     return bop;
   };
+  auto dval_of = [&](uint32_t raw) {
+    if constexpr (RF32) return __uint_as_float(raw);
+    else return to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(raw)));
+  };
   if (p > 0) {
-    const float gj = lane < p ? f.g_raw : 0.f;          // lane j < p holds g_j
-    // Lanes >= p hold g = 0, so the exclusive sum of lane p-1 is exactly 0
-    // (empty product = 1).
+    // entries at or past p read as g = 0: the exclusive sum of lane p-1 is
+    // exactly 0 (empty product = 1)
     float W, Wn;                                        // W_j = sum_{i>=j} g_i, W_{j+1}
-    wave_suffix_sums(gj, lane, p > 16, W, Wn);
+    wave_suffix_sums(__uint_as_float(f.g_raw), lane, p > 16, W, Wn);
     wj = (lane < p) ? __expf(Wn) : 0.f;                 // w_j = exp(W_{j+1})
     A = __expf(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(W))));
 #pragma unroll
     for (int c = 0; c < NPRE; ++c) {
       float dv1[4];
       if constexpr (RF32) {
-        dv1[0] = (4 * c + grp < p) ? f.d_raw[c] : 0.f;
+        dv1[0] = dval_of(f.d_raw[c]);
         dv1[1] = dv1[2] = dv1[3] = 0.f;
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dv1[i] = (4 * grp + i < p) ? to_f32<RING>(f.d_raw[i]) : 0.f;
+        for (int i = 0; i < 4; ++i) dv1[i] = dval_of(f.d_raw[i]);
       }
       bops[c] = bop_of(c, dv1);
     }
@@ -433,7 +454,6 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
   f4 S[NT];
   slab_decode<SD, DK>(S, R);
   if (p > 0) {
-    const RT* dsrc = static_cast<const RT*>(a.ring_d) + hs * a.L * a.dv + g.vcol;
     auto kstep = [&](int c, typename MM::op_t bop) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -449,37 +469,50 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
 #pragma unroll
     for (int c = 0; c < NPRE; ++c)
       if (c < nch) kstep(c, bops[c]);
-    for (int c = NPRE; c < nch; ++c) {                  // rings deeper than 16 entries
-      float dv1[4];
+    if (nch > NPRE) {                                   // rings deeper than 16 entries
+      const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
+      const char* dbase = static_cast<const char*>(a.ring_d) + hs * a.L * a.dv * RS;
+      const __amdgpu_buffer_rsrc_t rd = brsrc(dbase, static_cast<uint32_t>(p) * a.dv * RS);
+      for (int c = NPRE; c < nch; ++c) {
+        float dv1[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = RF32 ? (c * CH + grp) : (c * CH + 4 * grp + i);
-        dv1[i] = (j < p && (!RF32 || i == 0)) ? to_f32<RING>(dsrc[static_cast<size_t>(j) * a.dv]) : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (RF32) {
+            dv1[i] = i == 0 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                  rd, ((c * CH + grp) * a.dv + g.vcol) * 4, 0, 0))
+                            : 0.f;
+          } else {
+            dv1[i] = dval_of(__builtin_amdgcn_raw_buffer_load_b16(
+                rd, ((c * CH + 4 * grp + i) * a.dv + g.vcol) * 2, 0, 0));
+          }
+        }
+        kstep(c, bop_of(c, dv1));
       }
-      kstep(c, bop_of(c, dv1));
     }
   }
 
   // ---- tokens
-  const bool flush = row_ok && !a.window && (p == a.L - 1 || (a.ff_on && f.ff_raw != 0));
   const int wph = a.VB / 16;
+  const int wh = g.h - (g.hk * a.G + g.hc * a.GH);              // head within the workgroup
   const bool kwriter = (g.vb == 0) && (g.hc == 0) && (wave == 0);   // one key-ring writer per k-head
   const bool gwriter = (g.vb == 0) && (wave % wph == 0) && lane == 0;
+  const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
+  const size_t ks = static_cast<size_t>(r.sc) * a.Hk + g.hk;
   float vv = to_f32<QKV>(f.v_raw);
-  for (int tau = 0; tau < a.T; ++tau) {
+  for (int tau = 0; tau < T; ++tau) {
     const float* ql = qk + tau * 2 * DK;
     const float* kl = ql + DK;
-    const size_t ih = (static_cast<size_t>(g.b) * a.T + tau) * a.Hv + g.h;
+    const size_t ih = (static_cast<size_t>(g.b) * T + tau) * a.Hv + g.h;
     // the next window token's v is requested before this token's readout
-    const float v_next = tau + 1 < a.T ? load1<QKV>(a.v, (ih + a.Hv) * a.dv + g.vcol) : 0.f;
-    const float gv = lane_value(f.g_tok, tau);
-    const float bt = lane_value(f.b_tok, tau);
-    const float alpha = lane_value(al_tok, tau);
-    float sq, sk, kq, d, o;
-    slab_dots<SD>(S, ql, kl, grp, sq, sk, kq);
+    const float v_next = (!TT && tau + 1 < T) ? load1<QKV>(a.v, (ih + a.Hv) * a.dv + g.vcol) : 0.f;
+    const float* gt = gates + 3 * (wh * T + tau);
+    const float alpha = gt[0], bt = gt[1], gv = gt[2];
+    const float kq = kq_l[tau];
+    float sq, sk, d, o;
+    slab_dots<SD>(S, ql, kl, grp, sq, sk);
     token_out(sq, sk, kq, alpha, bt, vv, d, o);
-    if (grp == 0) store1<QKV>(a.o, ih * a.dv + g.vcol, row_ok ? o : 0.f);
-    if (row_ok && !flush) {
+    if (grp == 0) store1<QKV>(a.o, ih * a.dv + g.vcol, r.ok ? o : 0.f);
+    if (r.ok && !r.flush) {
       const int pos = p + tau;
       if (grp == 0) store1<RING>(a.ring_d, (hs * a.L + pos) * a.dv + g.vcol, d);
       if (gwriter) a.ring_g[hs * a.L + pos] = gv;
@@ -488,31 +521,32 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, i
         store4<RING>(a.ring_k, (ks * a.L + pos) * DK + 4 * lane, kv);
       }
     }
-    if (flush || (a.window && tau + 1 < a.T)) slab_update<SD>(S, kl, grp, alpha, d);
+    if (r.flush || (!TT && a.window && tau + 1 < T)) slab_update<SD>(S, kl, grp, alpha, d);
     vv = v_next;
   }
-  if (flush) {
+  if (r.flush) {
     using SE = typename Elem<SD>::T;
     store_slab<SD, DK>(static_cast<SE*>(a.state) + (hs * a.dv + g.vcol - col) * DK, S, col, grp);
   }
 }
 
-template <int DK, int QKV, int RING, int SD>
+template <int DK, int QKV, int RING, int SD, int TT>
 __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  float* dump = reinterpret_cast<float*>(smem + a.lds_buf);   // [64][8] write sink
+  float* dump = reinterpret_cast<float*>(smem + a.dump_off);    // [64][8] write sink
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4, col = lane & 15;
+  const int T = TT ? 1 : a.T;
   const ItemGeo g = item_geo(a, wave, col);
-  const int s = ld_uniform(a.slot, g.b);
+  const RowState r = row_state(a, g.b, T);
   Small<DK, QKV, RING> sm;
   SlabRaw<SD, DK> R;
-  fetch_small(sm, a, g, s, tid, lane, grp);
+  fetch_small<DK, QKV, RING, TT>(sm, a, g, r, T, tid, lane, grp, wave);
   __builtin_amdgcn_sched_barrier(0);
-  fetch_slab<SD, DK>(R, a, g, s, col, grp);
-  process(a, g, s, sm, R, smem, dump, tid, lane, grp, col, wave);
+  fetch_slab<SD, DK>(R, a, g, r, col, grp);
+  process<DK, QKV, RING, SD, TT>(a, g, r, T, sm, R, smem, dump, tid, lane, grp, col, wave);
 }
 
 // ============================================================= fold

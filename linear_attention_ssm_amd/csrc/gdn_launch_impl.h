@@ -41,13 +41,21 @@ hipError_t launch_packed(const DecodeArgs& a, int qkv, int sd, dim3 grid, dim3 b
   }
 }
 
+template <int DK, int QKV, int RING, int SD>
+static hipError_t launch_replay_s(const DecodeArgs& a, dim3 grid, dim3 block, size_t smem,
+                                  hipStream_t stream) {
+  // a single-token instance for T = 1 (decode steps, one-token windows)
+  if (a.T == 1) return launch(replay_decode_kernel<DK, QKV, RING, SD, 1>, a, grid, block, smem, stream);
+  return launch(replay_decode_kernel<DK, QKV, RING, SD, 0>, a, grid, block, smem, stream);
+}
+
 template <int DK, int QKV, int RING>
 static hipError_t launch_replay_r(const DecodeArgs& a, int sd, dim3 grid, dim3 block, size_t smem,
                                   hipStream_t stream) {
   switch (sd) {
-    case DT_F32: return launch(replay_decode_kernel<DK, QKV, RING, DT_F32>, a, grid, block, smem, stream);
-    case DT_BF16: return launch(replay_decode_kernel<DK, QKV, RING, DT_BF16>, a, grid, block, smem, stream);
-    case DT_F16: return launch(replay_decode_kernel<DK, QKV, RING, DT_F16>, a, grid, block, smem, stream);
+    case DT_F32: return launch_replay_s<DK, QKV, RING, DT_F32>(a, grid, block, smem, stream);
+    case DT_BF16: return launch_replay_s<DK, QKV, RING, DT_BF16>(a, grid, block, smem, stream);
+    case DT_F16: return launch_replay_s<DK, QKV, RING, DT_F16>(a, grid, block, smem, stream);
     default: return hipErrorInvalidValue;
   }
 }
