@@ -308,6 +308,62 @@ __device__ __forceinline__ void fetch_slab(SlabRaw<SD, DK>& R, const DecodeArgs&
     R.r[t] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * t, 0, 0);
 }
 
+// A token's small outputs leave in as few store instructions as possible (a
+// store at the end of a wavefront costs about as much as a large one): lanes
+// of group 0 write o, lanes of group 1 the ring d entry, two lanes of group 2
+// the ring g entry (as two halves when the others are 16-bit), all in one
+// instruction when o and d have the same width.
+//   oi, di, gi: element indices into o, ring_d, ring_g
+template <int QKV, int RING>
+__device__ __forceinline__ void small_stores(const DecodeArgs& a, size_t oi, size_t di, size_t gi,
+                                             float o, float d, float gv, bool app, bool gw,
+                                             int grp, int col) {
+  using OT = typename Elem<QKV>::T;
+  using DT = typename Elem<RING>::T;
+  if constexpr (sizeof(OT) == sizeof(DT)) {
+    using W = std::conditional_t<sizeof(OT) == 2, uint16_t, uint32_t>;
+    W* dst = nullptr;
+    W val = 0;
+    if (grp == 0) {
+      dst = reinterpret_cast<W*>(static_cast<OT*>(a.o) + oi);
+      val = __builtin_bit_cast(W, from_f32<QKV>(o));
+    } else if (grp == 1) {
+      dst = app ? reinterpret_cast<W*>(static_cast<DT*>(a.ring_d) + di) : nullptr;
+      val = __builtin_bit_cast(W, from_f32<RING>(d));
+    } else if (grp == 2) {
+      const uint32_t gb = __float_as_uint(gv);
+      if constexpr (sizeof(W) == 2) {
+        dst = (app && gw && col < 2) ? reinterpret_cast<W*>(a.ring_g + gi) + col : nullptr;
+        val = static_cast<W>(col ? gb >> 16 : gb & 0xffffu);
+      } else {
+        dst = (app && gw && col == 0) ? reinterpret_cast<W*>(a.ring_g + gi) : nullptr;
+        val = gb;
+      }
+    }
+    if (dst) *dst = val;
+  } else {
+    // o, and ring d with ring g, in two instructions
+    if (grp == 0) store1<QKV>(a.o, oi, o);
+    using W = std::conditional_t<sizeof(DT) == 2, uint16_t, uint32_t>;
+    W* dst = nullptr;
+    W val = 0;
+    if (grp == 1) {
+      dst = app ? reinterpret_cast<W*>(static_cast<DT*>(a.ring_d) + di) : nullptr;
+      val = __builtin_bit_cast(W, from_f32<RING>(d));
+    } else if (grp == 2) {
+      const uint32_t gb = __float_as_uint(gv);
+      if constexpr (sizeof(W) == 2) {
+        dst = (app && gw && col < 2) ? reinterpret_cast<W*>(a.ring_g + gi) + col : nullptr;
+        val = static_cast<W>(col ? gb >> 16 : gb & 0xffffu);
+      } else {
+        dst = (app && gw && col == 0) ? reinterpret_cast<W*>(a.ring_g + gi) : nullptr;
+        val = gb;
+      }
+    }
+    if (dst) *dst = val;
+  }
+}
+
 template <int DK, int QKV, int RING, int SD, int TT>
 __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, const RowState& r,
                                         int T, const Small<DK, QKV, RING>& f,
@@ -495,7 +551,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   const int wph = a.VB / 16;
   const int wh = g.h - (g.hk * a.G + g.hc * a.GH);              // head within the workgroup
   const bool kwriter = (g.vb == 0) && (g.hc == 0) && (wave == 0);   // one key-ring writer per k-head
-  const bool gwriter = (g.vb == 0) && (wave % wph == 0) && lane == 0;
+  const bool gwriter_wave = (g.vb == 0) && (wave % wph == 0);     // one g writer per head
   const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
   const size_t ks = static_cast<size_t>(r.sc) * a.Hk + g.hk;
   float vv = to_f32<QKV>(f.v_raw);
@@ -511,15 +567,14 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
     float sq, sk, d, o;
     slab_dots<SD>(S, ql, kl, grp, sq, sk);
     token_out(sq, sk, kq, alpha, bt, vv, d, o);
-    if (grp == 0) store1<QKV>(a.o, ih * a.dv + g.vcol, r.ok ? o : 0.f);
-    if (r.ok && !r.flush) {
-      const int pos = p + tau;
-      if (grp == 0) store1<RING>(a.ring_d, (hs * a.L + pos) * a.dv + g.vcol, d);
-      if (gwriter) a.ring_g[hs * a.L + pos] = gv;
-      if (kwriter && lane < C4) {
-        const f4 kv = *reinterpret_cast<const f4*>(kl + 4 * lane);
-        store4<RING>(a.ring_k, (ks * a.L + pos) * DK + 4 * lane, kv);
-      }
+    const bool app = r.ok && !r.flush;              // this token appends a ring entry
+    const int pos = p + tau;
+    small_stores<QKV, RING>(a, ih * a.dv + g.vcol, (hs * a.L + pos) * a.dv + g.vcol,
+                            hs * a.L + pos, r.ok ? o : 0.f, d, gv, app, gwriter_wave, grp,
+                            col);
+    if (app && kwriter && lane < C4) {
+      const f4 kv = *reinterpret_cast<const f4*>(kl + 4 * lane);
+      store4<RING>(a.ring_k, (ks * a.L + pos) * DK + 4 * lane, kv);
     }
     if (r.flush || (!TT && a.window && tau + 1 < T)) slab_update<SD>(S, kl, grp, alpha, d);
     vv = v_next;
