@@ -62,8 +62,16 @@
  *   gdn_packed_decode  rounds the updated state every step;
  *   gdn_replay_decode  rounds the checkpoint only on a flush;
  *   gdn_replay_fold    folds in fp32 and rounds the result once.
- * At L = 1 replay and packed decode therefore still agree bit for bit. The
- * bit-exact lossless-verify property (gdn_replay_fold) needs an fp32 state.
+ * At L = 1 replay and packed decode therefore still agree bit for bit.
+ *
+ * step_rounding = 1 (verify windows and folds only) rounds a 16-bit state
+ * after every step instead: the window rounds its on-chip state after each
+ * token's update and the fold after each entry, as the packed decode does.
+ * A verify window from an exact checkpoint (write_pos = 0) with an fp32 ring,
+ * committed and folded with step_rounding, then equals token-by-token packed
+ * decode bit for bit also for a 16-bit state (SGLang PR #42388: the ring
+ * stays fp32 whatever the state dtype, so bf16 state pools stay exact). With
+ * an fp32 state the flag changes nothing.
  */
 #ifndef GDN_REPLAY_H
 #define GDN_REPLAY_H
@@ -102,6 +110,8 @@ typedef struct {
     int32_t ring_dtype; /* gdn_dtype of ring_d and ring_k                        */
     int32_t window;     /* gdn_replay_decode: 0 = decode step, 1 = verify window */
     int32_t state_dtype;/* gdn_dtype of the state / checkpoint (0 = GDN_F32)     */
+    int32_t step_rounding; /* 1: round a 16-bit state after every step (verify
+                              window and fold only; see below), else 0    */
 } gdn_shape;
 
 /*

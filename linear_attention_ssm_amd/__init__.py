@@ -31,7 +31,7 @@ STATE_DTYPES = (torch.float32, torch.bfloat16, torch.float16)
 class gdn_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "N", "Hv", "Hk", "dk", "dv", "L", "qkv_dtype", "ring_dtype", "window",
-                 "state_dtype")]
+                 "state_dtype", "step_rounding")]
 
 
 class GdnError(RuntimeError):
@@ -60,7 +60,7 @@ for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_advance",
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 3
+ABI_VERSION = 4
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -169,9 +169,11 @@ def _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev):
 
 
 def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
-                      force_flush=None, o=None, err_flags=None, window=False, stream=None):
+                      force_flush=None, o=None, err_flags=None, window=False, stream=None,
+                      step_rounding=False):
     """ReplaySSM decode step (window=False, T=1) or verify window (window=True);
-    see gdn_replay_decode in gdn_replay.h. Returns o [B,T,Hv,dv]."""
+    see gdn_replay_decode in gdn_replay.h. step_rounding (windows only) rounds
+    a 16-bit state after every token. Returns o [B,T,Hv,dv]."""
     B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
     N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev)
     if force_flush is not None:
@@ -182,7 +184,7 @@ def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, 
         _check(err_flags, "err_flags", torch.int32, None, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
     sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)),
-                   _DT[ckpt.dtype])
+                   _DT[ckpt.dtype], int(bool(step_rounding)))
     _raise(_lib.gdn_replay_decode(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d), _ptr(ring_k),
                                   _ptr(ring_g), _ptr(write_pos), _ptr(force_flush), _ptr(o),
@@ -215,9 +217,10 @@ def gdn_replay_commit(slot_idx, accepted, write_pos, L, T, err_flags=None, strea
 
 
 def gdn_replay_fold(slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags=None,
-                    stream=None):
+                    stream=None, step_rounding=False):
     """Exact fold of one layer's valid ring entries into its checkpoint
-    (write_pos is only read); see gdn_replay_fold in gdn_replay.h."""
+    (write_pos is only read); see gdn_replay_fold in gdn_replay.h.
+    step_rounding rounds a 16-bit state after every entry."""
     _check(slot_idx, "slot_idx", torch.int32, 1)
     dev = slot_idx.device
     _check(ckpt, "ckpt", STATE_DTYPES, 4, dev)
@@ -225,7 +228,7 @@ def gdn_replay_fold(slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags
     Hk = ring_k.shape[1]
     _, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev)
     sh = gdn_shape(slot_idx.shape[0], 1, N, Hv, Hk, dk, dv, L, GDN_F32, _DT[ring_d.dtype], 0,
-                   _DT[ckpt.dtype])
+                   _DT[ckpt.dtype], int(bool(step_rounding)))
     _raise(_lib.gdn_replay_fold(ctypes.byref(sh), _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d),
                                 _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(err_flags),
                                 _stream(stream)), "gdn_replay_fold")

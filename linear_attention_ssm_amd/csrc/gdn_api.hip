@@ -12,7 +12,7 @@ using namespace gdn;
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -183,6 +183,7 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
   if (s->window != 0 && s->window != 1) return GDN_ERR_INVALID_ARG;
   if (s->window == 0 && s->T != 1) return GDN_ERR_INVALID_ARG;
   if (s->window == 1 && force_flush) return GDN_ERR_INVALID_ARG;
+  if (s->step_rounding != 0 && (s->step_rounding != 1 || s->window != 1)) return GDN_ERR_INVALID_ARG;
   if (s->T > s->L) return GDN_ERR_INVALID_ARG;
   if (!q || !k || !v || !g || !beta || !slot_idx || !ckpt || !ring_d || !ring_k || !ring_g ||
       !write_pos || !o)
@@ -199,6 +200,7 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.slot = slot_idx; a.state = ckpt;
   a.ring_d = ring_d; a.ring_k = ring_k; a.ring_g = ring_g; a.write_pos = write_pos;
   a.force_flush = force_flush; a.o = o; a.err = err_flags; a.window = s->window;
+  a.step_round = s->step_rounding;
   // the kernel reads one flag per row unconditionally; without
   // force_flush it reads the slot array and ignores the value
   a.ff_on = force_flush != nullptr;
@@ -271,6 +273,7 @@ gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, void* ck
   if (st != GDN_OK) return st;
   if (!slot_idx || !ckpt || !ring_d || !ring_k || !ring_g || !write_pos)
     return GDN_ERR_INVALID_ARG;
+  if (s->step_rounding != 0 && s->step_rounding != 1) return GDN_ERR_INVALID_ARG;
   const size_t rs = elem_size(s->ring_dtype);
   if (!aligned(ckpt, 16) || !aligned(ring_d, rs) || !aligned(ring_k, rs) ||
       !aligned(ring_g, 4) || !aligned(write_pos, 4) || !aligned(slot_idx, 4) ||
@@ -282,6 +285,7 @@ gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, void* ck
   a.write_pos = write_pos; a.err = err_flags;
   a.B = s->B; a.N = s->N; a.Hv = s->Hv; a.Hk = s->Hk; a.dv = s->dv; a.L = s->L;
   a.G = s->Hv / s->Hk;
+  a.step_round = s->step_rounding;
   const dim3 grid(static_cast<unsigned>(s->B) * s->Hv * (s->dv / 16));
   const dim3 block(static_cast<unsigned>(16 * s->dk / 4));
   const size_t smem = static_cast<size_t>(s->L) * (1 + 16 + s->dk) * sizeof(float);

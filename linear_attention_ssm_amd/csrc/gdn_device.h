@@ -437,6 +437,18 @@ __device__ __forceinline__ void store16_nt(float* base, int nbytes, int byte_off
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), rs, byte_off, 0, SC1_NT);
 }
 
+// A 16-bit state's on-chip values rounded to the format and widened back
+// (the state a step-by-step decode would hold); fp32 is left as is.
+template <int SD, int NT>
+__device__ __forceinline__ void slab_round(f4 (&S)[NT]) {
+  if constexpr (SD != DT_F32) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[t][i] = to_f32<SD>(state_round<SD>(S[t][i]));
+  }
+}
+
 // The 8-byte form of store16_nt.
 __device__ __forceinline__ void store8_nt(float* base, int nbytes, int byte_off, u16x4 x) {
   constexpr int SC1_NT = 16 | 2;
@@ -533,6 +545,7 @@ struct DecodeArgs {
   // LDS byte offsets: per-token k^T q, per (head, token) gates (alpha, beta,
   // g), the staged key ring
   int32_t kq_off, gate_off, kt_off;
+  int32_t step_round;      // round a 16-bit state after each window token
 };
 
 struct CursorArgs {
@@ -553,6 +566,7 @@ struct FoldArgs {
   const int32_t* write_pos;
   int32_t* err;
   int32_t B, N, Hv, Hk, dv, L, G;
+  int32_t step_round;      // round a 16-bit state after each folded entry
 };
 
 }  // namespace gdn

@@ -576,7 +576,10 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
       const f4 kv = *reinterpret_cast<const f4*>(kl + 4 * lane);
       store4<RING>(a.ring_k, (ks * a.L + pos) * DK + 4 * lane, kv);
     }
-    if (r.flush || (!TT && a.window && tau + 1 < T)) slab_update<SD>(S, kl, grp, alpha, d);
+    if (r.flush || (!TT && a.window && tau + 1 < T)) {
+      slab_update<SD>(S, kl, grp, alpha, d);
+      if (!TT && a.step_round) slab_round<SD>(S);
+    }
     vv = v_next;
   }
   if (r.flush) {
@@ -674,6 +677,14 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
       x.y = __builtin_fmaf(dj, kv.y, ty);
       x.z = __builtin_fmaf(dj, kv.z, tz);
       x.w = __builtin_fmaf(dj, kv.w, tw);
+      if constexpr (SD != DT_F32) {
+        if (a.step_round) {
+          x.x = to_f32<SD>(state_round<SD>(x.x));
+          x.y = to_f32<SD>(state_round<SD>(x.y));
+          x.z = to_f32<SD>(state_round<SD>(x.z));
+          x.w = to_f32<SD>(state_round<SD>(x.w));
+        }
+      }
     }
   }
   // fp32 result of the exact fold, rounded once to the state format

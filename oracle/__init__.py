@@ -356,17 +356,20 @@ class ReplayModel:
 
 # ------------------------------------------------------------------ O4
 
-def window_ref(S: np.ndarray, slot, q, k, v, g, beta, want_u: bool = False):
+def window_ref(S: np.ndarray, slot, q, k, v, g, beta, want_u: bool = False,
+               state_fmt: Optional[str] = None):
     """O4: the outputs of a T-token window, computed by running O1 token by
     token on a copy of the true state (vLLM PR #49887, Tests: the reference
     is the packed decode run on a clone through the window). S is not changed.
     q,k [B,T,Hk,dk], v [B,T,Hv,dv], g,beta [B,T,Hv]. Returns o [B,T,Hv,dv]
-    (and u [B,T,Hv,dv])."""
+    (and u [B,T,Hv,dv]). state_fmt: the state is stored in that 16-bit format
+    after every token (O5), as the packed decode with a 16-bit state does."""
     Sc = np.array(S, dtype=np.float64, copy=True)
     T = q.shape[1]
     outs, us = [], []
     for t in range(T):
-        o, u = gdn_step(Sc, slot, q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], want_u=True)
+        o, u = gdn_step(Sc, slot, q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], want_u=True,
+                        state_fmt=state_fmt)
         outs.append(o)
         us.append(u)
     o = np.stack(outs, axis=1)

@@ -28,7 +28,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
     for st in range(4):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -55,6 +55,8 @@ def packed(sh, ptrs=None):
     (dict(qkv_dtype=gdn.GDN_F16), gdn.GDN_ERR_UNSUPPORTED),
     (dict(ring_dtype=7), gdn.GDN_ERR_UNSUPPORTED),
     (dict(state_dtype=3), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(step_rounding=1), gdn.GDN_ERR_INVALID_ARG),   # decode step: windows only
+    (dict(T=2, window=1, step_rounding=2), gdn.GDN_ERR_INVALID_ARG),
     (dict(state_dtype=-1), gdn.GDN_ERR_UNSUPPORTED),
     (dict(T=2), gdn.GDN_ERR_INVALID_ARG),               # decode mode needs T = 1
     (dict(T=2, window=1, L=1), gdn.GDN_ERR_INVALID_ARG),  # window longer than the ring
