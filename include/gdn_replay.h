@@ -69,9 +69,9 @@
  * token's update and the fold after each entry, as the packed decode does.
  * A verify window from an exact checkpoint (write_pos = 0) with an fp32 ring,
  * committed and folded with step_rounding, then equals token-by-token packed
- * decode bit for bit also for a 16-bit state (SGLang PR #42388: the ring
- * stays fp32 whatever the state dtype, so bf16 state pools stay exact). With
- * an fp32 state the flag changes nothing.
+ * decode bit for bit also for a 16-bit state (SGLang PR #42388 keeps the
+ * ring in fp32 for every state dtype, which is what makes this possible).
+ * With an fp32 state the flag changes nothing.
  */
 #ifndef GDN_REPLAY_H
 #define GDN_REPLAY_H
