@@ -252,13 +252,16 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
     f.gate_g = a.g[gi];
     f.gate_b = a.beta[gi];
   }
-  // staging threads: four keys of q and k of token c / C4
+  // staging threads: four keys of q and k of token c / C4 (only the
+  // wavefronts that hold staging threads load them)
   const int nqk = T * C4;
-  const int cq = tid < nqk ? tid : nqk - 1;
-  const int tq = TT ? 0 : cq / C4;
-  const size_t qsrc = ((static_cast<size_t>(g.b) * T + tq) * a.Hk + g.hk) * DK + (cq - tq * C4) * 4;
-  f.q_raw = load4_raw<QKV>(a.q, qsrc);
-  f.k_raw = load4_raw<QKV>(a.k, qsrc);
+  if (64 * wave < nqk) {
+    const int cq = tid < nqk ? tid : nqk - 1;
+    const int tq = TT ? 0 : cq / C4;
+    const size_t qsrc = ((static_cast<size_t>(g.b) * T + tq) * a.Hk + g.hk) * DK + (cq - tq * C4) * 4;
+    f.q_raw = load4_raw<QKV>(a.q, qsrc);
+    f.k_raw = load4_raw<QKV>(a.k, qsrc);
+  }
   // the key ring of (slot, key head), the valid entries only
   const char* kbase = static_cast<const char*>(a.ring_k) +
                       (static_cast<size_t>(r.sc) * a.Hk + g.hk) * a.L * DK * RS;
@@ -302,10 +305,22 @@ __device__ __forceinline__ void fetch_slab(SlabRaw<SD, DK>& R, const DecodeArgs&
   const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
   const char* base = static_cast<const char*>(a.state) + (hs * a.dv + g.vcol - col) * DK * ES;
   const __amdgpu_buffer_rsrc_t rs = brsrc(base, r.ok ? 16 * DK * ES : 0);
-  const int off = (col * DK + (SD == DT_F32 ? 4 : 8) * grp) * ES;
+  if constexpr (SD == DT_F32) {
+    // whole 128-byte lines per instruction: rows 0-7 then rows 8-15 of keys
+    // 32u..32u+31; slab_decode trades the halves back
+    const bool lo = col < 8;
+    const int off = ((lo ? col : col - 8) * DK + (lo ? 0 : 16) + 4 * grp) * 4;
 #pragma unroll
-  for (int t = 0; t < SlabRaw<SD, DK>::NP; ++t)
-    R.r[t] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * t, 0, 0);
+    for (int u = 0; u < DK / 32; ++u) {
+      R.r[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 128 * u, 0, 0);
+      R.r[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 128 * u, 8 * DK * 4, 0);
+    }
+  } else {
+    const int off = (col * DK + 8 * grp) * ES;
+#pragma unroll
+    for (int t = 0; t < SlabRaw<SD, DK>::NP; ++t)
+      R.r[t] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * t, 0, 0);
+  }
 }
 
 // A token's small outputs leave in as few store instructions as possible (a
@@ -389,17 +404,15 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
 
   // ---- LDS staging. Every thread writes (threads past the last piece into a
   // per-lane dump area) so the early loads have unconditional uses.
-  {
+  if (64 * wave < nqk) {                         // waves holding staging threads
     const f4 qv = decode4<QKV>(f.q_raw), kv = decode4<QKV>(f.k_raw);
     const int tq = TT ? 0 : tid / C4;
     float* qdst = tid < nqk ? qk + tq * 2 * DK + (tid - tq * C4) * 4 : dump + lane * 8;
     float* kdst = tid < nqk ? qdst + DK : dump + lane * 8 + 4;
     *reinterpret_cast<f4*>(qdst) = qv;
     *reinterpret_cast<f4*>(kdst) = kv;
-    if (64 * wave < nqk) {                       // waves holding staging threads
-      const float kq0 = token_kq<DK>(qv, kv);
-      if (tid < nqk && tid - tq * C4 == 0) kq_l[tq] = kq0;
-    }
+    const float kq0 = token_kq<DK>(qv, kv);
+    if (tid < nqk && tid - tq * C4 == 0) kq_l[tq] = kq0;
   }
   for (int c = tid + nthr; c < nqk; c += nthr) {        // long windows only
     const int tau = c / C4, e4 = (c % C4) * 4;
@@ -509,6 +522,16 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   // ---- reconstruction S = A S0 + sum_j w_j d_j k_j^T
   f4 S[NT];
   slab_decode<SD, DK>(S, R);
+  if constexpr (SD == DT_F32) {
+    const bool lo = col < 8;
+#pragma unroll
+    for (int u = 0; u < NT / 2; ++u) {
+      const f4 A0 = S[2 * u], B0 = S[2 * u + 1];
+      const f4 z = row_swap8(lo ? B0 : A0);
+      S[2 * u] = lo ? A0 : z;
+      S[2 * u + 1] = lo ? z : B0;
+    }
+  }
   if (p > 0) {
     auto kstep = [&](int c, typename MM::op_t bop) {
 #pragma unroll
