@@ -10,6 +10,8 @@ Draws (per row, token and head), as the workloads specify:
   q, k ~ N(0, 1), L2-normalised in fp32, q scaled by dk**-0.5
   v    ~ N(0, 1)
   g    = logsigmoid(N(2, 1))                          log-decay, per v-head
+                                                      (per v-head and key channel
+                                                      for a per-key gate, KDA)
   beta = sigmoid(N(0, 1))                             delta-rule strength
 The draws are cast to the workload's I/O dtype; consumers that need the exact
 values the device sees should use `as_f64`, which upcasts the rounded values.
@@ -92,6 +94,8 @@ class Workload:
     stagger: bool = True   # one forced flush per slot during the first L steps
     bf16_values: bool = False  # fp32 tensors carrying bf16-representable values
     state: str = "f32"  # storage dtype of the checkpoint / packed state
+    gate: str = "head"  # "head": one log-decay per v-head (GDN); "key": one per
+                        # v-head and key channel (KDA)
     seed: int = 0
 
     @property
@@ -128,8 +132,20 @@ C6 = Workload("c6_lossless_verify", B=32, N=40, Hv=32, Hk=16, dk=128, dv=128,
               L=8, steps=8, ring="f32", T=5, n_pad=2, permute=True, stagger=False,
               seed=707)
 
+# Per-key gate (KDA, SGLang PR #28451 Modifications item 7) at the shapes the
+# pages benchmark it on (Hv=32, Hk=16, dk=dv=128, bf16, L=16), plus a tiny
+# fp32 case.
+C7 = replace(C2, name="c7_kda", gate="key", seed=808)
+C7_TINY = replace(C1, name="c7_kda_tiny", gate="key", seed=809)
+
 WORKLOADS = {w.name: w for w in (C1, C2, C3, c4(1), c4(4), c4(16), c4(32),
-                                 c4(16, "f32"), C5, C6)}
+                                 c4(16, "f32"), C5, C6, C7, C7_TINY)}
+
+
+def gate_shape(w: Workload, *lead: int) -> tuple:
+    """Shape of a gate tensor with leading dims `lead`: [..., Hv] for the
+    per-head gate, [..., Hv, dk] for the per-key gate."""
+    return (*lead, w.Hv) + ((w.dk,) if w.gate == "key" else ())
 
 
 def scaled(w: Workload, **kw) -> Workload:
@@ -188,7 +204,7 @@ class StepInputs:
     q: np.ndarray      # [B, T, Hk, dk]
     k: np.ndarray      # [B, T, Hk, dk]
     v: np.ndarray      # [B, T, Hv, dv]
-    g: np.ndarray      # [B, T, Hv] fp32
+    g: np.ndarray      # [B, T, Hv] fp32 ([B, T, Hv, dk] with a per-key gate)
     beta: np.ndarray   # [B, T, Hv] fp32
     dtype: str
 
@@ -208,7 +224,7 @@ def step_inputs(w: Workload, step: int, B: Optional[int] = None,
     q = (q * np.float32(w.dk ** -0.5)).astype(np.float32)
     k = _unit_rows(r.standard_normal((B, T, w.Hk, w.dk), dtype=np.float32))
     v = r.standard_normal((B, T, w.Hv, w.dv), dtype=np.float32)
-    g = _logsigmoid(r.normal(2.0, 1.0, (B, T, w.Hv))).astype(np.float32)
+    g = _logsigmoid(r.normal(2.0, 1.0, gate_shape(w, B, T))).astype(np.float32)
     beta = _sigmoid(r.standard_normal((B, T, w.Hv))).astype(np.float32)
     if w.bf16_values:
         q, k, v = (bf16_bits_to_f32(f32_to_bf16_bits(a)) for a in (q, k, v))
@@ -246,7 +262,7 @@ class RingContents:
     ckpt: np.ndarray     # [N, Hv, dv, dk] fp32
     d: np.ndarray        # [N, Hv, L, dv] ring dtype (bf16 as bits)
     k: np.ndarray        # [N, Hk, L, dk]
-    g: np.ndarray        # [N, Hv, L] fp32
+    g: np.ndarray        # [N, Hv, L] fp32 ([N, Hv, L, dk] with a per-key gate)
     write_pos: np.ndarray  # [N] int32
     dtype: str
 
@@ -258,7 +274,10 @@ def random_ring(w: Workload, seed_tag: int = 0, full: bool = False) -> RingConte
     ckpt = (0.1 * r.standard_normal((w.N, w.Hv, w.dv, w.dk), dtype=np.float32)).astype(np.float32)
     d = r.standard_normal((w.N, w.Hv, w.L, w.dv), dtype=np.float32)
     k = _unit_rows(r.standard_normal((w.N, w.Hk, w.L, w.dk), dtype=np.float32))
-    g = _logsigmoid(r.normal(2.0, 1.0, (w.N, w.Hv, w.L))).astype(np.float32)
+    if w.gate == "key":
+        g = _logsigmoid(r.normal(2.0, 1.0, (w.N, w.Hv, w.L, w.dk))).astype(np.float32)
+    else:
+        g = _logsigmoid(r.normal(2.0, 1.0, (w.N, w.Hv, w.L))).astype(np.float32)
     if full:
         wp = np.full(w.N, w.L, dtype=np.int32)
     else:

@@ -13,6 +13,10 @@ Parts:
   O4  window_ref        a verify window evaluated token by token with O1
   O5  quantize          exact rounding to a 16-bit state format (binary16 or
                         bfloat16), for the 16-bit checkpoint variant
+  O6  kda_step          the per-key-gate (KDA) recurrence in fp64 (C)
+  O7  fold_kda_f32      the pinned-rounding fold with a per-key gate (C)
+  O2, O4 take the per-key gate as well (ReplayModel(gate="key"), window_ref
+  with g [B, T, Hv, dk]).
 
 Every function states the passage it follows. The pages cited are: SGLang
 PR #28451 (ReplaySSM decode port), the ReplaySSM blog on llm.rainlin.net,
@@ -62,8 +66,12 @@ def lib():
         L.oracle_gdn_step_f64.restype = None
         L.oracle_fold_f32.argtypes = [i32] * 7 + [P] * 6 + [i32]
         L.oracle_fold_f32.restype = None
+        L.oracle_kda_step_f64.argtypes = [i32] * 6 + [P] * 9
+        L.oracle_kda_step_f64.restype = None
+        L.oracle_fold_kda_f32.argtypes = [i32] * 7 + [P] * 6
+        L.oracle_fold_kda_f32.restype = None
         L.oracle_version.restype = i32
-        assert L.oracle_version() == 1
+        assert L.oracle_version() == 2
         _lib = L
     return _lib
 
@@ -139,6 +147,45 @@ def gdn_step(S: np.ndarray, slot: np.ndarray, q, k, v, g, beta,
     return (o, u) if want_u else o
 
 
+# ------------------------------------------------------------------ O6
+
+def kda_step(S: np.ndarray, slot: np.ndarray, q, k, v, g, beta,
+             want_u: bool = False, state_fmt: Optional[str] = None):
+    """O6: one decode token of the delta rule with a per-key gate (KDA),
+    fp64, in place on S.
+
+    Follows SGLang PR #28451 (Modifications, item 7): the same delta rule as
+    O1 with the decay per key channel, S~ = S Diag(a), a = exp(g) over the dk
+    channels; u = beta (v - S~ k), S_t = S~ + u k^T, y = S_t q.
+    g [B, Hv, dk]; every other argument as gdn_step.
+    """
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    N, Hv, dv, dk = S.shape
+    B = slot.shape[0]
+    Hk = q.shape[1]
+    slot = _c(slot, np.int32)
+    q, k, v, g, beta = (_c(x, np.float64) for x in (q, k, v, g, beta))
+    assert q.shape == (B, Hk, dk) and k.shape == (B, Hk, dk)
+    assert v.shape == (B, Hv, dv) and g.shape == (B, Hv, dk) and beta.shape == (B, Hv)
+    o = np.empty((B, Hv, dv), np.float64)
+    u = np.empty((B, Hv, dv), np.float64) if want_u else None
+    lib().oracle_kda_step_f64(B, N, Hv, Hk, dk, dv, _p(slot), _p(S), _p(q), _p(k),
+                              _p(v), _p(g), _p(beta), _p(o), _p(u))
+    if state_fmt is not None:
+        for s in slot:
+            if 0 <= s < N:
+                S[s] = quantize(S[s], state_fmt)
+    return (o, u) if want_u else o
+
+
+def step(S: np.ndarray, slot: np.ndarray, q, k, v, g, beta, want_u: bool = False,
+         state_fmt: Optional[str] = None):
+    """O1 or O6, by the gate's shape: g [B, Hv] (per head) or [B, Hv, dk]
+    (per key channel)."""
+    f = kda_step if np.ndim(g) == 3 else gdn_step
+    return f(S, slot, q, k, v, g, beta, want_u=want_u, state_fmt=state_fmt)
+
+
 # ------------------------------------------------------------------ O3
 
 def fold_f32(ckpt: np.ndarray, slot: np.ndarray, write_pos: np.ndarray,
@@ -164,6 +211,27 @@ def fold_f32(ckpt: np.ndarray, slot: np.ndarray, write_pos: np.ndarray,
     assert ring_g.shape == (N, Hv, L)
     lib().oracle_fold_f32(slot.shape[0], N, Hv, Hk, dk, dv, L, _p(slot), _p(write_pos),
                           _p(ckpt), _p(ring_d), _p(ring_k), _p(ring_g), order)
+
+
+def fold_kda_f32(ckpt: np.ndarray, slot: np.ndarray, write_pos: np.ndarray,
+                 ring_d: np.ndarray, ring_k: np.ndarray, ring_g: np.ndarray) -> None:
+    """O7: the fold of O3 with a per-key gate: per element and entry,
+    x <- fma(d_j[v], k_j[c], RN(RN(exp(g_j[c])) * x)), then write_pos <- 0.
+
+    The KDA update S Diag(a) + d k^T (SGLang PR #28451, Modifications item 7)
+    in the two-instruction rounding of SGLang PR #42388 ("The idea").
+    ring_g [N, Hv, L, dk]; everything else as fold_f32.
+    """
+    assert ckpt.dtype == np.float32 and ckpt.flags.c_contiguous
+    assert write_pos.dtype == np.int32 and write_pos.flags.c_contiguous
+    N, Hv, dv, dk = ckpt.shape
+    Hk, L = ring_k.shape[1], ring_k.shape[2]
+    slot = _c(slot, np.int32)
+    ring_d, ring_k, ring_g = (_c(x, np.float32) for x in (ring_d, ring_k, ring_g))
+    assert ring_d.shape == (N, Hv, L, dv) and ring_k.shape == (N, Hk, L, dk)
+    assert ring_g.shape == (N, Hv, L, dk)
+    lib().oracle_fold_kda_f32(slot.shape[0], N, Hv, Hk, dk, dv, L, _p(slot), _p(write_pos),
+                              _p(ckpt), _p(ring_d), _p(ring_k), _p(ring_g))
 
 
 # ------------------------------------------------------------------ O2
@@ -202,10 +270,21 @@ class ReplayModel:
     state_fmt ('f16' / 'bf16'): the checkpoint is stored in that format. It is
     rounded (O5) only when it is written, at a flush and at the end of a fold;
     between writes the state lives in the ring and the replay.
+
+    gate ('head' / 'key'): 'key' is the per-key gate of KDA (SGLang PR #28451,
+    Modifications item 7): the ring keeps one log-decay per key channel
+    (ring_g [N, Hv, L, dk]), the products above run channel by channel,
+        S_{c+h} = S_c Diag(P_h) + sum_j u_j (w_{j,h} o k_j)^T,
+    with the decay folded onto the stored keys, and the token's own decay
+    a = exp(g) folds into q and k:
+        d_cur = beta (v - S (a o k)),  o = S (a o q) + d_cur (k^T q),
+    and a flush writes S Diag(a) + d_cur k^T.
     """
 
-    def __init__(self, S0: np.ndarray, Hk: int, L: int, state_fmt: Optional[str] = None):
-        assert L >= 1
+    def __init__(self, S0: np.ndarray, Hk: int, L: int, state_fmt: Optional[str] = None,
+                 gate: str = "head"):
+        assert L >= 1 and gate in ("head", "key")
+        self.gate = gate
         self.state_fmt = state_fmt
         self.N, self.Hv, self.dv, self.dk = S0.shape
         self.Hk, self.L = Hk, L
@@ -216,7 +295,7 @@ class ReplayModel:
                 "the initial checkpoint must hold values of the state format"
         self.ring_u = np.zeros((self.N, self.Hv, L, self.dv))
         self.ring_k = np.zeros((self.N, Hk, L, self.dk))
-        self.ring_g = np.zeros((self.N, self.Hv, L))
+        self.ring_g = np.zeros((self.N, self.Hv, L) + ((self.dk,) if gate == "key" else ()))
         self.write_pos = np.zeros(self.N, dtype=np.int64)
 
     def _store(self, X: np.ndarray) -> np.ndarray:
@@ -227,8 +306,10 @@ class ReplayModel:
     @staticmethod
     def replay(S_c: np.ndarray, us, ks, gs) -> np.ndarray:
         """Closed-form state after h entries (blog section 2.1) for one head.
-        S_c [dv,dk], us [h,dv], ks [h,dk], gs [h]."""
+        S_c [dv,dk], us [h,dv], ks [h,dk], gs [h] (or [h,dk]: per-key gate)."""
         h = len(gs)
+        if h and np.ndim(gs[0]) == 1:
+            return ReplayModel._replay_per_key(S_c, us, ks, gs)
         alpha = [float(np.exp(x)) for x in gs]
         P = 1.0
         for a in alpha:
@@ -240,6 +321,36 @@ class ReplayModel:
                 w *= alpha[i]
             S = S + w * np.outer(us[j], ks[j])
         return S
+
+    @staticmethod
+    def _replay_per_key(S_c: np.ndarray, us, ks, gs) -> np.ndarray:
+        """The closed form with a per-key gate: per channel c,
+        P[c] = prod_i exp(g_i[c]), w_j[c] = prod_{i>j} exp(g_i[c]),
+        S = S_c Diag(P) + sum_j u_j (w_j o k_j)^T."""
+        h = len(gs)
+        alpha = [np.exp(np.asarray(x, np.float64)) for x in gs]
+        P = np.ones(S_c.shape[1])
+        for a in alpha:
+            P = P * a
+        S = S_c * P[None, :]
+        for j in range(h):
+            w = np.ones(S_c.shape[1])
+            for i in range(j + 1, h):
+                w = w * alpha[i]
+            S = S + np.outer(us[j], w * np.asarray(ks[j]))
+        return S
+
+    def _readout(self, S, qv, kv, vv, gv, bt):
+        """(d_cur, o, decayed state) of one token for one head."""
+        if self.gate == "key":
+            a = np.exp(np.asarray(gv, np.float64))
+            d = bt * (vv - S @ (a * kv))
+            o = S @ (a * qv) + d * float(kv @ qv)
+            return d, o, S * a[None, :]
+        alpha = float(np.exp(gv))
+        d = bt * (vv - alpha * (S @ kv))
+        o = alpha * (S @ qv) + d * float(kv @ qv)
+        return d, o, alpha * S
 
     def head_state(self, s: int, h: int) -> np.ndarray:
         p = int(self.write_pos[s])
@@ -268,13 +379,10 @@ class ReplayModel:
             for h in range(self.Hv):
                 hk = h // self.G
                 S = self.head_state(s, h)
-                alpha = float(np.exp(g[b, h]))
-                Sk = S @ k[b, hk]
-                Sq = S @ q[b, hk]
-                d = beta[b, h] * (v[b, h] - alpha * Sk)
-                o[b, h] = alpha * Sq + d * float(k[b, hk] @ q[b, hk])
+                d, o[b, h], Sd = self._readout(S, q[b, hk], k[b, hk], v[b, h], g[b, h],
+                                               beta[b, h])
                 if flush[b]:
-                    self.ckpt[s, h] = self._store(alpha * S + np.outer(d, k[b, hk]))
+                    self.ckpt[s, h] = self._store(Sd + np.outer(d, k[b, hk]))
                 else:
                     self.ring_u[s, h, p] = d
                     self.ring_g[s, h, p] = g[b, h]
@@ -314,11 +422,8 @@ class ReplayModel:
                 gs = list(self.ring_g[s, h, :p])
                 for t in range(T):
                     S = self.replay(self.ckpt[s, h], us, ks, gs)
-                    alpha = float(np.exp(g[b, t, h]))
-                    Sk = S @ k[b, t, hk]
-                    Sq = S @ q[b, t, hk]
-                    d = beta[b, t, h] * (v[b, t, h] - alpha * Sk)
-                    o[b, t, h] = alpha * Sq + d * float(k[b, t, hk] @ q[b, t, hk])
+                    d, o[b, t, h], _ = self._readout(S, q[b, t, hk], k[b, t, hk], v[b, t, h],
+                                                     g[b, t, h], beta[b, t, h])
                     us.append(d)
                     ks.append(k[b, t, hk])
                     gs.append(g[b, t, h])
@@ -348,7 +453,8 @@ class ReplayModel:
                 hk = h // self.G
                 X = self.ckpt[s, h]
                 for j in range(p):
-                    X = np.exp(self.ring_g[s, h, j]) * X + np.outer(
+                    a = np.exp(self.ring_g[s, h, j])
+                    X = (X * a[None, :] if self.gate == "key" else a * X) + np.outer(
                         self.ring_u[s, h, j], self.ring_k[s, hk, j])
                 self.ckpt[s, h] = self._store(X)
             self.write_pos[s] = 0
@@ -361,15 +467,16 @@ def window_ref(S: np.ndarray, slot, q, k, v, g, beta, want_u: bool = False,
     """O4: the outputs of a T-token window, computed by running O1 token by
     token on a copy of the true state (vLLM PR #49887, Tests: the reference
     is the packed decode run on a clone through the window). S is not changed.
-    q,k [B,T,Hk,dk], v [B,T,Hv,dv], g,beta [B,T,Hv]. Returns o [B,T,Hv,dv]
+    q,k [B,T,Hk,dk], v [B,T,Hv,dv], g,beta [B,T,Hv] (g [B,T,Hv,dk] for the
+    per-key gate, which runs O6 instead of O1). Returns o [B,T,Hv,dv]
     (and u [B,T,Hv,dv]). state_fmt: the state is stored in that 16-bit format
     after every token (O5), as the packed decode with a 16-bit state does."""
     Sc = np.array(S, dtype=np.float64, copy=True)
     T = q.shape[1]
     outs, us = [], []
     for t in range(T):
-        o, u = gdn_step(Sc, slot, q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], want_u=True,
-                        state_fmt=state_fmt)
+        o, u = step(Sc, slot, q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], want_u=True,
+                    state_fmt=state_fmt)
         outs.append(o)
         us.append(u)
     o = np.stack(outs, axis=1)

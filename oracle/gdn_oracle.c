@@ -14,8 +14,9 @@
  *   S / ckpt   [N, Hv, dv, dk]   per value head a dv x dk matrix, dk fastest
  *   q, k       [B, Hk, dk]       one token per row
  *   v, o, u    [B, Hv, dv]
- *   g, beta    [B, Hv]
+ *   g, beta    [B, Hv]           (per-key gate, O6/O7: g [B, Hv, dk])
  *   ring_d     [N, Hv, L, dv]    ring_k [N, Hk, L, dk]    ring_g [N, Hv, L]
+ *                                (per-key gate: ring_g [N, Hv, L, dk])
  * Value head h reads key head h / (Hv / Hk) (contiguous GQA groups).
  * A row whose slot index is negative is a padding row: its outputs are zero
  * and no state is touched.
@@ -154,5 +155,121 @@ void oracle_fold_f32(int32_t B, int32_t N, int32_t Hv, int32_t Hk, int32_t dk,
     }
 }
 
+/*
+ * O6 -- one decode token of the delta rule with a per-key gate (KDA), in
+ * float64.
+ *
+ * SGLang PR #28451 (Modifications, item 7: one kernel for GDN and KDA) states
+ * that KDA is the same delta-rule decode with the decay applied per key
+ * channel instead of per head: the state update is S' = S Diag(a) + d k^T with
+ * a = exp(g) a vector over the dk key channels. Written out for one value head
+ * in the same materialise-then-read order as O1:
+ *     S~  = S_{t-1} Diag(a)       column c of the [dv x dk] state times a[c]
+ *     u   = beta * (v - S~ k)
+ *     S_t = S~ + u k^T
+ *     y   = S_t q
+ * With every a[c] equal this is O1 operation for operation.
+ * g is [B, Hv, dk] (one log-decay per key channel); everything else as O1.
+ */
+void oracle_kda_step_f64(int32_t B, int32_t N, int32_t Hv, int32_t Hk,
+                         int32_t dk, int32_t dv, const int32_t *slot,
+                         double *S, const double *q, const double *k,
+                         const double *v, const double *g, const double *beta,
+                         double *o, double *u_out)
+{
+    const int32_t G = Hv / Hk;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t s = slot[b];
+        for (int32_t h = 0; h < Hv; ++h) {
+            double *ob = o + ((size_t)b * Hv + h) * dv;
+            double *ub = u_out ? u_out + ((size_t)b * Hv + h) * dv : NULL;
+            if (s < 0 || s >= N) {
+                for (int32_t i = 0; i < dv; ++i) {
+                    ob[i] = 0.0;
+                    if (ub) ub[i] = 0.0;
+                }
+                continue;
+            }
+            const int32_t hk = h / G;
+            double *Sh = S + ((size_t)s * Hv + h) * dv * dk;
+            const double *qb = q + ((size_t)b * Hk + hk) * dk;
+            const double *kb = k + ((size_t)b * Hk + hk) * dk;
+            const double *vb = v + ((size_t)b * Hv + h) * dv;
+            const double *gb = g + ((size_t)b * Hv + h) * dk;
+            const double bt = beta[(size_t)b * Hv + h];
+
+            /* S~ = S Diag(a): every row scaled channel by channel */
+            for (int32_t i = 0; i < dv; ++i)
+                for (int32_t j = 0; j < dk; ++j)
+                    Sh[(size_t)i * dk + j] = exp(gb[j]) * Sh[(size_t)i * dk + j];
+            /* u = beta * (v - S~ k), then S = S~ + u k^T, row by row */
+            for (int32_t i = 0; i < dv; ++i) {
+                double *row = Sh + (size_t)i * dk;
+                double sk = 0.0;
+                for (int32_t j = 0; j < dk; ++j) sk += row[j] * kb[j];
+                const double u = bt * (vb[i] - sk);
+                if (ub) ub[i] = u;
+                for (int32_t j = 0; j < dk; ++j) row[j] = row[j] + u * kb[j];
+            }
+            /* y = S_t q */
+            for (int32_t i = 0; i < dv; ++i) {
+                const double *row = Sh + (size_t)i * dk;
+                double y = 0.0;
+                for (int32_t j = 0; j < dk; ++j) y += row[j] * qb[j];
+                ob[i] = y;
+            }
+        }
+    }
+}
+
+/*
+ * O7 -- fold of a slot's valid ring entries into its fp32 checkpoint with a
+ * per-key gate, rounding pinned as in O3 but with one decay per key channel:
+ * per element x = ckpt[v, c] and per entry j = 0 .. p-1 in order,
+ *     a = RN_f32(exp_f64(g_j[c]))
+ *     t = RN_f32(a * x)
+ *     x = fma_f32(d_j[v], k_j[c], t)
+ * (the KDA update S <- S Diag(a) + d k^T of SGLang PR #28451, Modifications
+ * item 7, in the two-instruction form of SGLang PR #42388, "The idea").
+ * ring_g is [N, Hv, L, dk]. Rows, cursors and the reset as O3.
+ */
+void oracle_fold_kda_f32(int32_t B, int32_t N, int32_t Hv, int32_t Hk, int32_t dk,
+                         int32_t dv, int32_t L, const int32_t *slot,
+                         int32_t *write_pos, float *ckpt, const float *ring_d,
+                         const float *ring_k, const float *ring_g)
+{
+    const int32_t G = Hv / Hk;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t s = slot[b];
+        if (s < 0 || s >= N) continue;
+        const int32_t p = write_pos[s];
+        if (p < 0 || p > L) continue;
+        for (int32_t h = 0; h < Hv; ++h) {
+            const int32_t hk = h / G;
+            float *X = ckpt + ((size_t)s * Hv + h) * dv * dk;
+            for (int32_t j = 0; j < p; ++j) {
+                const float *gj = ring_g + (((size_t)s * Hv + h) * L + j) * dk;
+                const float *dj = ring_d + (((size_t)s * Hv + h) * L + j) * dv;
+                const float *kj = ring_k + (((size_t)s * Hk + hk) * L + j) * dk;
+                for (int32_t i = 0; i < dv; ++i) {
+                    for (int32_t c = 0; c < dk; ++c) {
+                        float *x = X + (size_t)i * dk + c;
+                        const float a = (float)exp((double)gj[c]);
+                        const float t = a * (*x);
+                        *x = fmaf(dj[i], kj[c], t);
+                    }
+                }
+            }
+        }
+    }
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t s = slot[b];
+        if (s < 0 || s >= N) continue;
+        const int32_t p = write_pos[s];
+        if (p < 0 || p > L) continue;
+        write_pos[s] = 0;
+    }
+}
+
 /* ABI version of this oracle library, for the loader's sanity check. */
-int32_t oracle_version(void) { return 1; }
+int32_t oracle_version(void) { return 2; }
