@@ -34,13 +34,14 @@
  * Tensor layouts (all contiguous, row-major, base pointers 16-byte aligned):
  *   q, k           [B, T, Hk, dk]   qkv_dtype; q/k already normalised, q scaled
  *   v, o           [B, T, Hv, dv]   qkv_dtype (o is written in the same dtype)
- *   g, beta        [B, T, Hv]       fp32; g is the log-decay. Every kernel applies
+ *   g, beta        [B, T, Hv]       fp32 (per-key gate: g [B, T, Hv, dk]); g is the
+ *                                  log-decay. Every kernel applies
  *                                  the decay alpha = RN_f32(exp_f64(g)), one value per
  *                                  step, so that stored steps replay exactly
  *   state / ckpt   [N, Hv, dv, dk]  state_dtype, dk fastest (ReplaySSM blog, 2.2)
  *   ring_d         [N, Hv, L, dv]   ring_dtype  (the correction vectors d)
  *   ring_k         [N, Hk, L, dk]   ring_dtype  (keys, one per k-head)
- *   ring_g         [N, Hv, L]       fp32        (log-decays)
+ *   ring_g         [N, Hv, L]       fp32        (log-decays; [N, Hv, L, dk] per key)
  *   write_pos      [N]              int32, number of valid ring entries
  *   slot_idx       [B]              int32, row -> slot, negative = padding
  *   force_flush    [B]              int32, nullable (nonzero = force a flush)
@@ -72,6 +73,23 @@
  * decode bit for bit also for a 16-bit state (SGLang PR #42388 keeps the
  * ring in fp32 for every state dtype, which is what makes this possible).
  * With an fp32 state the flag changes nothing.
+ *
+ * Per-key gate (gate = GDN_GATE_KEY, KDA). SGLang PR #28451 (Modifications,
+ * item 7) runs KDA through the same kernels: KDA is the same delta rule with
+ * the decay taken per key channel, S' = S Diag(a) + d k^T with a = exp(g) a
+ * vector over the dk channels. Then
+ *   g       [B, T, Hv, dk] fp32 and ring_g [N, Hv, L, dk] fp32 (both
+ *           16-byte aligned), one log-decay per key channel;
+ *   readout d = beta (v - S (a o k)),  o = S (a o q) + d (k^T q): the token's
+ *           decays fold into q and k (a o q is the element-wise product);
+ *   update  S <- S Diag(a) + d k^T, rounded fma(d[v], k[c], RN(a[c] * S[v,c]));
+ *   replay  S = ckpt Diag(A) + sum_{j<p} d_j (w_j o k_j)^T with, per channel c,
+ *           A[c] = exp(sum_{i<p} g_i[c]), w_j[c] = exp(sum_{j<i<p} g_i[c]):
+ *           the decay products fold onto the stored keys;
+ *   fold    x <- fma(d_j[v], k_j[c], RN(a_j[c] * x)) with a_j[c] = RN_f32(exp_f64(g_j[c])).
+ * Everything else (ring d and k, cursors, flush, windows, state formats,
+ * step_rounding) is the same as with the per-head gate. Only gdn_packed_decode,
+ * gdn_replay_decode and gdn_replay_fold read the field; the cursor calls ignore it.
  */
 #ifndef GDN_REPLAY_H
 #define GDN_REPLAY_H
@@ -90,6 +108,12 @@ typedef enum {
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
+
+/* Granularity of the decay (gdn_shape.gate). */
+typedef enum {
+    GDN_GATE_HEAD = 0, /* GDN: one log-decay g per value head                       */
+    GDN_GATE_KEY = 1   /* KDA: one log-decay per value head and key channel          */
+} gdn_gate;
 
 /* Device-side data error bits OR-ed into *err_flags. */
 enum {
@@ -112,6 +136,7 @@ typedef struct {
     int32_t state_dtype;/* gdn_dtype of the state / checkpoint (0 = GDN_F32)     */
     int32_t step_rounding; /* 1: round a 16-bit state after every step (verify
                               window and fold only; see below), else 0    */
+    int32_t gate;       /* gdn_gate: GDN_GATE_HEAD (0) or GDN_GATE_KEY (1)       */
 } gdn_shape;
 
 /*

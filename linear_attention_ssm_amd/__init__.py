@@ -22,6 +22,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gdn_replay.h")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
+GDN_GATE_HEAD, GDN_GATE_KEY = 0, 1
 EF_SLOT_RANGE, EF_CURSOR_RANGE, EF_WINDOW, EF_ACCEPTED = 1, 2, 4, 8
 
 _DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
@@ -31,7 +32,7 @@ STATE_DTYPES = (torch.float32, torch.bfloat16, torch.float16)
 class gdn_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "N", "Hv", "Hk", "dk", "dv", "L", "qkv_dtype", "ring_dtype", "window",
-                 "state_dtype", "step_rounding")]
+                 "state_dtype", "step_rounding", "gate")]
 
 
 class GdnError(RuntimeError):
@@ -60,7 +61,7 @@ for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_advance",
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 4
+ABI_VERSION = 5
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -108,19 +109,23 @@ def _raise(status: int, what: str):
 
 
 def _io_shape(q, k, v, g, beta, slot_idx):
+    """Sizes of a call; the gate is per head when g is [B,T,Hv] and per key
+    channel (KDA) when g is [B,T,Hv,dk]."""
     _check(q, "q", (torch.float32, torch.bfloat16), 4)
     dev = q.device
     _check(k, "k", q.dtype, 4, dev)
     _check(v, "v", q.dtype, 4, dev)
-    _check(g, "g", torch.float32, 3, dev)
+    _check(g, "g", torch.float32, None, dev)
     _check(beta, "beta", torch.float32, 3, dev)
     _check(slot_idx, "slot_idx", torch.int32, 1, dev)
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
-    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv) \
+    gate = GDN_GATE_KEY if g.dim() == 4 else GDN_GATE_HEAD
+    g_shape = (B, T, Hv, dk) if gate == GDN_GATE_KEY else (B, T, Hv)
+    if k.shape != q.shape or v.shape[:2] != (B, T) or tuple(g.shape) != g_shape \
             or beta.shape != (B, T, Hv) or slot_idx.shape != (B,):
         raise ValueError("inconsistent q/k/v/g/beta/slot_idx shapes")
-    return B, T, Hk, dk, Hv, dv, dev
+    return B, T, Hk, dk, Hv, dv, dev, gate
 
 
 def _out(o, B, T, Hv, dv, dtype, dev):
@@ -136,9 +141,10 @@ def _out(o, B, T, Hv, dv, dtype, dev):
 
 def gdn_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None, stream=None):
     """Plain read-update-write decode step; see gdn_packed_decode in gdn_replay.h.
-    q,k [B,1,Hk,dk]; v [B,1,Hv,dv]; g,beta [B,1,Hv] fp32; slot_idx [B] int32;
-    state [N,Hv,dv,dk] fp32, bf16 or fp16 (updated in place). Returns o [B,1,Hv,dv]."""
-    B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
+    q,k [B,1,Hk,dk]; v [B,1,Hv,dv]; g,beta [B,1,Hv] fp32 (g [B,1,Hv,dk] for the
+    per-key gate); slot_idx [B] int32; state [N,Hv,dv,dk] fp32, bf16 or fp16
+    (updated in place). Returns o [B,1,Hv,dv]."""
+    B, T, Hk, dk, Hv, dv, dev, gate = _io_shape(q, k, v, g, beta, slot_idx)
     _check(state, "state", STATE_DTYPES, 4, dev)
     if tuple(state.shape[1:]) != (Hv, dv, dk):
         raise ValueError("state must be [N, Hv, dv, dk]")
@@ -146,23 +152,24 @@ def gdn_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None,
         _check(err_flags, "err_flags", torch.int32, None, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
     sh = gdn_shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0,
-                   _DT[state.dtype])
+                   _DT[state.dtype], 0, gate)
     _raise(_lib.gdn_packed_decode(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(slot_idx), _ptr(state), _ptr(o), _ptr(err_flags),
                                   _stream(stream)), "gdn_packed_decode")
     return o
 
 
-def _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev):
+def _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate):
     _check(ckpt, "ckpt", STATE_DTYPES, 4, dev)
     _check(ring_d, "ring_d", (torch.float32, torch.float16, torch.bfloat16), 4, dev)
     _check(ring_k, "ring_k", ring_d.dtype, 4, dev)
-    _check(ring_g, "ring_g", torch.float32, 3, dev)
+    _check(ring_g, "ring_g", torch.float32, 4 if gate == GDN_GATE_KEY else 3, dev)
     _check(write_pos, "write_pos", torch.int32, 1, dev)
     N = ckpt.shape[0]
     L = ring_d.shape[2]
+    g_shape = (N, Hv, L, dk) if gate == GDN_GATE_KEY else (N, Hv, L)
     if tuple(ckpt.shape) != (N, Hv, dv, dk) or tuple(ring_d.shape) != (N, Hv, L, dv) \
-            or tuple(ring_k.shape) != (N, Hk, L, dk) or tuple(ring_g.shape) != (N, Hv, L) \
+            or tuple(ring_k.shape) != (N, Hk, L, dk) or tuple(ring_g.shape) != g_shape \
             or tuple(write_pos.shape) != (N,):
         raise ValueError("inconsistent checkpoint / ring / write_pos shapes")
     return N, L
@@ -174,8 +181,8 @@ def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, 
     """ReplaySSM decode step (window=False, T=1) or verify window (window=True);
     see gdn_replay_decode in gdn_replay.h. step_rounding (windows only) rounds
     a 16-bit state after every token. Returns o [B,T,Hv,dv]."""
-    B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
-    N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev)
+    B, T, Hk, dk, Hv, dv, dev, gate = _io_shape(q, k, v, g, beta, slot_idx)
+    N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
     if force_flush is not None:
         _check(force_flush, "force_flush", torch.int32, 1, dev)
         if force_flush.shape != (B,):
@@ -184,7 +191,7 @@ def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, 
         _check(err_flags, "err_flags", torch.int32, None, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
     sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)),
-                   _DT[ckpt.dtype], int(bool(step_rounding)))
+                   _DT[ckpt.dtype], int(bool(step_rounding)), gate)
     _raise(_lib.gdn_replay_decode(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d), _ptr(ring_k),
                                   _ptr(ring_g), _ptr(write_pos), _ptr(force_flush), _ptr(o),
@@ -226,9 +233,10 @@ def gdn_replay_fold(slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags
     _check(ckpt, "ckpt", STATE_DTYPES, 4, dev)
     N, Hv, dv, dk = ckpt.shape
     Hk = ring_k.shape[1]
-    _, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev)
+    gate = GDN_GATE_KEY if ring_g.dim() == 4 else GDN_GATE_HEAD
+    _, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
     sh = gdn_shape(slot_idx.shape[0], 1, N, Hv, Hk, dk, dv, L, GDN_F32, _DT[ring_d.dtype], 0,
-                   _DT[ckpt.dtype], int(bool(step_rounding)))
+                   _DT[ckpt.dtype], int(bool(step_rounding)), gate)
     _raise(_lib.gdn_replay_fold(ctypes.byref(sh), _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d),
                                 _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(err_flags),
                                 _stream(stream)), "gdn_replay_fold")
@@ -267,13 +275,13 @@ def prepare_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring
                           force_flush=None, o=None, err_flags=None, window=False, stream=None):
     """gdn_replay_decode with the same arguments, prepared for repeated calls.
     Returns (call, o)."""
-    B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
-    N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev)
+    B, T, Hk, dk, Hv, dv, dev, gate = _io_shape(q, k, v, g, beta, slot_idx)
+    N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
     if force_flush is not None:
         _check(force_flush, "force_flush", torch.int32, 1, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
     sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)),
-                   _DT[ckpt.dtype])
+                   _DT[ckpt.dtype], 0, gate)
     args = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
             _ptr(ckpt), _ptr(ring_d), _ptr(ring_k), _ptr(ring_g), _ptr(write_pos),
             _ptr(force_flush), _ptr(o), _ptr(err_flags), _stream(stream))
@@ -285,11 +293,11 @@ def prepare_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring
 def prepare_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None,
                           stream=None):
     """gdn_packed_decode prepared for repeated calls. Returns (call, o)."""
-    B, T, Hk, dk, Hv, dv, dev = _io_shape(q, k, v, g, beta, slot_idx)
+    B, T, Hk, dk, Hv, dv, dev, gate = _io_shape(q, k, v, g, beta, slot_idx)
     _check(state, "state", STATE_DTYPES, 4, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
     sh = gdn_shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0,
-                   _DT[state.dtype])
+                   _DT[state.dtype], 0, gate)
     args = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
             _ptr(state), _ptr(o), _ptr(err_flags), _stream(stream))
     keep = (sh, q, k, v, g, beta, slot_idx, state, o, err_flags)

@@ -12,7 +12,7 @@ using namespace gdn;
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -53,6 +53,7 @@ gdn_status check_shape(const gdn_shape* s, bool need_ring) {
   if (s->qkv_dtype != GDN_F32 && s->qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
   if (s->state_dtype != GDN_F32 && s->state_dtype != GDN_BF16 && s->state_dtype != GDN_F16)
     return GDN_ERR_UNSUPPORTED;
+  if (s->gate != GDN_GATE_HEAD && s->gate != GDN_GATE_KEY) return GDN_ERR_INVALID_ARG;
   if (need_ring) {
     if (s->L < 1 || s->L > 64) return GDN_ERR_INVALID_ARG;
     if (s->ring_dtype != GDN_F32 && s->ring_dtype != GDN_F16 && s->ring_dtype != GDN_BF16)
@@ -68,35 +69,35 @@ uint32_t recip(int d) {
   return d <= 1 ? 0u : static_cast<uint32_t>(((1ull << 32) + static_cast<uint64_t>(d) - 1) / d);
 }
 
-hipError_t dispatch_packed(int dk, const DecodeArgs& a, int qkv, int sd, dim3 g, dim3 b,
+hipError_t dispatch_packed(int dk, const DecodeArgs& a, int qkv, int sd, int kg, dim3 g, dim3 b,
                            size_t sm, hipStream_t st) {
   switch (dk) {
-    case 32: return launch_packed<32>(a, qkv, sd, g, b, sm, st);
-    case 64: return launch_packed<64>(a, qkv, sd, g, b, sm, st);
-    case 128: return launch_packed<128>(a, qkv, sd, g, b, sm, st);
-    case 256: return launch_packed<256>(a, qkv, sd, g, b, sm, st);
+    case 32: return launch_packed<32>(a, qkv, sd, kg, g, b, sm, st);
+    case 64: return launch_packed<64>(a, qkv, sd, kg, g, b, sm, st);
+    case 128: return launch_packed<128>(a, qkv, sd, kg, g, b, sm, st);
+    case 256: return launch_packed<256>(a, qkv, sd, kg, g, b, sm, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t dispatch_replay(int dk, const DecodeArgs& a, int qkv, int ring, int sd, dim3 g,
-                           dim3 b, size_t sm, hipStream_t st) {
+hipError_t dispatch_replay(int dk, const DecodeArgs& a, int qkv, int ring, int sd, int kg,
+                           dim3 g, dim3 b, size_t sm, hipStream_t st) {
   switch (dk) {
-    case 32: return launch_replay<32>(a, qkv, ring, sd, g, b, sm, st);
-    case 64: return launch_replay<64>(a, qkv, ring, sd, g, b, sm, st);
-    case 128: return launch_replay<128>(a, qkv, ring, sd, g, b, sm, st);
-    case 256: return launch_replay<256>(a, qkv, ring, sd, g, b, sm, st);
+    case 32: return launch_replay<32>(a, qkv, ring, sd, kg, g, b, sm, st);
+    case 64: return launch_replay<64>(a, qkv, ring, sd, kg, g, b, sm, st);
+    case 128: return launch_replay<128>(a, qkv, ring, sd, kg, g, b, sm, st);
+    case 256: return launch_replay<256>(a, qkv, ring, sd, kg, g, b, sm, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t dispatch_fold(int dk, const FoldArgs& a, int ring, int sd, dim3 g, dim3 b,
+hipError_t dispatch_fold(int dk, const FoldArgs& a, int ring, int sd, int kg, dim3 g, dim3 b,
                          size_t sm, hipStream_t st) {
   switch (dk) {
-    case 32: return launch_fold<32>(a, ring, sd, g, b, sm, st);
-    case 64: return launch_fold<64>(a, ring, sd, g, b, sm, st);
-    case 128: return launch_fold<128>(a, ring, sd, g, b, sm, st);
-    case 256: return launch_fold<256>(a, ring, sd, g, b, sm, st);
+    case 32: return launch_fold<32>(a, ring, sd, kg, g, b, sm, st);
+    case 64: return launch_fold<64>(a, ring, sd, kg, g, b, sm, st);
+    case 128: return launch_fold<128>(a, ring, sd, kg, g, b, sm, st);
+    case 256: return launch_fold<256>(a, ring, sd, kg, g, b, sm, st);
   }
   return hipErrorInvalidValue;
 }
@@ -112,7 +113,7 @@ void fill_decode_geometry(const gdn_shape* s, DecodeArgs& a, dim3& grid, dim3& b
   block = dim3(64u * a.G * (a.VB / 16));
 }
 
-// Work-item geometry of the persistent replay kernel: GH value heads (a
+// Work-item geometry of the replay kernel: GH value heads (a
 // divisor of G) times VB value rows per item, one wavefront per 16 rows of
 // one head, at most 8 wavefronts (GDN_REPLAY_WAVES, default 4).
 void fill_replay_geometry(const gdn_shape* s, DecodeArgs& a, dim3& block, int& n_items) {
@@ -156,8 +157,9 @@ gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, c
   if (s->T != 1 || s->window != 0) return GDN_ERR_INVALID_ARG;
   if (!q || !k || !v || !g || !beta || !slot_idx || !state || !o) return GDN_ERR_INVALID_ARG;
   const size_t es = elem_size(s->qkv_dtype);
+  const size_t ga = s->gate == GDN_GATE_KEY ? 16 : 4;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state, 16) || !aligned(v, es) ||
-      !aligned(o, es) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(slot_idx, 4) ||
+      !aligned(o, es) || !aligned(g, ga) || !aligned(beta, 4) || !aligned(slot_idx, 4) ||
       (err_flags && !aligned(err_flags, 4)))
     return GDN_ERR_INVALID_ARG;
   if (s->B == 0) return GDN_OK;
@@ -168,9 +170,13 @@ gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, c
   fill_decode_geometry(s, a, grid, block);
   a.L = 1;
   a.dump_off = static_cast<int32_t>((2u * s->dk + 4) * sizeof(float));   // q, k, k^T q
-  const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
-  return from_hip(dispatch_packed(s->dk, a, s->qkv_dtype, s->state_dtype, grid, block, smem,
-                                  static_cast<hipStream_t>(stream)));
+  // per-key gate: [G][4][dk] floats of staged gates after the write sink
+  a.kg_off = a.dump_off + static_cast<int32_t>(64 * 8 * sizeof(float));
+  const size_t kg_bytes =
+      s->gate == GDN_GATE_KEY ? static_cast<size_t>(a.G) * 4 * s->dk * sizeof(float) : 0;
+  const size_t smem = a.kg_off + kg_bytes;
+  return from_hip(dispatch_packed(s->dk, a, s->qkv_dtype, s->state_dtype, s->gate, grid, block,
+                                  smem, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
@@ -189,9 +195,10 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
       !write_pos || !o)
     return GDN_ERR_INVALID_ARG;
   const size_t es = elem_size(s->qkv_dtype), rs = elem_size(s->ring_dtype);
+  const size_t ga = s->gate == GDN_GATE_KEY ? 16 : 4;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(ckpt, 16) || !aligned(ring_k, 16) ||
-      !aligned(ring_d, rs) || !aligned(v, es) || !aligned(o, es) || !aligned(g, 4) ||
-      !aligned(beta, 4) || !aligned(ring_g, 4) || !aligned(write_pos, 4) ||
+      !aligned(ring_d, rs) || !aligned(v, es) || !aligned(o, es) || !aligned(g, ga) ||
+      !aligned(beta, 4) || !aligned(ring_g, ga) || !aligned(write_pos, 4) ||
       !aligned(slot_idx, 4) || (err_flags && !aligned(err_flags, 4)) ||
       (force_flush && !aligned(force_flush, 4)))
     return GDN_ERR_INVALID_ARG;
@@ -230,10 +237,25 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
   a.kq_off = static_cast<int32_t>(qk_bytes);
   a.gate_off = static_cast<int32_t>(qk_bytes + 16 * sizeof(float));
   a.kt_off = static_cast<int32_t>(up16(a.gate_off + static_cast<size_t>(a.GH) * s->T * 3 * sizeof(float)));
-  a.dump_off = static_cast<int32_t>(up16(a.kt_off + kt_bytes));
-  a.lds_buf = a.dump_off;
+  size_t end = a.kt_off + kt_bytes;
+  if (s->gate == GDN_GATE_KEY) {
+    // per-key gate: no shared key ring; instead the staged gates [GH][T][4][dk],
+    // one weighted key ring per head (the scalar path's layout and padding) and
+    // the per-channel checkpoint decays [GH][dk]
+    end = a.kt_off;
+    a.kg_off = static_cast<int32_t>(end);
+    end = up16(end + static_cast<size_t>(a.GH) * s->T * 4 * s->dk * sizeof(float));
+    a.kw_off = static_cast<int32_t>(end);
+    const size_t kw_bytes = kt_bytes;
+    a.kw_head = static_cast<int32_t>(kw_bytes / elem_size(s->ring_dtype));
+    end = up16(end + static_cast<size_t>(a.GH) * kw_bytes);
+    a.acol_off = static_cast<int32_t>(end);
+    end += static_cast<size_t>(a.GH) * s->dk * sizeof(float);
+  }
+  a.dump_off = static_cast<int32_t>(up16(end));
   const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
-  return from_hip(dispatch_replay(s->dk, a, s->qkv_dtype, s->ring_dtype, s->state_dtype,
+  if (smem > 160 * 1024) return GDN_ERR_UNSUPPORTED;
+  return from_hip(dispatch_replay(s->dk, a, s->qkv_dtype, s->ring_dtype, s->state_dtype, s->gate,
                                   dim3(n_items), block,
                                   smem, static_cast<hipStream_t>(stream)));
 }
@@ -275,8 +297,9 @@ gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, void* ck
     return GDN_ERR_INVALID_ARG;
   if (s->step_rounding != 0 && s->step_rounding != 1) return GDN_ERR_INVALID_ARG;
   const size_t rs = elem_size(s->ring_dtype);
+  const size_t ga = s->gate == GDN_GATE_KEY ? 16 : 4;
   if (!aligned(ckpt, 16) || !aligned(ring_d, rs) || !aligned(ring_k, rs) ||
-      !aligned(ring_g, 4) || !aligned(write_pos, 4) || !aligned(slot_idx, 4) ||
+      !aligned(ring_g, ga) || !aligned(write_pos, 4) || !aligned(slot_idx, 4) ||
       (err_flags && !aligned(err_flags, 4)))
     return GDN_ERR_INVALID_ARG;
   if (s->B == 0) return GDN_OK;
@@ -288,9 +311,12 @@ gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, void* ck
   a.step_round = s->step_rounding;
   const dim3 grid(static_cast<unsigned>(s->B) * s->Hv * (s->dv / 16));
   const dim3 block(static_cast<unsigned>(16 * s->dk / 4));
-  const size_t smem = static_cast<size_t>(s->L) * (1 + 16 + s->dk) * sizeof(float);
-  return from_hip(dispatch_fold(s->dk, a, s->ring_dtype, s->state_dtype, grid, block, smem,
-                                static_cast<hipStream_t>(stream)));
+  // LDS: the ring's keys [L][dk], d [L][16] and decays ([L], or [L][dk] per key)
+  const size_t n_al = s->gate == GDN_GATE_KEY ? static_cast<size_t>(s->dk) : 1;
+  const size_t smem = static_cast<size_t>(s->L) * (n_al + 16 + s->dk) * sizeof(float);
+  if (smem > 160 * 1024) return GDN_ERR_UNSUPPORTED;
+  return from_hip(dispatch_fold(s->dk, a, s->ring_dtype, s->state_dtype, s->gate, grid, block,
+                                smem, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_replay_reset(const gdn_shape* s, const int32_t* slot_idx, int32_t* write_pos,

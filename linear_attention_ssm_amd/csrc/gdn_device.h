@@ -412,6 +412,49 @@ __device__ __forceinline__ void slab_update(f4 (&S)[NT], const float* k_l, int g
   }
 }
 
+// The same update with a per-key gate (KDA, SGLang PR #28451 Modifications
+// item 7): S <- S Diag(a) + d k^T, rounded as fma(d, k[c], RN(a[c] * S[c])).
+// a_l holds the token's decays a[c] = RN_f32(exp_f64(g[c])) in LDS.
+template <int SD, int NT>
+__device__ __forceinline__ void slab_update_key(f4 (&S)[NT], const float* k_l, const float* a_l,
+                                                int grp, float d) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const f4 kv = *reinterpret_cast<const f4*>(k_l + key_base<SD>(t, grp));
+    const f4 av = *reinterpret_cast<const f4*>(a_l + key_base<SD>(t, grp));
+    const float ax = av.x * S[t].x, ay = av.y * S[t].y;
+    const float az = av.z * S[t].z, aw = av.w * S[t].w;
+    S[t].x = __builtin_fmaf(d, kv.x, ax);
+    S[t].y = __builtin_fmaf(d, kv.y, ay);
+    S[t].z = __builtin_fmaf(d, kv.z, az);
+    S[t].w = __builtin_fmaf(d, kv.w, aw);
+  }
+}
+
+// A token's per-key gate for one head, staged in LDS as four rows of dk
+// floats: the decays a = RN_f32(exp_f64(g)), a o q, a o k, and g itself (for
+// the ring). The readout then is Sq = S (a o q), Sk = S (a o k): the token's
+// decay folds into q and k (SGLang PR #28451, Modifications item 7).
+// Four channels c4*4 .. +3 of the row; q and k as fp32.
+__device__ __forceinline__ void stage_key_gate(float* gl, int dk, int c4, f4 g4, f4 qv, f4 kv) {
+  f4 al;
+  al.x = decay_of(g4.x);
+  al.y = decay_of(g4.y);
+  al.z = decay_of(g4.z);
+  al.w = decay_of(g4.w);
+  f4 aq, ak;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    aq[i] = al[i] * qv[i];
+    ak[i] = al[i] * kv[i];
+  }
+  *reinterpret_cast<f4*>(gl + 4 * c4) = al;
+  *reinterpret_cast<f4*>(gl + dk + 4 * c4) = aq;
+  *reinterpret_cast<f4*>(gl + 2 * dk + 4 * c4) = ak;
+  *reinterpret_cast<f4*>(gl + 3 * dk + 4 * c4) = g4;
+}
+
 // The value lane `i` (wave-uniform) holds, in every lane.
 __device__ __forceinline__ float lane_value(float x, int i) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i));
@@ -536,7 +579,6 @@ struct DecodeArgs {
   int32_t window;          // 1: verify window (no flush, entries at p..p+T-1)
   int32_t kts;             // LDS row stride (elements) of the transposed key ring
   int32_t dump_off;        // LDS byte offset of the [64][8] fp32 write sink
-  int32_t lds_buf;         // bytes of one LDS staging buffer (replay: two, by item parity)
   // work-item mapping of the replay kernel without runtime divisions: the
   // divisors (items per key-side group, Hk, value blocks, waves per head) come
   // with their reciprocals m = ceil(2^32 / d) (0 for d = 1), see udiv()
@@ -546,6 +588,11 @@ struct DecodeArgs {
   // g), the staged key ring
   int32_t kq_off, gate_off, kt_off;
   int32_t step_round;      // round a 16-bit state after each window token
+  // per-key gate (KDA) only, LDS byte offsets: the staged gates of the
+  // workgroup's heads and tokens ([GH][T][4][dk] floats, see stage_key_gate),
+  // the weighted key rings of the heads (kw_head elements apart) and the
+  // per-channel checkpoint decays A ([GH][dk] floats)
+  int32_t kg_off, kw_off, acol_off, kw_head;
 };
 
 struct CursorArgs {

@@ -46,8 +46,10 @@ __device__ __forceinline__ void stage_qk(const DecodeArgs& a, float* lds, int b,
 // ============================================================= packed decode
 //
 // The plain read-update-write step (SGLang PR #28451: the packed decode that
-// reads the state, updates it and writes it back every step).
-template <int DK, int QKV, int SD>
+// reads the state, updates it and writes it back every step). KG = 1 takes
+// the per-key gate (KDA): g is [B, Hv, dk] and the decay is applied per key
+// channel.
+template <int DK, int QKV, int SD, int KG>
 __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   constexpr int NT = DK / 16;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   const auto k_raw = load4_raw<QKV>(a.k, qsrc);
   const size_t ih = static_cast<size_t>(b) * a.Hv + h;
   const auto v_raw = load1_raw<QKV>(a.v, ih * a.dv + vcol);
-  const float gv = ld_uniform(a.g, ih), bt = ld_uniform(a.beta, ih);
+  const float gv = KG ? 0.f : ld_uniform(a.g, ih), bt = ld_uniform(a.beta, ih);
 
   using SE = typename Elem<SD>::T;
   SE* st = static_cast<SE*>(a.state) + ((static_cast<size_t>(s) * a.Hv + h) * a.dv + vcol - col) * DK;
@@ -103,6 +105,17 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
       if (lane == 0) qk[2 * DK] = kq0;
     }
   }
+  float* kgl = reinterpret_cast<float*>(smem + a.kg_off);   // KG: [G][4][DK]
+  if constexpr (KG) {
+    // the per-key gates of the workgroup's G heads (while the state is in flight)
+    for (int i = tid; i < a.G * C4; i += blockDim.x) {
+      const int hh = i / C4, c4 = i - hh * C4;
+      const size_t qi = (static_cast<size_t>(b) * a.Hk + hk) * DK + 4 * c4;
+      const f4 g4 = *reinterpret_cast<const f4*>(
+          a.g + (static_cast<size_t>(b) * a.Hv + hk * a.G + hh) * DK + 4 * c4);
+      stage_key_gate(kgl + hh * 4 * DK, DK, c4, g4, load4<QKV>(a.q, qi), load4<QKV>(a.k, qi));
+    }
+  }
   const float alpha = decay_of(gv);   // while the state is in flight
   __syncthreads();
   const float vv = to_f32<QKV>(v_raw);
@@ -111,10 +124,17 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   slab_decode<SD, DK>(S, R);
   float sq, sk, d, o;
   const float kq = qk[2 * DK];
-  slab_dots<SD>(S, qk, qk + DK, grp, sq, sk);
-  token_out(sq, sk, kq, alpha, bt, vv, d, o);
+  if constexpr (KG) {
+    const float* gl = kgl + (h - hk * a.G) * 4 * DK;
+    slab_dots<SD>(S, gl + DK, gl + 2 * DK, grp, sq, sk);
+    token_out(sq, sk, kq, 1.f, bt, vv, d, o);
+  } else {
+    slab_dots<SD>(S, qk, qk + DK, grp, sq, sk);
+    token_out(sq, sk, kq, alpha, bt, vv, d, o);
+  }
   if (grp == 0) store1<QKV>(a.o, ih * a.dv + vcol, o);
-  slab_update<SD>(S, qk + DK, grp, alpha, d);
+  if constexpr (KG) slab_update_key<SD>(S, qk + DK, kgl + (h - hk * a.G) * 4 * DK, grp, d);
+  else slab_update<SD>(S, qk + DK, grp, alpha, d);
   store_slab<SD, DK>(st, S, col, grp);
 }
 
@@ -236,7 +256,7 @@ __device__ __forceinline__ RowState row_state(const DecodeArgs& a, int b, int T)
 // zero without a memory access (they are also the MFMA's zero padding). All
 // loads are unconditional (surplus lanes read a clamped address) so that they
 // issue before the slab.
-template <int DK, int QKV, int RING, int TT>
+template <int DK, int QKV, int RING, int TT, int KG>
 __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const DecodeArgs& a,
                                             const ItemGeo& g, const RowState& r, int T,
                                             int tid, int lane, int grp, int wave) {
@@ -249,7 +269,7 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
     const int l = lane < ng ? lane : 0;
     const int hh = TT ? l : l / T, t = TT ? 0 : l - hh * T;
     const size_t gi = (static_cast<size_t>(g.b) * T + t) * a.Hv + g.hk * a.G + g.hc * a.GH + hh;
-    f.gate_g = a.g[gi];
+    f.gate_g = KG ? 0.f : a.g[gi];     // a per-key gate is staged in process()
     f.gate_b = a.beta[gi];
   }
   // staging threads: four keys of q and k of token c / C4 (only the
@@ -266,7 +286,9 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
   const char* kbase = static_cast<const char*>(a.ring_k) +
                       (static_cast<size_t>(r.sc) * a.Hk + g.hk) * a.L * DK * RS;
   const __amdgpu_buffer_rsrc_t rk = brsrc(kbase, static_cast<uint32_t>(r.p) * DK * RS);
-  if constexpr (RF32) {
+  if constexpr (KG) {
+    f.kr = v4u{0u, 0u, 0u, 0u};   // the per-key path weights the keys in process()
+  } else if constexpr (RF32) {
     f.kr = __builtin_amdgcn_raw_buffer_load_b128(rk, tid * 16, 0, 0);   // chunk tid
   } else {
     // keys 8kg + 2sub, +1 of entries 4eg .. 4eg+3
@@ -277,8 +299,12 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
     for (int i = 0; i < 4; ++i) f.kr[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + i * DK * 2, 0, 0);
   }
   const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
-  const __amdgpu_buffer_rsrc_t rg = brsrc(a.ring_g + hs * a.L, static_cast<uint32_t>(r.p) * 4);
-  f.g_raw = __builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0);
+  if constexpr (KG) {
+    f.g_raw = 0u;
+  } else {
+    const __amdgpu_buffer_rsrc_t rg = brsrc(a.ring_g + hs * a.L, static_cast<uint32_t>(r.p) * 4);
+    f.g_raw = __builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0);
+  }
   // this lane's ring d entries: 16-bit rings j = 4*grp + i (one 16x16x16
   // k-step), fp32 rings j = 4*i + grp (four 16x16x4 k-steps)
   const char* dbase = static_cast<const char*>(a.ring_d) + hs * a.L * a.dv * RS;
@@ -379,7 +405,85 @@ __device__ __forceinline__ void small_stores(const DecodeArgs& a, size_t oi, siz
   }
 }
 
-template <int DK, int QKV, int RING, int SD, int TT>
+// The per-key gate (KDA) part of the reconstruction for the workgroup's GH
+// heads: per head and key channel c, A[c] = exp(sum_{j<p} g_j[c]) and the
+// MFMA key operand w_j[c] k_j[c] with w_j[c] = exp(sum_{j<i<p} g_i[c]): the
+// decay products fold onto the stored keys instead of onto d (SGLang PR
+// #28451, Modifications item 7). One thread per (head, four channels) runs
+// the per-channel suffix sums from the newest entry down; entries at or past
+// p read as g = 0, k = 0 through the bounded loads, so the padded tail of the
+// last k-step comes out as zeros. The operand lands in the layout the scalar
+// gate's staged key ring uses: [key][entry] (row stride kts) for 16-bit
+// rings, [entry][key] for fp32.
+template <int DK, int RING>
+__device__ __forceinline__ void weight_keys(const DecodeArgs& a, const ItemGeo& g,
+                                            const RowState& r, int lp, unsigned char* buf,
+                                            int tid, int nthr) {
+  using RT = typename Elem<RING>::T;
+  constexpr bool RF32 = (RING == DT_F32);
+  constexpr int RS = RF32 ? 4 : 2;
+  constexpr int C4 = DK / 4;
+  const int p = r.p;
+  const char* kbase = static_cast<const char*>(a.ring_k) +
+                      (static_cast<size_t>(r.sc) * a.Hk + g.hk) * a.L * DK * RS;
+  const __amdgpu_buffer_rsrc_t rk = brsrc(kbase, static_cast<uint32_t>(p) * DK * RS);
+  float* acol = reinterpret_cast<float*>(buf + a.acol_off);
+  for (int i = tid; i < a.GH * C4; i += nthr) {
+    const int hh = i / C4, c4 = i - hh * C4;
+    const size_t hsh = static_cast<size_t>(r.sc) * a.Hv + g.hk * a.G + g.hc * a.GH + hh;
+    const __amdgpu_buffer_rsrc_t rg =
+        brsrc(a.ring_g + hsh * a.L * DK, static_cast<uint32_t>(p) * DK * 4);
+    RT* kw = reinterpret_cast<RT*>(buf + a.kw_off) + hh * a.kw_head;
+    f4 W = {0.f, 0.f, 0.f, 0.f};            // sum of g over the entries after j
+    for (int eg = lp / 4 - 1; eg >= 0; --eg) {
+      f4 gq[4], kv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * eg + e;
+        gq[e] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rg, (j * DK + 4 * c4) * 4, 0, 0));
+        if constexpr (RF32) {
+          kv[e] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rk, (j * DK + 4 * c4) * 4, 0, 0));
+        } else {
+          const v2u w2 = __builtin_amdgcn_raw_buffer_load_b64(rk, (j * DK + 4 * c4) * 2, 0, 0);
+          kv[e].x = to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(w2.x & 0xffffu)));
+          kv[e].y = to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(w2.x >> 16)));
+          kv[e].z = to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(w2.y & 0xffffu)));
+          kv[e].w = to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(w2.y >> 16)));
+        }
+      }
+      uint16_t o16[4][4];                    // [key][entry] of this entry group
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        f4 kwv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kwv[c] = __expf(W[c]) * kv[e][c];
+        if constexpr (RF32) {
+          *reinterpret_cast<f4*>(kw + (4 * eg + e) * DK + 4 * c4) = kwv;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) o16[c][e] = __builtin_bit_cast(uint16_t, from_f32<RING>(kwv[c]));
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) W[c] += gq[e][c];
+      }
+      if constexpr (!RF32) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint2 pk;
+          pk.x = static_cast<uint32_t>(o16[c][0]) | (static_cast<uint32_t>(o16[c][1]) << 16);
+          pk.y = static_cast<uint32_t>(o16[c][2]) | (static_cast<uint32_t>(o16[c][3]) << 16);
+          *reinterpret_cast<uint2*>(kw + (4 * c4 + c) * a.kts + 4 * eg) = pk;
+        }
+      }
+    }
+    f4 A;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) A[c] = __expf(W[c]);
+    *reinterpret_cast<f4*>(acol + hh * DK + 4 * c4) = A;
+  }
+}
+
+template <int DK, int QKV, int RING, int SD, int TT, int KG>
 __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, const RowState& r,
                                         int T, const Small<DK, QKV, RING>& f,
                                         const SlabRaw<SD, DK>& R, unsigned char* buf, float* dump,
@@ -432,11 +536,27 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
       gates[3 * lane + 2] = f.gate_g;
     }
   }
+  float* kgl = reinterpret_cast<float*>(buf + a.kg_off);       // KG: [GH][T][4][DK]
+  if constexpr (KG) {
+    // per-key gates of the workgroup's heads for every token
+    for (int i = tid; i < a.GH * nqk; i += nthr) {
+      const int hh = i / nqk, c = i - hh * nqk;
+      const int tau = TT ? 0 : c / C4, c4 = c - tau * C4;
+      const size_t qi = ((static_cast<size_t>(g.b) * T + tau) * a.Hk + g.hk) * DK + 4 * c4;
+      const size_t gi = ((static_cast<size_t>(g.b) * T + tau) * a.Hv + g.hk * a.G + g.hc * a.GH + hh) * DK;
+      const f4 g4 = *reinterpret_cast<const f4*>(a.g + gi + 4 * c4);
+      stage_key_gate(kgl + (hh * T + tau) * 4 * DK, DK, c4, g4, load4<QKV>(a.q, qi),
+                     load4<QKV>(a.k, qi));
+    }
+    weight_keys<DK, RING>(a, g, r, lp, buf, tid, nthr);
+  }
   // the key ring, entries p..lp-1 as zeros (the bounded loads read them so)
   const char* kbase = static_cast<const char*>(a.ring_k) +
                       (static_cast<size_t>(r.sc) * a.Hk + g.hk) * a.L * DK * RS;
   const __amdgpu_buffer_rsrc_t rk = brsrc(kbase, static_cast<uint32_t>(p) * DK * RS);
-  if constexpr (RF32) {
+  if constexpr (KG) {
+    // staged by weight_keys
+  } else if constexpr (RF32) {
     const int nkz = lp * (DK / 4);               // 16-byte chunks up to lp
     *reinterpret_cast<v4u*>(tid < nkz ? kt + tid * 4 : reinterpret_cast<RT*>(dump + lane * 8)) = f.kr;
     for (int c = tid + nthr; c < nkz; c += nthr)
@@ -480,7 +600,17 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   typename MM::op_t bops[NPRE];
   auto bop_of = [&](int c, const float (&dval)[4]) {
     typename MM::op_t bop;
-    if constexpr (RF32) {
+    if constexpr (KG) {
+      // per-key gate: the weights sit on the keys, d enters as stored
+      if constexpr (RF32) {
+        bop = dval[0];
+      } else {
+        u16x4 bb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bb[i] = __builtin_bit_cast(uint16_t, from_f32<RING>(dval[i]));
+        bop = __builtin_bit_cast(typename MM::op_t, bb);
+      }
+    } else if constexpr (RF32) {
       bop = __shfl(wj, (c * CH + grp) & 63, 64) * dval[0];
     } else {
       u16x4 bb;
@@ -498,12 +628,14 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
     else return to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(raw)));
   };
   if (p > 0) {
-    // entries at or past p read as g = 0: the exclusive sum of lane p-1 is
-    // exactly 0 (empty product = 1)
-    float W, Wn;                                        // W_j = sum_{i>=j} g_i, W_{j+1}
-    wave_suffix_sums(__uint_as_float(f.g_raw), lane, p > 16, W, Wn);
-    wj = (lane < p) ? __expf(Wn) : 0.f;                 // w_j = exp(W_{j+1})
-    A = __expf(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(W))));
+    if constexpr (!KG) {
+      // entries at or past p read as g = 0: the exclusive sum of lane p-1 is
+      // exactly 0 (empty product = 1)
+      float W, Wn;                                      // W_j = sum_{i>=j} g_i, W_{j+1}
+      wave_suffix_sums(__uint_as_float(f.g_raw), lane, p > 16, W, Wn);
+      wj = (lane < p) ? __expf(Wn) : 0.f;               // w_j = exp(W_{j+1})
+      A = __expf(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(W))));
+    }
 #pragma unroll
     for (int c = 0; c < NPRE; ++c) {
       float dv1[4];
@@ -533,18 +665,26 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
     }
   }
   if (p > 0) {
+    const int wh0 = g.h - (g.hk * a.G + g.hc * a.GH);         // head within the workgroup
+    const RT* ko = KG ? reinterpret_cast<const RT*>(buf + a.kw_off) + wh0 * a.kw_head : kt;
     auto kstep = [&](int c, typename MM::op_t bop) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         typename MM::op_t aop;
         const int key = key_of_row<SD>(t, col);
-        if constexpr (RF32) aop = kt[(c * CH + grp) * DK + key];
-        else aop = *reinterpret_cast<const typename MM::op_t*>(kt + key * a.kts + c * CH + 4 * grp);
+        if constexpr (RF32) aop = ko[(c * CH + grp) * DK + key];
+        else aop = *reinterpret_cast<const typename MM::op_t*>(ko + key * a.kts + c * CH + 4 * grp);
         S[t] = MM::mma(aop, bop, S[t]);
       }
     };
+    if constexpr (KG) {
+      const float* acol = reinterpret_cast<const float*>(buf + a.acol_off) + wh0 * DK;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) S[t] *= A;
+      for (int t = 0; t < NT; ++t) S[t] *= *reinterpret_cast<const f4*>(acol + key_base<SD>(t, grp));
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) S[t] *= A;
+    }
 #pragma unroll
     for (int c = 0; c < NPRE; ++c)
       if (c < nch) kstep(c, bops[c]);
@@ -587,20 +727,32 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
     const float* gt = gates + 3 * (wh * T + tau);
     const float alpha = gt[0], bt = gt[1], gv = gt[2];
     const float kq = kq_l[tau];
+    const float* gl = kgl + (wh * T + tau) * 4 * DK;      // KG: a, a o q, a o k, g
     float sq, sk, d, o;
-    slab_dots<SD>(S, ql, kl, grp, sq, sk);
-    token_out(sq, sk, kq, alpha, bt, vv, d, o);
+    if constexpr (KG) {
+      slab_dots<SD>(S, gl + DK, gl + 2 * DK, grp, sq, sk);
+      token_out(sq, sk, kq, 1.f, bt, vv, d, o);
+    } else {
+      slab_dots<SD>(S, ql, kl, grp, sq, sk);
+      token_out(sq, sk, kq, alpha, bt, vv, d, o);
+    }
     const bool app = r.ok && !r.flush;              // this token appends a ring entry
     const int pos = p + tau;
     small_stores<QKV, RING>(a, ih * a.dv + g.vcol, (hs * a.L + pos) * a.dv + g.vcol,
-                            hs * a.L + pos, r.ok ? o : 0.f, d, gv, app, gwriter_wave, grp,
-                            col);
+                            hs * a.L + pos, r.ok ? o : 0.f, d, gv, app,
+                            KG ? false : gwriter_wave, grp, col);
+    if constexpr (KG) {
+      if (app && gwriter_wave && lane < C4)
+        *reinterpret_cast<f4*>(a.ring_g + (hs * a.L + pos) * DK + 4 * lane) =
+            *reinterpret_cast<const f4*>(gl + 3 * DK + 4 * lane);
+    }
     if (app && kwriter && lane < C4) {
       const f4 kv = *reinterpret_cast<const f4*>(kl + 4 * lane);
       store4<RING>(a.ring_k, (ks * a.L + pos) * DK + 4 * lane, kv);
     }
     if (r.flush || (!TT && a.window && tau + 1 < T)) {
-      slab_update<SD>(S, kl, grp, alpha, d);
+      if constexpr (KG) slab_update_key<SD>(S, kl, gl, grp, d);
+      else slab_update<SD>(S, kl, grp, alpha, d);
       if (!TT && a.step_round) slab_round<SD>(S);
     }
     vv = v_next;
@@ -611,7 +763,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   }
 }
 
-template <int DK, int QKV, int RING, int SD, int TT>
+template <int DK, int QKV, int RING, int SD, int TT, int KG>
 __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* dump = reinterpret_cast<float*>(smem + a.dump_off);    // [64][8] write sink
@@ -624,10 +776,10 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   const RowState r = row_state(a, g.b, T);
   Small<DK, QKV, RING> sm;
   SlabRaw<SD, DK> R;
-  fetch_small<DK, QKV, RING, TT>(sm, a, g, r, T, tid, lane, grp, wave);
+  fetch_small<DK, QKV, RING, TT, KG>(sm, a, g, r, T, tid, lane, grp, wave);
   __builtin_amdgcn_sched_barrier(0);
   fetch_slab<SD, DK>(R, a, g, r, col, grp);
-  process<DK, QKV, RING, SD, TT>(a, g, r, T, sm, R, smem, dump, tid, lane, grp, col, wave);
+  process<DK, QKV, RING, SD, TT, KG>(a, g, r, T, sm, R, smem, dump, tid, lane, grp, col, wave);
 }
 
 // ============================================================= fold
@@ -635,7 +787,9 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
 // Fold the valid ring entries into the checkpoint with the pinned two-step
 // rounding (SGLang PR #42388 "The idea"; SGLang PR #36821 fold). Workgroup =
 // (row, value head, 16 value rows); thread = one 16-byte group of 4 keys.
-template <int DK, int RING, int SD>
+// KG = 1: per-key gate (ring_g [N, Hv, L, dk]), each channel decays by its
+// own a_j[c].
+template <int DK, int RING, int SD, int KG>
 __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   constexpr int C4 = DK / 4;
   constexpr int FV = 16;
@@ -643,7 +797,7 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* kl = reinterpret_cast<float*>(smem);        // [L][DK]  key entries (16-byte rows)
   float* dl = kl + a.L * DK;                          // [L][FV]  d entries
-  float* al = dl + a.L * FV;                          // [L]      decays
+  float* al = dl + a.L * FV;                          // [L] decays ([L][DK] for KG)
 
   const int nvb = a.dv / FV;
   int blk = item_of_block(blockIdx.x, gridDim.x, nvb * a.G);
@@ -674,7 +828,17 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   SE* xbase = static_cast<SE*>(a.ckpt) + (hs * a.dv + vb * FV) * DK;   // the block's 16 rows
   f4 x = load4<SD>(xbase, row * DK + e4);
 
-  if (tid < p) al[tid] = decay_of(a.ring_g[hs * a.L + tid]);
+  if constexpr (KG) {
+    for (int c = tid; c < p * C4; c += blockDim.x) {
+      const int j = c / C4, q4 = (c % C4) * 4;
+      const f4 g4 = *reinterpret_cast<const f4*>(a.ring_g + (hs * a.L + j) * DK + q4);
+      f4 av;
+      av.x = decay_of(g4.x); av.y = decay_of(g4.y); av.z = decay_of(g4.z); av.w = decay_of(g4.w);
+      *reinterpret_cast<f4*>(al + j * DK + q4) = av;
+    }
+  } else {
+    if (tid < p) al[tid] = decay_of(a.ring_g[hs * a.L + tid]);
+  }
   for (int c = tid; c < p * FV; c += blockDim.x) {
     const int j = c / FV, r = c % FV;
     dl[c] = to_f32<RING>(static_cast<const RT*>(a.ring_d)[(hs * a.L + j) * a.dv + vb * FV + r]);
@@ -692,10 +856,12 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   {
 #pragma clang fp contract(off)
     for (int j = 0; j < p; ++j) {
-      const float aj = al[j];
+      f4 aj;
+      if constexpr (KG) aj = *reinterpret_cast<const f4*>(al + j * DK + e4);
+      else aj = f4{al[j], al[j], al[j], al[j]};
       const float dj = dl[j * FV + row];
       const f4 kv = *reinterpret_cast<const f4*>(kl + j * DK + e4);
-      const float tx = aj * x.x, ty = aj * x.y, tz = aj * x.z, tw = aj * x.w;
+      const float tx = aj.x * x.x, ty = aj.y * x.y, tz = aj.z * x.z, tw = aj.w * x.w;
       x.x = __builtin_fmaf(dj, kv.x, tx);
       x.y = __builtin_fmaf(dj, kv.y, ty);
       x.z = __builtin_fmaf(dj, kv.z, tz);

@@ -6,15 +6,16 @@
 
 namespace gdn {
 
+// kg: 0 = one decay per value head (GDN), 1 = one per key channel (KDA)
 template <int DK>
-hipError_t launch_packed(const DecodeArgs& a, int qkv, int sd, dim3 grid, dim3 block,
+hipError_t launch_packed(const DecodeArgs& a, int qkv, int sd, int kg, dim3 grid, dim3 block,
                          size_t smem, hipStream_t stream);
 template <int DK>
-hipError_t launch_replay(const DecodeArgs& a, int qkv, int ring, int sd, dim3 grid, dim3 block,
-                         size_t smem, hipStream_t stream);
+hipError_t launch_replay(const DecodeArgs& a, int qkv, int ring, int sd, int kg, dim3 grid,
+                         dim3 block, size_t smem, hipStream_t stream);
 template <int DK>
-hipError_t launch_fold(const FoldArgs& a, int ring, int sd, dim3 grid, dim3 block, size_t smem,
-                       hipStream_t stream);
+hipError_t launch_fold(const FoldArgs& a, int ring, int sd, int kg, dim3 grid, dim3 block,
+                       size_t smem, hipStream_t stream);
 
 hipError_t launch_reset(const CursorArgs& a, hipStream_t stream);
 hipError_t launch_advance(const CursorArgs& a, hipStream_t stream);

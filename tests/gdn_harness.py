@@ -19,7 +19,7 @@ import numpy as np
 import torch
 
 import gdn_inputs as gi
-from oracle import ReplayModel, gdn_step, next_cursor, rel_err
+from oracle import ReplayModel, next_cursor, rel_err, step
 
 DEV = torch.device("cuda:0")
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -78,14 +78,15 @@ class Pool:
         self.w = w
         self.ckpt = to_dev(S0)
         rdt = TORCH_DT[w.ring]
+        gshape = (w.N, w.Hv, w.L, w.dk) if w.gate == "key" else (w.N, w.Hv, w.L)
         if garbage:
             self.ring_d = to_dev(gi.garbage_like((w.N, w.Hv, w.L, w.dv), w.ring, 1), w.ring)
             self.ring_k = to_dev(gi.garbage_like((w.N, w.Hk, w.L, w.dk), w.ring, 2), w.ring)
-            self.ring_g = to_dev(gi.garbage_like((w.N, w.Hv, w.L), "f32", 3))
+            self.ring_g = to_dev(gi.garbage_like(gshape, "f32", 3))
         else:
             self.ring_d = torch.zeros((w.N, w.Hv, w.L, w.dv), dtype=rdt, device=DEV)
             self.ring_k = torch.zeros((w.N, w.Hk, w.L, w.dk), dtype=rdt, device=DEV)
-            self.ring_g = torch.zeros((w.N, w.Hv, w.L), dtype=torch.float32, device=DEV)
+            self.ring_g = torch.zeros(gshape, dtype=torch.float32, device=DEV)
         self.write_pos = torch.zeros(w.N, dtype=torch.int32, device=DEV)
         self.err = torch.zeros(1, dtype=torch.int32, device=DEV)
 
@@ -178,7 +179,7 @@ def run_decode(w: gi.Workload, kind: str = "replay", steps: Optional[int] = None
             wp_model[s] = nxt
         # oracle values on the sampled rows
         q, k, v, g, beta = (a[rows, 0] for a in x.f64())
-        o_ref = gdn_step(S_true, sub, q, k, v, g, beta)
+        o_ref = step(S_true, sub, q, k, v, g, beta)
         o_gpu = to_f64(o[rows, 0])
         e = rel_err(o_gpu, o_ref)
         rep.o_err.append(e)

@@ -28,7 +28,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 4
+    assert lib.gdn_abi_version() == 5
     for st in range(4):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -58,6 +58,10 @@ def packed(sh, ptrs=None):
     (dict(step_rounding=1), gdn.GDN_ERR_INVALID_ARG),   # decode step: windows only
     (dict(T=2, window=1, step_rounding=2), gdn.GDN_ERR_INVALID_ARG),
     (dict(state_dtype=-1), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(gate=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(gate=-1), gdn.GDN_ERR_INVALID_ARG),
+    # per-key gate, 16-token windows at dk = 256: the staged gates exceed LDS
+    (dict(gate=1, T=16, window=1, dk=256, L=64), gdn.GDN_ERR_UNSUPPORTED),
     (dict(T=2), gdn.GDN_ERR_INVALID_ARG),               # decode mode needs T = 1
     (dict(T=2, window=1, L=1), gdn.GDN_ERR_INVALID_ARG),  # window longer than the ring
     (dict(window=2), gdn.GDN_ERR_INVALID_ARG),
@@ -83,6 +87,14 @@ def test_replay_decode_rejects_bad_pointers():
     assert replay(shape(), p) == gdn.GDN_ERR_INVALID_ARG
     # force_flush is not allowed with a verify window
     assert replay(shape(T=2, window=1), ff=FAKE[13]) == gdn.GDN_ERR_INVALID_ARG
+    # a per-key gate reads g and ring_g in 16-byte pieces
+    for i in (3, 9):
+        p = list(FAKE[:12])
+        p[i] = ctypes.c_void_p(FAKE[i].value + 4)
+        assert replay(shape(gate=gdn.GDN_GATE_KEY), p) == gdn.GDN_ERR_INVALID_ARG, i
+    p = list(FAKE[:8])
+    p[3] = ctypes.c_void_p(FAKE[3].value + 4)
+    assert packed(shape(gate=gdn.GDN_GATE_KEY), p) == gdn.GDN_ERR_INVALID_ARG
 
 
 def test_empty_batch_is_a_no_op():
@@ -100,6 +112,13 @@ def test_packed_and_cursor_entry_points_validate():
     assert packed(shape(T=2)) == gdn.GDN_ERR_INVALID_ARG
     assert packed(shape(dk=48)) == gdn.GDN_ERR_UNSUPPORTED
     assert packed(shape(state_dtype=5)) == gdn.GDN_ERR_UNSUPPORTED
+    assert packed(shape(gate=3)) == gdn.GDN_ERR_INVALID_ARG
+    assert gdn.lib().gdn_replay_fold(ctypes.byref(shape(gate=3)), *FAKE[:6], None, None) \
+        == gdn.GDN_ERR_INVALID_ARG
+    p = list(FAKE[:6])
+    p[4] = ctypes.c_void_p(FAKE[4].value + 4)            # per-key ring_g misaligned
+    assert gdn.lib().gdn_replay_fold(ctypes.byref(shape(gate=1)), *p, None, None) \
+        == gdn.GDN_ERR_INVALID_ARG
     assert gdn.lib().gdn_replay_fold(ctypes.byref(shape(state_dtype=5)), *FAKE[:6], None, None) \
         == gdn.GDN_ERR_UNSUPPORTED
     p = list(FAKE[:8])

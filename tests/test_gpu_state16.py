@@ -23,7 +23,7 @@ import torch
 
 import gdn_inputs as gi
 from gdn_harness import DEV, Pool, bits, dev_inputs, log, to_dev, to_f64
-from oracle import ReplayModel, fold_f32, gdn_step, next_cursor, quantize, rel_err
+from oracle import ReplayModel, fold_f32, gdn_step, next_cursor, quantize, rel_err, step
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +64,7 @@ def run_packed16(gdn, w, n_sample=None):
         xi = dev_inputs(x)
         o = gdn.gdn_packed_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, state, err_flags=err)
         q, k, v, g, beta = (a[rows, 0] for a in x.f64())
-        o_ref = gdn_step(S_ref, sub, q, k, v, g, beta, state_fmt=w.state)
+        o_ref = step(S_ref, sub, q, k, v, g, beta, state_fmt=w.state)
         eo = rel_err(to_f64(o[rows, 0]), o_ref)
         es = rel_err(to_f64(state[torch.from_numpy(slots[rows]).to(DEV)]), S_ref)
         worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
@@ -77,7 +77,7 @@ def run_packed16(gdn, w, n_sample=None):
 def run_replay16(gdn, w, n_sample=None, check_untouched=False):
     slots = gi.slot_map(w)
     pool, S0 = make_pool(w)
-    model = ReplayModel(S0, w.Hk, w.L, state_fmt=w.state)
+    model = ReplayModel(S0, w.Hk, w.L, state_fmt=w.state, gate=w.gate)
     live = np.where(slots >= 0)[0]
     rows = live if n_sample is None else live[:n_sample]
     slot_t = to_dev(slots)
