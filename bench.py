@@ -60,16 +60,17 @@ def bytes_decode_head_step(w: gi.Workload, p: int, flush: bool, kind: str) -> fl
     rs = 2 if w.ring != "f32" else 4
     ss = 2 if w.state != "f32" else 4
     G = w.Hv // w.Hk
+    gb = 4 * w.dk if w.gate == "key" else 4            # g per value head (per key channel: KDA)
     state = ss * w.dv * w.dk
-    io = 2 * es * w.dk / G + 2 * es * w.dv + 8          # q, k (per k-head), v, o, g, beta
+    io = 2 * es * w.dk / G + 2 * es * w.dv + gb + 4     # q, k (per k-head), v, o, g, beta
     if kind == "packed":
         return 2 * state + io
     b = state + io
-    b += p * (rs * w.dv + rs * w.dk / G + 4)             # valid ring entries read
+    b += p * (rs * w.dv + rs * w.dk / G + gb)            # valid ring entries read
     if flush:
         b += state                                       # checkpoint written from registers
     else:
-        b += rs * w.dv + rs * w.dk / G + 4               # ring append
+        b += rs * w.dv + rs * w.dk / G + gb              # ring append
     return b
 
 
@@ -111,7 +112,8 @@ class LayerSet:
                 torch.bfloat16 if w.ring == "bf16" else torch.float32)
             self.ring_d = torch.zeros((w.N, w.Hv, w.L, w.dv), dtype=rdt, device=dev)
             self.ring_k = torch.zeros((w.N, w.Hk, w.L, w.dk), dtype=rdt, device=dev)
-            self.ring_g = torch.zeros((w.N, w.Hv, w.L), dtype=torch.float32, device=dev)
+            gshape = (w.N, w.Hv, w.L, w.dk) if w.gate == "key" else (w.N, w.Hv, w.L)
+            self.ring_g = torch.zeros(gshape, dtype=torch.float32, device=dev)
 
 
 def input_sets(w, n, dev, T=None):
@@ -218,7 +220,7 @@ def bench_replay(w, R, steps, warmup, dev, log):
     live = int(np.count_nonzero(slots >= 0))
     mean_p = float(np.mean([p for p, _ in cur]))
     flush_frac = float(np.mean([fl for _, fl in cur]))
-    log(f"replay [{w.state} state]: {ms_step * 1e3:.1f} us/step ({R} layers + advance), decode kernel "
+    log(f"replay [{w.state} state, {w.gate} gate]: {ms_step * 1e3:.1f} us/step ({R} layers + advance), decode kernel "
         f"{ms_dec * 1e3:.2f} us, {bytes_launch / 1e6:.2f} MB/launch, "
         f"mean p {mean_p:.2f}, flush frac {flush_frac:.4f}")
     return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
@@ -245,7 +247,7 @@ def bench_packed(w, R, steps, dev, log):
     ms_k = ms_step / R
     live = int(np.count_nonzero(slots >= 0))
     bytes_launch = live * w.Hv * bytes_decode_head_step(w, 0, False, "packed")
-    log(f"packed [{w.state} state]: {ms_step * 1e3:.1f} us/step ({R} layers), kernel {ms_k * 1e3:.2f} us, "
+    log(f"packed [{w.state} state, {w.gate} gate]: {ms_step * 1e3:.1f} us/step ({R} layers), kernel {ms_k * 1e3:.2f} us, "
         f"{bytes_launch / 1e6:.2f} MB/launch")
     return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
                 kernel_ms=ms_k, bytes_per_launch=bytes_launch)
@@ -426,6 +428,8 @@ def main():
     w16 = dataclasses.replace(w, state="bf16")
     rep16 = bench_replay(w16, R, steps, warmup, dev, log)
     pk16 = bench_packed(w16, R, steps, dev, log)
+    repk = bench_replay(gi.C7, R, steps, warmup, dev, log)
+    pkk = bench_packed(gi.C7, R, steps, dev, log)
     wf = bench_window_fold(gi.C5, R, max(4, steps // 8), dev, log)
     ll = bench_lossless(gi.C6, R, max(4, steps // 8), dev, log)
     if args.profile_pass:
@@ -484,6 +488,21 @@ def main():
             "packed_bytes_per_launch": pk16["bytes_per_launch"],
             "replay_vs_packed_kernel": pk16["kernel_ms"] / rep16["kernel_ms"],
             "replay_vs_fp32_replay": rep["kernel_ms"] / rep16["kernel_ms"],
+        },
+        "kda_c7": {
+            "note": ("the standard workload with a per-key gate (KDA): g [B, Hv, dk] and "
+                     "ring_g [N, Hv, L, dk]; replay vs the packed decode with the same gate"),
+            "replay_head_steps_per_s": repk["head_steps_per_s"],
+            "replay_kernel_us": repk["kernel_ms"] * 1e3,
+            "replay_gbs": repk["bytes_per_launch"] / (repk["kernel_ms"] / 1e3) / 1e9,
+            "replay_frac": repk["bytes_per_launch"] / (repk["kernel_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "replay_bytes_per_launch": repk["bytes_per_launch"],
+            "packed_head_steps_per_s": pkk["head_steps_per_s"],
+            "packed_kernel_us": pkk["kernel_ms"] * 1e3,
+            "packed_gbs": pkk["bytes_per_launch"] / (pkk["kernel_ms"] / 1e3) / 1e9,
+            "packed_bytes_per_launch": pkk["bytes_per_launch"],
+            "replay_vs_packed_kernel": pkk["kernel_ms"] / repk["kernel_ms"],
+            "replay_vs_packed": repk["head_steps_per_s"] / pkk["head_steps_per_s"],
         },
         "verify_window_c5": wf,
         "lossless_verify_c6": ll,

@@ -409,11 +409,13 @@ __device__ __forceinline__ void small_stores(const DecodeArgs& a, size_t oi, siz
 // heads: per head and key channel c, A[c] = exp(sum_{j<p} g_j[c]) and the
 // MFMA key operand w_j[c] k_j[c] with w_j[c] = exp(sum_{j<i<p} g_i[c]): the
 // decay products fold onto the stored keys instead of onto d (SGLang PR
-// #28451, Modifications item 7). One thread per (head, four channels) runs
-// the per-channel suffix sums from the newest entry down; entries at or past
-// p read as g = 0, k = 0 through the bounded loads, so the padded tail of the
-// last k-step comes out as zeros. The operand lands in the layout the scalar
-// gate's staged key ring uses: [key][entry] (row stride kts) for 16-bit
+// #28451, Modifications item 7). One thread per (head, key channel) runs the
+// channel's suffix sums from the newest entry down (spreading the channels
+// over every thread of the workgroup: one thread per four channels left three
+// quarters of the workgroup waiting on the first wavefront). Entries at or
+// past p read as g = 0, k = 0 through the bounded loads, so the padded tail of
+// the last k-step comes out as zeros. The operand lands in the layout of the
+// scalar gate's staged key ring: [key][entry] (row stride kts) for 16-bit
 // rings, [entry][key] for fp32.
 template <int DK, int RING>
 __device__ __forceinline__ void weight_keys(const DecodeArgs& a, const ItemGeo& g,
@@ -422,64 +424,46 @@ __device__ __forceinline__ void weight_keys(const DecodeArgs& a, const ItemGeo& 
   using RT = typename Elem<RING>::T;
   constexpr bool RF32 = (RING == DT_F32);
   constexpr int RS = RF32 ? 4 : 2;
-  constexpr int C4 = DK / 4;
   const int p = r.p;
   const char* kbase = static_cast<const char*>(a.ring_k) +
                       (static_cast<size_t>(r.sc) * a.Hk + g.hk) * a.L * DK * RS;
   const __amdgpu_buffer_rsrc_t rk = brsrc(kbase, static_cast<uint32_t>(p) * DK * RS);
   float* acol = reinterpret_cast<float*>(buf + a.acol_off);
-  for (int i = tid; i < a.GH * C4; i += nthr) {
-    const int hh = i / C4, c4 = i - hh * C4;
+  for (int i = tid; i < a.GH * DK; i += nthr) {
+    const int hh = i / DK, c = i - hh * DK;
     const size_t hsh = static_cast<size_t>(r.sc) * a.Hv + g.hk * a.G + g.hc * a.GH + hh;
     const __amdgpu_buffer_rsrc_t rg =
         brsrc(a.ring_g + hsh * a.L * DK, static_cast<uint32_t>(p) * DK * 4);
     RT* kw = reinterpret_cast<RT*>(buf + a.kw_off) + hh * a.kw_head;
-    f4 W = {0.f, 0.f, 0.f, 0.f};            // sum of g over the entries after j
+    float W = 0.f;                             // sum of g_i[c] over the entries after j
     for (int eg = lp / 4 - 1; eg >= 0; --eg) {
-      f4 gq[4], kv[4];
+      float gq[4], kv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 4 * eg + e;
-        gq[e] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rg, (j * DK + 4 * c4) * 4, 0, 0));
-        if constexpr (RF32) {
-          kv[e] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rk, (j * DK + 4 * c4) * 4, 0, 0));
-        } else {
-          const v2u w2 = __builtin_amdgcn_raw_buffer_load_b64(rk, (j * DK + 4 * c4) * 2, 0, 0);
-          kv[e].x = to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(w2.x & 0xffffu)));
-          kv[e].y = to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(w2.x >> 16)));
-          kv[e].z = to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(w2.y & 0xffffu)));
-          kv[e].w = to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(w2.y >> 16)));
-        }
+        gq[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, (j * DK + c) * 4, 0, 0));
+        if constexpr (RF32)
+          kv[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rk, (j * DK + c) * 4, 0, 0));
+        else
+          kv[e] = to_f32<RING>(from_bits<RING>(static_cast<uint16_t>(
+              __builtin_amdgcn_raw_buffer_load_b16(rk, (j * DK + c) * 2, 0, 0))));
       }
-      uint16_t o16[4][4];                    // [key][entry] of this entry group
+      uint16_t o16[4];
 #pragma unroll
       for (int e = 3; e >= 0; --e) {
-        f4 kwv;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kwv[c] = __expf(W[c]) * kv[e][c];
-        if constexpr (RF32) {
-          *reinterpret_cast<f4*>(kw + (4 * eg + e) * DK + 4 * c4) = kwv;
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) o16[c][e] = __builtin_bit_cast(uint16_t, from_f32<RING>(kwv[c]));
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) W[c] += gq[e][c];
+        const float kwv = __expf(W) * kv[e];
+        if constexpr (RF32) kw[(4 * eg + e) * DK + c] = kwv;
+        else o16[e] = __builtin_bit_cast(uint16_t, from_f32<RING>(kwv));
+        W += gq[e];
       }
       if constexpr (!RF32) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint2 pk;
-          pk.x = static_cast<uint32_t>(o16[c][0]) | (static_cast<uint32_t>(o16[c][1]) << 16);
-          pk.y = static_cast<uint32_t>(o16[c][2]) | (static_cast<uint32_t>(o16[c][3]) << 16);
-          *reinterpret_cast<uint2*>(kw + (4 * c4 + c) * a.kts + 4 * eg) = pk;
-        }
+        uint2 pk;
+        pk.x = static_cast<uint32_t>(o16[0]) | (static_cast<uint32_t>(o16[1]) << 16);
+        pk.y = static_cast<uint32_t>(o16[2]) | (static_cast<uint32_t>(o16[3]) << 16);
+        *reinterpret_cast<uint2*>(kw + c * a.kts + 4 * eg) = pk;
       }
     }
-    f4 A;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) A[c] = __expf(W[c]);
-    *reinterpret_cast<f4*>(acol + hh * DK + 4 * c4) = A;
+    acol[hh * DK + c] = __expf(W);
   }
 }
 
