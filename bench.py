@@ -3,8 +3,9 @@
 One step = one decode forward of the standard workload (B = 64 rows, Hv = 32,
 Hk = 16, dk = dv = 128, ring L = 16, fp32 checkpoint, bf16 q/k/v/o, fp16 d/k
 ring, staggered cursors) through R = 8 GDN layers: one gdn_replay_decode call
-per layer, each on its own checkpoint + ring set, then one gdn_replay_advance
-(the cursor is shared by the layers and advances once per forward). The 8
+per layer, each on its own checkpoint + ring set; the last layer's call is
+gdn_replay_decode_advance, which also advances the cursors (they are shared
+by the layers and advance once per forward). The 8
 layer sets (~1.1 GiB) exceed the 256 MB Infinity Cache, so the checkpoint is
 streamed from HBM as in a real multi-layer model.
 
@@ -191,9 +192,19 @@ def bench_replay(w, R, steps, warmup, dev, log):
             gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
                                   ls.ring_g, wp, force_flush=ff, o=o, err_flags=err)
 
+    arrive = gdn.arrive_workspace(w.B, dev)
+
     def forward(ff):
-        decodes(ff)
-        gdn.gdn_replay_advance(slot_t, wp, w.L, force_flush=ff, err_flags=err)
+        # the last layer's decode advances the cursors (fused advance)
+        for i, ls in enumerate(layers):
+            q, k, v, g, beta = ins[i % len(ins)]
+            if i < len(layers) - 1:
+                gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
+                                      ls.ring_g, wp, force_flush=ff, o=o, err_flags=err)
+            else:
+                gdn.gdn_replay_decode_advance(q, k, v, g, beta, slot_t, ls.state, ls.ring_d,
+                                              ls.ring_k, ls.ring_g, wp, arrive, force_flush=ff,
+                                              o=o, err_flags=err)
 
     # eager warm-up: the staggered forced flushes of the first L steps spread
     # the slots' flush phases evenly over the ring cycle
@@ -205,7 +216,7 @@ def bench_replay(w, R, steps, warmup, dev, log):
     g_fwd = graph_of(lambda: forward(no_ff))          # runs one forward eagerly, then captures
     n_fwd += 1
     g_dec = graph_of(lambda: decodes(no_ff))          # one decode-only run, then captures
-    # pass 1: whole-job throughput (R decodes + the advance per step)
+    # pass 1: whole-job throughput (R decodes, the last one advancing the cursors)
     ms_step = time_graph(g_fwd, steps)
     n_fwd += steps + 1                                # time_graph replays once before timing
     # pass 2: the R decode kernels alone, back to back in one graph (cursors
@@ -220,7 +231,7 @@ def bench_replay(w, R, steps, warmup, dev, log):
     live = int(np.count_nonzero(slots >= 0))
     mean_p = float(np.mean([p for p, _ in cur]))
     flush_frac = float(np.mean([fl for _, fl in cur]))
-    log(f"replay [{w.state} state, {w.gate} gate]: {ms_step * 1e3:.1f} us/step ({R} layers + advance), decode kernel "
+    log(f"replay [{w.state} state, {w.gate} gate]: {ms_step * 1e3:.1f} us/step ({R} layers, fused advance), decode kernel "
         f"{ms_dec * 1e3:.2f} us, {bytes_launch / 1e6:.2f} MB/launch, "
         f"mean p {mean_p:.2f}, flush frac {flush_frac:.4f}")
     return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
@@ -452,8 +463,9 @@ def main():
         "config": {
             "workload": (f"ReplaySSM GDN single-token decode, B={w.B} rows, Hv={w.Hv}, Hk={w.Hk}, "
                          f"dk=dv={w.dk}, ring L={w.L}, fp32 checkpoint, bf16 q/k/v/o, fp16 d/k "
-                         f"ring (fp16 MFMA operands), staggered cursors; one step = {R} layers "
-                         f"x gdn_replay_decode + 1 gdn_replay_advance"),
+                         f"ring (fp16 MFMA operands), staggered cursors; one step = {R} layers: "
+                         f"{R - 1} x gdn_replay_decode + 1 x gdn_replay_decode_advance (the "
+                         f"last layer advances the cursors)"),
             "global_batch": w.B, "layers_per_step": R, "ring_L": w.L,
             "head_steps_per_launch": rep["head_steps_per_launch"],
             "mean_valid_entries": round(rep["mean_p"], 3),

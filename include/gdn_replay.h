@@ -199,6 +199,34 @@ gdn_status gdn_replay_decode(const gdn_shape *shape, const void *q, const void *
                              void *stream);
 
 /*
+ * gdn_replay_decode_advance -- a decode step (window = 0, T = 1) with the
+ * cursor advance of gdn_replay_advance fused into it: the forward's last
+ * layer calls it instead of gdn_replay_decode followed by gdn_replay_advance
+ * (SGLang PR #28451, Design 3: the cursor advances once per forward, after
+ * every layer has read it). Outputs, checkpoint and ring writes are those of
+ * gdn_replay_decode; afterwards write_pos[s] holds what gdn_replay_advance
+ * with the same force_flush would have written. Rows that are padding or in
+ * error keep their cursor (and set the error bits as gdn_replay_decode does).
+ *   write_pos  (device) int32 [N], read and written.
+ *   arrive     (device) int32 [B * GDN_ARRIVE_STRIDE] workspace, owned by the
+ *              caller, 128-byte aligned: all zero before the call; the call
+ *              leaves it all zero. Row b's workgroups count themselves in
+ *              arrive[b * GDN_ARRIVE_STRIDE] after they have read the row's
+ *              cursor; the last one writes the advanced cursor. (One 128-byte
+ *              line per row: device-scope atomics on a shared line serialise.)
+ *              Two calls that share an arrive buffer must not overlap.
+ * Returns GDN_ERR_INVALID_ARG if arrive is NULL or misaligned, or if
+ * shape->window != 0. Every other argument as gdn_replay_decode.
+ */
+#define GDN_ARRIVE_STRIDE 32
+gdn_status gdn_replay_decode_advance(const gdn_shape *shape, const void *q, const void *k,
+                                     const void *v, const float *g, const float *beta,
+                                     const int32_t *slot_idx, void *ckpt, void *ring_d,
+                                     void *ring_k, float *ring_g, int32_t *write_pos,
+                                     const int32_t *force_flush, void *o, int32_t *arrive,
+                                     int32_t *err_flags, void *stream);
+
+/*
  * gdn_replay_advance -- the cursor advance that follows a forward's decode
  * calls (SGLang PR #28451, Design 3): for each row with slot s >= 0,
  *     write_pos[s] <- (write_pos[s] == L-1 || force_flush[b]) ? 0 : write_pos[s]+1.

@@ -23,6 +23,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gdn_replay.h")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
 GDN_GATE_HEAD, GDN_GATE_KEY = 0, 1
+ARRIVE_STRIDE = 32          # int32 per row in the arrive workspace (GDN_ARRIVE_STRIDE)
 EF_SLOT_RANGE, EF_CURSOR_RANGE, EF_WINDOW, EF_ACCEPTED = 1, 2, 4, 8
 
 _DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
@@ -51,11 +52,12 @@ _P = ctypes.c_void_p
 _S = ctypes.POINTER(gdn_shape)
 _lib.gdn_packed_decode.argtypes = [_S] + [_P] * 10
 _lib.gdn_replay_decode.argtypes = [_S] + [_P] * 15
+_lib.gdn_replay_decode_advance.argtypes = [_S] + [_P] * 16
 _lib.gdn_replay_advance.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_commit.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_fold.argtypes = [_S] + [_P] * 8
 _lib.gdn_replay_reset.argtypes = [_S] + [_P] * 4
-for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_advance",
+for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_decode_advance", "gdn_replay_advance",
            "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_reset"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -196,6 +198,40 @@ def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, 
                                   _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d), _ptr(ring_k),
                                   _ptr(ring_g), _ptr(write_pos), _ptr(force_flush), _ptr(o),
                                   _ptr(err_flags), _stream(stream)), "gdn_replay_decode")
+    return o
+
+
+def arrive_workspace(B: int, device) -> torch.Tensor:
+    """A zeroed arrive workspace for gdn_replay_decode_advance with B rows
+    (torch's allocations are 256-byte aligned)."""
+    return torch.zeros(B * ARRIVE_STRIDE, dtype=torch.int32, device=device)
+
+
+def gdn_replay_decode_advance(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g,
+                              write_pos, arrive, force_flush=None, o=None, err_flags=None,
+                              stream=None):
+    """A decode step with the cursor advance fused in (the forward's last
+    layer); see gdn_replay_decode_advance in gdn_replay.h. arrive: int32
+    [B * ARRIVE_STRIDE] workspace, all zero (the call leaves it zero); see
+    arrive_workspace(). Returns o [B,1,Hv,dv]."""
+    B, T, Hk, dk, Hv, dv, dev, gate = _io_shape(q, k, v, g, beta, slot_idx)
+    N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
+    _check(arrive, "arrive", torch.int32, 1, dev)
+    if arrive.shape != (B * ARRIVE_STRIDE,):
+        raise ValueError("arrive must be [B * ARRIVE_STRIDE]")
+    if force_flush is not None:
+        _check(force_flush, "force_flush", torch.int32, 1, dev)
+        if force_flush.shape != (B,):
+            raise ValueError("force_flush must be [B]")
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, None, dev)
+    o = _out(o, B, T, Hv, dv, q.dtype, dev)
+    sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], 0,
+                   _DT[ckpt.dtype], 0, gate)
+    _raise(_lib.gdn_replay_decode_advance(
+        ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
+        _ptr(ckpt), _ptr(ring_d), _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(force_flush),
+        _ptr(o), _ptr(arrive), _ptr(err_flags), _stream(stream)), "gdn_replay_decode_advance")
     return o
 
 

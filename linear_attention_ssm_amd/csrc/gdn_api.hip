@@ -13,6 +13,7 @@ using namespace gdn;
 namespace {
 
 constexpr int kAbiVersion = 5;
+static_assert(kArriveStride == GDN_ARRIVE_STRIDE, "arrival counter stride");
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -179,11 +180,17 @@ gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, c
                                   smem, static_cast<hipStream_t>(stream)));
 }
 
-gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
-                             const float* g, const float* beta, const int32_t* slot_idx,
-                             void* ckpt, void* ring_d, void* ring_k, float* ring_g,
-                             const int32_t* write_pos, const int32_t* force_flush, void* o,
-                             int32_t* err_flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_replay_decode and gdn_replay_decode_advance: arrive == nullptr is the
+// plain decode (write_pos only read); otherwise the cursor advance is fused.
+gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const int32_t* slot_idx,
+                         void* ckpt, void* ring_d, void* ring_k, float* ring_g,
+                         const int32_t* write_pos, const int32_t* force_flush, void* o,
+                         int32_t* arrive, int32_t* err_flags, void* stream) {
   const gdn_status st = check_shape(s, true);
   if (st != GDN_OK) return st;
   if (s->window != 0 && s->window != 1) return GDN_ERR_INVALID_ARG;
@@ -202,10 +209,13 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
       !aligned(slot_idx, 4) || (err_flags && !aligned(err_flags, 4)) ||
       (force_flush && !aligned(force_flush, 4)))
     return GDN_ERR_INVALID_ARG;
+  if (arrive && (s->window != 0 || !aligned(arrive, 128))) return GDN_ERR_INVALID_ARG;
   if (s->B == 0) return GDN_OK;
   DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.slot = slot_idx; a.state = ckpt;
   a.ring_d = ring_d; a.ring_k = ring_k; a.ring_g = ring_g; a.write_pos = write_pos;
+  a.arrive = arrive;
+  a.write_pos_w = const_cast<int32_t*>(write_pos);   // written only when arrive != null
   a.force_flush = force_flush; a.o = o; a.err = err_flags; a.window = s->window;
   a.step_round = s->step_rounding;
   // the kernel reads one flag per row unconditionally; without
@@ -217,6 +227,7 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
   if (static_cast<uint64_t>(s->B) * s->Hv * (s->dv / 16) >= (1ull << 31))
     return GDN_ERR_UNSUPPORTED;
   fill_replay_geometry(s, a, block, n_items);
+  a.wg_per_row = s->Hk * a.gsz;
   {
     // udiv() needs every numerator below 2^32 / divisor
     const uint64_t dmax = std::max({a.gsz, s->Hk, a.nvb, 16});
@@ -258,6 +269,30 @@ gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, c
   return from_hip(dispatch_replay(s->dk, a, s->qkv_dtype, s->ring_dtype, s->state_dtype, s->gate,
                                   dim3(n_items), block,
                                   smem, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_replay_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const int32_t* slot_idx,
+                             void* ckpt, void* ring_d, void* ring_k, float* ring_g,
+                             const int32_t* write_pos, const int32_t* force_flush, void* o,
+                             int32_t* err_flags, void* stream) {
+  return replay_decode(s, q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
+                       force_flush, o, nullptr, err_flags, stream);
+}
+
+gdn_status gdn_replay_decode_advance(const gdn_shape* s, const void* q, const void* k,
+                                     const void* v, const float* g, const float* beta,
+                                     const int32_t* slot_idx, void* ckpt, void* ring_d,
+                                     void* ring_k, float* ring_g, int32_t* write_pos,
+                                     const int32_t* force_flush, void* o, int32_t* arrive,
+                                     int32_t* err_flags, void* stream) {
+  if (!arrive) return GDN_ERR_INVALID_ARG;
+  return replay_decode(s, q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
+                       force_flush, o, arrive, err_flags, stream);
 }
 
 gdn_status gdn_replay_advance(const gdn_shape* s, const int32_t* slot_idx, int32_t* write_pos,

@@ -553,6 +553,9 @@ __device__ __forceinline__ void store_slab(void* slab, const f4 (&S)[DK / 16], i
 
 // ------------------------------------------------------------- kernel args
 
+// int32 elements between two rows' arrival counters (one 128-byte line each)
+constexpr int kArriveStride = 32;
+
 struct DecodeArgs {
   const void* q;
   const void* k;
@@ -593,6 +596,12 @@ struct DecodeArgs {
   // the weighted key rings of the heads (kw_head elements apart) and the
   // per-channel checkpoint decays A ([GH][dk] floats)
   int32_t kg_off, kw_off, acol_off, kw_head;
+  // cursor advance fused into a decode step (gdn_replay_decode_advance): the
+  // workgroups of a row count themselves in arrive[b] once every wavefront of
+  // theirs has read the cursor; the last one writes the advanced cursor
+  int32_t* arrive;         // [B][kArriveStride] int32, zero between calls; null: no advance
+  int32_t* write_pos_w;    // write_pos, writable (the same array)
+  int32_t wg_per_row;      // workgroups per row
 };
 
 struct CursorArgs {

@@ -635,6 +635,23 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   }
   __syncthreads();
 
+  // ---- fused cursor advance (decode steps only): past the barrier every
+  // wavefront of this workgroup has read the row's cursor, so the workgroup
+  // counts itself in; the row's last workgroup to arrive writes the advanced
+  // cursor (the rule of gdn_replay_advance) and clears the counter. Each
+  // row's counter has a 128-byte line of its own: device-scope atomics on one
+  // line serialise, and rows sharing a line made the launch ~20 us slower.
+  if constexpr (TT) {
+    if (a.arrive != nullptr && r.ok && tid == 0) {
+      int* cnt = a.arrive + static_cast<size_t>(g.b) * kArriveStride;
+      const int n = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (n == a.wg_per_row - 1) {
+        a.write_pos_w[r.s] = r.flush ? 0 : p + 1;
+        __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+
   // ---- reconstruction S = A S0 + sum_j w_j d_j k_j^T
   f4 S[NT];
   slab_decode<SD, DK>(S, R);

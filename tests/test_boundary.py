@@ -9,7 +9,8 @@ import linear_attention_ssm_amd as gdn
 from linear_attention_ssm_amd import gdn_shape
 
 EXPECTED = ["gdn_abi_version", "gdn_packed_decode", "gdn_replay_advance", "gdn_replay_commit",
-            "gdn_replay_decode", "gdn_replay_fold", "gdn_replay_reset", "gdn_status_string"]
+            "gdn_replay_decode", "gdn_replay_decode_advance", "gdn_replay_fold",
+            "gdn_replay_reset", "gdn_status_string"]
 
 # Fake, 256-byte aligned, non-null device addresses: never dereferenced, since
 # every call below must fail validation (or return early for B = 0) first.
@@ -95,6 +96,20 @@ def test_replay_decode_rejects_bad_pointers():
     p = list(FAKE[:8])
     p[3] = ctypes.c_void_p(FAKE[3].value + 4)
     assert packed(shape(gate=gdn.GDN_GATE_KEY), p) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_decode_advance_validates():
+    lib = gdn.lib()
+
+    def call(sh, arrive):
+        p = list(FAKE[:12])
+        return lib.gdn_replay_decode_advance(ctypes.byref(sh), *p[:11], None, p[11], arrive,
+                                             None, None)
+    assert call(shape(), None) == gdn.GDN_ERR_INVALID_ARG               # no workspace
+    assert call(shape(), ctypes.c_void_p(FAKE[14].value + 64)) == gdn.GDN_ERR_INVALID_ARG
+    assert call(shape(T=2, window=1), FAKE[14]) == gdn.GDN_ERR_INVALID_ARG   # windows: no
+    assert call(shape(dk=96), FAKE[14]) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(shape(B=0), FAKE[14]) == gdn.GDN_OK
 
 
 def test_empty_batch_is_a_no_op():

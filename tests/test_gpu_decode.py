@@ -185,3 +185,45 @@ def test_device_error_flags(gdn):
                          err_flags=pool.err)
     assert int(pool.err.item()) == gdn.EF_SLOT_RANGE
     assert pool.write_pos.cpu().tolist() == [0, 0, 0, 3]
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_decode_advance_equals_decode_then_advance(gdn, gate):
+    """gdn_replay_decode_advance (the cursor advance fused into the last
+    layer's decode) leaves outputs, checkpoints, rings and cursors bit for bit
+    as gdn_replay_decode followed by gdn_replay_advance, with forced flushes,
+    padding rows, a permuted pool and a row whose cursor is out of range; the
+    arrive workspace is back to zero after every call."""
+    w = gi.scaled(gi.C2, name=f"fused_adv_{gate}", B=16, N=20, L=4, steps=12, n_pad=2,
+                  permute=True, gate=gate, seed=61)
+    S0 = gi.initial_state(w)
+    slots = gi.slot_map(w)
+    a, b = Pool(w, S0), Pool(w, S0)
+    slot_t = to_dev(slots)
+    arrive = gdn.arrive_workspace(w.B, DEV)
+    live = slots[slots >= 0]
+    bad = int(live[3])
+    for t in range(w.steps):
+        if t == 5:                       # one slot's cursor out of range for one step
+            for p in (a, b):
+                p.write_pos[bad] = w.L
+        if t == 6:
+            for p in (a, b):
+                p.write_pos[bad] = 0
+        xi = dev_inputs(gi.step_inputs(w, t))
+        ff = to_dev(gi.force_flush_schedule(w, t, slots))
+        oa = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, a.ckpt, a.ring_d,
+                                   a.ring_k, a.ring_g, a.write_pos, force_flush=ff,
+                                   err_flags=a.err)
+        gdn.gdn_replay_advance(slot_t, a.write_pos, w.L, force_flush=ff, err_flags=a.err)
+        ob = gdn.gdn_replay_decode_advance(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, b.ckpt,
+                                           b.ring_d, b.ring_k, b.ring_g, b.write_pos, arrive,
+                                           force_flush=ff, err_flags=b.err)
+        assert torch.equal(bits(oa), bits(ob)), f"step {t}: outputs differ"
+        assert torch.equal(a.write_pos, b.write_pos), f"step {t}: cursors differ"
+        for x, y, name in zip((a.ckpt, a.ring_d, a.ring_k, a.ring_g),
+                              (b.ckpt, b.ring_d, b.ring_k, b.ring_g), ("ckpt", "d", "k", "g")):
+            assert torch.equal(bits(x), bits(y)), f"step {t}: {name} differs"
+        assert int(arrive.abs().sum().item()) == 0, f"step {t}: arrive not cleared"
+        assert int(a.err.item()) == int(b.err.item())
+    assert int(b.err.item()) == gdn.EF_CURSOR_RANGE

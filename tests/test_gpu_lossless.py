@@ -17,7 +17,7 @@ import torch
 
 import gdn_inputs as gi
 from gdn_harness import Pool, bits, dev_inputs, log, to_dev, to_f64, tol_o, tol_state
-from oracle import gdn_step, rel_err, window_ref
+from oracle import rel_err, step, window_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -32,11 +32,13 @@ def _tok(x, t):
     return x[:, t:t + 1].contiguous()
 
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "f16"])
-def test_lossless_rounds_bitwise_equal_packed(gdn, fmt):
+@pytest.mark.parametrize("fmt,gate", [("f32", "head"), ("bf16", "head"), ("f16", "head"),
+                                      ("f32", "key"), ("bf16", "key")])
+def test_lossless_rounds_bitwise_equal_packed(gdn, fmt, gate):
     """fp32 state, and 16-bit state pools with step_rounding (the window
-    rounds its state after each token, the fold after each entry)."""
-    w = dataclasses.replace(gi.C6, state=fmt) if fmt != "f32" else gi.C6
+    rounds its state after each token, the fold after each entry); per-head
+    and per-key (KDA) gates."""
+    w = dataclasses.replace(gi.C6, state=fmt, gate=gate)
     T, L = w.T, w.L
     stepr = fmt != "f32"
     sfmt = fmt if stepr else None
@@ -92,12 +94,12 @@ def test_lossless_rounds_bitwise_equal_packed(gdn, fmt):
             if s >= 0:
                 one = np.array([s], np.int32)
                 for t in range(int(acc[b])):
-                    gdn_step(S_true, one, *(a[b:b + 1, t] for a in x64), state_fmt=sfmt)
+                    step(S_true, one, *(a[b:b + 1, t] for a in x64), state_fmt=sfmt)
         worst_s = max(worst_s, rel_err(to_f64(pool.ckpt), S_true))
     assert int(err.item()) == 0
     assert worst_o <= tol_o(w), f"window outputs vs oracle: {worst_o:.3e}"
     assert worst_s <= (tol_state(w) if not stepr else 2e-2), f"state vs oracle: {worst_s:.3e}"
-    log(f"[{w.name}/{fmt}] {w.steps} rounds: state and {n_out} outputs bit-identical to packed "
+    log(f"[{w.name}/{fmt}/{gate}] {w.steps} rounds: state and {n_out} outputs bit-identical to packed "
         f"decode; vs oracle o {worst_o:.2e}, state {worst_s:.2e}")
 
 
