@@ -96,6 +96,8 @@ class Workload:
     state: str = "f32"  # storage dtype of the checkpoint / packed state
     gate: str = "head"  # "head": one log-decay per v-head (GDN); "key": one per
                         # v-head and key channel (KDA)
+    qk_raw: bool = False  # q, k as drawn (N(0,1)), for a decode that normalises
+                          # them itself
     seed: int = 0
 
     @property
@@ -220,9 +222,11 @@ def step_inputs(w: Workload, step: int, B: Optional[int] = None,
     B = w.B if B is None else B
     T = w.T if T is None else T
     r = _rng(w.seed, 2, step)
-    q = _unit_rows(r.standard_normal((B, T, w.Hk, w.dk), dtype=np.float32))
-    q = (q * np.float32(w.dk ** -0.5)).astype(np.float32)
-    k = _unit_rows(r.standard_normal((B, T, w.Hk, w.dk), dtype=np.float32))
+    q = r.standard_normal((B, T, w.Hk, w.dk), dtype=np.float32)
+    k = r.standard_normal((B, T, w.Hk, w.dk), dtype=np.float32)
+    if not w.qk_raw:
+        q = (_unit_rows(q) * np.float32(w.dk ** -0.5)).astype(np.float32)
+        k = _unit_rows(k)
     v = r.standard_normal((B, T, w.Hv, w.dv), dtype=np.float32)
     g = _logsigmoid(r.normal(2.0, 1.0, gate_shape(w, B, T))).astype(np.float32)
     beta = _sigmoid(r.standard_normal((B, T, w.Hv))).astype(np.float32)

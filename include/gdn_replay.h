@@ -90,6 +90,21 @@
  * Everything else (ring d and k, cursors, flush, windows, state formats,
  * step_rounding) is the same as with the per-head gate. Only gdn_packed_decode,
  * gdn_replay_decode and gdn_replay_fold read the field; the cursor calls ignore it.
+ *
+ * Strided inputs. The decode calls read q, k and v as rows of (b, t): element
+ * [b, t, h, i] of q (and k) is at q[(b*T + t) * qk_row_stride + h*dk + i], of v
+ * at v[(b*T + t) * v_row_stride + h*dv + i]. With the strides 0 the tensors are
+ * dense. Set both to 2*Hk*dk + Hv*dv, with k = q + Hk*dk and v = q + 2*Hk*dk,
+ * to read the packed mixed_qkv row [B, T, 2*Hk*dk + Hv*dv] that the serving
+ * stack hands to the decode (ReplaySSM blog, section 3.1). qk_row_stride must
+ * keep every q and k row 16-byte aligned. o, g and beta stay dense.
+ *
+ * Front end (qk_norm = 1). The pages hand the decode q and k already
+ * L2-normalised and q scaled (SGLang PR #28451, Modifications). With qk_norm
+ * the kernels do it themselves: q <- q / sqrt(sum q^2 + 1e-6) * dk^-1/2 and
+ * k <- k / sqrt(sum k^2 + 1e-6) per key head and token, in fp32, before the
+ * readout; the ring stores the normalised k. The packed and the replay decode
+ * normalise in the same order, so the L = 1 identity stays bitwise.
  */
 #ifndef GDN_REPLAY_H
 #define GDN_REPLAY_H
@@ -137,6 +152,11 @@ typedef struct {
     int32_t step_rounding; /* 1: round a 16-bit state after every step (verify
                               window and fold only; see below), else 0    */
     int32_t gate;       /* gdn_gate: GDN_GATE_HEAD (0) or GDN_GATE_KEY (1)       */
+    int32_t qk_row_stride; /* elements between the q (and k) of consecutive (b, t)
+                              rows; 0 = dense (Hk*dk). See "Strided inputs". */
+    int32_t v_row_stride;  /* the same for v; 0 = dense (Hv*dv)              */
+    int32_t qk_norm;    /* 1: L2-normalise q and k in the kernel and scale q by
+                           dk^-1/2 (see "Front end"); 0: take them as given */
 } gdn_shape;
 
 /*

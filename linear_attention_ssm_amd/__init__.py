@@ -33,7 +33,8 @@ STATE_DTYPES = (torch.float32, torch.bfloat16, torch.float16)
 class gdn_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "N", "Hv", "Hk", "dk", "dv", "L", "qkv_dtype", "ring_dtype", "window",
-                 "state_dtype", "step_rounding", "gate")]
+                 "state_dtype", "step_rounding", "gate", "qk_row_stride", "v_row_stride",
+                 "qk_norm")]
 
 
 class GdnError(RuntimeError):
@@ -63,7 +64,7 @@ for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_decode_advance"
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 5
+ABI_VERSION = 6
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -110,13 +111,48 @@ def _raise(status: int, what: str):
         raise GdnError(status, what)
 
 
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    """Elements between consecutive (b, t) rows of a [B, T, H, d] input whose
+    [H, d] part is dense: q, k and v may be views into one packed mixed_qkv
+    row (the C ABI's qk_row_stride / v_row_stride)."""
+    B, T, H, d = t.shape
+    s0, s1, s2, s3 = t.stride()
+    if s3 != 1 or s2 != d:
+        raise ValueError(f"{name}: each row's [heads, d] block must be dense, got strides "
+                         f"{t.stride()} for shape {tuple(t.shape)}")
+    if T > 1:
+        rs = s1
+        if B > 1 and s0 != T * s1:
+            raise ValueError(f"{name}: rows must be evenly spaced over (b, t)")
+    else:
+        rs = s0 if B > 1 else H * d
+    if rs < H * d:
+        raise ValueError(f"{name}: rows overlap (row stride {rs} < {H * d})")
+    return int(rs)
+
+
+def _check_rows(t, name, dtype, dev):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be a device tensor on {dev}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must have 4 dims, got {tuple(t.shape)}")
+
+
 def _io_shape(q, k, v, g, beta, slot_idx):
     """Sizes of a call; the gate is per head when g is [B,T,Hv] and per key
-    channel (KDA) when g is [B,T,Hv,dk]."""
-    _check(q, "q", (torch.float32, torch.bfloat16), 4)
+    channel (KDA) when g is [B,T,Hv,dk]. q, k, v may be strided views (rows of
+    [heads, d] dense), e.g. into a packed mixed_qkv tensor."""
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a torch.Tensor")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"q has dtype {q.dtype}")
     dev = q.device
-    _check(k, "k", q.dtype, 4, dev)
-    _check(v, "v", q.dtype, 4, dev)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check_rows(t, name, q.dtype, dev)
     _check(g, "g", torch.float32, None, dev)
     _check(beta, "beta", torch.float32, 3, dev)
     _check(slot_idx, "slot_idx", torch.int32, 1, dev)
@@ -127,7 +163,10 @@ def _io_shape(q, k, v, g, beta, slot_idx):
     if k.shape != q.shape or v.shape[:2] != (B, T) or tuple(g.shape) != g_shape \
             or beta.shape != (B, T, Hv) or slot_idx.shape != (B,):
         raise ValueError("inconsistent q/k/v/g/beta/slot_idx shapes")
-    return B, T, Hk, dk, Hv, dv, dev, gate
+    qs, ks, vs = _row_stride(q, "q"), _row_stride(k, "k"), _row_stride(v, "v")
+    if ks != qs:
+        raise ValueError("q and k must have the same row stride")
+    return B, T, Hk, dk, Hv, dv, dev, gate, qs, vs
 
 
 def _out(o, B, T, Hv, dv, dtype, dev):
@@ -141,20 +180,30 @@ def _out(o, B, T, Hv, dv, dtype, dev):
 
 # ------------------------------------------------------------------ entry points
 
-def gdn_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None, stream=None):
+def _shape(B, T, N, Hv, Hk, dk, dv, L, qkv, ring, window, state, stepr, gate, qs, vs, qk_norm):
+    """The gdn_shape of a decode call (dense strides passed as 0)."""
+    return gdn_shape(B, T, N, Hv, Hk, dk, dv, L, qkv, ring, int(bool(window)), state,
+                     int(bool(stepr)), gate, 0 if qs == Hk * dk else qs,
+                     0 if vs == Hv * dv else vs, int(bool(qk_norm)))
+
+
+def gdn_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None, stream=None,
+                      qk_norm=False):
     """Plain read-update-write decode step; see gdn_packed_decode in gdn_replay.h.
     q,k [B,1,Hk,dk]; v [B,1,Hv,dv]; g,beta [B,1,Hv] fp32 (g [B,1,Hv,dk] for the
     per-key gate); slot_idx [B] int32; state [N,Hv,dv,dk] fp32, bf16 or fp16
-    (updated in place). Returns o [B,1,Hv,dv]."""
-    B, T, Hk, dk, Hv, dv, dev, gate = _io_shape(q, k, v, g, beta, slot_idx)
+    (updated in place). q, k, v may be strided views (e.g. into a packed
+    mixed_qkv row); qk_norm L2-normalises q and k in the kernel and scales q.
+    Returns o [B,1,Hv,dv]."""
+    B, T, Hk, dk, Hv, dv, dev, gate, qs, vs = _io_shape(q, k, v, g, beta, slot_idx)
     _check(state, "state", STATE_DTYPES, 4, dev)
     if tuple(state.shape[1:]) != (Hv, dv, dk):
         raise ValueError("state must be [N, Hv, dv, dk]")
     if err_flags is not None:
         _check(err_flags, "err_flags", torch.int32, None, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
-    sh = gdn_shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0,
-                   _DT[state.dtype], 0, gate)
+    sh = _shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0,
+                _DT[state.dtype], 0, gate, qs, vs, qk_norm)
     _raise(_lib.gdn_packed_decode(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(slot_idx), _ptr(state), _ptr(o), _ptr(err_flags),
                                   _stream(stream)), "gdn_packed_decode")
@@ -179,11 +228,11 @@ def _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, ga
 
 def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
                       force_flush=None, o=None, err_flags=None, window=False, stream=None,
-                      step_rounding=False):
+                      step_rounding=False, qk_norm=False):
     """ReplaySSM decode step (window=False, T=1) or verify window (window=True);
     see gdn_replay_decode in gdn_replay.h. step_rounding (windows only) rounds
     a 16-bit state after every token. Returns o [B,T,Hv,dv]."""
-    B, T, Hk, dk, Hv, dv, dev, gate = _io_shape(q, k, v, g, beta, slot_idx)
+    B, T, Hk, dk, Hv, dv, dev, gate, qs, vs = _io_shape(q, k, v, g, beta, slot_idx)
     N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
     if force_flush is not None:
         _check(force_flush, "force_flush", torch.int32, 1, dev)
@@ -192,8 +241,8 @@ def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, 
     if err_flags is not None:
         _check(err_flags, "err_flags", torch.int32, None, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
-    sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)),
-                   _DT[ckpt.dtype], int(bool(step_rounding)), gate)
+    sh = _shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], window,
+                _DT[ckpt.dtype], step_rounding, gate, qs, vs, qk_norm)
     _raise(_lib.gdn_replay_decode(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d), _ptr(ring_k),
                                   _ptr(ring_g), _ptr(write_pos), _ptr(force_flush), _ptr(o),
@@ -209,12 +258,12 @@ def arrive_workspace(B: int, device) -> torch.Tensor:
 
 def gdn_replay_decode_advance(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g,
                               write_pos, arrive, force_flush=None, o=None, err_flags=None,
-                              stream=None):
+                              stream=None, qk_norm=False):
     """A decode step with the cursor advance fused in (the forward's last
     layer); see gdn_replay_decode_advance in gdn_replay.h. arrive: int32
     [B * ARRIVE_STRIDE] workspace, all zero (the call leaves it zero); see
     arrive_workspace(). Returns o [B,1,Hv,dv]."""
-    B, T, Hk, dk, Hv, dv, dev, gate = _io_shape(q, k, v, g, beta, slot_idx)
+    B, T, Hk, dk, Hv, dv, dev, gate, qs, vs = _io_shape(q, k, v, g, beta, slot_idx)
     N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
     _check(arrive, "arrive", torch.int32, 1, dev)
     if arrive.shape != (B * ARRIVE_STRIDE,):
@@ -226,8 +275,8 @@ def gdn_replay_decode_advance(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, 
     if err_flags is not None:
         _check(err_flags, "err_flags", torch.int32, None, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
-    sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], 0,
-                   _DT[ckpt.dtype], 0, gate)
+    sh = _shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], 0,
+                _DT[ckpt.dtype], 0, gate, qs, vs, qk_norm)
     _raise(_lib.gdn_replay_decode_advance(
         ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
         _ptr(ckpt), _ptr(ring_d), _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(force_flush),
@@ -308,16 +357,17 @@ class Prepared:
 
 
 def prepare_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
-                          force_flush=None, o=None, err_flags=None, window=False, stream=None):
+                          force_flush=None, o=None, err_flags=None, window=False, stream=None,
+                          qk_norm=False):
     """gdn_replay_decode with the same arguments, prepared for repeated calls.
     Returns (call, o)."""
-    B, T, Hk, dk, Hv, dv, dev, gate = _io_shape(q, k, v, g, beta, slot_idx)
+    B, T, Hk, dk, Hv, dv, dev, gate, qs, vs = _io_shape(q, k, v, g, beta, slot_idx)
     N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
     if force_flush is not None:
         _check(force_flush, "force_flush", torch.int32, 1, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
-    sh = gdn_shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], int(bool(window)),
-                   _DT[ckpt.dtype], 0, gate)
+    sh = _shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], window,
+                _DT[ckpt.dtype], 0, gate, qs, vs, qk_norm)
     args = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
             _ptr(ckpt), _ptr(ring_d), _ptr(ring_k), _ptr(ring_g), _ptr(write_pos),
             _ptr(force_flush), _ptr(o), _ptr(err_flags), _stream(stream))
@@ -327,13 +377,13 @@ def prepare_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring
 
 
 def prepare_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None,
-                          stream=None):
+                          stream=None, qk_norm=False):
     """gdn_packed_decode prepared for repeated calls. Returns (call, o)."""
-    B, T, Hk, dk, Hv, dv, dev, gate = _io_shape(q, k, v, g, beta, slot_idx)
+    B, T, Hk, dk, Hv, dv, dev, gate, qs, vs = _io_shape(q, k, v, g, beta, slot_idx)
     _check(state, "state", STATE_DTYPES, 4, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
-    sh = gdn_shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0,
-                   _DT[state.dtype], 0, gate)
+    sh = _shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0,
+                _DT[state.dtype], 0, gate, qs, vs, qk_norm)
     args = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
             _ptr(state), _ptr(o), _ptr(err_flags), _stream(stream))
     keep = (sh, q, k, v, g, beta, slot_idx, state, o, err_flags)

@@ -12,7 +12,7 @@ using namespace gdn;
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 static_assert(kArriveStride == GDN_ARRIVE_STRIDE, "arrival counter stride");
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -55,6 +55,17 @@ gdn_status check_shape(const gdn_shape* s, bool need_ring) {
   if (s->state_dtype != GDN_F32 && s->state_dtype != GDN_BF16 && s->state_dtype != GDN_F16)
     return GDN_ERR_UNSUPPORTED;
   if (s->gate != GDN_GATE_HEAD && s->gate != GDN_GATE_KEY) return GDN_ERR_INVALID_ARG;
+  if (s->qk_norm != 0 && s->qk_norm != 1) return GDN_ERR_INVALID_ARG;
+  {
+    // input row strides: 0 = dense; else at least the dense width, and q/k
+    // rows 16-byte aligned
+    const int64_t es = s->qkv_dtype == GDN_F32 ? 4 : 2;
+    if (s->qk_row_stride != 0 &&
+        (s->qk_row_stride < static_cast<int64_t>(s->Hk) * s->dk || (s->qk_row_stride * es) % 16 != 0))
+      return GDN_ERR_INVALID_ARG;
+    if (s->v_row_stride != 0 && s->v_row_stride < static_cast<int64_t>(s->Hv) * s->dv)
+      return GDN_ERR_INVALID_ARG;
+  }
   if (need_ring) {
     if (s->L < 1 || s->L > 64) return GDN_ERR_INVALID_ARG;
     if (s->ring_dtype != GDN_F32 && s->ring_dtype != GDN_F16 && s->ring_dtype != GDN_BF16)
@@ -64,6 +75,13 @@ gdn_status check_shape(const gdn_shape* s, bool need_ring) {
 }
 
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+// The input row strides and the front-end switch of a decode call.
+void fill_inputs(const gdn_shape* s, DecodeArgs& a) {
+  a.qk_rs = s->qk_row_stride ? s->qk_row_stride : s->Hk * s->dk;
+  a.v_rs = s->v_row_stride ? s->v_row_stride : s->Hv * s->dv;
+  a.qk_norm = s->qk_norm;
+}
 
 // ceil(2^32 / d) for the device's udiv (0 encodes d = 1).
 uint32_t recip(int d) {
@@ -167,6 +185,7 @@ gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, c
   DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.slot = slot_idx; a.state = state;
   a.o = o; a.err = err_flags;
+  fill_inputs(s, a);
   dim3 grid, block;
   fill_decode_geometry(s, a, grid, block);
   a.L = 1;
@@ -217,6 +236,7 @@ gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const
   a.arrive = arrive;
   a.write_pos_w = const_cast<int32_t*>(write_pos);   // written only when arrive != null
   a.force_flush = force_flush; a.o = o; a.err = err_flags; a.window = s->window;
+  fill_inputs(s, a);
   a.step_round = s->step_rounding;
   // the kernel reads one flag per row unconditionally; without
   // force_flush it reads the slot array and ignores the value

@@ -372,6 +372,33 @@ __device__ __forceinline__ float token_kq(f4 qv, f4 kv) {
   return group_sum<DK / 4>(x);
 }
 
+// In-kernel q/k normalisation (the decode's front end: q and k L2-normalised
+// per key head, q scaled by dk^-1/2; SGLang PR #28451, Modifications). Each of
+// the DK/4 staging threads of a token holds four elements of q and of k; the
+// group of DK/4 lanes sums the squares (one order, shared by every kernel).
+// x <- x / sqrt(sum x^2 + 1e-6); q is then multiplied by dk^-1/2.
+template <int DK>
+__device__ __forceinline__ void token_l2norm(f4& qv, f4& kv) {
+  float sq = qv.x * qv.x, sk = kv.x * kv.x;
+  sq = __builtin_fmaf(qv.y, qv.y, sq);
+  sk = __builtin_fmaf(kv.y, kv.y, sk);
+  sq = __builtin_fmaf(qv.z, qv.z, sq);
+  sk = __builtin_fmaf(kv.z, kv.z, sk);
+  sq = __builtin_fmaf(qv.w, qv.w, sq);
+  sk = __builtin_fmaf(kv.w, kv.w, sk);
+  sq = group_sum<DK / 4>(sq);
+  sk = group_sum<DK / 4>(sk);
+  constexpr float kScale = DK == 32 ? 0.17677669529663688f : DK == 64 ? 0.125f
+                         : DK == 128 ? 0.08838834764831845f : 0.0625f;   // dk^-1/2
+  const float rq = kScale / __builtin_sqrtf(sq + 1e-6f);
+  const float rk = 1.f / __builtin_sqrtf(sk + 1e-6f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    qv[i] = qv[i] * rq;
+    kv[i] = kv[i] * rk;
+  }
+}
+
 // alpha = exp(g) of one step, evaluated in double and rounded once to fp32.
 // Every kernel that applies a step's decay to a state (packed decode, the
 // replay readout and flush, the verify window, the fold) uses this one value,
@@ -602,6 +629,11 @@ struct DecodeArgs {
   int32_t* arrive;         // [B][kArriveStride] int32, zero between calls; null: no advance
   int32_t* write_pos_w;    // write_pos, writable (the same array)
   int32_t wg_per_row;      // workgroups per row
+  // input rows: elements between the q (and k) of consecutive (row, token)
+  // pairs, and between their v (Hk*dk and Hv*dv for dense tensors; the width
+  // of the packed mixed_qkv row when q, k, v are views into it)
+  int32_t qk_rs, v_rs;
+  int32_t qk_norm;         // 1: L2-normalise q and k in the kernel, scale q
 };
 
 struct CursorArgs {

@@ -27,22 +27,6 @@ __device__ __forceinline__ void zero_rows(const DecodeArgs& a, int b, int h, int
   }
 }
 
-// Stage the row's q and k for all T tokens into LDS as fp32:
-// lds[tau][0][:] = q, lds[tau][1][:] = k.
-template <int DK, int QKV>
-__device__ __forceinline__ void stage_qk(const DecodeArgs& a, float* lds, int b, int hk) {
-  constexpr int C4 = DK / 4;
-  const int total = a.T * C4;
-  for (int c = threadIdx.x; c < total; c += blockDim.x) {
-    const int tau = c / C4, e4 = (c % C4) * 4;
-    const size_t src = ((static_cast<size_t>(b) * a.T + tau) * a.Hk + hk) * DK + e4;
-    const f4 qv = load4<QKV>(a.q, src);
-    const f4 kv = load4<QKV>(a.k, src);
-    *reinterpret_cast<f4*>(lds + (tau * 2 + 0) * DK + e4) = qv;
-    *reinterpret_cast<f4*>(lds + (tau * 2 + 1) * DK + e4) = kv;
-  }
-}
-
 // ============================================================= packed decode
 //
 // The plain read-update-write step (SGLang PR #28451: the packed decode that
@@ -79,11 +63,11 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   constexpr int C4 = DK / 4;
   const int tid = threadIdx.x;
   const int cq = tid < C4 ? tid : C4 - 1;
-  const size_t qsrc = (static_cast<size_t>(b) * a.Hk + hk) * DK + cq * 4;
+  const size_t qsrc = static_cast<size_t>(b) * a.qk_rs + hk * DK + cq * 4;
   const auto q_raw = load4_raw<QKV>(a.q, qsrc);
   const auto k_raw = load4_raw<QKV>(a.k, qsrc);
   const size_t ih = static_cast<size_t>(b) * a.Hv + h;
-  const auto v_raw = load1_raw<QKV>(a.v, ih * a.dv + vcol);
+  const auto v_raw = load1_raw<QKV>(a.v, static_cast<size_t>(b) * a.v_rs + h * a.dv + vcol);
   const float gv = KG ? 0.f : ld_uniform(a.g, ih), bt = ld_uniform(a.beta, ih);
 
   using SE = typename Elem<SD>::T;
@@ -95,7 +79,8 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
     // unconditional writes (surplus threads into the dump area) keep the
     // early q/k loads ahead of the state loads
     float* dump = reinterpret_cast<float*>(smem + a.dump_off);
-    const f4 qv = decode4<QKV>(q_raw), kv = decode4<QKV>(k_raw);
+    f4 qv = decode4<QKV>(q_raw), kv = decode4<QKV>(k_raw);
+    if (a.qk_norm && wave == 0) token_l2norm<DK>(qv, kv);
     float* qdst = tid < C4 ? qk + 4 * tid : dump + lane * 8;
     float* kdst = tid < C4 ? qk + DK + 4 * tid : dump + lane * 8 + 4;
     *reinterpret_cast<f4*>(qdst) = qv;
@@ -106,18 +91,19 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
     }
   }
   float* kgl = reinterpret_cast<float*>(smem + a.kg_off);   // KG: [G][4][DK]
-  if constexpr (KG) {
-    // the per-key gates of the workgroup's G heads (while the state is in flight)
-    for (int i = tid; i < a.G * C4; i += blockDim.x) {
-      const int hh = i / C4, c4 = i - hh * C4;
-      const size_t qi = (static_cast<size_t>(b) * a.Hk + hk) * DK + 4 * c4;
-      const f4 g4 = *reinterpret_cast<const f4*>(
-          a.g + (static_cast<size_t>(b) * a.Hv + hk * a.G + hh) * DK + 4 * c4);
-      stage_key_gate(kgl + hh * 4 * DK, DK, c4, g4, load4<QKV>(a.q, qi), load4<QKV>(a.k, qi));
-    }
-  }
   const float alpha = decay_of(gv);   // while the state is in flight
   __syncthreads();
+  if constexpr (KG) {
+    // the per-key gates of the workgroup's G heads, from the staged q and k
+    for (int i = tid; i < a.G * C4; i += blockDim.x) {
+      const int hh = i / C4, c4 = i - hh * C4;
+      const f4 g4 = *reinterpret_cast<const f4*>(
+          a.g + (static_cast<size_t>(b) * a.Hv + hk * a.G + hh) * DK + 4 * c4);
+      stage_key_gate(kgl + hh * 4 * DK, DK, c4, g4, *reinterpret_cast<const f4*>(qk + 4 * c4),
+                     *reinterpret_cast<const f4*>(qk + DK + 4 * c4));
+    }
+    __syncthreads();
+  }
   const float vv = to_f32<QKV>(v_raw);
 
   f4 S[NT];
@@ -278,7 +264,7 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
   if (64 * wave < nqk) {
     const int cq = tid < nqk ? tid : nqk - 1;
     const int tq = TT ? 0 : cq / C4;
-    const size_t qsrc = ((static_cast<size_t>(g.b) * T + tq) * a.Hk + g.hk) * DK + (cq - tq * C4) * 4;
+    const size_t qsrc = (static_cast<size_t>(g.b) * T + tq) * a.qk_rs + g.hk * DK + (cq - tq * C4) * 4;
     f.q_raw = load4_raw<QKV>(a.q, qsrc);
     f.k_raw = load4_raw<QKV>(a.k, qsrc);
   }
@@ -318,7 +304,7 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.d_raw[i] = __builtin_amdgcn_raw_buffer_load_b16(rd, off, 2 * i * a.dv, 0);
   }
-  f.v_raw = load1_raw<QKV>(a.v, (static_cast<size_t>(g.b) * T * a.Hv + g.h) * a.dv + g.vcol);
+  f.v_raw = load1_raw<QKV>(a.v, static_cast<size_t>(g.b) * T * a.v_rs + g.h * a.dv + g.vcol);
 }
 
 // Request an item's 16-row checkpoint slab: 16-byte loads in the lane order
@@ -493,7 +479,8 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   // ---- LDS staging. Every thread writes (threads past the last piece into a
   // per-lane dump area) so the early loads have unconditional uses.
   if (64 * wave < nqk) {                         // waves holding staging threads
-    const f4 qv = decode4<QKV>(f.q_raw), kv = decode4<QKV>(f.k_raw);
+    f4 qv = decode4<QKV>(f.q_raw), kv = decode4<QKV>(f.k_raw);
+    if (a.qk_norm) token_l2norm<DK>(qv, kv);
     const int tq = TT ? 0 : tid / C4;
     float* qdst = tid < nqk ? qk + tq * 2 * DK + (tid - tq * C4) * 4 : dump + lane * 8;
     float* kdst = tid < nqk ? qdst + DK : dump + lane * 8 + 4;
@@ -504,8 +491,9 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   }
   for (int c = tid + nthr; c < nqk; c += nthr) {        // long windows only
     const int tau = c / C4, e4 = (c % C4) * 4;
-    const size_t src = ((static_cast<size_t>(g.b) * T + tau) * a.Hk + g.hk) * DK + e4;
-    const f4 qv = load4<QKV>(a.q, src), kv = load4<QKV>(a.k, src);
+    const size_t src = (static_cast<size_t>(g.b) * T + tau) * a.qk_rs + g.hk * DK + e4;
+    f4 qv = load4<QKV>(a.q, src), kv = load4<QKV>(a.k, src);
+    if (a.qk_norm) token_l2norm<DK>(qv, kv);
     *reinterpret_cast<f4*>(qk + (tau * 2 + 0) * DK + e4) = qv;
     *reinterpret_cast<f4*>(qk + (tau * 2 + 1) * DK + e4) = kv;
     const float kq0 = token_kq<DK>(qv, kv);   // groups of C4 lanes stay aligned
@@ -522,17 +510,18 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   }
   float* kgl = reinterpret_cast<float*>(buf + a.kg_off);       // KG: [GH][T][4][DK]
   if constexpr (KG) {
+    weight_keys<DK, RING>(a, g, r, lp, buf, tid, nthr);
+    __syncthreads();                               // q and k staged (and normalised)
     // per-key gates of the workgroup's heads for every token
     for (int i = tid; i < a.GH * nqk; i += nthr) {
       const int hh = i / nqk, c = i - hh * nqk;
       const int tau = TT ? 0 : c / C4, c4 = c - tau * C4;
-      const size_t qi = ((static_cast<size_t>(g.b) * T + tau) * a.Hk + g.hk) * DK + 4 * c4;
       const size_t gi = ((static_cast<size_t>(g.b) * T + tau) * a.Hv + g.hk * a.G + g.hc * a.GH + hh) * DK;
       const f4 g4 = *reinterpret_cast<const f4*>(a.g + gi + 4 * c4);
-      stage_key_gate(kgl + (hh * T + tau) * 4 * DK, DK, c4, g4, load4<QKV>(a.q, qi),
-                     load4<QKV>(a.k, qi));
+      stage_key_gate(kgl + (hh * T + tau) * 4 * DK, DK, c4, g4,
+                     *reinterpret_cast<const f4*>(qk + tau * 2 * DK + 4 * c4),
+                     *reinterpret_cast<const f4*>(qk + tau * 2 * DK + DK + 4 * c4));
     }
-    weight_keys<DK, RING>(a, g, r, lp, buf, tid, nthr);
   }
   // the key ring, entries p..lp-1 as zeros (the bounded loads read them so)
   const char* kbase = static_cast<const char*>(a.ring_k) +
@@ -724,7 +713,9 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
     const float* kl = ql + DK;
     const size_t ih = (static_cast<size_t>(g.b) * T + tau) * a.Hv + g.h;
     // the next window token's v is requested before this token's readout
-    const float v_next = (!TT && tau + 1 < T) ? load1<QKV>(a.v, (ih + a.Hv) * a.dv + g.vcol) : 0.f;
+    const float v_next = (!TT && tau + 1 < T)
+        ? load1<QKV>(a.v, (static_cast<size_t>(g.b) * T + tau + 1) * a.v_rs + g.h * a.dv + g.vcol)
+        : 0.f;
     const float* gt = gates + 3 * (wh * T + tau);
     const float alpha = gt[0], bt = gt[1], gv = gt[2];
     const float kq = kq_l[tau];

@@ -15,6 +15,7 @@ Parts:
                         bfloat16), for the 16-bit checkpoint variant
   O6  kda_step          the per-key-gate (KDA) recurrence in fp64 (C)
   O7  fold_kda_f32      the pinned-rounding fold with a per-key gate (C)
+  O8  l2norm_qk         the decode's front end: q/k L2-normalised, q scaled
   O2, O4 take the per-key gate as well (ReplayModel(gate="key"), window_ref
   with g [B, T, Hv, dk]).
 
@@ -184,6 +185,24 @@ def step(S: np.ndarray, slot: np.ndarray, q, k, v, g, beta, want_u: bool = False
     (per key channel)."""
     f = kda_step if np.ndim(g) == 3 else gdn_step
     return f(S, slot, q, k, v, g, beta, want_u=want_u, state_fmt=state_fmt)
+
+
+# ------------------------------------------------------------------ O8
+
+QK_NORM_EPS = 1e-6
+
+
+def l2norm_qk(q, k):
+    """O8: the front end the pages put before the decode (SGLang PR #28451,
+    Modifications: q arrives L2-normalised and scaled): over the last axis
+    (dk), q <- q / sqrt(sum q^2 + eps) * dk^-1/2 and k <- k / sqrt(sum k^2 +
+    eps), eps = 1e-6, in fp64. Returns (q, k)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    dk = q.shape[-1]
+    nq = np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + QK_NORM_EPS)
+    nk = np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + QK_NORM_EPS)
+    return q / nq * dk ** -0.5, k / nk
 
 
 # ------------------------------------------------------------------ O3

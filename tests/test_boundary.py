@@ -29,7 +29,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 5
+    assert lib.gdn_abi_version() == 6
     for st in range(4):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -60,6 +60,10 @@ def packed(sh, ptrs=None):
     (dict(T=2, window=1, step_rounding=2), gdn.GDN_ERR_INVALID_ARG),
     (dict(state_dtype=-1), gdn.GDN_ERR_UNSUPPORTED),
     (dict(gate=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(qk_norm=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(qk_row_stride=100), gdn.GDN_ERR_INVALID_ARG),     # < Hk * dk: rows overlap
+    (dict(qk_row_stride=260), gdn.GDN_ERR_INVALID_ARG),     # rows not 16-byte aligned
+    (dict(v_row_stride=200), gdn.GDN_ERR_INVALID_ARG),      # < Hv * dv
     (dict(gate=-1), gdn.GDN_ERR_INVALID_ARG),
     # per-key gate, 16-token windows at dk = 256: the staged gates exceed LDS
     (dict(gate=1, T=16, window=1, dk=256, L=64), gdn.GDN_ERR_UNSUPPORTED),
