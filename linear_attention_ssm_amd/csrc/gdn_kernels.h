@@ -91,19 +91,29 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
     }
   }
   float* kgl = reinterpret_cast<float*>(smem + a.kg_off);   // KG: [G][4][DK]
-  const float alpha = decay_of(gv);   // while the state is in flight
-  __syncthreads();
   if constexpr (KG) {
-    // the per-key gates of the workgroup's G heads, from the staged q and k
+    // the per-key gates of the workgroup's G heads (while the state is in
+    // flight), from q and k as given, or (normalised in the kernel) from
+    // their staged copies
+    if (a.qk_norm) __syncthreads();
     for (int i = tid; i < a.G * C4; i += blockDim.x) {
       const int hh = i / C4, c4 = i - hh * C4;
       const f4 g4 = *reinterpret_cast<const f4*>(
           a.g + (static_cast<size_t>(b) * a.Hv + hk * a.G + hh) * DK + 4 * c4);
-      stage_key_gate(kgl + hh * 4 * DK, DK, c4, g4, *reinterpret_cast<const f4*>(qk + 4 * c4),
-                     *reinterpret_cast<const f4*>(qk + DK + 4 * c4));
+      f4 qv, kv;
+      if (a.qk_norm) {
+        qv = *reinterpret_cast<const f4*>(qk + 4 * c4);
+        kv = *reinterpret_cast<const f4*>(qk + DK + 4 * c4);
+      } else {
+        const size_t qi = static_cast<size_t>(b) * a.qk_rs + hk * DK + 4 * c4;
+        qv = load4<QKV>(a.q, qi);
+        kv = load4<QKV>(a.k, qi);
+      }
+      stage_key_gate(kgl + hh * 4 * DK, DK, c4, g4, qv, kv);
     }
-    __syncthreads();
   }
+  const float alpha = decay_of(gv);   // while the state is in flight
+  __syncthreads();
   const float vv = to_f32<QKV>(v_raw);
 
   f4 S[NT];
@@ -453,7 +463,7 @@ __device__ __forceinline__ void weight_keys(const DecodeArgs& a, const ItemGeo& 
   }
 }
 
-template <int DK, int QKV, int RING, int SD, int TT, int KG>
+template <int DK, int QKV, int RING, int SD, int TT, int KG, int NRM>
 __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, const RowState& r,
                                         int T, const Small<DK, QKV, RING>& f,
                                         const SlabRaw<SD, DK>& R, unsigned char* buf, float* dump,
@@ -480,7 +490,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   // per-lane dump area) so the early loads have unconditional uses.
   if (64 * wave < nqk) {                         // waves holding staging threads
     f4 qv = decode4<QKV>(f.q_raw), kv = decode4<QKV>(f.k_raw);
-    if (a.qk_norm) token_l2norm<DK>(qv, kv);
+    if constexpr (NRM) token_l2norm<DK>(qv, kv);
     const int tq = TT ? 0 : tid / C4;
     float* qdst = tid < nqk ? qk + tq * 2 * DK + (tid - tq * C4) * 4 : dump + lane * 8;
     float* kdst = tid < nqk ? qdst + DK : dump + lane * 8 + 4;
@@ -493,7 +503,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
     const int tau = c / C4, e4 = (c % C4) * 4;
     const size_t src = (static_cast<size_t>(g.b) * T + tau) * a.qk_rs + g.hk * DK + e4;
     f4 qv = load4<QKV>(a.q, src), kv = load4<QKV>(a.k, src);
-    if (a.qk_norm) token_l2norm<DK>(qv, kv);
+    if constexpr (NRM) token_l2norm<DK>(qv, kv);
     *reinterpret_cast<f4*>(qk + (tau * 2 + 0) * DK + e4) = qv;
     *reinterpret_cast<f4*>(qk + (tau * 2 + 1) * DK + e4) = kv;
     const float kq0 = token_kq<DK>(qv, kv);   // groups of C4 lanes stay aligned
@@ -511,16 +521,24 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   float* kgl = reinterpret_cast<float*>(buf + a.kg_off);       // KG: [GH][T][4][DK]
   if constexpr (KG) {
     weight_keys<DK, RING>(a, g, r, lp, buf, tid, nthr);
-    __syncthreads();                               // q and k staged (and normalised)
-    // per-key gates of the workgroup's heads for every token
+    // per-key gates of the workgroup's heads for every token, from q and k as
+    // given, or (normalised in the kernel) from their staged copies
+    if constexpr (NRM) __syncthreads();
     for (int i = tid; i < a.GH * nqk; i += nthr) {
       const int hh = i / nqk, c = i - hh * nqk;
       const int tau = TT ? 0 : c / C4, c4 = c - tau * C4;
       const size_t gi = ((static_cast<size_t>(g.b) * T + tau) * a.Hv + g.hk * a.G + g.hc * a.GH + hh) * DK;
       const f4 g4 = *reinterpret_cast<const f4*>(a.g + gi + 4 * c4);
-      stage_key_gate(kgl + (hh * T + tau) * 4 * DK, DK, c4, g4,
-                     *reinterpret_cast<const f4*>(qk + tau * 2 * DK + 4 * c4),
-                     *reinterpret_cast<const f4*>(qk + tau * 2 * DK + DK + 4 * c4));
+      f4 qv, kv;
+      if constexpr (NRM) {
+        qv = *reinterpret_cast<const f4*>(qk + tau * 2 * DK + 4 * c4);
+        kv = *reinterpret_cast<const f4*>(qk + tau * 2 * DK + DK + 4 * c4);
+      } else {
+        const size_t qi = (static_cast<size_t>(g.b) * T + tau) * a.qk_rs + g.hk * DK + 4 * c4;
+        qv = load4<QKV>(a.q, qi);
+        kv = load4<QKV>(a.k, qi);
+      }
+      stage_key_gate(kgl + (hh * T + tau) * 4 * DK, DK, c4, g4, qv, kv);
     }
   }
   // the key ring, entries p..lp-1 as zeros (the bounded loads read them so)
@@ -755,7 +773,8 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   }
 }
 
-template <int DK, int QKV, int RING, int SD, int TT, int KG>
+// NRM = 1: q and k are L2-normalised (q scaled) in the kernel (a.qk_norm).
+template <int DK, int QKV, int RING, int SD, int TT, int KG, int NRM>
 __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* dump = reinterpret_cast<float*>(smem + a.dump_off);    // [64][8] write sink
@@ -771,7 +790,7 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   fetch_small<DK, QKV, RING, TT, KG>(sm, a, g, r, T, tid, lane, grp, wave);
   __builtin_amdgcn_sched_barrier(0);
   fetch_slab<SD, DK>(R, a, g, r, col, grp);
-  process<DK, QKV, RING, SD, TT, KG>(a, g, r, T, sm, R, smem, dump, tid, lane, grp, col, wave);
+  process<DK, QKV, RING, SD, TT, KG, NRM>(a, g, r, T, sm, R, smem, dump, tid, lane, grp, col, wave);
 }
 
 // ============================================================= fold
