@@ -3,11 +3,10 @@
  * decode library (libgdn_replay.so).
  *
  * The method: a slot's recurrent state is kept as one checkpoint (fp32, or a
- * 16-bit format) plus a ring of the last L steps' (d, k, g) entries. A decode
- * step rebuilds the pre-token state from them, reads the output out of it,
- * appends its own entry to the ring, and writes the full state back only on a
- * flush
- * (ReplaySSM blog, llm.rainlin.net, sections 2-3; SGLang PR #28451,
+ * 16-bit format) plus a ring holding the (d, k, g) entries of its L most
+ * recent steps. A decode step rebuilds the pre-token state from them, reads
+ * the output out of it, appends its own entry to the ring, and writes the
+ * full state back only on a flush (ReplaySSM blog, llm.rainlin.net, sections 2-3; SGLang PR #28451,
  * Modifications and Design 1-5).
  *
  * Conventions for every entry point
@@ -54,7 +53,7 @@
  * state_dtype in {GDN_F32, GDN_BF16, GDN_F16}.
  *
  * 16-bit state (state_dtype GDN_BF16 or GDN_F16). vLLM PR #49887 (Out of
- * scope) notes that the decode code handles fp16 and bf16 state; its review
+ * scope) notes that fp16 and bf16 states are supported by its decode code; its review
  * thread contrasts a decode that stores the state in 16 bits after every
  * token with ReplaySSM, which keeps the state in fp32 between checkpoint
  * writes and rounds only when the buffer is full. The library follows that
@@ -272,8 +271,9 @@ gdn_status gdn_replay_commit(const gdn_shape *shape, const int32_t *slot_idx,
 /*
  * gdn_replay_fold -- fold each listed slot's p = write_pos[s] valid ring
  * entries of one layer into that layer's checkpoint (SGLang PR #36821,
- * Technical principle: the accepted prefix is folded into the persistent
- * checkpoint by a bit-clone of the recurrence). Per element, for j = 0..p-1:
+ * Technical principle: at commit the kept entries are applied to the
+ * checkpoint in place, replaying the recurrence with its exact operation
+ * order). Per element, for j = 0..p-1:
  *     a = RN_f32(exp_f64(g_j));  x <- fma(d_j[v], k_j[c], RN(a*x))
  * with the two-instruction rounding of SGLang PR #42388 ("The idea"). The
  * result is bit-identical to that sequential recurrence on the stored entries.

@@ -101,9 +101,10 @@ void oracle_gdn_step_f64(int32_t B, int32_t N, int32_t Hv, int32_t Hk,
  * This is the recurrence S <- alpha*S + d k^T driven by the stored entries, in
  * the two-instruction form SGLang PR #42388 ("The idea") prescribes for an exact
  * replay: the decayed state is rounded on its own and the update is a single
- * FMA. The fold is the checkpoint update of the SGLang PR #36821 commit ("the
- * accepted prefix is folded back into the persistent checkpoint"), here for the
- * GDN (d, k, g) ring. The ring values are taken as their exact fp32 upcasts.
+ * FMA. It is the checkpoint update SGLang PR #36821 (Technical principle)
+ * performs at commit, where the kept entries are applied to the checkpoint in
+ * place, here for the GDN (d, k, g) ring. The ring values are taken as their
+ * exact fp32 upcasts.
  *
  * order = 0 is the pinned form above. order = 1 is a deliberately different
  * association, x = fma_f32(a, x, RN_f32(d*k)), kept only so that a test can

@@ -67,7 +67,7 @@ def test_ragged_shapes(gdn, ring, dims):
 
 
 def test_L1_replay_equals_packed_bitwise(gdn):
-    """At L = 1 the ring is always empty and every step flushes, so the replay
+    """At L = 1 no entry is ever kept (each step flushes), so the replay
     decode must reproduce the packed decode bit for bit (SGLang PR #28451,
     Design 1: the L = 1 kernel reduces to the packed decode)."""
     w = dataclasses.replace(gi.c4(1), steps=6, n_pad=2, permute=True, N=80)

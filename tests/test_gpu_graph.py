@@ -27,9 +27,12 @@ def _state(p):
     return [bits(t).clone() for t in (p.ckpt, p.ring_d, p.ring_k, p.ring_g)] + [p.write_pos.clone()]
 
 
-def test_graph_replays_match_eager(gdn):
+@pytest.mark.parametrize("fused,gate", [(False, "head"), (True, "head"), (True, "key")])
+def test_graph_replays_match_eager(gdn, fused, gate):
+    """fused: the second layer's call is gdn_replay_decode_advance (its
+    arrival counters must come back to zero after every replay)."""
     w = gi.scaled(gi.C2, name="graph", B=8, N=12, L=4, steps=1, stagger=False, permute=True,
-                  n_pad=1, seed=71)
+                  n_pad=1, gate=gate, seed=71)
     S0 = gi.initial_state(w)
     slots = to_dev(gi.slot_map(w))
     eager = [Pool(w, S0), Pool(w, S0)]           # two layers sharing one cursor array
@@ -40,21 +43,29 @@ def test_graph_replays_match_eager(gdn):
     o_e = torch.empty((w.B, 1, w.Hv, w.dv), dtype=torch.bfloat16, device=DEV)
     o_g = torch.empty_like(o_e)
 
-    def forward(pools, wp, o):
-        for p in pools:
-            gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slots, p.ckpt, p.ring_d,
-                                  p.ring_k, p.ring_g, wp, o=o)
-        gdn.gdn_replay_advance(slots, wp, w.L)
+    arrive_e = gdn.arrive_workspace(w.B, DEV)
+    arrive_g = gdn.arrive_workspace(w.B, DEV)
+
+    def forward(pools, wp, o, arrive):
+        for i, p in enumerate(pools):
+            if fused and i == len(pools) - 1:
+                gdn.gdn_replay_decode_advance(xi.q, xi.k, xi.v, xi.g, xi.beta, slots, p.ckpt,
+                                              p.ring_d, p.ring_k, p.ring_g, wp, arrive, o=o)
+            else:
+                gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slots, p.ckpt, p.ring_d,
+                                      p.ring_k, p.ring_g, wp, o=o)
+        if not fused:
+            gdn.gdn_replay_advance(slots, wp, w.L)
 
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=s):
-        forward(graphd, wp_g, o_g)
+        forward(graphd, wp_g, o_g, arrive_g)
     torch.cuda.synchronize()
     for step in range(6):                          # crosses a natural flush (L = 4)
-        forward(eager, wp_e, o_e)
+        forward(eager, wp_e, o_e, arrive_e)
         g.replay()
         torch.cuda.synchronize()
         _ = (o_e.float() * 2).sum().item()         # unrelated eager work between replays
@@ -62,6 +73,7 @@ def test_graph_replays_match_eager(gdn):
         for a, b in zip(_state(eager[0]) + _state(eager[1]), _state(graphd[0]) + _state(graphd[1])):
             assert torch.equal(a, b), f"replay {step}: state differs"
         assert torch.equal(wp_e, wp_g)
+        assert int(arrive_g.abs().sum().item()) == 0 and int(arrive_e.abs().sum().item()) == 0
     assert int(wp_e.max().item()) < w.L
 
 

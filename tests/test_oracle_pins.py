@@ -146,7 +146,7 @@ def test_flush_period_and_forced_flush():
         p = nxt
     assert seq == [(0, False), (1, True), (0, False), (1, False), (2, False),
                    (3, True), (0, False), (1, False)]
-    # L = 1: the ring is always empty and every step flushes
+    # L = 1: no entry is ever kept, each step flushes
     p = 0
     for _ in range(5):
         f, p = next_cursor(p, 1, False)
