@@ -179,3 +179,47 @@ def test_fold_bitwise_against_oracle(gdn, ring):
     assert int(err.item()) == 0
     log(f"[fold/{ring}] bit-exact over {got.size} elements, "
         f"{int(wp[live].sum())} entries folded")
+
+
+@pytest.mark.parametrize("T", [2, 4, 6, 8])
+def test_window_length_sweep_verify_commit_verify(gdn, T):
+    """Windows of T in {2, 4, 6, 8} tokens (vLLM PR #49887, Tests) at B = 16:
+    a single-token history, a verify window, a commit of a ~ U{0..T}, then a
+    second window that reads the committed entries; both windows against the
+    oracle, the cursors exact."""
+    w = gi.scaled(gi.C5, name=f"win_T{T}", B=16, N=16, T=T, steps=2, seed=640 + T)
+    L = w.L
+    S0 = gi.initial_state(w)
+    slots = gi.slot_map(w)
+    slot_t = to_dev(slots)
+    pool = Pool(w, S0, garbage=True)
+    S_true = S0.astype(np.float64)
+    # history: h_s single-token steps, never reaching a flush, p + 2T <= L after it
+    hist = np.random.default_rng(w.seed).integers(0, L - 2 * T + 1, size=w.N)
+    for i in range(int(hist.max())):
+        sl = np.array([s if hist[s] > i else -1 for s in slots], np.int32)
+        x = gi.step_inputs(w, 100 + i, T=1)
+        xi = dev_inputs(x)
+        gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, to_dev(sl), pool.ckpt,
+                              pool.ring_d, pool.ring_k, pool.ring_g, pool.write_pos,
+                              err_flags=pool.err)
+        gdn.gdn_replay_advance(to_dev(sl), pool.write_pos, L, err_flags=pool.err)
+        q, k, v, g, beta = (a[:, 0] for a in x.f64())
+        gdn_step(S_true, sl, q, k, v, g, beta)
+    wp = hist[slots].astype(np.int64)
+    assert np.array_equal(pool.write_pos.cpu().numpy()[slots], wp)
+    for r in range(w.steps):
+        x = gi.step_inputs(w, 200 + r)
+        xi = dev_inputs(x)
+        o = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, pool.ckpt,
+                                  pool.ring_d, pool.ring_k, pool.ring_g, pool.write_pos,
+                                  err_flags=pool.err, window=True)
+        x64 = x.f64()
+        e = rel_err(to_f64(o), window_ref(S_true, slots, *x64))
+        assert e <= tol_o(w), f"T={T} round {r}: window rel err {e:.3e}"
+        acc = gi.accepted_counts(w, r)
+        gdn.gdn_replay_commit(slot_t, to_dev(acc), pool.write_pos, L, T, err_flags=pool.err)
+        _advance_true(S_true, slots, x64, acc)
+        wp += acc
+        assert np.array_equal(pool.write_pos.cpu().numpy()[slots], wp)
+    assert int(pool.err.item()) == 0
