@@ -353,7 +353,7 @@ gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, void* ck
   if (s->step_rounding != 0 && s->step_rounding != 1) return GDN_ERR_INVALID_ARG;
   const size_t rs = elem_size(s->ring_dtype);
   const size_t ga = s->gate == GDN_GATE_KEY ? 16 : 4;
-  if (!aligned(ckpt, 16) || !aligned(ring_d, rs) || !aligned(ring_k, rs) ||
+  if (!aligned(ckpt, 16) || !aligned(ring_d, 16) || !aligned(ring_k, 16) ||
       !aligned(ring_g, ga) || !aligned(write_pos, 4) || !aligned(slot_idx, 4) ||
       (err_flags && !aligned(err_flags, 4)))
     return GDN_ERR_INVALID_ARG;
@@ -364,11 +364,14 @@ gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, void* ck
   a.B = s->B; a.N = s->N; a.Hv = s->Hv; a.Hk = s->Hk; a.dv = s->dv; a.L = s->L;
   a.G = s->Hv / s->Hk;
   a.step_round = s->step_rounding;
-  const dim3 grid(static_cast<unsigned>(s->B) * s->Hv * (s->dv / 16));
+  // value rows per workgroup: 64 (or the largest of 32, 16 dividing dv), so
+  // that the ring entries staged in LDS serve several rows per thread
+  a.fv = s->dv % 64 == 0 ? 64 : (s->dv % 32 == 0 ? 32 : 16);
+  const dim3 grid(static_cast<unsigned>(s->B) * s->Hv * (s->dv / a.fv));
   const dim3 block(static_cast<unsigned>(16 * s->dk / 4));
-  // LDS: the ring's keys [L][dk], d [L][16] and decays ([L], or [L][dk] per key)
+  // LDS: the ring's keys [L][dk], d [L][fv] and decays ([L], or [L][dk] per key)
   const size_t n_al = s->gate == GDN_GATE_KEY ? static_cast<size_t>(s->dk) : 1;
-  const size_t smem = static_cast<size_t>(s->L) * (n_al + 16 + s->dk) * sizeof(float);
+  const size_t smem = static_cast<size_t>(s->L) * (n_al + a.fv + s->dk) * sizeof(float);
   if (smem > 160 * 1024) return GDN_ERR_UNSUPPORTED;
   return from_hip(dispatch_fold(s->dk, a, s->ring_dtype, s->state_dtype, s->gate, grid, block,
                                 smem, static_cast<hipStream_t>(stream)));

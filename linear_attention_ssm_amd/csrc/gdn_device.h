@@ -655,6 +655,7 @@ struct FoldArgs {
   int32_t* err;
   int32_t B, N, Hv, Hk, dv, L, G;
   int32_t step_round;      // round a 16-bit state after each folded entry
+  int32_t fv;              // value rows per workgroup (16, 32 or 64, divides dv)
 };
 
 }  // namespace gdn

@@ -797,15 +797,17 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
 //
 // Fold the valid ring entries into the checkpoint with the pinned two-step
 // rounding (SGLang PR #42388 "The idea"; SGLang PR #36821 fold). Workgroup =
-// (row, value head, 16 value rows); thread = one 16-byte group of 4 keys.
+// (row, value head, FV value rows); thread = one 16-byte group of 4 keys in
+// FV/16 rows (the ring entries staged in LDS serve all of them).
 // KG = 1: per-key gate (ring_g [N, Hv, L, dk]), each channel decays by its
 // own a_j[c].
 template <int DK, int RING, int SD, int KG>
 __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   constexpr int C4 = DK / 4;
-  constexpr int FV = 16;
-  using RT = typename Elem<RING>::T;
+  constexpr int MAXR = 4;                             // rows per thread, at most
   extern __shared__ __align__(16) unsigned char smem[];
+  const int FV = a.fv;                                // value rows per workgroup (16, 32 or 64)
+  const int nr = FV >> 4;                             // rows per thread
   float* kl = reinterpret_cast<float*>(smem);        // [L][DK]  key entries (16-byte rows)
   float* dl = kl + a.L * DK;                          // [L][FV]  d entries
   float* al = dl + a.L * FV;                          // [L] decays ([L][DK] for KG)
@@ -832,12 +834,14 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   const size_t hs = static_cast<size_t>(s) * a.Hv + h;
   const size_t ks = static_cast<size_t>(s) * a.Hk + hk;
   const int tid = threadIdx.x;
-  const int row = tid / C4, e4 = (tid % C4) * 4;
-  const int v = vb * FV + row;
+  const int row = tid / C4, e4 = (tid % C4) * 4;      // rows row, row + 16, ...
 
   using SE = typename Elem<SD>::T;
-  SE* xbase = static_cast<SE*>(a.ckpt) + (hs * a.dv + vb * FV) * DK;   // the block's 16 rows
-  f4 x = load4<SD>(xbase, row * DK + e4);
+  SE* xbase = static_cast<SE*>(a.ckpt) + (hs * a.dv + vb * FV) * DK;   // the block's FV rows
+  f4 x[MAXR];
+#pragma unroll
+  for (int m = 0; m < MAXR; ++m)
+    if (m < nr) x[m] = load4<SD>(xbase, (row + 16 * m) * DK + e4);
 
   if constexpr (KG) {
     for (int c = tid; c < p * C4; c += blockDim.x) {
@@ -850,17 +854,15 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   } else {
     if (tid < p) al[tid] = decay_of(a.ring_g[hs * a.L + tid]);
   }
-  for (int c = tid; c < p * FV; c += blockDim.x) {
-    const int j = c / FV, r = c % FV;
-    dl[c] = to_f32<RING>(static_cast<const RT*>(a.ring_d)[(hs * a.L + j) * a.dv + vb * FV + r]);
+  const int F4 = FV >> 2;                             // four d entries per item
+  for (int c = tid; c < p * F4; c += blockDim.x) {
+    const int j = c / F4, r4 = (c - j * F4) * 4;
+    *reinterpret_cast<f4*>(dl + j * FV + r4) =
+        load4<RING>(a.ring_d, (hs * a.L + j) * a.dv + vb * FV + r4);
   }
   for (int c = tid; c < p * C4; c += blockDim.x) {
     const int j = c / C4, q4 = (c % C4) * 4;
-    const RT* src = static_cast<const RT*>(a.ring_k) + (ks * a.L + j) * DK + q4;
-    f4 kv;
-    kv.x = to_f32<RING>(src[0]); kv.y = to_f32<RING>(src[1]);
-    kv.z = to_f32<RING>(src[2]); kv.w = to_f32<RING>(src[3]);
-    *reinterpret_cast<f4*>(kl + j * DK + q4) = kv;
+    *reinterpret_cast<f4*>(kl + j * DK + q4) = load4<RING>(a.ring_k, (ks * a.L + j) * DK + q4);
   }
   __syncthreads();
 
@@ -870,33 +872,45 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
       f4 aj;
       if constexpr (KG) aj = *reinterpret_cast<const f4*>(al + j * DK + e4);
       else aj = f4{al[j], al[j], al[j], al[j]};
-      const float dj = dl[j * FV + row];
       const f4 kv = *reinterpret_cast<const f4*>(kl + j * DK + e4);
-      const float tx = aj.x * x.x, ty = aj.y * x.y, tz = aj.z * x.z, tw = aj.w * x.w;
-      x.x = __builtin_fmaf(dj, kv.x, tx);
-      x.y = __builtin_fmaf(dj, kv.y, ty);
-      x.z = __builtin_fmaf(dj, kv.z, tz);
-      x.w = __builtin_fmaf(dj, kv.w, tw);
-      if constexpr (SD != DT_F32) {
-        if (a.step_round) {
-          x.x = to_f32<SD>(state_round<SD>(x.x));
-          x.y = to_f32<SD>(state_round<SD>(x.y));
-          x.z = to_f32<SD>(state_round<SD>(x.z));
-          x.w = to_f32<SD>(state_round<SD>(x.w));
+#pragma unroll
+      for (int m = 0; m < MAXR; ++m) {
+        if (m < nr) {
+          const float dj = dl[j * FV + row + 16 * m];
+          f4& y = x[m];
+          const float tx = aj.x * y.x, ty = aj.y * y.y, tz = aj.z * y.z, tw = aj.w * y.w;
+          y.x = __builtin_fmaf(dj, kv.x, tx);
+          y.y = __builtin_fmaf(dj, kv.y, ty);
+          y.z = __builtin_fmaf(dj, kv.z, tz);
+          y.w = __builtin_fmaf(dj, kv.w, tw);
+          if constexpr (SD != DT_F32) {
+            if (a.step_round) {
+              y.x = to_f32<SD>(state_round<SD>(y.x));
+              y.y = to_f32<SD>(state_round<SD>(y.y));
+              y.z = to_f32<SD>(state_round<SD>(y.z));
+              y.w = to_f32<SD>(state_round<SD>(y.w));
+            }
+          }
         }
       }
     }
   }
   // fp32 result of the exact fold, rounded once to the state format
-  if constexpr (SD == DT_F32) {
-    store16_nt(reinterpret_cast<float*>(xbase), FV * DK * 4, (row * DK + e4) * 4, x);
-  } else {
-    u16x4 r;
-    r.x = __builtin_bit_cast(uint16_t, state_round<SD>(x.x));
-    r.y = __builtin_bit_cast(uint16_t, state_round<SD>(x.y));
-    r.z = __builtin_bit_cast(uint16_t, state_round<SD>(x.z));
-    r.w = __builtin_bit_cast(uint16_t, state_round<SD>(x.w));
-    store8_nt(reinterpret_cast<float*>(xbase), FV * DK * 2, (row * DK + e4) * 2, r);
+#pragma unroll
+  for (int m = 0; m < MAXR; ++m) {
+    if (m < nr) {
+      const int off = (row + 16 * m) * DK + e4;
+      if constexpr (SD == DT_F32) {
+        store16_nt(reinterpret_cast<float*>(xbase), FV * DK * 4, off * 4, x[m]);
+      } else {
+        u16x4 r;
+        r.x = __builtin_bit_cast(uint16_t, state_round<SD>(x[m].x));
+        r.y = __builtin_bit_cast(uint16_t, state_round<SD>(x[m].y));
+        r.z = __builtin_bit_cast(uint16_t, state_round<SD>(x[m].z));
+        r.w = __builtin_bit_cast(uint16_t, state_round<SD>(x[m].w));
+        store8_nt(reinterpret_cast<float*>(xbase), FV * DK * 2, off * 2, r);
+      }
+    }
   }
 }
 
