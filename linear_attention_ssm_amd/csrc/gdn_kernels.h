@@ -1,12 +1,12 @@
 // gdn_kernels.h -- the gfx950 kernels of the GDN decode path (templates).
 //
 // Workgroup = (row b, key head hk, value block vb). It holds the G = Hv/Hk
-// value heads that share key head hk, and VB value rows of each of them; one
-// wavefront per 16 value rows of one head. Everything a row needs from the
-// key side (q, k, the key ring) is staged once per workgroup in LDS and shared
-// by the G heads, so the key ring is read once per key head, as the ring
-// layout intends (ReplaySSM blog, section 2.2: same-group value heads share
-// the key entries).
+// value heads that share key head hk (the replay kernel: a chunk of GH of
+// them), and VB value rows of each; one wavefront per 16 value rows of one
+// head. Everything a row needs from the key side (q, k, the key ring) is
+// staged once per workgroup in LDS and shared by its heads, so the key ring
+// is read once per key head and chunk, as the ring layout intends (ReplaySSM
+// blog, section 2.2: same-group value heads share the key entries).
 #pragma once
 
 #include <type_traits>
@@ -141,17 +141,20 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
 //
 // One workgroup per work item (row, key head, head chunk, value block); one
 // wavefront per 16 value rows of one head. Per item:
-//   fetch:   the cursor, the flush flag and the gates (scalar loads), q/k, one
-//            key-ring chunk per thread, the wave's ring d entries and g, v (all
-//            unconditional, clamped into their buffers), then the 16-row
-//            checkpoint slab in 16-byte loads straight into accumulator layout;
-//   process: stage q/k and the key ring (transposed to [key][entry] for the
-//            MFMA A operand) in LDS; suffix-
-//            sum the ring's log-decays with a wave scan, A = exp(sum g),
-//            w_j = exp(sum_{i>j} g_i); S = A*S0 + K^T (w o D) on the MFMA units;
-//            per token Sq, Sk, k^T q -> d, o; append the ring entry (non-flush)
-//            or update the slab on chip (window tokens, flush) and write it to
-//            the checkpoint on a flush.
+//   fetch:   the cursor and the flush flag (scalar loads), the gates, q/k,
+//            one key-ring piece per thread, the wave's ring d entries and g,
+//            v (ring reads bounded by the cursor through buffer resources),
+//            then the 16-row checkpoint slab in 16-byte loads of whole lines;
+//   process: stage q/k (normalised if asked) and the key ring (transposed to
+//            [key][entry] for the MFMA A operand) in LDS; suffix-sum the
+//            ring's log-decays with a wave scan, A = exp(sum g),
+//            w_j = exp(sum_{i>j} g_i); S = A*S0 + K^T (w o D) on the MFMA
+//            units; per token Sq, Sk, k^T q -> d, o; append the ring entry
+//            (non-flush) or update the slab on chip (window tokens, flush)
+//            and write it to the checkpoint on a flush. With the per-key
+//            gate (KG) the decays are per channel and fold onto the keys
+//            (weight_keys) instead of onto d. With a fused cursor advance the
+//            row's last workgroup writes the advanced cursor.
 // The small operands are requested before the slab: vector loads retire in
 // issue order, so the staging and the MFMA operand build can proceed while
 // the slab is still in flight.
