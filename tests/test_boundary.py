@@ -170,3 +170,26 @@ def test_python_binding_checks_tensors_before_calling():
     with pytest.raises(ValueError):
         gdn.gdn_packed_decode(q, q, q, torch.zeros(2, 1, 4), torch.zeros(2, 1, 4),
                               torch.zeros(2, dtype=torch.int32), torch.zeros(4, 4, 128, 128))
+
+
+def test_binding_reads_row_strides_off_views():
+    """q, k, v as views into a packed [B, T, 2*Hk*dk + Hv*dv] row: the
+    binding derives the row strides the C ABI takes (0 for dense tensors)."""
+    import torch
+    from linear_attention_ssm_amd import _row_stride, _shape
+    B, T, Hk, dk, Hv, dv = 3, 2, 2, 32, 4, 16
+    rw = 2 * Hk * dk + Hv * dv
+    m = torch.zeros(B, T, rw)
+    q = m[..., :Hk * dk].view(B, T, Hk, dk)
+    v = m[..., 2 * Hk * dk:].view(B, T, Hv, dv)
+    assert _row_stride(q, "q") == rw and _row_stride(v, "v") == rw
+    dense = torch.zeros(B, T, Hk, dk)
+    assert _row_stride(dense, "q") == Hk * dk
+    one = torch.zeros(B, 1, rw)[..., :Hk * dk].view(B, 1, Hk, dk)     # T = 1: stride of b
+    assert _row_stride(one, "q") == rw
+    sh = _shape(B, T, 8, Hv, Hk, dk, dv, 4, 1, 2, 0, 0, 0, 0, rw, Hv * dv, 1)
+    assert (sh.qk_row_stride, sh.v_row_stride, sh.qk_norm) == (rw, 0, 1)
+    with pytest.raises(ValueError):
+        _row_stride(torch.zeros(B, T, dk, Hk).transpose(2, 3), "q")     # [H, d] not dense
+    with pytest.raises(ValueError):
+        _row_stride(torch.zeros(T, B, Hk, dk).transpose(0, 1), "q")     # rows not in (b, t) order
