@@ -117,12 +117,23 @@ class LayerSet:
             self.ring_g = torch.zeros(gshape, dtype=torch.float32, device=dev)
 
 
-def input_sets(w, n, dev, T=None):
+def input_sets(w, n, dev, T=None, mixed=False):
+    """n seeded input sets on the device. mixed: q, k, v as views into one
+    packed [B, T, 2*Hk*dk + Hv*dv] row per token (the mixed_qkv layout)."""
+    import torch
     out = []
     for i in range(n):
         x = gi.step_inputs(w, 10_000 + i, T=T)
-        out.append(tuple(dev_tensor(a, x.dtype if j < 3 else None, dev)
-                         for j, a in enumerate((x.q, x.k, x.v, x.g, x.beta))))
+        q, k, v, g, beta = (dev_tensor(a, x.dtype if j < 3 else None, dev)
+                            for j, a in enumerate((x.q, x.k, x.v, x.g, x.beta)))
+        if mixed:
+            B, TT = q.shape[:2]
+            nq, nv = w.Hk * w.dk, w.Hv * w.dv
+            m = torch.cat([q.reshape(B, TT, nq), k.reshape(B, TT, nq), v.reshape(B, TT, nv)], -1)
+            q = m[..., :nq].view(B, TT, w.Hk, w.dk)
+            k = m[..., nq:2 * nq].view(B, TT, w.Hk, w.dk)
+            v = m[..., 2 * nq:].view(B, TT, w.Hv, w.dv)
+        out.append((q, k, v, g, beta))
     return out
 
 
@@ -173,14 +184,17 @@ def load_traffic(name: str):
 
 # ------------------------------------------------------------------ benches
 
-def bench_replay(w, R, steps, warmup, dev, log):
+def bench_replay(w, R, steps, warmup, dev, log, front_end=False):
+    """front_end: q, k, v read from the packed mixed_qkv row and normalised in
+    the kernel (the workload draws raw q, k)."""
     import torch
     import linear_attention_ssm_amd as gdn
     slots = gi.slot_map(w)
     slot_t = dev_tensor(slots, None, dev)
     layers = [LayerSet(w, w.seed + 17 * i, dev) for i in range(R)]
     wp = torch.zeros(w.N, dtype=torch.int32, device=dev)
-    ins = input_sets(w, 4, dev)
+    ins = input_sets(w, 4, dev, mixed=front_end)
+    fe = dict(qk_norm=True) if front_end else {}
     ff_sched = [dev_tensor(gi.force_flush_schedule(w, t, slots), None, dev) for t in range(w.L)]
     no_ff = torch.zeros(w.B, dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -190,7 +204,7 @@ def bench_replay(w, R, steps, warmup, dev, log):
         for i, ls in enumerate(layers):
             q, k, v, g, beta = ins[i % len(ins)]
             gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
-                                  ls.ring_g, wp, force_flush=ff, o=o, err_flags=err)
+                                  ls.ring_g, wp, force_flush=ff, o=o, err_flags=err, **fe)
 
     arrive = gdn.arrive_workspace(w.B, dev)
 
@@ -200,11 +214,11 @@ def bench_replay(w, R, steps, warmup, dev, log):
             q, k, v, g, beta = ins[i % len(ins)]
             if i < len(layers) - 1:
                 gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
-                                      ls.ring_g, wp, force_flush=ff, o=o, err_flags=err)
+                                      ls.ring_g, wp, force_flush=ff, o=o, err_flags=err, **fe)
             else:
                 gdn.gdn_replay_decode_advance(q, k, v, g, beta, slot_t, ls.state, ls.ring_d,
                                               ls.ring_k, ls.ring_g, wp, arrive, force_flush=ff,
-                                              o=o, err_flags=err)
+                                              o=o, err_flags=err, **fe)
 
     # eager warm-up: the staggered forced flushes of the first L steps spread
     # the slots' flush phases evenly over the ring cycle
@@ -231,7 +245,7 @@ def bench_replay(w, R, steps, warmup, dev, log):
     live = int(np.count_nonzero(slots >= 0))
     mean_p = float(np.mean([p for p, _ in cur]))
     flush_frac = float(np.mean([fl for _, fl in cur]))
-    log(f"replay [{w.state} state, {w.gate} gate]: {ms_step * 1e3:.1f} us/step ({R} layers, fused advance), decode kernel "
+    log(f"replay [{w.state} state, {w.gate} gate{', front end' if front_end else ''}]: {ms_step * 1e3:.1f} us/step ({R} layers, fused advance), decode kernel "
         f"{ms_dec * 1e3:.2f} us, {bytes_launch / 1e6:.2f} MB/launch, "
         f"mean p {mean_p:.2f}, flush frac {flush_frac:.4f}")
     return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
@@ -440,6 +454,8 @@ def main():
     rep16 = bench_replay(w16, R, steps, warmup, dev, log)
     pk16 = bench_packed(w16, R, steps, dev, log)
     repk = bench_replay(gi.C7, R, steps, warmup, dev, log)
+    w_fe = dataclasses.replace(w, qk_raw=True)
+    repf = bench_replay(w_fe, R, steps, warmup, dev, log, front_end=True)
     pkk = bench_packed(gi.C7, R, steps, dev, log)
     wf = bench_window_fold(gi.C5, R, max(4, steps // 8), dev, log)
     ll = bench_lossless(gi.C6, R, max(4, steps // 8), dev, log)
@@ -515,6 +531,14 @@ def main():
             "packed_bytes_per_launch": pkk["bytes_per_launch"],
             "replay_vs_packed_kernel": pkk["kernel_ms"] / repk["kernel_ms"],
             "replay_vs_packed": repk["head_steps_per_s"] / pkk["head_steps_per_s"],
+        },
+        "front_end_c2": {
+            "note": ("the standard workload with q, k, v read from the packed mixed_qkv row "
+                     "and q/k L2-normalised (q scaled) in the kernel"),
+            "replay_head_steps_per_s": repf["head_steps_per_s"],
+            "replay_kernel_us": repf["kernel_ms"] * 1e3,
+            "replay_gbs": repf["bytes_per_launch"] / (repf["kernel_ms"] / 1e3) / 1e9,
+            "vs_plain_replay_kernel": rep["kernel_ms"] / repf["kernel_ms"],
         },
         "verify_window_c5": wf,
         "lossless_verify_c6": ll,
