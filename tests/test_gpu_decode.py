@@ -11,7 +11,7 @@ import torch
 
 import gdn_inputs as gi
 from gdn_harness import DEV, Pool, bits, dev_inputs, log, run_decode, to_dev, to_f64
-from oracle import gdn_step, rel_err
+from oracle import gdn_step, rel_err, step
 
 pytestmark = pytest.mark.gpu
 
@@ -227,3 +227,43 @@ def test_decode_advance_equals_decode_then_advance(gdn, gate):
         assert int(arrive.abs().sum().item()) == 0, f"step {t}: arrive not cleared"
         assert int(a.err.item()) == int(b.err.item())
     assert int(b.err.item()) == gdn.EF_CURSOR_RANGE
+
+
+@pytest.mark.parametrize("ring,gate", [("f16", "head"), ("f32", "head"), ("f16", "key")])
+def test_maximum_sizes(gdn, ring, gate):
+    """The largest supported sizes: dk = 256, dv = 512, L = 64 (70 decode steps,
+    crossing the natural flush at step 64), then a T = 16 verify window (T = 4
+    with the per-key gate, whose staged gates for 16 tokens exceed LDS at
+    dk = 256) and its fold; against the oracle."""
+    qkv = "f32" if ring == "f32" else "bf16"
+    w = gi.Workload(f"max_{ring}_{gate}", B=3, N=4, Hv=2, Hk=1, dk=256, dv=512, L=64,
+                    steps=70, qkv=qkv, ring=ring, n_pad=1, permute=True, stagger=False,
+                    bf16_values=(ring == "f32"), gate=gate, seed=990)
+    TW = 16 if gate == "head" else 4
+    rep = run_decode(w, "replay", garbage=True, recon_every=35)
+    assert rep.flushes == 2                         # two live rows, one natural flush each
+    run_decode(dataclasses.replace(w, steps=3), "packed")
+    wv = dataclasses.replace(w, T=TW, steps=1)
+    S0 = gi.initial_state(wv)
+    slots = gi.slot_map(wv)
+    pool = Pool(wv, S0)
+    x = gi.step_inputs(wv, 7)
+    xi = dev_inputs(x)
+    o = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, to_dev(slots), pool.ckpt,
+                              pool.ring_d, pool.ring_k, pool.ring_g, pool.write_pos,
+                              err_flags=pool.err, window=True)
+    from oracle import window_ref
+    o_ref = window_ref(S0.astype(np.float64), slots, *x.f64())
+    tol = 1e-4 if ring == "f32" else 2e-2
+    assert rel_err(to_f64(o), o_ref) <= tol
+    acc = to_dev(np.full(wv.B, TW, np.int32))
+    gdn.gdn_replay_commit(to_dev(slots), acc, pool.write_pos, wv.L, TW, err_flags=pool.err)
+    gdn.gdn_replay_fold(to_dev(slots), pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
+                        pool.write_pos, err_flags=pool.err)
+    S_true = S0.astype(np.float64)
+    q, k, v, g, beta = x.f64()
+    for t in range(TW):
+        step(S_true, slots, q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t])
+    live = slots[slots >= 0]
+    assert rel_err(to_f64(pool.ckpt[torch.from_numpy(live).to(DEV)]), S_true[live]) <= tol
+    assert int(pool.err.item()) == 0
