@@ -143,8 +143,12 @@ void fill_replay_geometry(const gdn_shape* s, DecodeArgs& a, dim3& block, int& n
   }();
   a.B = s->B; a.T = s->T; a.N = s->N; a.Hv = s->Hv; a.Hk = s->Hk; a.dv = s->dv; a.L = s->L;
   a.G = s->Hv / s->Hk;
+  // value heads per workgroup: with a per-head gate, as many as fit (they
+  // share the staged key ring); with the per-key gate one, since each head
+  // brings a dk-wide log-decay per ring entry, which every workgroup of the
+  // head re-reads and weights
   int gh = 1;
-  for (int d = 1; d <= a.G; ++d)
+  for (int d = 1; d <= a.G && s->gate != GDN_GATE_KEY; ++d)
     if (a.G % d == 0 && d <= tw) gh = d;
   a.GH = gh;
   a.nhc = a.G / gh;
@@ -282,6 +286,21 @@ gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const
     end = up16(end + static_cast<size_t>(a.GH) * kw_bytes);
     a.acol_off = static_cast<int32_t>(end);
     end += static_cast<size_t>(a.GH) * s->dk * sizeof(float);
+    // early copy of the ring log-decays and keys (rings of at most 16
+    // entries, one 32-channel group per wavefront) and of the token gates
+    const int nw = static_cast<int>(block.x / 64);
+    const uint64_t g_bytes = static_cast<uint64_t>(s->B) * s->T * s->Hv * s->dk * sizeof(float);
+    if (s->L <= 16 && a.GH * s->dk == 32 * nw && g_bytes < 0xfffffff0ull) {
+      a.kdma = 1;
+      a.g_bytes = static_cast<uint32_t>(g_bytes);
+      a.kraw_wave = s->ring_dtype == GDN_F32 ? 4096 : 3072;
+      end = up16(end);
+      a.kraw_off = static_cast<int32_t>(end);
+      end += static_cast<size_t>(nw) * a.kraw_wave;
+      a.tg_off = static_cast<int32_t>(end);
+      const int ntg = std::min(a.GH * s->T * (s->dk / 4), static_cast<int>(block.x));
+      end += static_cast<size_t>((ntg + 63) / 64) * 1024;
+    }
   }
   a.dump_off = static_cast<int32_t>(up16(end));
   const size_t smem = a.dump_off + 64 * 8 * sizeof(float);

@@ -231,6 +231,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, uint32
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, 0x00020000);
 }
 
+// The memory unit copies 16 bytes per active lane into LDS, lane l's at
+// lds + 16 l (lds wavefront-uniform). From a bounded buffer, bytes past its
+// end arrive as zeros.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds,
+                                                uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(lds), 16, voff, 0, 0, 0);
+}
+
 // x from lane l + n of the same 16-lane row (0 past the row end), by DPP.
 template <int N>
 __device__ __forceinline__ float row_shl(float x) {
@@ -623,6 +632,15 @@ struct DecodeArgs {
   // the weighted key rings of the heads (kw_head elements apart) and the
   // per-channel checkpoint decays A ([GH][dk] floats)
   int32_t kg_off, kw_off, acol_off, kw_head;
+  // per-key gate, early copy (kdma = 1: ring depth <= 16 and one 32-channel
+  // group of the workgroup's GH*dk channels per wavefront): before the
+  // checkpoint slab is requested, each wavefront has the memory unit copy the
+  // ring log-decays and keys of its channels into LDS (kraw_wave bytes per
+  // wavefront from kraw_off) and the first piece of each thread's token gates
+  // (16 bytes per lane from tg_off), so the weighting waits on no load issued
+  // after the slab; g_bytes is the size of the token gates g
+  int32_t kdma, kraw_off, kraw_wave, tg_off;
+  uint32_t g_bytes;
   // cursor advance fused into a decode step (gdn_replay_decode_advance): the
   // workgroups of a row count themselves in arrive[b] once every wavefront of
   // theirs has read the cursor; the last one writes the advanced cursor

@@ -153,8 +153,11 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
 //            (non-flush) or update the slab on chip (window tokens, flush)
 //            and write it to the checkpoint on a flush. With the per-key
 //            gate (KG) the decays are per channel and fold onto the keys
-//            (weight_keys) instead of onto d. With a fused cursor advance the
-//            row's last workgroup writes the advanced cursor.
+//            (weight_keys) instead of onto d; for rings of up to 16 entries
+//            the memory unit copies the ring's log-decays and keys into LDS
+//            ahead of the slab (fetch_key_gate, weight_keys_lds). With a
+//            fused cursor advance the row's last workgroup writes the
+//            advanced cursor.
 // The small operands are requested before the slab: vector loads retire in
 // issue order, so the staging and the MFMA operand build can proceed while
 // the slab is still in flight.
@@ -320,6 +323,54 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
   f.v_raw = load1_raw<QKV>(a.v, static_cast<size_t>(g.b) * T * a.v_rs + g.h * a.dv + g.vcol);
 }
 
+// Per-key gate, early copy (a.kdma != 0). Each wavefront has the memory unit
+// copy the ring log-decays and keys of its 32 channels, ring entries 0..15,
+// into LDS as [16 entries][32 channels] (zeros past the valid entries), and
+// each gate-staging thread its first 16 bytes of token gates. Issued before
+// the slab, these arrive with the other small operands, so weight_keys_lds
+// and the gate staging do not wait for loads queued behind the slab.
+template <int DK, int RING>
+__device__ __forceinline__ void fetch_key_gate(const DecodeArgs& a, const ItemGeo& g,
+                                               const RowState& r, int T, unsigned char* buf,
+                                               int tid, int lane, int wave) {
+  constexpr bool RF32 = (RING == DT_F32);
+  constexpr int RS = RF32 ? 4 : 2;
+  const uint32_t p = static_cast<uint32_t>(r.p);
+  const char* kbase = static_cast<const char*>(a.ring_k) +
+                      (static_cast<size_t>(r.sc) * a.Hk + g.hk) * a.L * DK * RS;
+  const __amdgpu_buffer_rsrc_t rk = brsrc(kbase, p * DK * RS);
+  unsigned char* d = buf + a.kraw_off + wave * a.kraw_wave;
+  const int e8 = lane >> 3, q8 = 4 * (lane & 7);   // entry and channel offset of 16-byte pieces
+  const int ch = wave * 32;
+  const int hh = ch / DK, c0 = ch % DK;
+  const size_t hsh = static_cast<size_t>(r.sc) * a.Hv + g.hk * a.G + g.hc * a.GH + hh;
+  const __amdgpu_buffer_rsrc_t rg = brsrc(a.ring_g + hsh * a.L * DK, p * DK * 4);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    buffer_to_lds16(rg, d + 1024 * i, ((8 * i + e8) * DK + c0 + q8) * 4);
+  if constexpr (RF32) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      buffer_to_lds16(rk, d + 2048 + 1024 * i, ((8 * i + e8) * DK + c0 + q8) * 4);
+  } else {
+    buffer_to_lds16(rk, d + 2048, ((lane >> 2) * DK + c0 + 8 * (lane & 3)) * 2);
+  }
+  // token gates: thread tid stages piece i = tid (head hh, token tau, four
+  // channels from 4 c4)
+  constexpr int C4 = DK / 4;
+  const int nqk = T * C4;
+  // (a buffer copy: lanes past the last piece read at the end of g, out of
+  // range, and copy zeros, so the copy needs no lane condition)
+  if (64 * wave < a.GH * nqk) {
+    const int hh = tid / nqk, c = tid - hh * nqk;
+    const int tau = c / C4, c4 = c - tau * C4;
+    const uint32_t gi = ((static_cast<uint32_t>(g.b) * T + tau) * a.Hv + g.hk * a.G + g.hc * a.GH + hh) * DK;
+    const __amdgpu_buffer_rsrc_t rt = brsrc(a.g, a.g_bytes);
+    buffer_to_lds16(rt, buf + a.tg_off + wave * 1024,
+                    tid < a.GH * nqk ? (gi + 4 * c4) * 4 : a.g_bytes);
+  }
+}
+
 // Request an item's 16-row checkpoint slab: 16-byte loads in the lane order
 // of the accumulator layout (widened to fp32 in process()). A masked row
 // reads nothing (zeros).
@@ -466,6 +517,68 @@ __device__ __forceinline__ void weight_keys(const DecodeArgs& a, const ItemGeo& 
   }
 }
 
+// weight_keys from the early copy (a.kdma != 0, entries 0..15): two lanes
+// per channel, lanes 32..63 take entries 15..8 and lanes 0..31 entries 7..0.
+// The lower half starts its running sum from the upper half's total, so every
+// W and weight is the same float as in weight_keys' sequential sum.
+// NSLAB: the vector loads of the slab, the only ones issued after the copy.
+template <int DK, int RING, int NSLAB>
+__device__ __forceinline__ void weight_keys_lds(const DecodeArgs& a, int lp, unsigned char* buf,
+                                                int lane, int wave) {
+  using RT = typename Elem<RING>::T;
+  constexpr bool RF32 = (RING == DT_F32);
+  // The compiler does not order LDS reads after a copy into LDS by the
+  // memory unit: wait here until at most the NSLAB slab loads (issued after
+  // the copy, in order) are outstanding, so the copy has landed. Encoding:
+  // vmcnt in bits 3:0 and 15:14, expcnt (7) and lgkmcnt (15) left open.
+  static_assert(NSLAB < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((NSLAB & 15) | (7 << 4) | (15 << 8) | ((NSLAB >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
+  const int cl = lane & 31, e0 = (lane >> 5) ? 8 : 0;
+  float* acol = reinterpret_cast<float*>(buf + a.acol_off);
+  const unsigned char* w = buf + a.kraw_off + wave * a.kraw_wave;
+  {
+    const int ch = wave * 32 + cl;
+    const int hh = ch / DK, c = ch % DK;
+    const float* gr = reinterpret_cast<const float*>(w);
+    const RT* kr = reinterpret_cast<const RT*>(w + 2048);
+    float gv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gv[e] = gr[(e0 + e) * 32 + cl];
+    float t = 0.f;                                 // the upper half's total
+#pragma unroll
+    for (int e = 7; e >= 0; --e) t += gv[e];
+    // every lane takes part in the exchange (a shuffle under a lane condition
+    // would leave the source lanes' totals uncomputed)
+    const float tu = __shfl(t, cl + 32, 64);
+    float W = e0 ? 0.f : tu;
+    float kwv[8];
+#pragma unroll
+    for (int e = 7; e >= 0; --e) {
+      kwv[e] = __expf(W) * to_f32<RING>(kr[(e0 + e) * 32 + cl]);
+      W += gv[e];
+    }
+    RT* kw = reinterpret_cast<RT*>(buf + a.kw_off) + hh * a.kw_head;
+    if constexpr (RF32) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e0 + e < lp) kw[(e0 + e) * DK + c] = kwv[e];
+    } else if (e0 < lp) {                          // lp is 16 here (0 for an empty ring)
+      uint2 pk[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        pk[h].x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_f32<RING>(kwv[4 * h]))) |
+                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_f32<RING>(kwv[4 * h + 1]))) << 16);
+        pk[h].y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_f32<RING>(kwv[4 * h + 2]))) |
+                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_f32<RING>(kwv[4 * h + 3]))) << 16);
+      }
+      *reinterpret_cast<uint2*>(kw + c * a.kts + e0) = pk[0];
+      *reinterpret_cast<uint2*>(kw + c * a.kts + e0 + 4) = pk[1];
+    }
+    if (e0 == 0) acol[hh * DK + c] = __expf(W);
+  }
+}
+
 template <int DK, int QKV, int RING, int SD, int TT, int KG, int NRM>
 __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, const RowState& r,
                                         int T, const Small<DK, QKV, RING>& f,
@@ -523,17 +636,22 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   }
   float* kgl = reinterpret_cast<float*>(buf + a.kg_off);       // KG: [GH][T][4][DK]
   if constexpr (KG) {
-    weight_keys<DK, RING>(a, g, r, lp, buf, tid, nthr);
-    // per-key gates of the workgroup's heads for every token, from q and k as
-    // given, or (normalised in the kernel) from their staged copies
+    if (a.kdma) weight_keys_lds<DK, RING, SlabRaw<SD, DK>::NP>(a, lp, buf, lane, wave);
+    else weight_keys<DK, RING>(a, g, r, lp, buf, tid, nthr);
+    // per-key gates of the workgroup's heads for every token, from the staged
+    // q and k (normalised in the kernel: once every wavefront has staged;
+    // as given: a thread below nqk reads back its own staging, the others
+    // load them); a thread's first piece of gates comes from the early copy
     if constexpr (NRM) __syncthreads();
     for (int i = tid; i < a.GH * nqk; i += nthr) {
       const int hh = i / nqk, c = i - hh * nqk;
       const int tau = TT ? 0 : c / C4, c4 = c - tau * C4;
       const size_t gi = ((static_cast<size_t>(g.b) * T + tau) * a.Hv + g.hk * a.G + g.hc * a.GH + hh) * DK;
-      const f4 g4 = *reinterpret_cast<const f4*>(a.g + gi + 4 * c4);
+      const f4 g4 = (a.kdma && i == tid)
+                        ? *reinterpret_cast<const f4*>(buf + a.tg_off + wave * 1024 + lane * 16)
+                        : *reinterpret_cast<const f4*>(a.g + gi + 4 * c4);
       f4 qv, kv;
-      if constexpr (NRM) {
+      if (NRM || (i == tid && tid < nqk)) {
         qv = *reinterpret_cast<const f4*>(qk + tau * 2 * DK + 4 * c4);
         kv = *reinterpret_cast<const f4*>(qk + tau * 2 * DK + DK + 4 * c4);
       } else {
@@ -791,6 +909,9 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   Small<DK, QKV, RING> sm;
   SlabRaw<SD, DK> R;
   fetch_small<DK, QKV, RING, TT, KG>(sm, a, g, r, T, tid, lane, grp, wave);
+  if constexpr (KG) {
+    if (a.kdma) fetch_key_gate<DK, RING>(a, g, r, T, smem, tid, lane, wave);
+  }
   __builtin_amdgcn_sched_barrier(0);
   fetch_slab<SD, DK>(R, a, g, r, col, grp);
   process<DK, QKV, RING, SD, TT, KG, NRM>(a, g, r, T, sm, R, smem, dump, tid, lane, grp, col, wave);

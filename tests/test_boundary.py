@@ -65,8 +65,9 @@ def packed(sh, ptrs=None):
     (dict(qk_row_stride=260), gdn.GDN_ERR_INVALID_ARG),     # rows not 16-byte aligned
     (dict(v_row_stride=200), gdn.GDN_ERR_INVALID_ARG),      # < Hv * dv
     (dict(gate=-1), gdn.GDN_ERR_INVALID_ARG),
-    # per-key gate, 16-token windows at dk = 256: the staged gates exceed LDS
-    (dict(gate=1, T=16, window=1, dk=256, L=64), gdn.GDN_ERR_UNSUPPORTED),
+    # per-key gate, 16-token windows at dk = 256, L = 64 with an fp32 ring: the
+    # staged gates and weighted keys exceed LDS
+    (dict(gate=1, T=16, window=1, dk=256, L=64, ring_dtype=gdn.GDN_F32), gdn.GDN_ERR_UNSUPPORTED),
     (dict(T=2), gdn.GDN_ERR_INVALID_ARG),               # decode mode needs T = 1
     (dict(T=2, window=1, L=1), gdn.GDN_ERR_INVALID_ARG),  # window longer than the ring
     (dict(window=2), gdn.GDN_ERR_INVALID_ARG),

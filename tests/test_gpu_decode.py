@@ -232,14 +232,13 @@ def test_decode_advance_equals_decode_then_advance(gdn, gate):
 @pytest.mark.parametrize("ring,gate", [("f16", "head"), ("f32", "head"), ("f16", "key")])
 def test_maximum_sizes(gdn, ring, gate):
     """The largest supported sizes: dk = 256, dv = 512, L = 64 (70 decode steps,
-    crossing the natural flush at step 64), then a T = 16 verify window (T = 4
-    with the per-key gate, whose staged gates for 16 tokens exceed LDS at
-    dk = 256) and its fold; against the oracle."""
+    crossing the natural flush at step 64), then a T = 16 verify window and its
+    fold; against the oracle."""
     qkv = "f32" if ring == "f32" else "bf16"
     w = gi.Workload(f"max_{ring}_{gate}", B=3, N=4, Hv=2, Hk=1, dk=256, dv=512, L=64,
                     steps=70, qkv=qkv, ring=ring, n_pad=1, permute=True, stagger=False,
                     bf16_values=(ring == "f32"), gate=gate, seed=990)
-    TW = 16 if gate == "head" else 4
+    TW = 16
     rep = run_decode(w, "replay", garbage=True, recon_every=35)
     assert rep.flushes == 2                         # two live rows, one natural flush each
     run_decode(dataclasses.replace(w, steps=3), "packed")
