@@ -249,7 +249,8 @@ __device__ __forceinline__ RowState row_state(const DecodeArgs& a, int b, int T)
                     : ((p_raw < 0 || p_raw > a.L - 1) ? EF_CURSOR : 0);
   r.ok = r.slot_ok && r.ef == 0;
   r.p = r.ok ? p_raw : 0;
-  r.flush = r.ok && !a.window && (p_raw == a.L - 1 || (a.ff_on && ff != 0));
+  // bitwise, not short-circuit: no branch holds the flag load back
+  r.flush = r.ok & (a.window == 0) & ((p_raw == a.L - 1) | ((a.ff_on != 0) & (ff != 0)));
   return r;
 }
 
@@ -904,6 +905,10 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4, col = lane & 15;
   const int T = TT ? 1 : a.T;
+  // The row's metadata pointers are needed right after the work-item
+  // mapping; used here, they are loaded with the mapping's arguments, so the
+  // chain before the first vector load is arguments -> slot -> cursor.
+  asm volatile("" ::"s"(a.slot), "s"(a.write_pos), "s"(a.ff_flags));
   const ItemGeo g = item_geo(a, wave, col);
   const RowState r = row_state(a, g.b, T);
   Small<DK, QKV, RING> sm;
