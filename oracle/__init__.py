@@ -16,6 +16,8 @@ Parts:
   O6  kda_step          the per-key-gate (KDA) recurrence in fp64 (C)
   O7  fold_kda_f32      the pinned-rounding fold with a per-key gate (C)
   O8  l2norm_qk         the decode's front end: q/k L2-normalised, q scaled
+  O9  conv_update       the causal convolution (width W, SiLU) and its state
+                        in front of the decode
   O2, O4 take the per-key gate as well (ReplayModel(gate="key"), window_ref
   with g [B, T, Hv, dk]).
 
@@ -203,6 +205,34 @@ def l2norm_qk(q, k):
     nq = np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + QK_NORM_EPS)
     nk = np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + QK_NORM_EPS)
     return q / nq * dk ** -0.5, k / nk
+
+
+# ------------------------------------------------------------------ O9
+
+def conv_update(x, w, conv_state: np.ndarray, slot) -> np.ndarray:
+    """O9: the causal convolution step in front of the decode (ReplaySSM
+    blog, section 3.1: the decode path updates the causal convolution first;
+    SGLang PR #36821, Technical principle: x_hat_t = SiLU(w * x_{t-3:t})).
+    Per channel, the window holds the W-1 previous inputs (conv_state[s],
+    [W-1, C], oldest first) and the current one; the output is SiLU of the
+    tap-weighted sum (tap W-1 on the current input), in fp64; the window then
+    moves by one input. Rows with a slot outside [0, N) are padding: zero
+    output, no state change. x [B, C], w [C, W]; conv_state [N, W-1, C] is
+    updated in place (fp64). Returns y [B, C] (fp64)."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    B, C = x.shape
+    N = conv_state.shape[0]
+    y = np.zeros((B, C))
+    for b in range(B):
+        s = int(slot[b])
+        if s < 0 or s >= N:
+            continue
+        window = np.concatenate([conv_state[s], x[b][None, :]], axis=0)   # [W, C]
+        acc = np.einsum("cw,wc->c", w, window)
+        y[b] = acc / (1.0 + np.exp(-acc))
+        conv_state[s] = window[1:]
+    return y
 
 
 # ------------------------------------------------------------------ O3
