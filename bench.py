@@ -184,9 +184,11 @@ def load_traffic(name: str):
 
 # ------------------------------------------------------------------ benches
 
-def bench_replay(w, R, steps, warmup, dev, log, front_end=False):
+def bench_replay(w, R, steps, warmup, dev, log, front_end=False, conv=False):
     """front_end: q, k, v read from the packed mixed_qkv row and normalised in
-    the kernel (the workload draws raw q, k)."""
+    the kernel (the workload draws raw q, k). conv: each layer first runs the
+    causal convolution (width 4) on a raw packed row and the decode reads the
+    convolved row; the figures then cover both launches of a layer."""
     import torch
     import linear_attention_ssm_amd as gdn
     slots = gi.slot_map(w)
@@ -195,6 +197,23 @@ def bench_replay(w, R, steps, warmup, dev, log, front_end=False):
     wp = torch.zeros(w.N, dtype=torch.int32, device=dev)
     ins = input_sets(w, 4, dev, mixed=front_end)
     fe = dict(qk_norm=True) if front_end else {}
+    if conv:
+        nq = w.Hk * w.dk
+        ci = [gi.conv_inputs(w, 1, W=4, seed_tag=i) for i in range(R)]
+        taps = [dev_tensor(c.w, c.dtype, dev) for c in ci]
+        cstate = [dev_tensor(c.state, c.dtype, dev) for c in ci]
+        xraw = [dev_tensor(c.x[0], c.dtype, dev) for c in ci]
+        ybuf = [torch.empty_like(x) for x in xraw]
+
+        def qkv_of(i):
+            gdn.gdn_conv_update(xraw[i], taps[i], cstate[i], slot_t, y=ybuf[i])
+            y = ybuf[i]
+            _, _, _, g, beta = ins[i % len(ins)]
+            return (y[:, :nq].view(w.B, 1, w.Hk, w.dk), y[:, nq:2 * nq].view(w.B, 1, w.Hk, w.dk),
+                    y[:, 2 * nq:].view(w.B, 1, w.Hv, w.dv), g, beta)
+    else:
+        def qkv_of(i):
+            return ins[i % len(ins)]
     ff_sched = [dev_tensor(gi.force_flush_schedule(w, t, slots), None, dev) for t in range(w.L)]
     no_ff = torch.zeros(w.B, dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -202,7 +221,7 @@ def bench_replay(w, R, steps, warmup, dev, log, front_end=False):
 
     def decodes(ff):
         for i, ls in enumerate(layers):
-            q, k, v, g, beta = ins[i % len(ins)]
+            q, k, v, g, beta = qkv_of(i)
             gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
                                   ls.ring_g, wp, force_flush=ff, o=o, err_flags=err, **fe)
 
@@ -211,7 +230,7 @@ def bench_replay(w, R, steps, warmup, dev, log, front_end=False):
     def forward(ff):
         # the last layer's decode advances the cursors (fused advance)
         for i, ls in enumerate(layers):
-            q, k, v, g, beta = ins[i % len(ins)]
+            q, k, v, g, beta = qkv_of(i)
             if i < len(layers) - 1:
                 gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
                                       ls.ring_g, wp, force_flush=ff, o=o, err_flags=err, **fe)
@@ -245,12 +264,40 @@ def bench_replay(w, R, steps, warmup, dev, log, front_end=False):
     live = int(np.count_nonzero(slots >= 0))
     mean_p = float(np.mean([p for p, _ in cur]))
     flush_frac = float(np.mean([fl for _, fl in cur]))
-    log(f"replay [{w.state} state, {w.gate} gate{', front end' if front_end else ''}]: {ms_step * 1e3:.1f} us/step ({R} layers, fused advance), decode kernel "
+    fe_tag = ", conv + front end" if conv else (", front end" if front_end else "")
+    log(f"replay [{w.state} state, {w.gate} gate{fe_tag}]: {ms_step * 1e3:.1f} us/step ({R} layers, fused advance), decode kernel "
         f"{ms_dec * 1e3:.2f} us, {bytes_launch / 1e6:.2f} MB/launch, "
         f"mean p {mean_p:.2f}, flush frac {flush_frac:.4f}")
     return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
                 kernel_ms=ms_dec, bytes_per_launch=bytes_launch,
                 head_steps_per_launch=live * w.Hv, mean_p=mean_p, flush_frac=flush_frac)
+
+
+def bench_conv(w, R, steps, dev, log):
+    """The causal convolution alone (width 4) on the packed mixed_qkv row of
+    the workload: R launches (one per layer) in a graph, per-launch time."""
+    import torch
+    import linear_attention_ssm_amd as gdn
+    slot_t = dev_tensor(gi.slot_map(w), None, dev)
+    ci = [gi.conv_inputs(w, 1, W=4, seed_tag=i) for i in range(R)]
+    taps = [dev_tensor(c.w, c.dtype, dev) for c in ci]
+    cstate = [dev_tensor(c.state, c.dtype, dev) for c in ci]
+    xraw = [dev_tensor(c.x[0], c.dtype, dev) for c in ci]
+    ybuf = [torch.empty_like(x) for x in xraw]
+
+    def run():
+        for i in range(R):
+            gdn.gdn_conv_update(xraw[i], taps[i], cstate[i], slot_t, y=ybuf[i])
+
+    g = graph_of(run)
+    ms = time_graph(g, steps) / R
+    C, es = gi.conv_channels(w), (4 if w.qkv == "f32" else 2)
+    live = int(np.count_nonzero(gi.slot_map(w) >= 0))
+    # x, three window rows read, three written, y; the taps once
+    nbytes = live * C * es * 8 + C * 4 * es
+    log(f"conv update (W=4, C={C}, B={w.B}): {ms * 1e3:.2f} us/launch, "
+        f"{nbytes / 1e6:.2f} MB/launch ({nbytes / (ms / 1e3) / 1e9:.0f} GB/s)")
+    return dict(kernel_ms=ms, bytes_per_launch=nbytes)
 
 
 def bench_packed(w, R, steps, dev, log):
@@ -456,6 +503,8 @@ def main():
     repk = bench_replay(gi.C7, R, steps, warmup, dev, log)
     w_fe = dataclasses.replace(w, qk_raw=True)
     repf = bench_replay(w_fe, R, steps, warmup, dev, log, front_end=True)
+    repc = bench_replay(w_fe, R, steps, warmup, dev, log, front_end=True, conv=True)
+    cv = bench_conv(w_fe, R, steps, dev, log)
     pkk = bench_packed(gi.C7, R, steps, dev, log)
     wf = bench_window_fold(gi.C5, R, max(4, steps // 8), dev, log)
     ll = bench_lossless(gi.C6, R, max(4, steps // 8), dev, log)
@@ -539,6 +588,18 @@ def main():
             "replay_kernel_us": repf["kernel_ms"] * 1e3,
             "replay_gbs": repf["bytes_per_launch"] / (repf["kernel_ms"] / 1e3) / 1e9,
             "vs_plain_replay_kernel": rep["kernel_ms"] / repf["kernel_ms"],
+        },
+        "front_end_conv_c2": {
+            "note": ("the front end with the causal convolution: per layer, the convolution "
+                     "(width 4, SiLU) of a raw packed mixed_qkv row, then the replay decode "
+                     "reading the convolved row with q/k normalised in the kernel"),
+            "step_us": repc["ms_per_step"] * 1e3,
+            "head_steps_per_s": repc["head_steps_per_s"],
+            "conv_plus_decode_us_per_layer": repc["kernel_ms"] * 1e3,
+            "conv_kernel_us": cv["kernel_ms"] * 1e3,
+            "conv_bytes_per_launch": cv["bytes_per_launch"],
+            "conv_gbs": cv["bytes_per_launch"] / (cv["kernel_ms"] / 1e3) / 1e9,
+            "vs_plain_replay_step": rep["ms_per_step"] / repc["ms_per_step"],
         },
         "verify_window_c5": wf,
         "lossless_verify_c6": ll,

@@ -13,6 +13,8 @@ Draws (per row, token and head), as the workloads specify:
                                                       (per v-head and key channel
                                                       for a per-key gate, KDA)
   beta = sigmoid(N(0, 1))                             delta-rule strength
+  conv front end: raw packed row x ~ N(0, 1), taps ~ N(0, 1/W), first
+  window ~ N(0, 1)
 The draws are cast to the workload's I/O dtype; consumers that need the exact
 values the device sees should use `as_f64`, which upcasts the rounded values.
 
@@ -287,6 +289,39 @@ def random_ring(w: Workload, seed_tag: int = 0, full: bool = False) -> RingConte
     else:
         wp = r.integers(0, w.L + 1, size=w.N).astype(np.int32)
     return RingContents(ckpt, cast(d, w.ring), cast(k, w.ring), g, wp, w.ring)
+
+
+# ---------------------------------------------------------------- conv front end
+
+@dataclass
+class ConvInputs:
+    """Raw mixed_qkv rows, taps and a first window for the causal convolution
+    in front of the decode (storage dtypes, bf16 as bits)."""
+    x: np.ndarray      # [steps, B, C]
+    w: np.ndarray      # [C, W]
+    state: np.ndarray  # [N, W-1, C]
+    dtype: str
+
+    def f64(self):
+        return (as_f64(self.x, self.dtype), as_f64(self.w, self.dtype),
+                as_f64(self.state, self.dtype))
+
+
+def conv_channels(w: Workload) -> int:
+    """Channels of the packed mixed_qkv row, 2*Hk*dk + Hv*dv."""
+    return 2 * w.Hk * w.dk + w.Hv * w.dv
+
+
+def conv_inputs(w: Workload, steps: int, W: int = 4, C: Optional[int] = None,
+                seed_tag: int = 0) -> ConvInputs:
+    """x ~ N(0, 1) per channel (raw projection outputs), taps ~ N(0, 1/W) (a
+    filter that keeps the input's scale), first window ~ N(0, 1)."""
+    C = conv_channels(w) if C is None else C
+    r = _rng(w.seed, 6, seed_tag)
+    x = r.standard_normal((steps, w.B, C), dtype=np.float32)
+    taps = (r.standard_normal((C, W), dtype=np.float32) / np.float32(np.sqrt(W))).astype(np.float32)
+    st = r.standard_normal((w.N, W - 1, C), dtype=np.float32)
+    return ConvInputs(cast(x, w.qkv), cast(taps, w.qkv), cast(st, w.qkv), w.qkv)
 
 
 def garbage_like(shape, dtype: str, seed: int = 7) -> np.ndarray:

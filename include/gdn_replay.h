@@ -304,6 +304,47 @@ gdn_status gdn_replay_fold(const gdn_shape *shape, const int32_t *slot_idx,
 gdn_status gdn_replay_reset(const gdn_shape *shape, const int32_t *slot_idx,
                             int32_t *write_pos, int32_t *err_flags, void *stream);
 
+/*
+ * gdn_conv_update -- the causal convolution step in front of the decode
+ * (ReplaySSM blog, section 3.1: the decode path first updates the causal
+ * convolution and hands the convolved packed row to the kernel; SGLang PR
+ * #36821, Technical principle: x_hat_t = SiLU(w * x_{t-3:t}), a depthwise
+ * convolution over the current input and the three before it, then SiLU).
+ * Per row b with slot s = slot_idx[b] >= 0 and channel c < C, with the W
+ * inputs z_0..z_{W-1} of the window, oldest first,
+ *     z_i = conv_state[s, i, c] (i < W-1),  z_{W-1} = x[b, c]:
+ *     acc     = sum_{i<W} w[c, i] z_i      fp32, one fma per tap, i ascending
+ *     y[b, c] = acc / (1 + exp(-acc))      SiLU in fp32, rounded to dtype
+ *     conv_state[s, i, c] <- z_{i+1}       (i < W-1): the window moves by one
+ * Tap W-1 multiplies the current input. Padding rows (s < 0) get y = 0 and
+ * leave every state untouched; s >= N sets GDN_EF_SLOT_RANGE and the row is
+ * handled as padding. The non-negative slots of one call must be distinct.
+ * Feed y to the decode as its packed mixed_qkv row (the row strides of
+ * gdn_shape, with qk_norm = 1 to normalise q and k in the kernel).
+ *   x           (device) dtype [B, C], row b at x + b * x_row_stride.
+ *   w           (device) dtype [C, W], the taps of channel c contiguous.
+ *   conv_state  (device) dtype [N, W-1, C], read and written (rows s of live
+ *               rows only).
+ *   y           (device) dtype [B, C], row b at y + b * y_row_stride; written
+ *               for every row. May not overlap x or conv_state.
+ * Sizes: C a multiple of 4, 4 <= C <= 2^20; 2 <= W <= 4; B >= 0, N >= 1;
+ * dtype GDN_F32 or GDN_BF16; every base pointer and row 16-byte aligned for
+ * fp32, 8-byte aligned for bf16.
+ */
+typedef struct {
+    int32_t B;            /* rows in the call                                    */
+    int32_t N;            /* slots in the conv-state pool                        */
+    int32_t C;            /* channels (2*Hk*dk + Hv*dv for the mixed_qkv row)    */
+    int32_t W;            /* convolution width (taps), 2..4                      */
+    int32_t dtype;        /* gdn_dtype of x, w, conv_state and y                 */
+    int32_t x_row_stride; /* elements between rows of x; 0 = dense (C)           */
+    int32_t y_row_stride; /* elements between rows of y; 0 = dense (C)           */
+} gdn_conv_shape;
+
+gdn_status gdn_conv_update(const gdn_conv_shape *shape, const void *x, const void *w,
+                           void *conv_state, const int32_t *slot_idx, void *y,
+                           int32_t *err_flags, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *gdn_status_string(gdn_status status);
 

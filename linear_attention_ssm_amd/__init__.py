@@ -37,6 +37,11 @@ class gdn_shape(ctypes.Structure):
                  "qk_norm")]
 
 
+class gdn_conv_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "N", "C", "W", "dtype", "x_row_stride", "y_row_stride")]
+
+
 class GdnError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {lib().gdn_status_string(status).decode()} (status {status})")
@@ -58,13 +63,14 @@ _lib.gdn_replay_advance.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_commit.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_fold.argtypes = [_S] + [_P] * 8
 _lib.gdn_replay_reset.argtypes = [_S] + [_P] * 4
+_lib.gdn_conv_update.argtypes = [ctypes.POINTER(gdn_conv_shape)] + [_P] * 7
 for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_decode_advance", "gdn_replay_advance",
-           "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_reset"):
+           "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_reset", "gdn_conv_update"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 6
+ABI_VERSION = 7
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -338,6 +344,42 @@ def gdn_replay_reset(slot_idx, write_pos, err_flags=None, stream=None):
 
 
 # ------------------------------------------------------------------ prepared calls
+
+def gdn_conv_update(x, w, conv_state, slot_idx, y=None, err_flags=None, stream=None):
+    """Causal convolution step in front of the decode; see gdn_conv_update in
+    gdn_replay.h. x [B, C] fp32 or bf16 (rows may be strided, channels dense);
+    w [C, W] and conv_state [N, W-1, C] (updated in place) of x's dtype;
+    slot_idx [B] int32. Returns y [B, C] (SiLU of the tap sum), the convolved
+    mixed_qkv row for the decode."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"x has dtype {x.dtype}")
+    dev = x.device
+    if not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a [B, C] device tensor with dense channels")
+    B, C = x.shape
+    xs = int(x.stride(0)) if B > 1 else C
+    _check(w, "w", x.dtype, 2, dev)
+    _check(conv_state, "conv_state", x.dtype, 3, dev)
+    _check(slot_idx, "slot_idx", torch.int32, 1, dev)
+    W = w.shape[1]
+    if w.shape[0] != C or tuple(conv_state.shape[1:]) != (W - 1, C) or slot_idx.shape != (B,):
+        raise ValueError("inconsistent x / w / conv_state / slot_idx shapes")
+    if y is None:
+        y = torch.empty((B, C), dtype=x.dtype, device=dev)
+    else:
+        if not isinstance(y, torch.Tensor) or y.dtype != x.dtype or y.device != dev \
+                or tuple(y.shape) != (B, C) or y.stride(1) != 1:
+            raise ValueError("y must be a [B, C] device tensor of x's dtype with dense channels")
+    ys = int(y.stride(0)) if B > 1 else C
+    sh = gdn_conv_shape(B, conv_state.shape[0], C, W, _DT[x.dtype], 0 if xs == C else xs,
+                        0 if ys == C else ys)
+    _raise(_lib.gdn_conv_update(ctypes.byref(sh), _ptr(x), _ptr(w), _ptr(conv_state),
+                                _ptr(slot_idx), _ptr(y), _ptr(err_flags), _stream(stream)),
+           "gdn_conv_update")
+    return y
+
 
 class Prepared:
     """A library call with its arguments checked and marshalled once, for

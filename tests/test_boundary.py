@@ -8,7 +8,8 @@ import pytest
 import linear_attention_ssm_amd as gdn
 from linear_attention_ssm_amd import gdn_shape
 
-EXPECTED = ["gdn_abi_version", "gdn_packed_decode", "gdn_replay_advance", "gdn_replay_commit",
+EXPECTED = ["gdn_abi_version", "gdn_conv_update", "gdn_packed_decode", "gdn_replay_advance",
+            "gdn_replay_commit",
             "gdn_replay_decode", "gdn_replay_decode_advance", "gdn_replay_fold",
             "gdn_replay_reset", "gdn_status_string"]
 
@@ -29,7 +30,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 6
+    assert lib.gdn_abi_version() == 7
     for st in range(4):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -194,3 +195,40 @@ def test_binding_reads_row_strides_off_views():
         _row_stride(torch.zeros(B, T, dk, Hk).transpose(2, 3), "q")     # [H, d] not dense
     with pytest.raises(ValueError):
         _row_stride(torch.zeros(T, B, Hk, dk).transpose(0, 1), "q")     # rows not in (b, t) order
+
+
+def test_conv_update_validates():
+    """gdn_conv_update's host checks (sizes, dtype, strides, alignment,
+    overlap), all before any launch."""
+    lib = gdn.lib()
+
+    def call(p=None, **kw):
+        d = dict(B=2, N=3, C=64, W=4, dtype=gdn.GDN_BF16, x_row_stride=0, y_row_stride=0)
+        d.update(kw)
+        sh = gdn.gdn_conv_shape(**d)
+        p = list(FAKE[:5]) if p is None else p
+        return lib.gdn_conv_update(ctypes.byref(sh), *p, None, None)
+    assert call(C=62) == gdn.GDN_ERR_UNSUPPORTED                 # not a multiple of 4
+    assert call(C=0) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(W=1) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(W=5) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(dtype=gdn.GDN_F16) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(B=-1) == gdn.GDN_ERR_INVALID_ARG
+    assert call(N=0) == gdn.GDN_ERR_INVALID_ARG
+    assert call(x_row_stride=60) == gdn.GDN_ERR_INVALID_ARG     # rows overlap
+    assert call(y_row_stride=66) == gdn.GDN_ERR_INVALID_ARG     # rows not 8-byte aligned
+    assert call(dtype=gdn.GDN_F32, x_row_stride=70) == gdn.GDN_ERR_INVALID_ARG
+    assert call(B=0) == gdn.GDN_OK
+    for i in range(5):
+        p = list(FAKE[:5])
+        p[i] = None
+        assert call(p) == gdn.GDN_ERR_INVALID_ARG, i
+    p = list(FAKE[:5])
+    p[0] = ctypes.c_void_p(FAKE[0].value + 4)                   # x not 8-byte aligned
+    assert call(p) == gdn.GDN_ERR_INVALID_ARG
+    p = list(FAKE[:5])
+    p[4] = ctypes.c_void_p(FAKE[0].value + 64)                  # y overlaps x
+    assert call(p) == gdn.GDN_ERR_INVALID_ARG
+    p = list(FAKE[:5])
+    p[4] = FAKE[2]                                              # y is the state
+    assert call(p) == gdn.GDN_ERR_INVALID_ARG
