@@ -102,3 +102,63 @@ def test_prepared_call_matches_plain_call(gdn):
     o_q = gdn.gdn_packed_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slots, st)
     torch.cuda.synchronize()
     assert torch.equal(bits(o_p), bits(o_q)) and torch.equal(bits(pa.ckpt), bits(st))
+
+
+def test_graph_conv_front_end_matches_eager(gdn):
+    """The front end with the convolution under capture: per layer
+    gdn_conv_update on a raw packed row, then the replay decode reading the
+    convolved row with q/k normalised in the kernel; the last layer advances
+    the cursors. Every replay (eager work between) equals the eager run on
+    twin buffers bit for bit, conv windows included."""
+    w = gi.scaled(gi.C2, name="graph_conv", B=8, N=12, L=4, steps=6, stagger=False,
+                  permute=True, n_pad=1, qk_raw=True, seed=73)
+    S0 = gi.initial_state(w)
+    slots = to_dev(gi.slot_map(w))
+    ci = gi.conv_inputs(w, w.steps, W=4)
+    taps = to_dev(ci.w, "bf16")
+    nq = w.Hk * w.dk
+    xi = dev_inputs(gi.step_inputs(w, 0))             # g and beta
+    xs = to_dev(ci.x[0], "bf16")
+
+    def twin():
+        return dict(pools=[Pool(w, S0), Pool(w, S0)],
+                    cst=[to_dev(ci.state, "bf16"), to_dev(ci.state, "bf16")],
+                    y=[torch.empty_like(xs), torch.empty_like(xs)],
+                    o=torch.empty((w.B, 1, w.Hv, w.dv), dtype=torch.bfloat16, device=DEV),
+                    wp=torch.zeros(w.N, dtype=torch.int32, device=DEV),
+                    arrive=gdn.arrive_workspace(w.B, DEV))
+
+    def forward(t):
+        for i, p in enumerate(t["pools"]):
+            y = gdn.gdn_conv_update(xs, taps, t["cst"][i], slots, y=t["y"][i])
+            q = y[:, :nq].view(w.B, 1, w.Hk, w.dk)
+            k = y[:, nq:2 * nq].view(w.B, 1, w.Hk, w.dk)
+            v = y[:, 2 * nq:].view(w.B, 1, w.Hv, w.dv)
+            if i == len(t["pools"]) - 1:
+                gdn.gdn_replay_decode_advance(q, k, v, xi.g, xi.beta, slots, p.ckpt, p.ring_d,
+                                              p.ring_k, p.ring_g, t["wp"], t["arrive"],
+                                              o=t["o"], qk_norm=True)
+            else:
+                gdn.gdn_replay_decode(q, k, v, xi.g, xi.beta, slots, p.ckpt, p.ring_d,
+                                      p.ring_k, p.ring_g, t["wp"], o=t["o"], qk_norm=True)
+
+    e, gd = twin(), twin()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        forward(gd)
+    torch.cuda.synchronize()
+    for step in range(w.steps):                    # crosses a natural flush (L = 4)
+        forward(e)
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (e["o"].float() * 2).sum().item()      # unrelated eager work between replays
+        assert torch.equal(bits(e["o"]), bits(gd["o"])), f"replay {step}: outputs differ"
+        for i in range(2):
+            assert torch.equal(bits(e["cst"][i]), bits(gd["cst"][i])), f"replay {step}: window"
+            assert torch.equal(bits(e["y"][i]), bits(gd["y"][i]))
+            for a, b in zip(_state(e["pools"][i]), _state(gd["pools"][i])):
+                assert torch.equal(a, b), f"replay {step}: state differs"
+        assert torch.equal(e["wp"], gd["wp"])
