@@ -326,7 +326,7 @@ gdn_status gdn_replay_reset(const gdn_shape *shape, const int32_t *slot_idx,
  *   conv_state  (device) dtype [N, W-1, C], read and written (rows s of live
  *               rows only).
  *   y           (device) dtype [B, C], row b at y + b * y_row_stride; written
- *               for every row. May not overlap x or conv_state.
+ *               for every row. x, y and conv_state must not overlap.
  * Sizes: C a multiple of 4, 4 <= C <= 2^20; 2 <= W <= 4; B >= 0, N >= 1;
  * dtype GDN_F32 or GDN_BF16; every base pointer and row 16-byte aligned for
  * fp32, 8-byte aligned for bf16.

@@ -119,7 +119,8 @@ extern "C" gdn_status gdn_conv_update(const gdn_conv_shape* s, const void* x, co
   const size_t x_bytes = (static_cast<size_t>(s->B - 1) * xs + s->C) * es;
   const size_t y_bytes = (static_cast<size_t>(s->B - 1) * ys + s->C) * es;
   const size_t st_bytes = static_cast<size_t>(s->N) * (s->W - 1) * s->C * es;
-  if (overlap(y, y_bytes, x, x_bytes) || overlap(y, y_bytes, conv_state, st_bytes))
+  if (overlap(y, y_bytes, x, x_bytes) || overlap(y, y_bytes, conv_state, st_bytes) ||
+      overlap(x, x_bytes, conv_state, st_bytes))
     return GDN_ERR_INVALID_ARG;
   ConvArgs a{};
   a.x = x; a.w = w; a.state = conv_state; a.slot = slot_idx; a.y = y; a.err = err_flags;

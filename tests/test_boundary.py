@@ -232,3 +232,6 @@ def test_conv_update_validates():
     p = list(FAKE[:5])
     p[4] = FAKE[2]                                              # y is the state
     assert call(p) == gdn.GDN_ERR_INVALID_ARG
+    p = list(FAKE[:5])
+    p[0] = ctypes.c_void_p(FAKE[2].value + 256)                 # x inside the state
+    assert call(p) == gdn.GDN_ERR_INVALID_ARG
