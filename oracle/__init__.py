@@ -18,6 +18,8 @@ Parts:
   O8  l2norm_qk         the decode's front end: q/k L2-normalised, q scaled
   O9  conv_update       the causal convolution (width W, SiLU) and its state
                         in front of the decode
+  O10 kda_gates         the per-key gate and beta activations in front of a
+                        per-key-gate (KDA) decode
   O2, O4 take the per-key gate as well (ReplayModel(gate="key"), window_ref
   with g [B, T, Hv, dk]).
 
@@ -233,6 +235,24 @@ def conv_update(x, w, conv_state: np.ndarray, slot) -> np.ndarray:
         y[b] = acc / (1.0 + np.exp(-acc))
         conv_state[s] = window[1:]
     return y
+
+
+# ------------------------------------------------------------------ O10
+
+def kda_gates(a, b, A, dt_bias, lower_bound: float):
+    """O10: the gate activations in front of a per-key-gate (KDA) decode
+    (SGLang PR #36821, Technical principle): per key channel the log-decay
+    g = lower_bound * sigmoid(exp(A_h) * (a + dt_bias_{h,c})), and per head
+    beta = sigmoid(b), in fp64. a [B, T, Hv, dk], b [B, T, Hv], A [Hv],
+    dt_bias [Hv, dk], lower_bound < 0 a scalar. Returns (g, beta)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    A = np.asarray(A, np.float64)
+    dt = np.asarray(dt_bias, np.float64)
+    z = np.exp(A)[:, None] * (a + dt)
+    g = lower_bound / (1.0 + np.exp(-z))
+    beta = 1.0 / (1.0 + np.exp(-b))
+    return g, beta
 
 
 # ------------------------------------------------------------------ O3
