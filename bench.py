@@ -300,6 +300,27 @@ def bench_conv(w, R, steps, dev, log):
     return dict(kernel_ms=ms, bytes_per_launch=nbytes)
 
 
+def bench_gates(w, R, steps, dev, log):
+    """The per-key gate and beta activations (gdn_kda_gates) for one decode
+    step of the workload: R launches (one per layer) in a graph."""
+    import torch
+    import linear_attention_ssm_amd as gdn
+    r = np.random.default_rng(w.seed)
+    mk = lambda *shape: torch.from_numpy(r.standard_normal(shape).astype(np.float32)).to(dev)
+    ins = [(mk(w.B, 1, w.Hv, w.dk), mk(w.B, 1, w.Hv), mk(w.Hv), mk(w.Hv, w.dk)) for _ in range(R)]
+    outs = [(torch.empty_like(a), torch.empty_like(b)) for a, b, _, _ in ins]
+
+    def run():
+        for (a, b, A, dt), (g, beta) in zip(ins, outs):
+            gdn.gdn_kda_gates(a, b, A, dt, -5.0, g=g, beta=beta)
+
+    ms = time_graph(graph_of(run), steps) / R
+    nbytes = w.B * w.Hv * (w.dk * 8 + 8) + w.Hv * (w.dk + 1) * 4
+    log(f"kda gates (B={w.B}, Hv={w.Hv}, dk={w.dk}): {ms * 1e3:.2f} us/launch, "
+        f"{nbytes / 1e6:.2f} MB/launch")
+    return dict(kernel_ms=ms, bytes_per_launch=nbytes)
+
+
 def bench_packed(w, R, steps, dev, log):
     import torch
     import linear_attention_ssm_amd as gdn
@@ -506,6 +527,7 @@ def main():
     repc = bench_replay(w_fe, R, steps, warmup, dev, log, front_end=True, conv=True)
     cv = bench_conv(w_fe, R, steps, dev, log)
     pkk = bench_packed(gi.C7, R, steps, dev, log)
+    gts = bench_gates(gi.C7, R, steps, dev, log)
     wf = bench_window_fold(gi.C5, R, max(4, steps // 8), dev, log)
     ll = bench_lossless(gi.C6, R, max(4, steps // 8), dev, log)
     if args.profile_pass:
@@ -580,6 +602,8 @@ def main():
             "packed_bytes_per_launch": pkk["bytes_per_launch"],
             "replay_vs_packed_kernel": pkk["kernel_ms"] / repk["kernel_ms"],
             "replay_vs_packed": repk["head_steps_per_s"] / pkk["head_steps_per_s"],
+            "gates_kernel_us": gts["kernel_ms"] * 1e3,
+            "gates_bytes_per_launch": gts["bytes_per_launch"],
         },
         "front_end_c2": {
             "note": ("the standard workload with q, k, v read from the packed mixed_qkv row "

@@ -345,6 +345,29 @@ gdn_status gdn_conv_update(const gdn_conv_shape *shape, const void *x, const voi
                            void *conv_state, const int32_t *slot_idx, void *y,
                            int32_t *err_flags, void *stream);
 
+/*
+ * gdn_kda_gates -- the gate activations in front of a per-key-gate (KDA)
+ * decode (SGLang PR #36821, Technical principle): from the raw projections,
+ * per (row b, token t, value head h) and key channel c,
+ *     g[b,t,h,c]  = lower_bound * sigmoid(exp(A[h]) * (a[b,t,h,c] + dt_bias[h,c]))
+ *     beta[b,t,h] = sigmoid(b_raw[b,t,h])
+ * in fp32 (sigmoid(x) = 1 / (1 + exp(-x))). g is a log-decay in
+ * [lower_bound, 0] and feeds gdn_replay_decode / gdn_packed_decode with
+ * gate = GDN_GATE_KEY, beta their beta.
+ *   a, g     (device) fp32 [B, T, Hv, dk], 16-byte aligned.
+ *   b, beta  (device) fp32 [B, T, Hv].
+ *   A        (device) fp32 [Hv]; dt_bias (device) fp32 [Hv, dk], 16-byte aligned.
+ * Sizes: dk a multiple of 4, 4..1024; lower_bound < 0.
+ */
+typedef struct {
+    int32_t B, T, Hv, dk;
+    float lower_bound;    /* l < 0: the log-decay's lower bound */
+} gdn_gate_shape;
+
+gdn_status gdn_kda_gates(const gdn_gate_shape *shape, const float *a, const float *b,
+                         const float *A, const float *dt_bias, float *g, float *beta,
+                         void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *gdn_status_string(gdn_status status);
 

@@ -42,6 +42,11 @@ class gdn_conv_shape(ctypes.Structure):
                 ("B", "N", "C", "W", "dtype", "x_row_stride", "y_row_stride")]
 
 
+class gdn_gate_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hv", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("lower_bound", ctypes.c_float)]
+
+
 class GdnError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {lib().gdn_status_string(status).decode()} (status {status})")
@@ -64,13 +69,15 @@ _lib.gdn_replay_commit.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_fold.argtypes = [_S] + [_P] * 8
 _lib.gdn_replay_reset.argtypes = [_S] + [_P] * 4
 _lib.gdn_conv_update.argtypes = [ctypes.POINTER(gdn_conv_shape)] + [_P] * 7
+_lib.gdn_kda_gates.argtypes = [ctypes.POINTER(gdn_gate_shape)] + [_P] * 7
 for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_decode_advance", "gdn_replay_advance",
-           "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_reset", "gdn_conv_update"):
+           "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_reset", "gdn_conv_update",
+           "gdn_kda_gates"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 7
+ABI_VERSION = 8
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -379,6 +386,30 @@ def gdn_conv_update(x, w, conv_state, slot_idx, y=None, err_flags=None, stream=N
                                 _ptr(slot_idx), _ptr(y), _ptr(err_flags), _stream(stream)),
            "gdn_conv_update")
     return y
+
+
+def gdn_kda_gates(a, b, A, dt_bias, lower_bound: float, g=None, beta=None, stream=None):
+    """Gate activations in front of a per-key-gate decode; see gdn_kda_gates in
+    gdn_replay.h. a [B, T, Hv, dk], b [B, T, Hv], A [Hv], dt_bias [Hv, dk], all
+    fp32. Returns (g [B, T, Hv, dk], beta [B, T, Hv])."""
+    _check(a, "a", torch.float32, 4)
+    dev = a.device
+    B, T, Hv, dk = a.shape
+    _check(b, "b", torch.float32, 3, dev)
+    _check(A, "A", torch.float32, 1, dev)
+    _check(dt_bias, "dt_bias", torch.float32, 2, dev)
+    if tuple(b.shape) != (B, T, Hv) or tuple(A.shape) != (Hv,) or tuple(dt_bias.shape) != (Hv, dk):
+        raise ValueError("inconsistent a / b / A / dt_bias shapes")
+    g = torch.empty_like(a) if g is None else g
+    beta = torch.empty_like(b) if beta is None else beta
+    _check(g, "g", torch.float32, 4, dev)
+    _check(beta, "beta", torch.float32, 3, dev)
+    if g.shape != a.shape or beta.shape != b.shape:
+        raise ValueError("g and beta must have the shapes of a and b")
+    sh = gdn_gate_shape(B, T, Hv, dk, float(lower_bound))
+    _raise(_lib.gdn_kda_gates(ctypes.byref(sh), _ptr(a), _ptr(b), _ptr(A), _ptr(dt_bias), _ptr(g),
+                              _ptr(beta), _stream(stream)), "gdn_kda_gates")
+    return g, beta
 
 
 class Prepared:

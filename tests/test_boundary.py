@@ -8,8 +8,8 @@ import pytest
 import linear_attention_ssm_amd as gdn
 from linear_attention_ssm_amd import gdn_shape
 
-EXPECTED = ["gdn_abi_version", "gdn_conv_update", "gdn_packed_decode", "gdn_replay_advance",
-            "gdn_replay_commit",
+EXPECTED = ["gdn_abi_version", "gdn_conv_update", "gdn_kda_gates", "gdn_packed_decode",
+            "gdn_replay_advance", "gdn_replay_commit",
             "gdn_replay_decode", "gdn_replay_decode_advance", "gdn_replay_fold",
             "gdn_replay_reset", "gdn_status_string"]
 
@@ -30,7 +30,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 7
+    assert lib.gdn_abi_version() == 8
     for st in range(4):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -234,4 +234,28 @@ def test_conv_update_validates():
     assert call(p) == gdn.GDN_ERR_INVALID_ARG
     p = list(FAKE[:5])
     p[0] = ctypes.c_void_p(FAKE[2].value + 256)                 # x inside the state
+    assert call(p) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_kda_gates_validates():
+    lib = gdn.lib()
+
+    def call(p=None, **kw):
+        d = dict(B=2, T=1, Hv=4, dk=128, lower_bound=-5.0)
+        d.update(kw)
+        sh = gdn.gdn_gate_shape(**d)
+        p = list(FAKE[:6]) if p is None else p
+        return lib.gdn_kda_gates(ctypes.byref(sh), *p, None)
+    assert call(dk=6) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(dk=2048) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(lower_bound=0.0) == gdn.GDN_ERR_INVALID_ARG
+    assert call(lower_bound=float("nan")) == gdn.GDN_ERR_INVALID_ARG
+    assert call(T=0) == gdn.GDN_ERR_INVALID_ARG
+    assert call(B=0) == gdn.GDN_OK
+    for i in range(6):
+        p = list(FAKE[:6])
+        p[i] = None
+        assert call(p) == gdn.GDN_ERR_INVALID_ARG, i
+    p = list(FAKE[:6])
+    p[0] = ctypes.c_void_p(FAKE[0].value + 8)           # a not 16-byte aligned
     assert call(p) == gdn.GDN_ERR_INVALID_ARG
