@@ -12,7 +12,6 @@
 // never rounded. HBM-bound: 2 W C es bytes per row plus the taps once.
 #include <hip/hip_runtime.h>
 
-#include <algorithm>
 #include <cstdint>
 
 #include "gdn_device.h"
