@@ -86,3 +86,25 @@ def test_gates_then_kda_decode(gdn):
             else:
                 wp[s] += 1
     log(f"[gates -> kda decode] o {worst:.2e}")
+
+
+def test_gates_then_kda_verify_window(gdn):
+    """A 5-token verify window of the per-key-gate decode fed by the kernel's
+    gates, against O10 -> O5 -> O4 (the window token by token through O6)."""
+    from oracle import window_ref
+    w = gi.scaled(gi.C7, name="gates_window", B=6, N=6, L=8, T=5, steps=1, seed=951)
+    S0 = gi.initial_state(w)
+    slots = gi.slot_map(w)
+    pool = Pool(w, S0)
+    x = gi.step_inputs(w, 0)
+    a, b, A, dt = gate_inputs(7100, w.B, w.T, w.Hv, w.dk)
+    g, beta = gdn.gdn_kda_gates(to_dev(a), to_dev(b), to_dev(A), to_dev(dt), -5.0)
+    xi = [to_dev(arr, x.dtype) for arr in (x.q, x.k, x.v)]
+    o = gdn.gdn_replay_decode(*xi, g, beta, to_dev(slots), pool.ckpt, pool.ring_d, pool.ring_k,
+                              pool.ring_g, pool.write_pos, window=True)
+    g_ref, b_ref = kda_gates(a, b, A, dt, -5.0)
+    q64, k64, v64, _, _ = x.f64()
+    o_ref = window_ref(S0.astype(np.float64), slots, q64, k64, v64, quantize(g_ref, "f32"),
+                       quantize(b_ref, "f32"))
+    e = rel_err(to_f64(o), o_ref)
+    assert e <= tol_o(w), f"window rel err {e:.3e}"
