@@ -219,32 +219,17 @@ def bench_replay(w, R, steps, warmup, dev, log, front_end=False, conv=False):
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     o = torch.empty((w.B, 1, w.Hv, w.dv), dtype=torch.bfloat16, device=dev)
 
-    arrive = gdn.arrive_workspace(w.B, dev)
-    if conv == "fused":
-        conv_arrive = gdn.conv_arrive_workspace(w.B, w.Hk, dev)
-
-        def fused(i, ls, ff, adv):
-            _, _, _, g, beta = ins[i % len(ins)]
-            gdn.gdn_replay_decode_conv(xraw[i], taps[i], cstate[i], conv_arrive, g, beta, slot_t,
-                                       ls.state, ls.ring_d, ls.ring_k, ls.ring_g, wp, w.Hk, w.dk,
-                                       force_flush=ff, o=o, arrive=arrive if adv else None,
-                                       err_flags=err)
-
     def decodes(ff):
         for i, ls in enumerate(layers):
-            if conv == "fused":
-                fused(i, ls, ff, False)
-                continue
             q, k, v, g, beta = qkv_of(i)
             gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
                                   ls.ring_g, wp, force_flush=ff, o=o, err_flags=err, **fe)
 
+    arrive = gdn.arrive_workspace(w.B, dev)
+
     def forward(ff):
         # the last layer's decode advances the cursors (fused advance)
         for i, ls in enumerate(layers):
-            if conv == "fused":
-                fused(i, ls, ff, i == len(layers) - 1)
-                continue
             q, k, v, g, beta = qkv_of(i)
             if i < len(layers) - 1:
                 gdn.gdn_replay_decode(q, k, v, g, beta, slot_t, ls.state, ls.ring_d, ls.ring_k,
@@ -279,8 +264,7 @@ def bench_replay(w, R, steps, warmup, dev, log, front_end=False, conv=False):
     live = int(np.count_nonzero(slots >= 0))
     mean_p = float(np.mean([p for p, _ in cur]))
     flush_frac = float(np.mean([fl for _, fl in cur]))
-    fe_tag = (", fused conv + front end" if conv == "fused" else ", conv + front end" if conv
-              else ", front end" if front_end else "")
+    fe_tag = ", conv + front end" if conv else (", front end" if front_end else "")
     log(f"replay [{w.state} state, {w.gate} gate{fe_tag}]: {ms_step * 1e3:.1f} us/step ({R} layers, fused advance), decode kernel "
         f"{ms_dec * 1e3:.2f} us, {bytes_launch / 1e6:.2f} MB/launch, "
         f"mean p {mean_p:.2f}, flush frac {flush_frac:.4f}")
@@ -541,7 +525,6 @@ def main():
     w_fe = dataclasses.replace(w, qk_raw=True)
     repf = bench_replay(w_fe, R, steps, warmup, dev, log, front_end=True)
     repc = bench_replay(w_fe, R, steps, warmup, dev, log, front_end=True, conv=True)
-    repcf = bench_replay(w_fe, R, steps, warmup, dev, log, front_end=True, conv="fused")
     cv = bench_conv(w_fe, R, steps, dev, log)
     pkk = bench_packed(gi.C7, R, steps, dev, log)
     gts = bench_gates(gi.C7, R, steps, dev, log)
@@ -641,14 +624,6 @@ def main():
             "conv_bytes_per_launch": cv["bytes_per_launch"],
             "conv_gbs": cv["bytes_per_launch"] / (cv["kernel_ms"] / 1e3) / 1e9,
             "vs_plain_replay_step": rep["ms_per_step"] / repc["ms_per_step"],
-            "fused": {
-                "note": ("gdn_replay_decode_conv: convolution, q/k normalisation and decode in "
-                         "one launch per layer"),
-                "step_us": repcf["ms_per_step"] * 1e3,
-                "head_steps_per_s": repcf["head_steps_per_s"],
-                "kernel_us": repcf["kernel_ms"] * 1e3,
-                "vs_separate_step": repc["ms_per_step"] / repcf["ms_per_step"],
-            },
         },
         "verify_window_c5": wf,
         "lossless_verify_c6": ll,

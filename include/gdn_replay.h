@@ -368,43 +368,6 @@ gdn_status gdn_kda_gates(const gdn_gate_shape *shape, const float *a, const floa
                          const float *A, const float *dt_bias, float *g, float *beta,
                          void *stream);
 
-/*
- * gdn_replay_decode_conv -- a decode step (T = 1, window = 0) with the causal
- * convolution of gdn_conv_update (width 4) and the q/k normalisation fused in
- * front (the front end of ReplaySSM blog, section 3.1, in one launch). The
- * kernel reads the raw packed row x [B, C], C = 2*Hk*dk + Hv*dv, convolves
- * q, k and v with the row's window exactly as gdn_conv_update does (the same
- * fp32 operations, the result rounded to qkv_dtype), normalises q and k as
- * qk_norm = 1 does, and runs the replay decode step on them. Every output,
- * checkpoint, ring entry, cursor and window equals what gdn_conv_update
- * followed by gdn_replay_decode (or gdn_replay_decode_advance) with qk_norm
- * on the convolved row leaves, bit for bit. Rows that are padding or in
- * error keep their window.
- *   shape        T = 1, window = 0, qk_norm = 1; qk_row_stride is the row
- *                stride of x (0 = dense C), v_row_stride 0 or the same;
- *                qkv_dtype GDN_F32 or GDN_BF16 (the dtype of x, conv_w and
- *                conv_state).
- *   x            (device) [B, C] raw packed rows, read only.
- *   conv_w       (device) [C, 4] taps; conv_state (device) [N, 3, C], the
- *                windows, moved by one input for every live row. Both
- *                aligned to four elements.
- *   conv_arrive  (device) int32 [B * Hk * GDN_ARRIVE_STRIDE] workspace,
- *                128-byte aligned, all zero before the call; the call leaves
- *                it zero. The workgroups of a (row, key head) all read its
- *                q/k window; they count themselves in and the last one moves
- *                the window. Two calls sharing conv_arrive must not overlap.
- *   arrive       (device) NULL for a plain decode step (write_pos only
- *                read), or the workspace of gdn_replay_decode_advance to
- *                fuse the cursor advance too (write_pos read and written).
- * Every other argument as gdn_replay_decode.
- */
-gdn_status gdn_replay_decode_conv(const gdn_shape *shape, const void *x, const void *conv_w,
-                                  void *conv_state, int32_t *conv_arrive, const float *g,
-                                  const float *beta, const int32_t *slot_idx, void *ckpt,
-                                  void *ring_d, void *ring_k, float *ring_g, int32_t *write_pos,
-                                  const int32_t *force_flush, void *o, int32_t *arrive,
-                                  int32_t *err_flags, void *stream);
-
 /* Static description of a status code (never NULL). */
 const char *gdn_status_string(gdn_status status);
 

@@ -70,15 +70,14 @@ _lib.gdn_replay_fold.argtypes = [_S] + [_P] * 8
 _lib.gdn_replay_reset.argtypes = [_S] + [_P] * 4
 _lib.gdn_conv_update.argtypes = [ctypes.POINTER(gdn_conv_shape)] + [_P] * 7
 _lib.gdn_kda_gates.argtypes = [ctypes.POINTER(gdn_gate_shape)] + [_P] * 7
-_lib.gdn_replay_decode_conv.argtypes = [_S] + [_P] * 17
 for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_decode_advance", "gdn_replay_advance",
            "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_reset", "gdn_conv_update",
-           "gdn_kda_gates", "gdn_replay_decode_conv"):
+           "gdn_kda_gates"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 9
+ABI_VERSION = 8
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -411,65 +410,6 @@ def gdn_kda_gates(a, b, A, dt_bias, lower_bound: float, g=None, beta=None, strea
     _raise(_lib.gdn_kda_gates(ctypes.byref(sh), _ptr(a), _ptr(b), _ptr(A), _ptr(dt_bias), _ptr(g),
                               _ptr(beta), _stream(stream)), "gdn_kda_gates")
     return g, beta
-def conv_arrive_workspace(B: int, Hk: int, device) -> torch.Tensor:
-    """The zeroed counter workspace of gdn_replay_decode_conv (one 128-byte
-    line per (row, key head)); every call leaves it zero again."""
-    return torch.zeros(B * Hk * ARRIVE_STRIDE, dtype=torch.int32, device=device)
-
-
-def gdn_replay_decode_conv(x, conv_w, conv_state, conv_arrive, g, beta, slot_idx, ckpt, ring_d,
-                           ring_k, ring_g, write_pos, Hk, dk, force_flush=None, o=None,
-                           arrive=None, err_flags=None, stream=None):
-    """Decode step with the causal convolution (width 4) and the q/k
-    normalisation fused in front; see gdn_replay_decode_conv in gdn_replay.h.
-    x [B, C] raw packed rows (C = 2*Hk*dk + Hv*dv; rows may be strided, channels
-    dense), conv_w [C, 4], conv_state [N, 3, C] (moved in place), conv_arrive
-    from conv_arrive_workspace; arrive (gdn_replay_decode_advance's workspace)
-    fuses the cursor advance. Returns o [B, 1, Hv, dv]."""
-    if not isinstance(x, torch.Tensor) or x.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("x must be an fp32 or bf16 torch.Tensor")
-    dev = x.device
-    if not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be a [B, C] device tensor with dense channels")
-    B, C = x.shape
-    _check(ckpt, "ckpt", STATE_DTYPES, 4, dev)
-    Hv, dv = ckpt.shape[1], ckpt.shape[2]
-    if C != 2 * Hk * dk + Hv * dv:
-        raise ValueError(f"x has {C} channels, expected 2*Hk*dk + Hv*dv")
-    xs = int(x.stride(0)) if B > 1 else C
-    _check(conv_w, "conv_w", x.dtype, 2, dev)
-    _check(conv_state, "conv_state", x.dtype, 3, dev)
-    _check(conv_arrive, "conv_arrive", torch.int32, 1, dev)
-    _check(g, "g", torch.float32, None, dev)
-    _check(beta, "beta", torch.float32, 3, dev)
-    _check(slot_idx, "slot_idx", torch.int32, 1, dev)
-    if tuple(conv_w.shape) != (C, 4) or tuple(conv_state.shape[1:]) != (3, C):
-        raise ValueError("conv_w must be [C, 4] and conv_state [N, 3, C]")
-    if conv_arrive.numel() < B * Hk * ARRIVE_STRIDE:
-        raise ValueError("conv_arrive is smaller than B * Hk * GDN_ARRIVE_STRIDE")
-    gate = GDN_GATE_KEY if g.dim() == 4 else GDN_GATE_HEAD
-    g_shape = (B, 1, Hv, dk) if gate == GDN_GATE_KEY else (B, 1, Hv)
-    if tuple(g.shape) != g_shape or tuple(beta.shape) != (B, 1, Hv) or slot_idx.shape != (B,):
-        raise ValueError("inconsistent x / g / beta / slot_idx shapes")
-    N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
-    if force_flush is not None:
-        _check(force_flush, "force_flush", torch.int32, 1, dev)
-        if force_flush.shape != (B,):
-            raise ValueError("force_flush must be [B]")
-    if arrive is not None:
-        _check(arrive, "arrive", torch.int32, 1, dev)
-    if err_flags is not None:
-        _check(err_flags, "err_flags", torch.int32, None, dev)
-    o = _out(o, B, 1, Hv, dv, x.dtype, dev)
-    sh = gdn_shape(B, 1, N, Hv, Hk, dk, dv, L, _DT[x.dtype], _DT[ring_d.dtype], 0,
-                   _DT[ckpt.dtype], 0, gate, 0 if xs == C else xs, 0, 1)
-    _raise(_lib.gdn_replay_decode_conv(ctypes.byref(sh), _ptr(x), _ptr(conv_w),
-                                       _ptr(conv_state), _ptr(conv_arrive), _ptr(g), _ptr(beta),
-                                       _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d), _ptr(ring_k),
-                                       _ptr(ring_g), _ptr(write_pos), _ptr(force_flush), _ptr(o),
-                                       _ptr(arrive), _ptr(err_flags), _stream(stream)),
-           "gdn_replay_decode_conv")
-    return o
 
 
 class Prepared:

@@ -12,7 +12,7 @@ using namespace gdn;
 
 namespace {
 
-constexpr int kAbiVersion = 9;
+constexpr int kAbiVersion = 8;
 static_assert(kArriveStride == GDN_ARRIVE_STRIDE, "arrival counter stride");
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -207,22 +207,13 @@ gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, c
 
 namespace {
 
-// The fused convolution's own buffers (gdn_replay_decode_conv).
-struct ConvIn {
-  const void* w;
-  void* st;
-  int32_t* arrive;
-};
-
-// gdn_replay_decode, gdn_replay_decode_advance and gdn_replay_decode_conv:
-// arrive == nullptr is the plain decode (write_pos only read), otherwise the
-// cursor advance is fused; cv != nullptr runs the causal convolution first.
+// gdn_replay_decode and gdn_replay_decode_advance: arrive == nullptr is the
+// plain decode (write_pos only read); otherwise the cursor advance is fused.
 gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const int32_t* slot_idx,
                          void* ckpt, void* ring_d, void* ring_k, float* ring_g,
                          const int32_t* write_pos, const int32_t* force_flush, void* o,
-                         int32_t* arrive, int32_t* err_flags, void* stream,
-                         const ConvIn* cv = nullptr) {
+                         int32_t* arrive, int32_t* err_flags, void* stream) {
   const gdn_status st = check_shape(s, true);
   if (st != GDN_OK) return st;
   if (s->window != 0 && s->window != 1) return GDN_ERR_INVALID_ARG;
@@ -242,9 +233,6 @@ gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const
       (force_flush && !aligned(force_flush, 4)))
     return GDN_ERR_INVALID_ARG;
   if (arrive && (s->window != 0 || !aligned(arrive, 128))) return GDN_ERR_INVALID_ARG;
-  if (cv && (!cv->w || !cv->st || !cv->arrive || !aligned(cv->w, 4 * es) ||
-             !aligned(cv->st, 4 * es) || !aligned(cv->arrive, 128)))
-    return GDN_ERR_INVALID_ARG;
   if (s->B == 0) return GDN_OK;
   DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.slot = slot_idx; a.state = ckpt;
@@ -314,22 +302,6 @@ gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const
       end += static_cast<size_t>((ntg + 63) / 64) * 1024;
     }
   }
-  if (cv) {
-    // the key head's q/k window (rows 0-2 by 64-lane copies of 16-byte
-    // pieces, row 3 the current input) and its q/k taps
-    const size_t pieces_win = 3 * 2 * static_cast<size_t>(s->dk) * es / 16;
-    const size_t pieces_tap = 2 * static_cast<size_t>(s->dk) * 4 * es / 16;
-    a.conv_C = 2 * s->Hk * s->dk + s->Hv * s->dv;
-    a.conv_w = cv->w;
-    a.conv_st = cv->st;
-    a.conv_arrive = cv->arrive;
-    a.conv_wg = a.gsz;
-    end = up16(end);
-    a.cv_off = static_cast<int32_t>(end);
-    end += up16(std::max((pieces_win + 63) / 64 * 1024, 8 * static_cast<size_t>(s->dk) * es));
-    a.cvt_off = static_cast<int32_t>(end);
-    end += (pieces_tap + 63) / 64 * 1024;
-  }
   a.dump_off = static_cast<int32_t>(up16(end));
   const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
   if (smem > 160 * 1024) return GDN_ERR_UNSUPPORTED;
@@ -360,32 +332,6 @@ gdn_status gdn_replay_decode_advance(const gdn_shape* s, const void* q, const vo
   if (!arrive) return GDN_ERR_INVALID_ARG;
   return replay_decode(s, q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
                        force_flush, o, arrive, err_flags, stream);
-}
-
-gdn_status gdn_replay_decode_conv(const gdn_shape* s, const void* x, const void* conv_w,
-                                  void* conv_state, int32_t* conv_arrive, const float* g,
-                                  const float* beta, const int32_t* slot_idx, void* ckpt,
-                                  void* ring_d, void* ring_k, float* ring_g, int32_t* write_pos,
-                                  const int32_t* force_flush, void* o, int32_t* arrive,
-                                  int32_t* err_flags, void* stream) {
-  if (!s) return GDN_ERR_INVALID_ARG;
-  if (s->T != 1 || s->window != 0 || s->qk_norm != 1) return GDN_ERR_INVALID_ARG;
-  if (s->qkv_dtype != GDN_F32 && s->qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
-  const int64_t C = 2ll * s->Hk * s->dk + static_cast<int64_t>(s->Hv) * s->dv;
-  const int64_t xs = s->qk_row_stride ? s->qk_row_stride : C;
-  if (xs < C || (s->v_row_stride != 0 && s->v_row_stride != xs) || xs > INT32_MAX)
-    return GDN_ERR_INVALID_ARG;
-  if (!x) return GDN_ERR_INVALID_ARG;
-  gdn_shape sx = *s;
-  sx.qk_row_stride = static_cast<int32_t>(xs);
-  sx.v_row_stride = static_cast<int32_t>(xs);
-  const size_t es = elem_size(s->qkv_dtype);
-  const char* xb = static_cast<const char*>(x);
-  const ConvIn cv{conv_w, conv_state, conv_arrive};
-  return replay_decode(&sx, xb, xb + static_cast<size_t>(s->Hk) * s->dk * es,
-                       xb + 2 * static_cast<size_t>(s->Hk) * s->dk * es, g, beta, slot_idx, ckpt,
-                       ring_d, ring_k, ring_g, write_pos, force_flush, o, arrive, err_flags,
-                       stream, &cv);
 }
 
 gdn_status gdn_replay_advance(const gdn_shape* s, const int32_t* slot_idx, int32_t* write_pos,

@@ -491,18 +491,6 @@ __device__ __forceinline__ void stage_key_gate(float* gl, int dk, int c4, f4 g4,
   *reinterpret_cast<f4*>(gl + 3 * dk + 4 * c4) = g4;
 }
 
-// SiLU of the tap sum of one channel's window z_0..z_3 (z_3 the current
-// input), one fma per tap in tap order, rounded to the I/O format and widened
-// back: the convolution kernel's arithmetic, so the fused front end reads the
-// same values the separate convolution stores.
-template <int DT>
-__device__ __forceinline__ float conv_silu(const float (&tap)[4], const float (&z)[4]) {
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc = fmaf(tap[i], z[i], acc);
-  return to_f32<DT>(from_f32<DT>(acc / (1.f + expf(-acc))));
-}
-
 // The value lane `i` (wave-uniform) holds, in every lane.
 __device__ __forceinline__ float lane_value(float x, int i) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i));
@@ -653,17 +641,6 @@ struct DecodeArgs {
   // after the slab; g_bytes is the size of the token gates g
   int32_t kdma, kraw_off, kraw_wave, tg_off;
   uint32_t g_bytes;
-  // causal convolution fused in front of a decode step (the NRM = 2
-  // kernels): q, k, v point into the raw packed row; taps conv_w [C, 4] and
-  // windows conv_st [N, 3, C] in the q/k/v dtype; conv_arrive [B*Hk][32]
-  // int32 counters (zero between calls) count the workgroups of a (row, key
-  // head) out; LDS from cv_off: the key head's q/k window, rows 0-2 copied
-  // by the memory unit and row 3 the current input ([4][2][dk]), then from
-  // cvt_off its q/k taps ([2][dk][4]); conv_wg workgroups per (row, key head)
-  const void* conv_w;
-  void* conv_st;
-  int32_t* conv_arrive;
-  int32_t conv_C, cv_off, cvt_off, conv_wg;
   // cursor advance fused into a decode step (gdn_replay_decode_advance): the
   // workgroups of a row count themselves in arrive[b] once every wavefront of
   // theirs has read the cursor; the last one writes the advanced cursor

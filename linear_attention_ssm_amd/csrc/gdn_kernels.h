@@ -224,8 +224,6 @@ struct Small {
   uint32_t d_raw[4];                    // this lane's ring d entries (raw bits)
   float gate_g, gate_b;                 // wave 0, lane hh*T+t: g and beta of head hh, token t
   typename Elem<QKV>::T v_raw;
-  typename Elem<QKV>::T cvw[3];         // fused convolution: this lane's value-channel window
-  typename Raw4<QKV>::T cvt;            //   and its four taps
 };
 
 // Where a row stands: its slot, its valid ring entries and whether it flushes.
@@ -520,50 +518,6 @@ __device__ __forceinline__ void weight_keys(const DecodeArgs& a, const ItemGeo& 
   }
 }
 
-// Fused causal convolution (NRM = 2, decode steps). Wavefront 0, which holds
-// the q/k staging threads, has the memory unit copy the key head's q/k window
-// rows 0-2 ([3][2][dk] of the [N, 3, C] windows) and taps ([2][dk][4]) into
-// LDS in 64-lane copies of 16-byte pieces (pieces past the end read out of
-// range and copy zeros, so no lane condition is needed). Every lane loads the
-// window and taps of its own value channel into registers.
-template <int DK, int QKV, int RING>
-__device__ __forceinline__ void fetch_conv(Small<DK, QKV, RING>& f, const DecodeArgs& a,
-                                           const ItemGeo& g, const RowState& r,
-                                           unsigned char* buf, int lane, int wave) {
-  using E = typename Elem<QKV>::T;
-  constexpr int ES = sizeof(E);
-  constexpr int PPR = DK * ES / 16;            // pieces per (window row, q or k)
-  constexpr int NWIN = 3 * 2 * PPR, NWI = (NWIN + 63) / 64;
-  constexpr int PPT = DK * 4 * ES / 16;        // pieces of the q (or k) taps
-  constexpr int NTAP = 2 * PPT, NTI = (NTAP + 63) / 64;
-  const uint32_t C = static_cast<uint32_t>(a.conv_C);
-  const char* st = static_cast<const char*>(a.conv_st) + static_cast<size_t>(r.sc) * 3 * C * ES;
-  if (wave == 0) {
-    const __amdgpu_buffer_rsrc_t rw = brsrc(st, 3 * C * ES);
-    const __amdgpu_buffer_rsrc_t rt = brsrc(a.conv_w, C * 4 * ES);
-    const uint32_t q0 = static_cast<uint32_t>(g.hk) * DK;   // the head's first q channel
-    const uint32_t kofs = static_cast<uint32_t>(a.Hk) * DK;  // k channels follow all q
-#pragma unroll
-    for (int j = 0; j < NWI; ++j) {
-      const int p = j * 64 + lane;
-      const int i = p / (2 * PPR), rem = p - i * 2 * PPR, part = rem / PPR, pc = rem - part * PPR;
-      const uint32_t off = p < NWIN ? (i * C + part * kofs + q0) * ES + pc * 16 : 3 * C * ES;
-      buffer_to_lds16(rw, buf + a.cv_off + j * 1024, off);
-    }
-#pragma unroll
-    for (int j = 0; j < NTI; ++j) {
-      const int p = j * 64 + lane;
-      const int part = p / PPT, pc = p - part * PPT;
-      const uint32_t off = p < NTAP ? (part * kofs + q0) * 4 * ES + pc * 16 : C * 4 * ES;
-      buffer_to_lds16(rt, buf + a.cvt_off + j * 1024, off);
-    }
-  }
-  const uint32_t cv = 2 * static_cast<uint32_t>(a.Hk) * DK + g.h * a.dv + g.vcol;
-#pragma unroll
-  for (int i = 0; i < 3; ++i) f.cvw[i] = load1_raw<QKV>(st, static_cast<size_t>(i) * C + cv);
-  f.cvt = load4_raw<QKV>(a.conv_w, static_cast<size_t>(cv) * 4);
-}
-
 // weight_keys from the early copy (a.kdma != 0, entries 0..15): two lanes
 // per channel, lanes 32..63 take entries 15..8 and lanes 0..31 entries 7..0.
 // The lower half starts its running sum from the upper half's total, so every
@@ -626,85 +580,6 @@ __device__ __forceinline__ void weight_keys_lds(const DecodeArgs& a, int lp, uns
   }
 }
 
-// Fused convolution of a staging thread's four q and four k channels from
-// the LDS copy of the key head's window and taps (fetch_conv); the current
-// inputs become window row 3. NSLAB: the slab's vector loads, the only ones
-// issued after the copy besides this lane's own value-channel loads.
-template <int DK, int QKV, int RING, int NSLAB>
-__device__ __forceinline__ void conv_qk(const DecodeArgs& a, const ItemGeo& g, const RowState& r,
-                                        const Small<DK, QKV, RING>& f, unsigned char* buf,
-                                        int tid, int lane, f4& qv, f4& kv, int& counted) {
-  using E = typename Elem<QKV>::T;
-  static_assert(NSLAB < 64, "vmcnt holds 6 bits");
-  // LDS reads are not ordered after a copy by the memory unit: wait for it
-  __builtin_amdgcn_s_waitcnt((NSLAB & 15) | (7 << 4) | (15 << 8) | ((NSLAB >> 4) << 14));
-  __builtin_amdgcn_sched_barrier(0);
-  // The window has been read: count this workgroup in now (lane 0 of a live
-  // row; the other lanes address past the counter, which the bounded buffer
-  // drops). The count is only looked at when the workgroup ends.
-  {
-    int* cnt = a.conv_arrive + (static_cast<size_t>(g.b) * a.Hk + g.hk) * kArriveStride;
-    const __amdgpu_buffer_rsrc_t rc = brsrc(cnt, 4);
-    counted = __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, rc, (r.ok && lane == 0) ? 0 : 4, 0, 0);
-  }
-  using R4 = typename Raw4<QKV>::T;
-  const int c0 = 4 * (tid < DK / 4 ? tid : DK / 4 - 1);
-  E* win = reinterpret_cast<E*>(buf + a.cv_off);                 // [4][2][DK]
-  const E* tp = reinterpret_cast<const E*>(buf + a.cvt_off);     // [2][DK][4]
-#pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    f4& x = part ? kv : qv;
-    // the window rows of the four channels (packed), then channel by
-    // channel its taps, decoded where used
-    R4 zr[3];
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-      zr[i] = *reinterpret_cast<const R4*>(win + (i * 2 + part) * DK + c0);
-    f4 y;
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      const f4 t4 = decode4<QKV>(*reinterpret_cast<const R4*>(tp + (part * DK + c0 + ch) * 4));
-      const float tap[4] = {t4.x, t4.y, t4.z, t4.w};
-      const float z[4] = {decode4<QKV>(zr[0])[ch], decode4<QKV>(zr[1])[ch],
-                          decode4<QKV>(zr[2])[ch], x[ch]};
-      y[ch] = conv_silu<QKV>(tap, z);
-    }
-    if (tid < DK / 4)
-      *reinterpret_cast<R4*>(win + (6 + part) * DK + c0) = part ? f.k_raw : f.q_raw;
-    x = y;
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// The q/k window of a (row, key head) is read by each of its conv_wg
-// workgroups (fetch_conv), so it moves only after all of them have read it:
-// each workgroup counts itself in once its copy has landed (conv_qk), and the
-// last one, at its end, writes rows 1-3 of its LDS window as the new rows 0-2
-// and clears the counter (one 128-byte line per counter).
-template <int DK, int QKV>
-__device__ __forceinline__ void conv_qk_window(const DecodeArgs& a, const ItemGeo& g,
-                                               const RowState& r, unsigned char* buf, int tid,
-                                               int lane, int wave, int counted) {
-  using E = typename Elem<QKV>::T;
-  using R4 = typename Raw4<QKV>::T;
-  if (wave != 0 || !r.ok) return;
-  int* cnt = a.conv_arrive + (static_cast<size_t>(g.b) * a.Hk + g.hk) * kArriveStride;
-  const int n = __builtin_amdgcn_readfirstlane(counted);     // lane 0's count
-  if (n != a.conv_wg - 1) return;
-  if (tid < DK / 4) {
-    const E* win = reinterpret_cast<const E*>(buf + a.cv_off);
-    E* st = static_cast<E*>(a.conv_st) + static_cast<size_t>(r.sc) * 3 * a.conv_C +
-            g.hk * DK + 4 * tid;
-#pragma unroll
-    for (int part = 0; part < 2; ++part)
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        *reinterpret_cast<R4*>(st + static_cast<size_t>(i) * a.conv_C + part * a.Hk * DK) =
-            *reinterpret_cast<const R4*>(win + ((i + 1) * 2 + part) * DK + 4 * tid);
-  }
-  if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <int DK, int QKV, int RING, int SD, int TT, int KG, int NRM>
 __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, const RowState& r,
                                         int T, const Small<DK, QKV, RING>& f,
@@ -730,11 +605,8 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
 
   // ---- LDS staging. Every thread writes (threads past the last piece into a
   // per-lane dump area) so the early loads have unconditional uses.
-  int counted = 0;                               // fused convolution: this workgroup's count
   if (64 * wave < nqk) {                         // waves holding staging threads
     f4 qv = decode4<QKV>(f.q_raw), kv = decode4<QKV>(f.k_raw);
-    if constexpr (NRM == 2)
-      conv_qk<DK, QKV, RING, SlabRaw<SD, DK>::NP>(a, g, r, f, buf, tid, lane, qv, kv, counted);
     if constexpr (NRM) token_l2norm<DK>(qv, kv);
     const int tq = TT ? 0 : tid / C4;
     float* qdst = tid < nqk ? qk + tq * 2 * DK + (tid - tq * C4) * 4 : dump + lane * 8;
@@ -753,24 +625,6 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
     *reinterpret_cast<f4*>(qk + (tau * 2 + 1) * DK + e4) = kv;
     const float kq0 = token_kq<DK>(qv, kv);   // groups of C4 lanes stay aligned
     if (e4 == 0) kq_l[tau] = kq0;
-  }
-  // fused convolution of this lane's value channel; its window moves now
-  // (the channel is this lane's alone: grp 0 writes it)
-  float vconv = 0.f;
-  if constexpr (NRM == 2) {
-    const f4 t4 = decode4<QKV>(f.cvt);
-    const float tap[4] = {t4.x, t4.y, t4.z, t4.w};
-    const float z[4] = {to_f32<QKV>(f.cvw[0]), to_f32<QKV>(f.cvw[1]), to_f32<QKV>(f.cvw[2]),
-                        to_f32<QKV>(f.v_raw)};
-    vconv = conv_silu<QKV>(tap, z);
-    if (r.ok && grp == 0) {
-      using E = typename Elem<QKV>::T;
-      E* w = static_cast<E*>(a.conv_st) + static_cast<size_t>(r.sc) * 3 * a.conv_C +
-             2 * a.Hk * DK + g.h * a.dv + g.vcol;
-      w[0] = f.cvw[1];
-      w[a.conv_C] = f.cvw[2];
-      w[2 * static_cast<size_t>(a.conv_C)] = f.v_raw;
-    }
   }
   // gates of the workgroup's heads (wave 0): alpha = RN_f32(exp_f64(g))
   if (wave == 0) {
@@ -993,7 +847,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   const bool gwriter_wave = (g.vb == 0) && (wave % wph == 0);     // one g writer per head
   const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
   const size_t ks = static_cast<size_t>(r.sc) * a.Hk + g.hk;
-  float vv = NRM == 2 ? vconv : to_f32<QKV>(f.v_raw);
+  float vv = to_f32<QKV>(f.v_raw);
   for (int tau = 0; tau < T; ++tau) {
     const float* ql = qk + tau * 2 * DK;
     const float* kl = ql + DK;
@@ -1039,13 +893,9 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
     using SE = typename Elem<SD>::T;
     store_slab<SD, DK>(static_cast<SE*>(a.state) + (hs * a.dv + g.vcol - col) * DK, S, col, grp);
   }
-  // last: the wait for the counter's atomic then holds nothing up
-  if constexpr (NRM == 2) conv_qk_window<DK, QKV>(a, g, r, buf, tid, lane, wave, counted);
 }
 
-// NRM = 1: q and k are L2-normalised (q scaled) in the kernel (a.qk_norm);
-// NRM = 2: the causal convolution runs first, on the raw packed row (decode
-// steps only).
+// NRM = 1: q and k are L2-normalised (q scaled) in the kernel (a.qk_norm).
 template <int DK, int QKV, int RING, int SD, int TT, int KG, int NRM>
 __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1067,7 +917,6 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   if constexpr (KG) {
     if (a.kdma) fetch_key_gate<DK, RING>(a, g, r, T, smem, tid, lane, wave);
   }
-  if constexpr (NRM == 2) fetch_conv<DK, QKV, RING>(sm, a, g, r, smem, lane, wave);
   __builtin_amdgcn_sched_barrier(0);
   fetch_slab<SD, DK>(R, a, g, r, col, grp);
   process<DK, QKV, RING, SD, TT, KG, NRM>(a, g, r, T, sm, R, smem, dump, tid, lane, grp, col, wave);

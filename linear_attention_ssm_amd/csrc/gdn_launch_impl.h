@@ -52,11 +52,7 @@ template <int DK, int QKV, int RING, int SD>
 static hipError_t launch_replay_s(const DecodeArgs& a, int kg, dim3 grid, dim3 block, size_t smem,
                                   hipStream_t stream) {
   // a single-token instance for T = 1 (decode steps, one-token windows)
-  // (gate, in-kernel q/k normalisation, fused convolution) select the instance
-  if (a.conv_C) {          // decode steps only (T = 1)
-    if (kg) return launch(replay_decode_kernel<DK, QKV, RING, SD, 1, 1, 2>, a, grid, block, smem, stream);
-    return launch(replay_decode_kernel<DK, QKV, RING, SD, 1, 0, 2>, a, grid, block, smem, stream);
-  }
+  // (gate, in-kernel q/k normalisation) select the instance
   if (a.qk_norm) {
     if (kg) {
       if (a.T == 1) return launch(replay_decode_kernel<DK, QKV, RING, SD, 1, 1, 1>, a, grid, block, smem, stream);

@@ -9,8 +9,8 @@ import linear_attention_ssm_amd as gdn
 from linear_attention_ssm_amd import gdn_shape
 
 EXPECTED = ["gdn_abi_version", "gdn_conv_update", "gdn_kda_gates", "gdn_packed_decode",
-            "gdn_replay_advance", "gdn_replay_commit", "gdn_replay_decode",
-            "gdn_replay_decode_advance", "gdn_replay_decode_conv", "gdn_replay_fold",
+            "gdn_replay_advance", "gdn_replay_commit",
+            "gdn_replay_decode", "gdn_replay_decode_advance", "gdn_replay_fold",
             "gdn_replay_reset", "gdn_status_string"]
 
 # Fake, 256-byte aligned, non-null device addresses: never dereferenced, since
@@ -30,7 +30,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 9
+    assert lib.gdn_abi_version() == 8
     for st in range(4):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -259,28 +259,3 @@ def test_kda_gates_validates():
     p = list(FAKE[:6])
     p[0] = ctypes.c_void_p(FAKE[0].value + 8)           # a not 16-byte aligned
     assert call(p) == gdn.GDN_ERR_INVALID_ARG
-
-
-def test_replay_decode_conv_validates():
-    lib = gdn.lib()
-
-    def call(sh, p=None):
-        p = list(FAKE[:16]) if p is None else p
-        # x, conv_w, conv_state, conv_arrive, g, beta, slot, ckpt, ring_d, ring_k, ring_g,
-        # write_pos, force_flush, o, arrive, err_flags, stream
-        return lib.gdn_replay_decode_conv(ctypes.byref(sh), *p[:12], None, p[13], None, None,
-                                          None)
-    ok = dict(qk_norm=1)
-    assert call(shape(B=0, **ok)) == gdn.GDN_OK
-    assert call(shape(T=2, window=1, **ok)) == gdn.GDN_ERR_INVALID_ARG   # decode steps only
-    assert call(shape(qk_norm=0)) == gdn.GDN_ERR_INVALID_ARG             # the front end is on
-    assert call(shape(v_row_stride=1000, **ok)) == gdn.GDN_ERR_INVALID_ARG
-    assert call(shape(qk_row_stride=100, **ok)) == gdn.GDN_ERR_INVALID_ARG   # < C
-    assert call(shape(dk=96, **ok)) == gdn.GDN_ERR_UNSUPPORTED
-    for i in (1, 2, 3):                                   # conv_w, conv_state, conv_arrive
-        p = list(FAKE[:16])
-        p[i] = None
-        assert call(shape(**ok), p) == gdn.GDN_ERR_INVALID_ARG, i
-    p = list(FAKE[:16])
-    p[3] = ctypes.c_void_p(FAKE[3].value + 64)            # counters not on 128-byte lines
-    assert call(shape(**ok), p) == gdn.GDN_ERR_INVALID_ARG
