@@ -927,7 +927,7 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
 // Fold the valid ring entries into the checkpoint with the pinned two-step
 // rounding (SGLang PR #42388 "The idea"; SGLang PR #36821 fold). Workgroup =
 // (row, value head, FV value rows); thread = one 16-byte group of 4 keys in
-// FV/16 rows (the ring entries staged in LDS serve all of them).
+// FV/16 consecutive rows (the ring entries staged in LDS serve all of them).
 // KG = 1: per-key gate (ring_g [N, Hv, L, dk]), each channel decays by its
 // own a_j[c].
 template <int DK, int RING, int SD, int KG>
@@ -963,14 +963,14 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   const size_t hs = static_cast<size_t>(s) * a.Hv + h;
   const size_t ks = static_cast<size_t>(s) * a.Hk + hk;
   const int tid = threadIdx.x;
-  const int row = tid / C4, e4 = (tid % C4) * 4;      // rows row, row + 16, ...
+  const int row = (tid / C4) * nr, e4 = (tid % C4) * 4;   // rows row .. row + nr - 1
 
   using SE = typename Elem<SD>::T;
   SE* xbase = static_cast<SE*>(a.ckpt) + (hs * a.dv + vb * FV) * DK;   // the block's FV rows
   f4 x[MAXR];
 #pragma unroll
   for (int m = 0; m < MAXR; ++m)
-    if (m < nr) x[m] = load4<SD>(xbase, (row + 16 * m) * DK + e4);
+    if (m < nr) x[m] = load4<SD>(xbase, (row + m) * DK + e4);
 
   if constexpr (KG) {
     for (int c = tid; c < p * C4; c += blockDim.x) {
@@ -1002,10 +1002,18 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
       if constexpr (KG) aj = *reinterpret_cast<const f4*>(al + j * DK + e4);
       else aj = f4{al[j], al[j], al[j], al[j]};
       const f4 kv = *reinterpret_cast<const f4*>(kl + j * DK + e4);
+      // the thread's nr consecutive rows: one 16-byte read of d when nr = 4
+      f4 d4;
+      if (nr == MAXR) {
+        d4 = *reinterpret_cast<const f4*>(dl + j * FV + row);
+      } else {
+#pragma unroll
+        for (int m = 0; m < MAXR; ++m) d4[m] = m < nr ? dl[j * FV + row + m] : 0.f;
+      }
 #pragma unroll
       for (int m = 0; m < MAXR; ++m) {
         if (m < nr) {
-          const float dj = dl[j * FV + row + 16 * m];
+          const float dj = d4[m];
           f4& y = x[m];
           const float tx = aj.x * y.x, ty = aj.y * y.y, tz = aj.z * y.z, tw = aj.w * y.w;
           y.x = __builtin_fmaf(dj, kv.x, tx);
@@ -1028,7 +1036,7 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
 #pragma unroll
   for (int m = 0; m < MAXR; ++m) {
     if (m < nr) {
-      const int off = (row + 16 * m) * DK + e4;
+      const int off = (row + m) * DK + e4;
       if constexpr (SD == DT_F32) {
         store16_nt(reinterpret_cast<float*>(xbase), FV * DK * 4, off * 4, x[m]);
       } else {
