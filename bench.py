@@ -39,8 +39,12 @@ import gdn_inputs as gi  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 METRIC = "GDN decode head-steps/sec and achieved HBM GB/s (% of peak) at B=64, L=16"
 PROFILES = os.path.join(ROOT, "profiles")
+# every source that decides what the timed kernels do: the kernels, the
+# launch geometry and dispatch
 KERNEL_SOURCES = ["linear_attention_ssm_amd/csrc/gdn_kernels.h",
-                  "linear_attention_ssm_amd/csrc/gdn_device.h"]
+                  "linear_attention_ssm_amd/csrc/gdn_device.h",
+                  "linear_attention_ssm_amd/csrc/gdn_api.hip",
+                  "linear_attention_ssm_amd/csrc/gdn_launch_impl.h"]
 
 
 def kernel_hash() -> str:

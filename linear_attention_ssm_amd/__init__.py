@@ -182,6 +182,27 @@ def _io_shape(q, k, v, g, beta, slot_idx):
     return B, T, Hk, dk, Hv, dv, dev, gate, qs, vs
 
 
+def _row_flags(t, name, B, dev):
+    """An optional int32 [B] per-row array (force_flush, accepted)."""
+    if t is not None:
+        _check(t, name, torch.int32, 1, dev)
+        if tuple(t.shape) != (B,):
+            raise ValueError(f"{name} must be [B] = [{B}], got {tuple(t.shape)}")
+
+
+def _err_word(err_flags, dev):
+    if err_flags is not None:
+        _check(err_flags, "err_flags", torch.int32, None, dev)
+        if err_flags.numel() < 1:
+            raise ValueError("err_flags must hold at least one int32")
+
+
+def _state_of(state, Hv, dv, dk, dev):
+    _check(state, "state", STATE_DTYPES, 4, dev)
+    if tuple(state.shape[1:]) != (Hv, dv, dk):
+        raise ValueError("state must be [N, Hv, dv, dk]")
+
+
 def _out(o, B, T, Hv, dv, dtype, dev):
     if o is None:
         return torch.empty((B, T, Hv, dv), dtype=dtype, device=dev)
@@ -209,11 +230,8 @@ def gdn_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=None,
     mixed_qkv row); qk_norm L2-normalises q and k in the kernel and scales q.
     Returns o [B,1,Hv,dv]."""
     B, T, Hk, dk, Hv, dv, dev, gate, qs, vs = _io_shape(q, k, v, g, beta, slot_idx)
-    _check(state, "state", STATE_DTYPES, 4, dev)
-    if tuple(state.shape[1:]) != (Hv, dv, dk):
-        raise ValueError("state must be [N, Hv, dv, dk]")
-    if err_flags is not None:
-        _check(err_flags, "err_flags", torch.int32, None, dev)
+    _state_of(state, Hv, dv, dk, dev)
+    _err_word(err_flags, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
     sh = _shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0,
                 _DT[state.dtype], 0, gate, qs, vs, qk_norm)
@@ -247,12 +265,8 @@ def gdn_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, 
     a 16-bit state after every token. Returns o [B,T,Hv,dv]."""
     B, T, Hk, dk, Hv, dv, dev, gate, qs, vs = _io_shape(q, k, v, g, beta, slot_idx)
     N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
-    if force_flush is not None:
-        _check(force_flush, "force_flush", torch.int32, 1, dev)
-        if force_flush.shape != (B,):
-            raise ValueError("force_flush must be [B]")
-    if err_flags is not None:
-        _check(err_flags, "err_flags", torch.int32, None, dev)
+    _row_flags(force_flush, "force_flush", B, dev)
+    _err_word(err_flags, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
     sh = _shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], window,
                 _DT[ckpt.dtype], step_rounding, gate, qs, vs, qk_norm)
@@ -281,12 +295,8 @@ def gdn_replay_decode_advance(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, 
     _check(arrive, "arrive", torch.int32, 1, dev)
     if arrive.shape != (B * ARRIVE_STRIDE,):
         raise ValueError("arrive must be [B * ARRIVE_STRIDE]")
-    if force_flush is not None:
-        _check(force_flush, "force_flush", torch.int32, 1, dev)
-        if force_flush.shape != (B,):
-            raise ValueError("force_flush must be [B]")
-    if err_flags is not None:
-        _check(err_flags, "err_flags", torch.int32, None, dev)
+    _row_flags(force_flush, "force_flush", B, dev)
+    _err_word(err_flags, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
     sh = _shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], 0,
                 _DT[ckpt.dtype], 0, gate, qs, vs, qk_norm)
@@ -301,8 +311,8 @@ def gdn_replay_advance(slot_idx, write_pos, L, force_flush=None, err_flags=None,
     """Cursor advance once per forward; see gdn_replay_advance in gdn_replay.h."""
     _check(slot_idx, "slot_idx", torch.int32, 1)
     _check(write_pos, "write_pos", torch.int32, 1, slot_idx.device)
-    if force_flush is not None:
-        _check(force_flush, "force_flush", torch.int32, 1, slot_idx.device)
+    _row_flags(force_flush, "force_flush", slot_idx.shape[0], slot_idx.device)
+    _err_word(err_flags, slot_idx.device)
     sh = gdn_shape(slot_idx.shape[0], 1, write_pos.shape[0], 1, 1, 32, 16, int(L), 0, 0, 0, 0)
     _raise(_lib.gdn_replay_advance(ctypes.byref(sh), _ptr(slot_idx), _ptr(write_pos),
                                    _ptr(force_flush), _ptr(err_flags), _stream(stream)),
@@ -313,7 +323,9 @@ def gdn_replay_commit(slot_idx, accepted, write_pos, L, T, err_flags=None, strea
     """write_pos[slot] += accepted; see gdn_replay_commit in gdn_replay.h."""
     _check(slot_idx, "slot_idx", torch.int32, 1)
     _check(accepted, "accepted", torch.int32, 1, slot_idx.device)
+    _row_flags(accepted, "accepted", slot_idx.shape[0], slot_idx.device)
     _check(write_pos, "write_pos", torch.int32, 1, slot_idx.device)
+    _err_word(err_flags, slot_idx.device)
     sh = gdn_shape(slot_idx.shape[0], int(T), write_pos.shape[0], 1, 1, 32, 16, int(L), 0, 0, 0,
                    0)
     _raise(_lib.gdn_replay_commit(ctypes.byref(sh), _ptr(slot_idx), _ptr(accepted),
@@ -333,6 +345,7 @@ def gdn_replay_fold(slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags
     Hk = ring_k.shape[1]
     gate = GDN_GATE_KEY if ring_g.dim() == 4 else GDN_GATE_HEAD
     _, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
+    _err_word(err_flags, dev)
     sh = gdn_shape(slot_idx.shape[0], 1, N, Hv, Hk, dk, dv, L, GDN_F32, _DT[ring_d.dtype], 0,
                    _DT[ckpt.dtype], int(bool(step_rounding)), gate)
     _raise(_lib.gdn_replay_fold(ctypes.byref(sh), _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d),
@@ -345,6 +358,7 @@ def gdn_replay_reset(slot_idx, write_pos, err_flags=None, stream=None):
     in gdn_replay.h."""
     _check(slot_idx, "slot_idx", torch.int32, 1)
     _check(write_pos, "write_pos", torch.int32, 1, slot_idx.device)
+    _err_word(err_flags, slot_idx.device)
     sh = gdn_shape(slot_idx.shape[0], 1, write_pos.shape[0], 1, 1, 32, 16, 1, 0, 0, 0, 0)
     _raise(_lib.gdn_replay_reset(ctypes.byref(sh), _ptr(slot_idx), _ptr(write_pos),
                                  _ptr(err_flags), _stream(stream)), "gdn_replay_reset")
@@ -436,8 +450,8 @@ def prepare_replay_decode(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring
     Returns (call, o)."""
     B, T, Hk, dk, Hv, dv, dev, gate, qs, vs = _io_shape(q, k, v, g, beta, slot_idx)
     N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
-    if force_flush is not None:
-        _check(force_flush, "force_flush", torch.int32, 1, dev)
+    _row_flags(force_flush, "force_flush", B, dev)
+    _err_word(err_flags, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
     sh = _shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], window,
                 _DT[ckpt.dtype], 0, gate, qs, vs, qk_norm)
@@ -453,7 +467,8 @@ def prepare_packed_decode(q, k, v, g, beta, slot_idx, state, o=None, err_flags=N
                           stream=None, qk_norm=False):
     """gdn_packed_decode prepared for repeated calls. Returns (call, o)."""
     B, T, Hk, dk, Hv, dv, dev, gate, qs, vs = _io_shape(q, k, v, g, beta, slot_idx)
-    _check(state, "state", STATE_DTYPES, 4, dev)
+    _state_of(state, Hv, dv, dk, dev)
+    _err_word(err_flags, dev)
     o = _out(o, B, T, Hv, dv, q.dtype, dev)
     sh = _shape(B, T, state.shape[0], Hv, Hk, dk, dv, 1, _DT[q.dtype], GDN_F32, 0,
                 _DT[state.dtype], 0, gate, qs, vs, qk_norm)

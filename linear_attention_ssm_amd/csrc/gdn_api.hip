@@ -21,23 +21,13 @@ size_t elem_size(int dt) { return dt == GDN_F32 ? 4 : 2; }
 
 bool dk_supported(int dk) { return dk == 32 || dk == 64 || dk == 128 || dk == 256; }
 
-// Waves per decode workgroup (a tuning knob; GDN_WAVES_PER_WG overrides the
-// default of 8 for experiments).
-int target_waves() {
-  static int w = [] {
-    const char* e = std::getenv("GDN_WAVES_PER_WG");
-    int v = e ? std::atoi(e) : 8;
-    if (v < 1) v = 1;
-    if (v > 16) v = 16;
-    return v;
-  }();
-  return w;
-}
+// Waves per packed-decode workgroup.
+constexpr int kPackedWaves = 8;
 
 // Value rows per head per workgroup: the largest multiple of 16 dividing dv
 // with G * VB / 16 <= target waves (at least 16, so at most 16 waves).
 int pick_vb(int dv, int G) {
-  const int tw = target_waves();
+  const int tw = kPackedWaves;
   int best = 16;
   for (int vb = 16; vb <= dv; vb += 16)
     if (dv % vb == 0 && G * (vb / 16) <= (tw > G ? tw : G)) best = vb;
@@ -132,15 +122,14 @@ void fill_decode_geometry(const gdn_shape* s, DecodeArgs& a, dim3& grid, dim3& b
   block = dim3(64u * a.G * (a.VB / 16));
 }
 
-// Work-item geometry of the replay kernel: GH value heads (a
-// divisor of G) times VB value rows per item, one wavefront per 16 rows of
-// one head, at most 8 wavefronts (GDN_REPLAY_WAVES, default 4).
+// Work-item geometry of the replay kernel: GH value heads (a divisor of G)
+// times VB value rows per item, one wavefront per 16 rows of one head, at
+// most kReplayWaves wavefronts. Wavefront 0 stages the gates of the item's GH
+// heads and T tokens, one (head, token) pair per lane, so GH * T <= 64.
+constexpr int kReplayWaves = 4;
+
 void fill_replay_geometry(const gdn_shape* s, DecodeArgs& a, dim3& block, int& n_items) {
-  static const int tw = [] {
-    const char* e = std::getenv("GDN_REPLAY_WAVES");
-    int v = e ? std::atoi(e) : 4;
-    return v < 1 ? 1 : (v > 8 ? 8 : v);
-  }();
+  const int tw = kReplayWaves;
   a.B = s->B; a.T = s->T; a.N = s->N; a.Hv = s->Hv; a.Hk = s->Hk; a.dv = s->dv; a.L = s->L;
   a.G = s->Hv / s->Hk;
   // value heads per workgroup: with a per-head gate, as many as fit (they
@@ -149,7 +138,7 @@ void fill_replay_geometry(const gdn_shape* s, DecodeArgs& a, dim3& block, int& n
   // head re-reads and weights
   int gh = 1;
   for (int d = 1; d <= a.G && s->gate != GDN_GATE_KEY; ++d)
-    if (a.G % d == 0 && d <= tw) gh = d;
+    if (a.G % d == 0 && d <= tw && d * s->T <= 64) gh = d;
   a.GH = gh;
   a.nhc = a.G / gh;
   int vb = 16;

@@ -71,24 +71,70 @@ def dev_inputs(x: gi.StepInputs) -> DevInputs:
                      to_dev(x.g), to_dev(x.beta))
 
 
-class Pool:
-    """Device buffers of one layer: checkpoint, rings, cursors, error word."""
+CANARY_BYTES = 4096         # guard bytes on each side of a canary tensor
 
-    def __init__(self, w: gi.Workload, S0: np.ndarray, garbage: bool = False):
+
+class CanaryTensor:
+    """A device tensor placed inside a larger buffer whose CANARY_BYTES before
+    and after it hold a fixed byte pattern (a garbage template around the
+    buffer, SGLang PR #36821, Tests): check() asserts that no kernel wrote
+    outside the tensor. The tensor is 256-byte aligned, like torch's own
+    allocations."""
+
+    PATTERN = 0xA5
+
+    def __init__(self, shape, dt, init: Optional[torch.Tensor] = None):
+        dtype = TORCH_DT[dt] if isinstance(dt, str) else dt
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        self.buf = torch.full((CANARY_BYTES + n + CANARY_BYTES,), self.PATTERN,
+                              dtype=torch.uint8, device=DEV)
+        self.n = n
+        self.t = self.buf[CANARY_BYTES:CANARY_BYTES + n].view(dtype).view(shape)
+        if init is not None:
+            self.t.copy_(init)
+        else:
+            self.t.zero_()
+
+    def check(self, what: str) -> None:
+        head = self.buf[:CANARY_BYTES]
+        tail = self.buf[CANARY_BYTES + self.n:]
+        assert bool((head == self.PATTERN).all()), f"{what}: bytes before the tensor changed"
+        assert bool((tail == self.PATTERN).all()), f"{what}: bytes after the tensor changed"
+
+
+class Pool:
+    """Device buffers of one layer: checkpoint, rings, cursors, error word.
+    canary: each of them sits inside a guarded buffer (CanaryTensor)."""
+
+    def __init__(self, w: gi.Workload, S0: np.ndarray, garbage: bool = False,
+                 canary: bool = False):
         self.w = w
-        self.ckpt = to_dev(S0)
         rdt = TORCH_DT[w.ring]
         gshape = (w.N, w.Hv, w.L, w.dk) if w.gate == "key" else (w.N, w.Hv, w.L)
+        dshape, kshape = (w.N, w.Hv, w.L, w.dv), (w.N, w.Hk, w.L, w.dk)
         if garbage:
-            self.ring_d = to_dev(gi.garbage_like((w.N, w.Hv, w.L, w.dv), w.ring, 1), w.ring)
-            self.ring_k = to_dev(gi.garbage_like((w.N, w.Hk, w.L, w.dk), w.ring, 2), w.ring)
-            self.ring_g = to_dev(gi.garbage_like(gshape, "f32", 3))
+            init = (to_dev(S0), to_dev(gi.garbage_like(dshape, w.ring, 1), w.ring),
+                    to_dev(gi.garbage_like(kshape, w.ring, 2), w.ring),
+                    to_dev(gi.garbage_like(gshape, "f32", 3)))
         else:
-            self.ring_d = torch.zeros((w.N, w.Hv, w.L, w.dv), dtype=rdt, device=DEV)
-            self.ring_k = torch.zeros((w.N, w.Hk, w.L, w.dk), dtype=rdt, device=DEV)
-            self.ring_g = torch.zeros(gshape, dtype=torch.float32, device=DEV)
-        self.write_pos = torch.zeros(w.N, dtype=torch.int32, device=DEV)
+            init = (to_dev(S0), torch.zeros(dshape, dtype=rdt, device=DEV),
+                    torch.zeros(kshape, dtype=rdt, device=DEV),
+                    torch.zeros(gshape, dtype=torch.float32, device=DEV))
+        self.guards = []
+        if canary:
+            for x in init:
+                self.guards.append(CanaryTensor(tuple(x.shape), x.dtype, init=x))
+            self.guards.append(CanaryTensor((w.N,), torch.int32))
+            self.ckpt, self.ring_d, self.ring_k, self.ring_g, self.write_pos = \
+                (c.t for c in self.guards)
+        else:
+            self.ckpt, self.ring_d, self.ring_k, self.ring_g = init
+            self.write_pos = torch.zeros(w.N, dtype=torch.int32, device=DEV)
         self.err = torch.zeros(1, dtype=torch.int32, device=DEV)
+
+    def check_canaries(self, what: str) -> None:
+        for c, name in zip(self.guards, ("ckpt", "ring_d", "ring_k", "ring_g", "write_pos")):
+            c.check(f"{what}: {name}")
 
     def ring_bits(self):
         return bits(self.ring_d).clone(), bits(self.ring_k).clone(), bits(self.ring_g).clone()
@@ -119,30 +165,29 @@ class Report:
                 f"flushes {self.flushes}")
 
 
-def sample_rows(slots: np.ndarray, n: Optional[int], seed: int = 0) -> np.ndarray:
-    live = np.where(slots >= 0)[0]
-    if n is None or n >= len(live):
-        return live
-    r = np.random.default_rng(seed)
-    return np.sort(r.choice(live, size=n, replace=False))
-
-
 def run_decode(w: gi.Workload, kind: str = "replay", steps: Optional[int] = None,
-               n_sample: Optional[int] = None, garbage: bool = False,
-               recon_every: int = 0, check_untouched: bool = False) -> Report:
+               garbage: bool = False, recon_every: int = 0,
+               check_untouched: bool = False, canary: bool = True) -> Report:
     """Drive `steps` single-token forwards of workload w through the library
     (kind 'replay': decode + advance; kind 'packed': packed decode) and the
-    oracle, asserting parity at every step. Cursors and flush positions are
-    checked for every row; values on the sampled rows."""
+    oracle, asserting parity at every step, on every live row: the outputs of
+    every row and head, every flushed checkpoint (replay) or the whole state
+    (packed) against the fp64 recurrence, cursors and flush positions bit for
+    bit. recon_every: every so many steps, the state each live slot's
+    checkpoint and valid ring entries represent is decoded in fp64 and
+    compared too. canary: o, the checkpoint pool and the rings are views into
+    larger buffers whose tails hold a fixed pattern, checked unchanged after
+    every step."""
     import linear_attention_ssm_amd as gdn
 
     steps = w.steps if steps is None else steps
     S0 = gi.initial_state(w)
     slots = gi.slot_map(w)
-    rows = sample_rows(slots, n_sample, seed=w.seed)
+    rows = np.where(slots >= 0)[0]
     sub = np.arange(len(rows), dtype=np.int32)
     S_true = S0[slots[rows]].astype(np.float64)
-    pool = Pool(w, S0, garbage=garbage)
+    pool = Pool(w, S0, garbage=garbage, canary=canary)
+    o_buf = CanaryTensor((w.B, 1, w.Hv, w.dv), w.qkv) if canary else None
     slot_t = to_dev(slots)
     wp_model = np.zeros(w.N, dtype=np.int64)
     written = np.zeros((w.N, w.L), dtype=bool)        # ring positions written so far
@@ -158,15 +203,19 @@ def run_decode(w: gi.Workload, kind: str = "replay", steps: Optional[int] = None
         ff = gi.force_flush_schedule(w, t, slots)
         ff_t = to_dev(ff)
         ck_before = pool.ckpt.clone() if kind == "replay" else None
+        o_arg = o_buf.t if o_buf is not None else None
         if kind == "replay":
             o = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, pool.ckpt,
                                       pool.ring_d, pool.ring_k, pool.ring_g, pool.write_pos,
-                                      force_flush=ff_t, err_flags=pool.err)
+                                      force_flush=ff_t, o=o_arg, err_flags=pool.err)
             gdn.gdn_replay_advance(slot_t, pool.write_pos, w.L, force_flush=ff_t,
                                    err_flags=pool.err)
         else:
             o = gdn.gdn_packed_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, pool.ckpt,
-                                      err_flags=pool.err)
+                                      o=o_arg, err_flags=pool.err)
+        if o_buf is not None:
+            o_buf.check(f"{w.name} step {t}: o")
+            pool.check_canaries(f"{w.name} step {t}")
         # expected cursors / flushes (integer state machine)
         exp_flush = np.zeros(w.N, dtype=bool)
         for b, s in enumerate(slots):
@@ -177,7 +226,7 @@ def run_decode(w: gi.Workload, kind: str = "replay", steps: Optional[int] = None
             if not fl:
                 written[s, wp_model[s]] = True
             wp_model[s] = nxt
-        # oracle values on the sampled rows
+        # oracle values on every live row
         q, k, v, g, beta = (a[rows, 0] for a in x.f64())
         o_ref = step(S_true, sub, q, k, v, g, beta)
         o_gpu = to_f64(o[rows, 0])
@@ -194,20 +243,24 @@ def run_decode(w: gi.Workload, kind: str = "replay", steps: Optional[int] = None
             assert np.array_equal(changed[live], exp_flush[live]), \
                 f"{w.name} step {t}: flush positions differ"
             rep.flushes += int(exp_flush.sum())
-            for i, r in enumerate(rows):
-                s = slots[r]
-                if exp_flush[s]:
-                    es = rel_err(to_f64(pool.ckpt[s]), S_true[i])
+            fl_i = np.array([i for i, r in enumerate(rows) if exp_flush[slots[r]]], np.int64)
+            if len(fl_i):
+                # every flushed checkpoint, each slot against its own true state
+                ck = to_f64(pool.ckpt[torch.from_numpy(slots[rows[fl_i]].astype(np.int64)).to(DEV)])
+                for j, i in enumerate(fl_i):
+                    es = rel_err(ck[j], S_true[i])
                     rep.state_err.append(es)
-                    assert es <= tol_s_, f"{w.name} step {t}: ckpt rel err {es:.3e}"
+                    assert es <= tol_s_, \
+                        f"{w.name} step {t}: row {rows[i]} ckpt rel err {es:.3e}"
             if recon_every and (t % recon_every == recon_every - 1 or t == steps - 1):
-                for i, r in enumerate(rows[:4]):
+                for i, r in enumerate(rows):
                     s = slots[r]
                     er = rel_err(reconstruct(pool, s, int(wp_model[s])), S_true[i])
                     rep.recon_err.append(er)
-                    assert er <= tol_s_, f"{w.name} step {t}: reconstructed state {er:.3e}"
+                    assert er <= tol_s_, \
+                        f"{w.name} step {t}: row {r} reconstructed state {er:.3e}"
         else:
-            ck = to_f64(pool.ckpt[torch.from_numpy(slots[rows]).to(DEV)])
+            ck = to_f64(pool.ckpt[torch.from_numpy(slots[rows].astype(np.int64)).to(DEV)])
             es = rel_err(ck, S_true)
             rep.state_err.append(es)
             assert es <= tol_s_, f"{w.name} step {t}: packed state rel err {es:.3e}"

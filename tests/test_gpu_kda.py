@@ -40,23 +40,23 @@ def test_kda_tiny_fp32_packed(gdn):
 
 
 def test_kda_standard_replay(gdn):
-    run_decode(gi.C7, "replay", n_sample=6, garbage=True, recon_every=16)
+    run_decode(gi.C7, "replay", garbage=True, recon_every=16)
 
 
 def test_kda_standard_packed(gdn):
-    run_decode(gi.C7, "packed", n_sample=6)
+    run_decode(gi.C7, "packed")
 
 
 @pytest.mark.parametrize("L", [1, 4, 32])
 def test_kda_ring_depth(gdn, L):
     w = dataclasses.replace(gi.C7, name=f"c7_kda_L{L}", L=L, steps=40, seed=810 + L)
-    run_decode(w, "replay", n_sample=4, recon_every=20 if L > 1 else 0)
+    run_decode(w, "replay", recon_every=20 if L > 1 else 0)
 
 
 def test_kda_fp32_ring(gdn):
     w = dataclasses.replace(gi.C7, name="c7_kda_f32ring", ring="f32", qkv="f32",
                             bf16_values=True, steps=40, seed=850)
-    run_decode(w, "replay", n_sample=4, recon_every=16)
+    run_decode(w, "replay", recon_every=16)
 
 
 @pytest.mark.parametrize("ring", ["f16", "bf16", "f32"])
@@ -100,8 +100,8 @@ def test_kda_L1_replay_equals_packed_bitwise(gdn, fmt):
 def test_kda_state16(gdn, fmt):
     w = dataclasses.replace(gi.C7, name=f"c7_kda_{fmt}", state=fmt, B=16, N=16, steps=34,
                             seed=870)
-    run_packed16(gdn, w, n_sample=4)
-    assert run_replay16(gdn, w, n_sample=4) > 0
+    run_packed16(gdn, w)
+    assert run_replay16(gdn, w) > 0
 
 
 @pytest.mark.parametrize("ring", ["f16", "f32"])
@@ -132,8 +132,8 @@ def test_kda_verify_commit_fold(gdn, ring):
         e = rel_err(to_f64(o), o_ref)
         worst["win"] = max(worst["win"], e)
         assert e <= tol_o(w), f"round {r}: window output rel err {e:.3e}"
-        rd = to_f64(pool.ring_d)
-        d_gpu = np.stack([rd[s, :, p_before[s]:p_before[s] + T].transpose(1, 0, 2)
+        # only the written entries are converted (the rest hold a garbage template)
+        d_gpu = np.stack([to_f64(pool.ring_d[s, :, p_before[s]:p_before[s] + T]).transpose(1, 0, 2)
                           for s in slots])
         ed = rel_err(d_gpu, u_ref)
         worst["d"] = max(worst["d"], ed)

@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import gdn_inputs as gi
-from gdn_harness import (DEV, TORCH_DT, Pool, bits, dev_inputs, log, to_dev, to_f64, tol_o,
-                         tol_state)
+from gdn_harness import (DEV, TORCH_DT, CanaryTensor, Pool, bits, dev_inputs, log, to_dev,
+                         to_f64, tol_o, tol_state)
 from oracle import fold_f32, gdn_step, rel_err, window_ref
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +47,8 @@ def test_c5_verify_commit_fold_protocol(gdn, ring):
     S0 = gi.initial_state(w)
     slots = gi.slot_map(w)
     hist = gi.history_lengths(w)
-    pool = Pool(w, S0, garbage=True)
+    pool = Pool(w, S0, garbage=True, canary=True)
+    o_win = CanaryTensor((w.B, T, w.Hv, w.dv), w.qkv)
     S_true = S0.astype(np.float64)
     wp = np.zeros(w.N, dtype=np.int64)
     tol_o_, tol_s_ = tol_o(w), tol_state(w)
@@ -78,15 +79,17 @@ def test_c5_verify_commit_fold_protocol(gdn, ring):
         assert np.all(p_before[slots] + T <= L)
         o = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, pool.ckpt,
                                   pool.ring_d, pool.ring_k, pool.ring_g, pool.write_pos,
-                                  err_flags=pool.err, window=True)
+                                  o=o_win.t, err_flags=pool.err, window=True)
+        o_win.check(f"round {r}: window o")
+        pool.check_canaries(f"round {r}: window")
         x64 = x.f64()
         o_ref, u_ref = window_ref(S_true, slots, *x64, want_u=True)
         e = rel_err(to_f64(o), o_ref)
         errs["win"].append(e)
         assert e <= tol_o_, f"round {r}: window output rel err {e:.3e}"
         # the window's corrections were written at p .. p+T-1
-        rd = to_f64(pool.ring_d)
-        d_gpu = np.stack([rd[s, :, p_before[s]:p_before[s] + T].transpose(1, 0, 2)
+        # only the written entries are converted (the rest hold a garbage template)
+        d_gpu = np.stack([to_f64(pool.ring_d[s, :, p_before[s]:p_before[s] + T]).transpose(1, 0, 2)
                           for s in slots])                              # [B, T, Hv, dv]
         ed = rel_err(d_gpu, u_ref)
         errs["d"].append(ed)
@@ -102,6 +105,7 @@ def test_c5_verify_commit_fold_protocol(gdn, ring):
             sl = np.where(need, slots, -1).astype(np.int32)
             gdn.gdn_replay_fold(to_dev(sl), pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
                                 pool.write_pos, err_flags=pool.err)
+            pool.check_canaries(f"round {r}: fold")
             assert np.array_equal(pool.write_pos.cpu().numpy(), wp), "the fold moved a cursor"
             gdn.gdn_replay_reset(to_dev(sl), pool.write_pos, err_flags=pool.err)
             wp[slots[need]] = 0
@@ -112,6 +116,7 @@ def test_c5_verify_commit_fold_protocol(gdn, ring):
     gdn.gdn_replay_fold(slot_t, pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
                         pool.write_pos, err_flags=pool.err)
     gdn.gdn_replay_reset(slot_t, pool.write_pos, err_flags=pool.err)
+    pool.check_canaries("final fold and reset")
     ef = rel_err(to_f64(pool.ckpt), S_true)
     errs["fold"].append(ef)
     assert ef <= tol_s_
@@ -160,12 +165,14 @@ def test_fold_bitwise_against_oracle(gdn, ring):
     live = slots[slots >= 0]
     wp[live[0]] = w.L          # a full ring
     wp[live[1]] = 0            # an empty one
-    ckpt = to_dev(rc.ckpt)
+    ck_guard = CanaryTensor(rc.ckpt.shape, "f32", init=to_dev(rc.ckpt))
+    ckpt = ck_guard.t
     rd, rk = to_dev(rc.d, ring), to_dev(rc.k, ring)
     rg = to_dev(rc.g)
     wpt = to_dev(wp.astype(np.int32))
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     gdn.gdn_replay_fold(to_dev(slots), ckpt, rd, rk, rg, wpt, err_flags=err)
+    ck_guard.check("fold: ckpt")
     assert np.array_equal(wpt.cpu().numpy(), wp.astype(np.int32))
     gdn.gdn_replay_reset(to_dev(slots), wpt, err_flags=err)
     ref = rc.ckpt.copy()
