@@ -118,7 +118,8 @@ typedef enum {
     GDN_OK = 0,
     GDN_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size or mode    */
     GDN_ERR_UNSUPPORTED = 2, /* a size or dtype outside the compiled set        */
-    GDN_ERR_HIP = 3          /* the HIP runtime refused the launch              */
+    GDN_ERR_HIP = 3,         /* the HIP runtime refused the launch              */
+    GDN_ERR_SCRATCH_LIMIT = 4 /* B > GDN_SCRATCH_MAX_ROWS (the _noalloc call)   */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
@@ -244,6 +245,35 @@ gdn_status gdn_replay_decode_advance(const gdn_shape *shape, const void *q, cons
                                      void *ring_k, float *ring_g, int32_t *write_pos,
                                      const int32_t *force_flush, void *o, int32_t *arrive,
                                      int32_t *err_flags, void *stream);
+
+/*
+ * gdn_replay_decode_advance_noalloc -- gdn_replay_decode_advance for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. It allocates nothing, not
+ * even through the caller: the arrival counters live in a static device
+ * array of the library instead of the caller's `arrive` workspace.
+ *   Limit: B <= GDN_SCRATCH_MAX_ROWS (4096) rows; a larger B returns
+ *   GDN_ERR_SCRATCH_LIMIT before anything is enqueued. The array is 512 KiB
+ *   (one 128-byte line per row) on every device the library runs on, held
+ *   until the process ends.
+ *   Set-up: the first call on a device (the device current at the call)
+ *   looks up that device's copy of the array and enqueues one clear of it on
+ *   `stream`; make that first call outside stream capture.
+ *   Sharing: every call on one device uses the same array, which keeps what
+ *   the last call left (all zero after every completed call). Calls that
+ *   overlap on one device (different streams, or host threads racing on one
+ *   stream) race on the counters; calls ordered on one stream do not.
+ * Outputs, checkpoint, ring and cursor writes, error bits and every other
+ * argument are those of gdn_replay_decode_advance (with window = 0, T = 1).
+ */
+#define GDN_SCRATCH_MAX_ROWS 4096
+gdn_status gdn_replay_decode_advance_noalloc(const gdn_shape *shape, const void *q,
+                                             const void *k, const void *v, const float *g,
+                                             const float *beta, const int32_t *slot_idx,
+                                             void *ckpt, void *ring_d, void *ring_k,
+                                             float *ring_g, int32_t *write_pos,
+                                             const int32_t *force_flush, void *o,
+                                             int32_t *err_flags, void *stream);
 
 /*
  * gdn_replay_advance -- the cursor advance that follows a forward's decode

@@ -20,10 +20,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn_replay.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gdn_replay.h")
 
-GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP, GDN_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
 GDN_GATE_HEAD, GDN_GATE_KEY = 0, 1
 ARRIVE_STRIDE = 32          # int32 per row in the arrive workspace (GDN_ARRIVE_STRIDE)
+SCRATCH_MAX_ROWS = 4096     # rows of gdn_replay_decode_advance_noalloc (GDN_SCRATCH_MAX_ROWS)
 EF_SLOT_RANGE, EF_CURSOR_RANGE, EF_WINDOW, EF_ACCEPTED = 1, 2, 4, 8
 
 _DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
@@ -64,20 +65,22 @@ _S = ctypes.POINTER(gdn_shape)
 _lib.gdn_packed_decode.argtypes = [_S] + [_P] * 10
 _lib.gdn_replay_decode.argtypes = [_S] + [_P] * 15
 _lib.gdn_replay_decode_advance.argtypes = [_S] + [_P] * 16
+_lib.gdn_replay_decode_advance_noalloc.argtypes = [_S] + [_P] * 15
 _lib.gdn_replay_advance.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_commit.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_fold.argtypes = [_S] + [_P] * 8
 _lib.gdn_replay_reset.argtypes = [_S] + [_P] * 4
 _lib.gdn_conv_update.argtypes = [ctypes.POINTER(gdn_conv_shape)] + [_P] * 7
 _lib.gdn_kda_gates.argtypes = [ctypes.POINTER(gdn_gate_shape)] + [_P] * 7
-for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_decode_advance", "gdn_replay_advance",
+for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_decode_advance",
+           "gdn_replay_decode_advance_noalloc", "gdn_replay_advance",
            "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_reset", "gdn_conv_update",
            "gdn_kda_gates"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 8
+ABI_VERSION = 9
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -304,6 +307,30 @@ def gdn_replay_decode_advance(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, 
         ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
         _ptr(ckpt), _ptr(ring_d), _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(force_flush),
         _ptr(o), _ptr(arrive), _ptr(err_flags), _stream(stream)), "gdn_replay_decode_advance")
+    return o
+
+
+def gdn_replay_decode_advance_noalloc(q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g,
+                                      write_pos, o, force_flush=None, err_flags=None,
+                                      stream=None, qk_norm=False):
+    """gdn_replay_decode_advance without the arrive workspace, for callers that
+    cannot allocate: the library counts in its own static device scratch (at
+    most SCRATCH_MAX_ROWS rows); see gdn_replay_decode_advance_noalloc in
+    gdn_replay.h. o [B,1,Hv,dv] must be given (nothing is allocated here
+    either). Returns o."""
+    B, T, Hk, dk, Hv, dv, dev, gate, qs, vs = _io_shape(q, k, v, g, beta, slot_idx)
+    N, L = _ring_shape(ckpt, ring_d, ring_k, ring_g, write_pos, Hv, Hk, dk, dv, dev, gate)
+    _row_flags(force_flush, "force_flush", B, dev)
+    _err_word(err_flags, dev)
+    if o is None:
+        raise ValueError("o must be given: this call allocates nothing")
+    o = _out(o, B, T, Hv, dv, q.dtype, dev)
+    sh = _shape(B, T, N, Hv, Hk, dk, dv, L, _DT[q.dtype], _DT[ring_d.dtype], 0,
+                _DT[ckpt.dtype], 0, gate, qs, vs, qk_norm)
+    _raise(_lib.gdn_replay_decode_advance_noalloc(
+        ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx),
+        _ptr(ckpt), _ptr(ring_d), _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(force_flush),
+        _ptr(o), _ptr(err_flags), _stream(stream)), "gdn_replay_decode_advance_noalloc")
     return o
 
 

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "gdn_launch.h"
 #include "gdn_replay.h"
@@ -12,7 +13,7 @@ using namespace gdn;
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 static_assert(kArriveStride == GDN_ARRIVE_STRIDE, "arrival counter stride");
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -196,13 +197,19 @@ gdn_status gdn_packed_decode(const gdn_shape* s, const void* q, const void* k, c
 
 namespace {
 
-// gdn_replay_decode and gdn_replay_decode_advance: arrive == nullptr is the
-// plain decode (write_pos only read); otherwise the cursor advance is fused.
+gdn_status static_scratch(int32_t** out, hipStream_t stream);
+
+// gdn_replay_decode, gdn_replay_decode_advance and
+// gdn_replay_decode_advance_noalloc: arrive == nullptr and !use_scratch is the
+// plain decode (write_pos only read); otherwise the cursor advance is fused,
+// counting in the caller's arrive workspace or (use_scratch) in the library's
+// static scratch.
 gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const int32_t* slot_idx,
                          void* ckpt, void* ring_d, void* ring_k, float* ring_g,
                          const int32_t* write_pos, const int32_t* force_flush, void* o,
-                         int32_t* arrive, int32_t* err_flags, void* stream) {
+                         int32_t* arrive, int32_t* err_flags, void* stream,
+                         bool use_scratch = false) {
   const gdn_status st = check_shape(s, true);
   if (st != GDN_OK) return st;
   if (s->window != 0 && s->window != 1) return GDN_ERR_INVALID_ARG;
@@ -222,6 +229,7 @@ gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const
       (force_flush && !aligned(force_flush, 4)))
     return GDN_ERR_INVALID_ARG;
   if (arrive && (s->window != 0 || !aligned(arrive, 128))) return GDN_ERR_INVALID_ARG;
+  if (use_scratch && (s->window != 0 || s->B > GDN_SCRATCH_MAX_ROWS)) return GDN_ERR_INVALID_ARG;
   if (s->B == 0) return GDN_OK;
   DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.slot = slot_idx; a.state = ckpt;
@@ -294,9 +302,55 @@ gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const
   a.dump_off = static_cast<int32_t>(up16(end));
   const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
   if (smem > 160 * 1024) return GDN_ERR_UNSUPPORTED;
+  if (use_scratch) {
+    // every argument is valid: only now may the first call on a device set
+    // up the scratch (address lookup, one clear enqueued on the stream)
+    const gdn_status ss = static_scratch(&a.arrive, static_cast<hipStream_t>(stream));
+    if (ss != GDN_OK) return ss;
+  }
   return from_hip(dispatch_replay(s->dk, a, s->qkv_dtype, s->ring_dtype, s->state_dtype, s->gate,
                                   dim3(n_items), block,
                                   smem, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+// ------------------------------------------------------------- static scratch
+//
+// The arrival counters of gdn_replay_decode_advance_noalloc: one 128-byte
+// line (GDN_ARRIVE_STRIDE int32) per row for up to GDN_SCRATCH_MAX_ROWS rows,
+// 512 KiB held on every device the library runs on until the process ends.
+// In host code `scratch` is only a host-side stand-in for the device array:
+// its device address is looked up once per device with hipGetSymbolAddress
+// (that device current) and kept in scratch_ptr, which is what kernels and
+// launches receive.
+static __device__ __align__(256) int32_t scratch[GDN_SCRATCH_MAX_ROWS * GDN_ARRIVE_STRIDE];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+int32_t* scratch_ptr[kMaxDevices];   // per device, set on its first call
+
+// The current device's copy of the scratch. The first call on a device looks
+// up its address and enqueues one clear of the whole array on `stream` (the
+// counters must start at zero; every completed call leaves them zero).
+gdn_status static_scratch(int32_t** out, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GDN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return GDN_ERR_HIP;
+    int32_t* sp = static_cast<int32_t*>(p);
+    if (launch_zero(sp, GDN_SCRATCH_MAX_ROWS * GDN_ARRIVE_STRIDE, stream) != hipSuccess)
+      return GDN_ERR_HIP;
+    scratch_ptr[dev] = sp;
+  }
+  *out = scratch_ptr[dev];
+  return GDN_OK;
 }
 
 }  // namespace
@@ -321,6 +375,17 @@ gdn_status gdn_replay_decode_advance(const gdn_shape* s, const void* q, const vo
   if (!arrive) return GDN_ERR_INVALID_ARG;
   return replay_decode(s, q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
                        force_flush, o, arrive, err_flags, stream);
+}
+
+gdn_status gdn_replay_decode_advance_noalloc(const gdn_shape* s, const void* q, const void* k,
+                                             const void* v, const float* g, const float* beta,
+                                             const int32_t* slot_idx, void* ckpt, void* ring_d,
+                                             void* ring_k, float* ring_g, int32_t* write_pos,
+                                             const int32_t* force_flush, void* o,
+                                             int32_t* err_flags, void* stream) {
+  if (s && s->B > GDN_SCRATCH_MAX_ROWS) return GDN_ERR_SCRATCH_LIMIT;
+  return replay_decode(s, q, k, v, g, beta, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos,
+                       force_flush, o, nullptr, err_flags, stream, true);
 }
 
 gdn_status gdn_replay_advance(const gdn_shape* s, const int32_t* slot_idx, int32_t* write_pos,
@@ -404,6 +469,8 @@ const char* gdn_status_string(gdn_status status) {
     case GDN_ERR_INVALID_ARG: return "invalid argument";
     case GDN_ERR_UNSUPPORTED: return "unsupported size or dtype";
     case GDN_ERR_HIP: return "HIP launch error";
+    case GDN_ERR_SCRATCH_LIMIT:
+      return "more rows than the static scratch holds (GDN_SCRATCH_MAX_ROWS)";
   }
   return "unknown status";
 }

@@ -59,6 +59,11 @@ __global__ static void commit_kernel(CursorArgs a) {
   a.write_pos[s] = p + acc;
 }
 
+// n int32 zeros at p (one thread per element).
+__global__ static void zero_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
 
 static hipError_t launch_rows(void (*kernel)(CursorArgs), const CursorArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(kernel, dim3((a.B + 255) / 256), dim3(256), 0, st, a);
@@ -68,5 +73,11 @@ static hipError_t launch_rows(void (*kernel)(CursorArgs), const CursorArgs& a, h
 hipError_t launch_reset(const CursorArgs& a, hipStream_t st) { return launch_rows(reset_kernel, a, st); }
 hipError_t launch_advance(const CursorArgs& a, hipStream_t st) { return launch_rows(advance_kernel, a, st); }
 hipError_t launch_commit(const CursorArgs& a, hipStream_t st) { return launch_rows(commit_kernel, a, st); }
+
+hipError_t launch_zero(int32_t* p, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
 
 }  // namespace gdn

@@ -20,5 +20,6 @@ hipError_t launch_fold(const FoldArgs& a, int ring, int sd, int kg, dim3 grid, d
 hipError_t launch_reset(const CursorArgs& a, hipStream_t stream);
 hipError_t launch_advance(const CursorArgs& a, hipStream_t stream);
 hipError_t launch_commit(const CursorArgs& a, hipStream_t stream);
+hipError_t launch_zero(int32_t* p, int n, hipStream_t stream);
 
 }  // namespace gdn

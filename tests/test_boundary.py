@@ -10,7 +10,8 @@ from linear_attention_ssm_amd import gdn_shape
 
 EXPECTED = ["gdn_abi_version", "gdn_conv_update", "gdn_kda_gates", "gdn_packed_decode",
             "gdn_replay_advance", "gdn_replay_commit",
-            "gdn_replay_decode", "gdn_replay_decode_advance", "gdn_replay_fold",
+            "gdn_replay_decode", "gdn_replay_decode_advance",
+            "gdn_replay_decode_advance_noalloc", "gdn_replay_fold",
             "gdn_replay_reset", "gdn_status_string"]
 
 # Fake, 256-byte aligned, non-null device addresses: never dereferenced, since
@@ -30,8 +31,8 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 8
-    for st in range(4):
+    assert lib.gdn_abi_version() == 9
+    for st in range(5):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
 
@@ -116,6 +117,27 @@ def test_decode_advance_validates():
     assert call(shape(T=2, window=1), FAKE[14]) == gdn.GDN_ERR_INVALID_ARG   # windows: no
     assert call(shape(dk=96), FAKE[14]) == gdn.GDN_ERR_UNSUPPORTED
     assert call(shape(B=0), FAKE[14]) == gdn.GDN_OK
+
+
+def test_decode_advance_noalloc_validates():
+    """The no-allocation variant rejects more rows than its static scratch
+    holds with its own status, and otherwise validates like the workspace
+    variant (all before any HIP call)."""
+    lib = gdn.lib()
+
+    def call(sh):
+        p = list(FAKE[:12])
+        return lib.gdn_replay_decode_advance_noalloc(ctypes.byref(sh), *p[:11], None, p[11],
+                                                     None, None)
+    assert call(shape(B=gdn.SCRATCH_MAX_ROWS + 1, N=8192)) == gdn.GDN_ERR_SCRATCH_LIMIT
+    assert call(shape(T=2, window=1)) == gdn.GDN_ERR_INVALID_ARG     # windows: no
+    assert call(shape(dk=96)) == gdn.GDN_ERR_UNSUPPORTED
+    p = list(FAKE[:12])
+    p[0] = ctypes.c_void_p(FAKE[0].value + 4)                        # misaligned q
+    assert lib.gdn_replay_decode_advance_noalloc(ctypes.byref(shape()), *p[:11], None, p[11],
+                                                 None, None) == gdn.GDN_ERR_INVALID_ARG
+    assert call(shape(B=0)) == gdn.GDN_OK
+    assert lib.gdn_status_string(gdn.GDN_ERR_SCRATCH_LIMIT).startswith(b"more rows")
 
 
 def test_empty_batch_is_a_no_op():
