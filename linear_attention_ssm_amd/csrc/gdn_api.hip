@@ -299,6 +299,9 @@ gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const
       end += static_cast<size_t>((ntg + 63) / 64) * 1024;
     }
   }
+  // a window's v values, [waves][16 tokens][16 rows] floats
+  a.v_off = static_cast<int32_t>(up16(end));
+  if (s->T > 1) end = a.v_off + static_cast<size_t>(block.x / 64) * 16 * 16 * sizeof(float);
   a.dump_off = static_cast<int32_t>(up16(end));
   const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
   if (smem > 160 * 1024) return GDN_ERR_UNSUPPORTED;

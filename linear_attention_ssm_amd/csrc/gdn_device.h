@@ -626,6 +626,7 @@ struct DecodeArgs {
   // LDS byte offsets: per-token k^T q, per (head, token) gates (alpha, beta,
   // g), the staged key ring
   int32_t kq_off, gate_off, kt_off;
+  int32_t v_off;           // LDS byte offset of the window's v values ([waves][16][16] floats)
   int32_t step_round;      // round a 16-bit state after each window token
   // per-key gate (KDA) only, LDS byte offsets: the staged gates of the
   // workgroup's heads and tokens ([GH][T][4][dk] floats, see stage_key_gate),
