@@ -239,6 +239,11 @@ gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const
   a.force_flush = force_flush; a.o = o; a.err = err_flags; a.window = s->window;
   fill_inputs(s, a);
   a.step_round = s->step_rounding;
+  // windows over a 16-bit ring are read out in chunked form (products on the
+  // MFMA units); an fp32 ring keeps the token-by-token update, whose rounding
+  // matches the packed decode bit for bit (lossless verify)
+  a.win_mfma = (s->window == 1 && s->T >= 2 && s->T <= 8 && s->gate == GDN_GATE_HEAD &&
+                s->step_rounding == 0 && s->ring_dtype != GDN_F32) ? 1 : 0;
   // the kernel reads one flag per row unconditionally; without
   // force_flush it reads the slot array and ignores the value
   a.ff_on = force_flush != nullptr;

@@ -505,15 +505,22 @@ __device__ __forceinline__ f4 row_swap8(f4 x) {
   return r;
 }
 
-// One 16-byte store with the device-scope, non-temporal cache policy (sc1 nt)
-// through a buffer resource over `nbytes` bytes at the wave-uniform `base`.
-// A checkpoint line written this way goes on to memory at once instead of
-// staying dirty in L2 until the state stream evicts it at some later point,
-// between other reads; nothing reads it again in the same launch.
-__device__ __forceinline__ void store16_nt(float* base, int nbytes, int byte_off, f4 x) {
-  constexpr int SC1_NT = 16 | 2;
+// Cache-policy bits of the gfx950 buffer stores (sc0 = 1, nt = 2, sc1 = 16).
+// Measured on MI355X, per kernel:
+//   sc1 nt  the packed decode's state write-back: a line goes on to memory at
+//           once instead of staying dirty in L2 until the state stream evicts
+//           it between other reads (49.8 us per launch, 54-56 us otherwise);
+//   sc1     the replay decode's flush, whose checkpoint loads are
+//           non-temporal: 0.4 us faster per launch than sc1 nt.
+constexpr int kCpolSc1Nt = 16 | 2;
+constexpr int kCpolSc1 = 16;
+
+// One 16-byte store with cache policy CP through a buffer resource over
+// `nbytes` bytes at the wave-uniform `base`.
+template <int CP>
+__device__ __forceinline__ void store16(float* base, int nbytes, int byte_off, f4 x) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), rs, byte_off, 0, SC1_NT);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), rs, byte_off, 0, CP);
 }
 
 // A 16-bit state's on-chip values rounded to the format and widened back
@@ -528,11 +535,11 @@ __device__ __forceinline__ void slab_round(f4 (&S)[NT]) {
   }
 }
 
-// The 8-byte form of store16_nt.
-__device__ __forceinline__ void store8_nt(float* base, int nbytes, int byte_off, u16x4 x) {
-  constexpr int SC1_NT = 16 | 2;
+// The 8-byte form of store16.
+template <int CP>
+__device__ __forceinline__ void store8(float* base, int nbytes, int byte_off, u16x4 x) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, x), rs, byte_off, 0, SC1_NT);
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, x), rs, byte_off, 0, CP);
 }
 
 // Store a wavefront's 16-row slab, rounded to the state format (round to
@@ -543,9 +550,8 @@ __device__ __forceinline__ void store8_nt(float* base, int nbytes, int byte_off,
 // rows 8-15, each covering the pair's 2 x 64 bytes of all eight rows. A slab
 // with one piece per lane (16-bit, dk = 32) is written piece by piece.
 // `slab` is the wave-uniform address of row 0; rows are DK elements apart.
-// The stores use store16_nt: a slab goes to memory in one burst. Needs all 64
-// lanes active.
-template <int SD, int DK>
+// The stores carry cache policy CP. Needs all 64 lanes active.
+template <int SD, int DK, int CP>
 __device__ __forceinline__ void store_slab(void* slab, const f4 (&S)[DK / 16], int col, int grp) {
   constexpr int ES = SD == DT_F32 ? 4 : 2;          // bytes per element
   constexpr int NP = SlabRaw<SD, DK>::NP;
@@ -572,7 +578,7 @@ __device__ __forceinline__ void store_slab(void* slab, const f4 (&S)[DK / 16], i
     }
   }
   if constexpr (NP == 1) {
-    store16_nt(base, NB, (col * DK + KG * grp) * ES, X[0]);
+    store16<CP>(base, NB, (col * DK + KG * grp) * ES, X[0]);
   } else {
     const bool lo = col < 8;
     const int r = col & 7;
@@ -581,8 +587,8 @@ __device__ __forceinline__ void store_slab(void* slab, const f4 (&S)[DK / 16], i
     for (int u = 0; u < NP / 2; ++u) {
       const f4 x0 = X[2 * u], x1 = X[2 * u + 1];
       const f4 z = row_swap8(lo ? x1 : x0);
-      store16_nt(base, NB, (r * DK + 2 * KP * u + k0) * ES, lo ? x0 : z);
-      store16_nt(base, NB, ((r + 8) * DK + 2 * KP * u + k0) * ES, lo ? z : x1);
+      store16<CP>(base, NB, (r * DK + 2 * KP * u + k0) * ES, lo ? x0 : z);
+      store16<CP>(base, NB, ((r + 8) * DK + 2 * KP * u + k0) * ES, lo ? z : x1);
     }
   }
 }
@@ -616,6 +622,7 @@ struct DecodeArgs {
   int32_t VB;              // value rows per head per work item (multiple of 16)
   int32_t nvb;             // dv / VB
   int32_t window;          // 1: verify window (no flush, entries at p..p+T-1)
+  int32_t win_mfma;        // window read out in chunked form (see window_chunked)
   int32_t kts;             // LDS row stride (elements) of the transposed key ring
   int32_t dump_off;        // LDS byte offset of the [64][8] fp32 write sink
   // work-item mapping of the replay kernel without runtime divisions: the

@@ -49,7 +49,8 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   const int b = blk / a.Hk;
   const int wph = a.VB / 16;
   const int h = hk * a.G + wave / wph;
-  const int vcol = vb * a.VB + (wave % wph) * 16 + col;
+  const int vrow0 = vb * a.VB + (wave % wph) * 16;   // the wavefront's first value row
+  const int vcol = vrow0 + col;
 
   const int s = ld_uniform(a.slot, b);
   if (s < 0 || s >= a.N) {
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   const float gv = KG ? 0.f : ld_uniform(a.g, ih), bt = ld_uniform(a.beta, ih);
 
   using SE = typename Elem<SD>::T;
-  SE* st = static_cast<SE*>(a.state) + ((static_cast<size_t>(s) * a.Hv + h) * a.dv + vcol - col) * DK;
+  SE* st = static_cast<SE*>(a.state) + ((static_cast<size_t>(s) * a.Hv + h) * a.dv + vrow0) * DK;
   SlabRaw<SD, DK> R;
   slab_load<SD, DK>(R, st, col, grp);
 
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
   if (grp == 0) store1<QKV>(a.o, ih * a.dv + vcol, o);
   if constexpr (KG) slab_update_key<SD>(S, qk + DK, kgl + (h - hk * a.G) * 4 * DK, grp, d);
   else slab_update<SD>(S, qk + DK, grp, alpha, d);
-  store_slab<SD, DK>(st, S, col, grp);
+  store_slab<SD, DK, kCpolSc1Nt>(st, S, col, grp);
 }
 
 // ============================================================= replay decode
@@ -187,7 +188,9 @@ template <> struct RingMfma<DT_F32> {
 
 // Where a work item sits, and which head / value row this lane holds in it.
 struct ItemGeo {
-  int b, hk, hc, vb, h, vcol;
+  int b, hk, hc, vb, h;
+  int vrow0;   // the wavefront's first value row (wave-uniform: slab base addresses)
+  int vcol;    // this lane's value row
 };
 
 __device__ __forceinline__ ItemGeo item_geo(const DecodeArgs& a, int wave, int col) {
@@ -211,7 +214,8 @@ __device__ __forceinline__ ItemGeo item_geo(const DecodeArgs& a, int wave, int c
   const int wph = a.VB / 16;                    // wavefronts per head
   const int wh = static_cast<int>(udiv(static_cast<uint32_t>(wave), a.m_wph));
   g.h = g.hk * a.G + g.hc * a.GH + wh;
-  g.vcol = g.vb * a.VB + (wave - wh * wph) * 16 + col;
+  g.vrow0 = g.vb * a.VB + (wave - wh * wph) * 16;
+  g.vcol = g.vrow0 + col;
   return g;
 }
 
@@ -401,7 +405,7 @@ __device__ __forceinline__ void fetch_slab(SlabRaw<SD, DK>& R, const DecodeArgs&
                                            const ItemGeo& g, const RowState& r, int col, int grp) {
   constexpr int ES = SD == DT_F32 ? 4 : 2;
   const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
-  const char* base = static_cast<const char*>(a.state) + (hs * a.dv + g.vcol - col) * DK * ES;
+  const char* base = static_cast<const char*>(a.state) + (hs * a.dv + g.vrow0) * DK * ES;
   const __amdgpu_buffer_rsrc_t rs = brsrc(base, r.ok ? 16 * DK * ES : 0);
   if constexpr (SD == DT_F32) {
     // whole 128-byte lines per instruction: rows 0-7 then rows 8-15 of keys
@@ -599,6 +603,107 @@ __device__ __forceinline__ void weight_keys_lds(const DecodeArgs& a, int lp, uns
       *reinterpret_cast<uint2*>(kw + c * a.kts + e0 + 4) = pk[1];
     }
     if (e0 == 0) acol[hh * DK + c] = __expf(W);
+  }
+}
+
+// Verify window in chunked form (a.win_mfma: 16-bit ring, 2 <= T <= 8, gate
+// per head, no per-step rounding). The window's tokens are read out of the
+// pre-window slab S_0 without updating it token by token: the recurrence
+// S_{t+1} = alpha_t S_t + d_t k_t^T gives, for any vector x,
+//     S_{t+1} x = alpha_t (S_t x) + d_t (k_t . x),
+// so every S_t q_t and S_t k_t follows from the products S_0 q_m, S_0 k_m of
+// all window tokens m and the window's inner products k_j . q_m, k_j . k_m
+// (the causal mask over the window, vLLM PR #49887, Core concept). Both sets
+// of products are dense contractions and run on the MFMA units
+// (16x16x4 fp32): with the lane's A operand the window vector x_m (m = the
+// lane's column; q_m for m < 8, k_{m-8} else), P = X^T S_0^T takes the slab
+// registers as the B operand, and the Gram matrix X^T X the same operand
+// twice. The per-row recurrence over the T tokens then costs O(T^2) scalar
+// operations instead of two passes over the 16 x dk slab per token. The
+// results differ from the token-by-token update only in rounding.
+template <int DK, int QKV, int RING, int SD>
+__device__ __forceinline__ void window_chunked(const DecodeArgs& a, const ItemGeo& g,
+                                               const RowState& r, int T, const f4 (&S)[DK / 16],
+                                               const float* qk, const float* vl, const float* gts,
+                                               size_t hs, size_t ks, bool kwriter,
+                                               bool gwriter_wave, int grp, int col, int lane) {
+  constexpr int NT = DK / 16;
+  constexpr int C4 = DK / 4;
+  // this lane's window vector (vector slots past T read q_0; their rows of
+  // the products are never used)
+  const int tv = col & 7;
+  const float* xv = qk + (tv < T ? tv : 0) * 2 * DK + (col >= 8 ? DK : 0);
+  f4 P = {0.f, 0.f, 0.f, 0.f}, Gm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const f4 xa = *reinterpret_cast<const f4*>(xv + key_base<SD>(t, grp));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      P = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i], S[t][i], P, 0, 0, 0);
+      Gm = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i], xa[i], Gm, 0, 0, 0);
+    }
+  }
+  // P: lane (row col, group grp) holds x_m . S_0[row] for m = 4 grp + i in
+  // register i. Gather all 16 into every lane of the row: v_permlane16_swap
+  // pairs groups (0,1) and (2,3), v_permlane32_swap the two halves.
+  float pv[16];
+  {
+    float e[4], o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(P[i]), __float_as_uint(P[i]),
+                                                      false, false);
+      e[i] = __uint_as_float(w[0]);   // from the pair's even group
+      o[i] = __uint_as_float(w[1]);   // from its odd group
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto we = __builtin_amdgcn_permlane32_swap(__float_as_uint(e[i]), __float_as_uint(e[i]),
+                                                       false, false);
+      const auto wo = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[i]), __float_as_uint(o[i]),
+                                                       false, false);
+      pv[i] = __uint_as_float(we[0]);        // group 0
+      pv[8 + i] = __uint_as_float(we[1]);    // group 2
+      pv[4 + i] = __uint_as_float(wo[0]);    // group 1
+      pv[12 + i] = __uint_as_float(wo[1]);   // group 3
+    }
+  }
+  // Gram entry (u, v) = x_u . x_v sits in lane v + 16 (u / 4), register u % 4
+  auto gram = [&](int u, int v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Gm[u & 3]), v + 16 * (u >> 2)));
+  };
+  float pq[8], pk[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    pq[m] = pv[m];
+    pk[m] = pv[8 + m];
+  }
+  const bool app = r.ok;                       // a window never flushes
+#pragma unroll
+  for (int tau = 0; tau < 8; ++tau) {
+    if (tau < T) {
+      const float* gt = gts + 3 * tau;
+      const float alpha = gt[0], bt = gt[1], gv = gt[2];
+      const float vv = vl[tau * 16 + col];
+      float d, o;
+      token_out(pq[tau], pk[tau], gram(8 + tau, tau), alpha, bt, vv, d, o);
+      const size_t ih = (static_cast<size_t>(g.b) * T + tau) * a.Hv + g.h;
+      const int pos = r.p + tau;
+      small_stores<QKV, RING>(a, ih * a.dv + g.vcol, (hs * a.L + pos) * a.dv + g.vcol,
+                              hs * a.L + pos, r.ok ? o : 0.f, d, gv, app, gwriter_wave, grp, col);
+      if (app && kwriter && lane < C4) {
+        const f4 kv = *reinterpret_cast<const f4*>(qk + tau * 2 * DK + DK + 4 * lane);
+        store4<RING>(a.ring_k, (ks * a.L + pos) * DK + 4 * lane, kv);
+      }
+      // the later tokens' products after this token's update
+#pragma unroll
+      for (int m = tau + 1; m < 8; ++m) {
+        if (m < T) {
+          pq[m] = __builtin_fmaf(d, gram(8 + tau, m), alpha * pq[m]);
+          pk[m] = __builtin_fmaf(d, gram(8 + tau, 8 + m), alpha * pk[m]);
+        }
+      }
+    }
   }
 }
 
@@ -876,6 +981,13 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   const bool gwriter_wave = (g.vb == 0) && (wave % wph == 0);     // one g writer per head
   const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
   const size_t ks = static_cast<size_t>(r.sc) * a.Hk + g.hk;
+  if constexpr (!TT && !KG) {
+    if (a.win_mfma) {
+      window_chunked<DK, QKV, RING, SD>(a, g, r, T, S, qk, vl, gates + 3 * wh * T, hs, ks, kwriter,
+                                        gwriter_wave, grp, col, lane);
+      return;
+    }
+  }
   for (int tau = 0; tau < T; ++tau) {
     const float* ql = qk + tau * 2 * DK;
     const float* kl = ql + DK;
@@ -915,7 +1027,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   }
   if (r.flush) {
     using SE = typename Elem<SD>::T;
-    store_slab<SD, DK>(static_cast<SE*>(a.state) + (hs * a.dv + g.vcol - col) * DK, S, col, grp);
+    store_slab<SD, DK, kCpolSc1>(static_cast<SE*>(a.state) + (hs * a.dv + g.vrow0) * DK, S, col, grp);
   }
 }
 
@@ -954,6 +1066,10 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
 // FV/16 consecutive rows (the ring entries staged in LDS serve all of them).
 // KG = 1: per-key gate (ring_g [N, Hv, L, dk]), each channel decays by its
 // own a_j[c].
+// The fold reads each checkpoint line and writes it back: its stores go on
+// to memory at once (sc1 nt), as the packed decode's do.
+constexpr int kFoldStorePolicy = kCpolSc1Nt;
+
 template <int DK, int RING, int SD, int KG>
 __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   constexpr int C4 = DK / 4;
@@ -1062,14 +1178,14 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
     if (m < nr) {
       const int off = (row + m) * DK + e4;
       if constexpr (SD == DT_F32) {
-        store16_nt(reinterpret_cast<float*>(xbase), FV * DK * 4, off * 4, x[m]);
+        store16<kFoldStorePolicy>(reinterpret_cast<float*>(xbase), FV * DK * 4, off * 4, x[m]);
       } else {
         u16x4 r;
         r.x = __builtin_bit_cast(uint16_t, state_round<SD>(x[m].x));
         r.y = __builtin_bit_cast(uint16_t, state_round<SD>(x[m].y));
         r.z = __builtin_bit_cast(uint16_t, state_round<SD>(x[m].z));
         r.w = __builtin_bit_cast(uint16_t, state_round<SD>(x[m].w));
-        store8_nt(reinterpret_cast<float*>(xbase), FV * DK * 2, off * 2, r);
+        store8<kFoldStorePolicy>(reinterpret_cast<float*>(xbase), FV * DK * 2, off * 2, r);
       }
     }
   }
