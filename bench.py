@@ -5,14 +5,18 @@ Hk = 16, dk = dv = 128, ring L = 16, fp32 checkpoint, bf16 q/k/v/o, fp16 d/k
 ring, staggered cursors) through R = 8 GDN layers: one gdn_replay_decode call
 per layer, each on its own checkpoint + ring set; the last layer's call is
 gdn_replay_decode_advance, which also advances the cursors (they are shared
-by the layers and advance once per forward). The 8
-layer sets (~1.1 GiB) exceed the 256 MB Infinity Cache, so the checkpoint is
-streamed from HBM as in a real multi-layer model.
+by the layers and advance once per forward). The 8 layer sets (~1.1 GiB)
+exceed the 256 MB Infinity Cache, so the checkpoint is streamed from HBM as in
+a real multi-layer model.
 
 Printed: one JSON line with head-steps/s (value), the HBM roofline of the
-replay decode kernel (per-launch HIP events on the launch stream), the packed
-read-update-write decode built alongside it on the same workload, the verify
-window + fold of the speculative workload, and the CPU oracle baseline.
+replay decode kernel (per-launch HIP events on the launch stream, against the
+8 TB/s specification and against the read bandwidth measured on the same GPU
+with the library's read probe), the packed read-update-write decode built
+alongside it, the no-flush ("best") mode, the large-pool and ring-depth
+workloads, the 16-bit-state, per-key-gate and front-end variants, the verify
+window + fold of the speculative workload, lossless verify, the pages' own
+context figures, and the CPU oracle baseline on the host's cores.
 
 Modes for profiling runs (same kernels, fewer steps, no CPU baseline):
   --profile-pass   warmup + a few timed steps of each kernel
@@ -108,10 +112,17 @@ def dev_tensor(x, dt, dev):
 
 
 class LayerSet:
+    """One layer's checkpoint (or packed state) and rings. The state is drawn
+    on the device, S0 ~ N(0, 0.1^2) from a seeded generator, and rounded to
+    the state dtype (the workload's distribution; the timing does not depend
+    on the values). Rings start empty (zeros)."""
+
     def __init__(self, w, seed, dev, with_ring=True):
         import torch
-        ws = dataclasses.replace(w, seed=seed)
-        self.state = dev_tensor(gi.stored_state(ws), ws.state, dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        sdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.state]
+        self.state = (0.1 * torch.randn((w.N, w.Hv, w.dv, w.dk), generator=gen, device=dev)).to(sdt)
         if with_ring:
             rdt = torch.float16 if w.ring == "f16" else (
                 torch.bfloat16 if w.ring == "bf16" else torch.float32)
@@ -158,18 +169,33 @@ def graph_of(fn):
     return g
 
 
-def time_graph(g, reps):
-    """Mean milliseconds per replay, HIP events on the replay stream."""
+def time_graph(g, reps, samples=False):
+    """Mean milliseconds per replay, HIP events on the replay stream (one pair
+    around all replays). samples=True also records an event between replays
+    and returns (mean, per-replay list)."""
     import torch
     g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    if not samples:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
         g.replay()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    return ev[0].elapsed_time(ev[reps]) / reps, per
+
+
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs, np.float64), q))
 
 
 def load_traffic(name: str):
@@ -188,7 +214,7 @@ def load_traffic(name: str):
 
 # ------------------------------------------------------------------ benches
 
-def bench_replay(w, R, steps, warmup, dev, log, front_end=False, conv=False):
+def bench_replay(w, R, steps, warmup, dev, log, front_end=False, conv=False, best=False):
     """front_end: q, k, v read from the packed mixed_qkv row and normalised in
     the kernel (the workload draws raw q, k). conv: each layer first runs the
     causal convolution (width 4) on a raw packed row and the decode reads the
@@ -221,7 +247,8 @@ def bench_replay(w, R, steps, warmup, dev, log, front_end=False, conv=False):
     ff_sched = [dev_tensor(gi.force_flush_schedule(w, t, slots), None, dev) for t in range(w.L)]
     no_ff = torch.zeros(w.B, dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    o = torch.empty((w.B, 1, w.Hv, w.dv), dtype=torch.bfloat16, device=dev)
+    odt = torch.float32 if w.qkv == "f32" else torch.bfloat16
+    o = torch.empty((w.B, 1, w.Hv, w.dv), dtype=odt, device=dev)
 
     def decodes(ff):
         for i, ls in enumerate(layers):
@@ -259,8 +286,12 @@ def bench_replay(w, R, steps, warmup, dev, log, front_end=False, conv=False):
     # pass 2: the R decode kernels alone, back to back in one graph (cursors
     # frozen at this phase; the decodes do not move them). HIP events on the
     # replay stream bracket the timed replays; per-kernel figure = total / R
-    # (it includes the short gap between two kernels of a graph).
-    ms_dec = time_graph(g_dec, steps) / R
+    # (it includes the short gap between two kernels of a graph). An event
+    # between replays gives the spread: p10 / p50 / p90 of the per-launch mean
+    # of each replay.
+    ms_dec, per = time_graph(g_dec, steps, samples=True)
+    ms_dec /= R
+    per = [x / R for x in per]
     assert int(err.item()) == 0, f"device error flags {int(err.item())}"
     seq = cursor_sequence(w, slots, n_fwd + 1)
     cur = seq[n_fwd]                                   # the phase the frozen decodes see
@@ -269,12 +300,34 @@ def bench_replay(w, R, steps, warmup, dev, log, front_end=False, conv=False):
     mean_p = float(np.mean([p for p, _ in cur]))
     flush_frac = float(np.mean([fl for _, fl in cur]))
     fe_tag = ", conv + front end" if conv else (", front end" if front_end else "")
-    log(f"replay [{w.state} state, {w.gate} gate{fe_tag}]: {ms_step * 1e3:.1f} us/step ({R} layers, fused advance), decode kernel "
-        f"{ms_dec * 1e3:.2f} us, {bytes_launch / 1e6:.2f} MB/launch, "
-        f"mean p {mean_p:.2f}, flush frac {flush_frac:.4f}")
-    return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
-                kernel_ms=ms_dec, bytes_per_launch=bytes_launch,
-                head_steps_per_launch=live * w.Hv, mean_p=mean_p, flush_frac=flush_frac)
+    log(f"replay [{w.name}: {w.state} state, {w.gate} gate, {w.ring} ring, L={w.L}{fe_tag}]: "
+        f"{ms_step * 1e3:.1f} us/step ({R} layers, fused advance), decode kernel "
+        f"{ms_dec * 1e3:.2f} us (p10 {pct(per, 10) * 1e3:.2f}, p90 {pct(per, 90) * 1e3:.2f}), "
+        f"{bytes_launch / 1e6:.2f} MB/launch, mean p {mean_p:.2f}, flush frac {flush_frac:.4f}")
+    out = dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
+               kernel_ms=ms_dec, kernel_us_p10=pct(per, 10) * 1e3,
+               kernel_us_p50=pct(per, 50) * 1e3, kernel_us_p90=pct(per, 90) * 1e3,
+               bytes_per_launch=bytes_launch, head_steps_per_launch=live * w.Hv,
+               mean_p=mean_p, flush_frac=flush_frac)
+    if best and w.L > 1:
+        # "best" mode: every row on a step that does not flush (the cursor of
+        # every slot set to pb = (L - 1) // 2, so each reads pb entries and
+        # appends one); the same decode graph, now reading these cursors
+        pb = (w.L - 1) // 2
+        wp.fill_(pb)
+        ms_b, per_b = time_graph(g_dec, steps, samples=True)
+        ms_b /= R
+        assert int(err.item()) == 0, f"device error flags {int(err.item())}"
+        b_best = live * w.Hv * bytes_decode_head_step(w, pb, False, "replay")
+        log(f"replay best mode (no flush, p = {pb}): decode kernel {ms_b * 1e3:.2f} us, "
+            f"{b_best / 1e6:.2f} MB/launch ({b_best / ms_b / 1e6:.0f} GB/s)")
+        out["best"] = dict(kernel_us=ms_b * 1e3, valid_entries=pb,
+                           kernel_us_p10=pct(per_b, 10) / R * 1e3,
+                           kernel_us_p90=pct(per_b, 90) / R * 1e3,
+                           bytes_per_launch=b_best, achieved_gbs=b_best / ms_b / 1e6,
+                           frac=b_best / ms_b / 1e6 / HBM_PEAK_GBS,
+                           head_steps_per_s=live * w.Hv / (ms_b / 1e3))
+    return out
 
 
 def bench_conv(w, R, steps, dev, log):
@@ -332,7 +385,8 @@ def bench_packed(w, R, steps, dev, log):
     slot_t = dev_tensor(slots, None, dev)
     layers = [LayerSet(w, w.seed + 17 * i, dev, with_ring=False) for i in range(R)]
     ins = input_sets(w, 4, dev)
-    o = torch.empty((w.B, 1, w.Hv, w.dv), dtype=torch.bfloat16, device=dev)
+    odt = torch.float32 if w.qkv == "f32" else torch.bfloat16
+    o = torch.empty((w.B, 1, w.Hv, w.dv), dtype=odt, device=dev)
 
     def forward():
         for i, ls in enumerate(layers):
@@ -340,20 +394,24 @@ def bench_packed(w, R, steps, dev, log):
             gdn.gdn_packed_decode(q, k, v, g, beta, slot_t, ls.state, o=o)
 
     g = graph_of(forward)
-    ms_step = time_graph(g, steps)
+    ms_step, per = time_graph(g, steps, samples=True)
     ms_k = ms_step / R
     live = int(np.count_nonzero(slots >= 0))
     bytes_launch = live * w.Hv * bytes_decode_head_step(w, 0, False, "packed")
-    log(f"packed [{w.state} state, {w.gate} gate]: {ms_step * 1e3:.1f} us/step ({R} layers), kernel {ms_k * 1e3:.2f} us, "
+    log(f"packed [{w.name}: {w.state} state, {w.gate} gate]: {ms_step * 1e3:.1f} us/step ({R} layers), "
+        f"kernel {ms_k * 1e3:.2f} us (p10 {pct(per, 10) / R * 1e3:.2f}, p90 {pct(per, 90) / R * 1e3:.2f}), "
         f"{bytes_launch / 1e6:.2f} MB/launch")
     return dict(ms_per_step=ms_step, head_steps_per_s=live * w.Hv * R / (ms_step / 1e3),
-                kernel_ms=ms_k, bytes_per_launch=bytes_launch)
+                kernel_ms=ms_k, kernel_us_p10=pct(per, 10) / R * 1e3,
+                kernel_us_p90=pct(per, 90) / R * 1e3, bytes_per_launch=bytes_launch)
 
 
 def bench_window_fold(w, R, steps, dev, log):
-    """Verify window (T tokens from checkpoint + ring with p0 = L - T - 1
-    valid entries) and the fold of a ring holding p0 + T entries, R layer
-    sets each."""
+    """Kernel figures at the speculative workload's shapes (B = 32, T = 5,
+    L = 16): a verify window read from checkpoint + ring with a fixed
+    p0 = L - T - 1 valid entries, and the fold of a ring holding p0 + T
+    entries, R layer sets each. (The verify-commit-fold protocol itself, with
+    its random acceptance, is exercised by the tests.)"""
     import torch
     import linear_attention_ssm_amd as gdn
     slots = gi.slot_map(w)
@@ -443,7 +501,8 @@ def bench_lossless(w, R, steps, dev, log):
     es = 2
     vb = nh * (4 * w.dv * w.dk + w.T * ent + w.T * (2 * es * w.dk / G + 2 * es * w.dv + 8))
     a_sum = float(acc_np[live].sum()) * w.Hv
-    fb = nh * 8 * w.dv * w.dk + a_sum * ent
+    n_fold = int(np.count_nonzero(acc_np[live] > 0)) * w.Hv     # heads with entries to fold
+    fb = n_fold * 8 * w.dv * w.dk + a_sum * ent
     log(f"lossless verify T={w.T}: round {m_round * 1e3:.1f} us ({R} layers: verify, commit, "
         f"fold, reset); verify {m_verify * 1e3:.2f} us/launch ({vb / m_verify / 1e6:.0f} GB/s), "
         f"fold {m_fold * 1e3:.2f} us/launch ({fb / m_fold / 1e6:.0f} GB/s)")
@@ -454,29 +513,115 @@ def bench_lossless(w, R, steps, dev, log):
                 mean_accepted=float(acc_np[live].mean()))
 
 
+def read_probe(R, reps, dev, log):
+    """The library's read probe over R buffers of 128 MiB (the decode's layer
+    rotation): the read bandwidth this GPU reaches for the checkpoint's access
+    pattern. HIP events around `reps` rounds of R launches."""
+    import torch
+    import linear_attention_ssm_amd as gdn
+    nb = 128 << 20
+    bufs = [torch.zeros(nb // 4, dtype=torch.float32, device=dev) for _ in range(R)]
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def run():
+        for b in bufs:
+            gdn.gdn_hbm_read_probe(b, sink)
+
+    ms = time_graph(graph_of(run), reps) / R
+    gbs = nb / (ms / 1e3) / 1e9
+    log(f"read probe: 128 MiB in {ms * 1e3:.2f} us ({gbs:.0f} GB/s)")
+    del bufs
+    return dict(bytes=nb, us=ms * 1e3, gbs=gbs)
+
+
+def copy_probe_timed(reps, dev, log):
+    """A plain device copy of 1 GiB (torch's copy kernel): read + write."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    ms = time_graph(graph_of(lambda: b.copy_(a)), reps)
+    gbs = 2 * 4 * n / (ms / 1e3) / 1e9
+    log(f"copy probe: 1 GiB copied in {ms * 1e3:.1f} us ({gbs:.0f} GB/s read + write)")
+    del a, b
+    return dict(bytes=2 * 4 * n, us=ms * 1e3, gbs=gbs)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s, log):
-    """The CPU oracle (sequential fp64 recurrence, single thread) on a bounded
-    sample of the same workload: the c2 batch for as many steps as fit in
-    the time budget."""
+    """The CPU oracle's sequential decode recurrence (O1), fp64 and its fp32
+    instance, on a bounded sample of the standard workload: the c2 batch
+    stepped for about budget_s / 4 seconds per configuration, on one thread
+    and on all the host cores this process may use (the OpenMP loop over
+    (row, value head) of a -O3 build of the same C source for this host)."""
+    import tempfile
     import oracle
-    S = gi.initial_state(w).astype(np.float64)
+    L, flags = oracle.timing_library(tempfile.mkdtemp(prefix="gdn_oracle_"))
+    avail = len(os.sched_getaffinity(0))
+    n_all = min(avail, int(os.environ.get("OMP_NUM_THREADS", avail)))
     slots = gi.slot_map(w)
     live = int(np.count_nonzero(slots >= 0))
     xs = [gi.step_inputs(w, i) for i in range(4)]
-    x64 = [tuple(a[:, 0] for a in x.f64()) for x in xs]
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.gdn_step(S, slots, *x64[n % 4])
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    hs = live * w.Hv * n / el
-    log(f"cpu oracle: {n} steps of {live}x{w.Hv} head-steps in {el:.1f} s -> {hs:.0f} head-steps/s")
-    return dict(value=hs, unit="head-steps/s", cores=1, kind="oracle",
-                sample=f"{n} decode steps of the B={live} x Hv={w.Hv} (dk=dv={w.dk}) batch "
-                       f"through the fp64 sequential recurrence, single thread, {el:.1f} s")
+    x64 = [tuple(np.ascontiguousarray(a[:, 0]) for a in x.f64()) for x in xs]
+    x32 = [tuple(a.astype(np.float32) for a in x) for x in x64]
+    per = budget_s / 4
+    res = {}
+    for prec in ("f64", "f32"):
+        for nt in (1, n_all):
+            used = L.oracle_threads(nt)
+            S = gi.initial_state(w).astype(np.float64 if prec == "f64" else np.float32)
+            n, t0 = 0, time.perf_counter()
+            while True:
+                if prec == "f64":
+                    _oracle_step(L, S, slots, x64[n % 4], np.float64)
+                else:
+                    _oracle_step(L, S, slots, x32[n % 4], np.float32)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= per:
+                    break
+            hs = live * w.Hv * n / el
+            res[(prec, nt)] = dict(head_steps_per_s=hs, threads=used, steps=n, seconds=el,
+                                   gbs=hs * 8 * w.dv * w.dk * (2 if prec == "f64" else 1) / 1e9)
+            log(f"cpu oracle {prec}, {used} thread(s): {n} steps of {live}x{w.Hv} head-steps in "
+                f"{el:.1f} s -> {hs:.0f} head-steps/s")
+    top = res[("f64", n_all)]
+    return dict(value=top["head_steps_per_s"], unit="head-steps/s", cores=top["threads"],
+                kind="oracle",
+                sample=(f"{top['steps']} decode steps of the B={live} x Hv={w.Hv} (dk=dv={w.dk}) "
+                        f"batch through the fp64 sequential recurrence on {top['threads']} threads, "
+                        f"{top['seconds']:.1f} s"),
+                cpu_model=cpu_model(), host_cpus_available=avail, build_flags=flags,
+                fp64_1_thread=res[("f64", 1)]["head_steps_per_s"],
+                fp32_1_thread=res[("f32", 1)]["head_steps_per_s"],
+                fp32_all_threads=res[("f32", n_all)]["head_steps_per_s"],
+                fp64_all_threads=top["head_steps_per_s"])
+
+
+def _oracle_step(L, S, slots, x, dt):
+    """One decode step of the timing library's fp64 or fp32 recurrence."""
+    import oracle
+    q, k, v, g, beta = x
+    B, Hk, dk = q.shape
+    N, Hv, dv, _ = S.shape
+    o = np.empty((B, Hv, dv), dt)
+    sl = oracle._p(slots.astype(np.int32))
+    if dt == np.float64:
+        L.oracle_gdn_step_f64(B, N, Hv, Hk, dk, dv, sl, oracle._p(S), oracle._p(q), oracle._p(k),
+                              oracle._p(v), oracle._p(g), oracle._p(beta), oracle._p(o), None)
+    else:
+        L.oracle_gdn_step_f32(B, N, Hv, Hk, dk, dv, sl, oracle._p(S), oracle._p(q), oracle._p(k),
+                              oracle._p(v), oracle._p(g), oracle._p(beta), oracle._p(o))
+    return o
 
 
 def copy_probe(dev, log):
@@ -490,13 +635,46 @@ def copy_probe(dev, log):
     log(f"copy probe: 3 copies of {n * 4} bytes")
 
 
+def summary(r, pk=None, w=None):
+    """The usual figures of one replay bench (and its packed counterpart)."""
+    gbs = r["bytes_per_launch"] / (r["kernel_ms"] / 1e3) / 1e9
+    d = dict(replay_kernel_us=r["kernel_ms"] * 1e3, replay_kernel_us_p10=r["kernel_us_p10"],
+             replay_kernel_us_p90=r["kernel_us_p90"], replay_gbs=gbs, replay_frac=gbs / HBM_PEAK_GBS,
+             replay_bytes_per_launch=r["bytes_per_launch"],
+             replay_head_steps_per_s=r["head_steps_per_s"], mean_valid_entries=r["mean_p"],
+             flush_fraction=r["flush_frac"])
+    if pk is not None:
+        pg = pk["bytes_per_launch"] / (pk["kernel_ms"] / 1e3) / 1e9
+        d.update(packed_kernel_us=pk["kernel_ms"] * 1e3, packed_gbs=pg, packed_frac=pg / HBM_PEAK_GBS,
+                 packed_bytes_per_launch=pk["bytes_per_launch"],
+                 packed_head_steps_per_s=pk["head_steps_per_s"],
+                 replay_vs_packed_kernel=pk["kernel_ms"] / r["kernel_ms"],
+                 replay_vs_packed=r["head_steps_per_s"] / pk["head_steps_per_s"])
+    return d
+
+
+# The pages' own figures for this path, with the hardware they were taken on
+# (context, not targets; the pages publish no absolute head-steps/s or GB/s).
+PAGES_CONTEXT = {
+    "packed_decode_hbm_bound": ("the packed (read-update-write) GDN decode is 70-79% bound by HBM "
+                                "bandwidth at batch >= 64 on H20-3e, fp32 state (SGLang PR #28451, "
+                                "Motivation)"),
+    "state_bytes_per_head_step": ("about 8*dv*dk bytes of state per head-step for the packed decode "
+                                  "(read + write) against about 4*dv*dk for the replay decode "
+                                  "(read only), fp32 state (SGLang PR #28451, Motivation; "
+                                  "ReplaySSM blog, section 5.1)"),
+    "replay_vs_packed_kernel_h20": ("1.2-1.5x at batch >= 16 with L = 8, slightly slower at batch 1, "
+                                    "on H20-3e (SGLang PR #28451, Performance)"),
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--layers", type=int, default=8)
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=16.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -520,24 +698,38 @@ def main():
     steps, warmup = args.steps, args.warmup
     if args.profile_pass:
         steps, warmup = 4, 16
-    rep = bench_replay(w, R, steps, warmup, dev, log)
+    small = max(4, steps // 4)
+    # the packed baseline first (it also brings the GPU to its working clocks)
     pk = bench_packed(w, R, steps, dev, log)
+    rep = bench_replay(w, R, steps, warmup, dev, log, best=True)
+    rp = read_probe(R, small, dev, log)
+    cp = copy_probe_timed(small, dev, log)
     w16 = dataclasses.replace(w, state="bf16")
-    rep16 = bench_replay(w16, R, steps, warmup, dev, log)
+    rep16 = bench_replay(w16, R, steps, warmup, dev, log, best=True)
     pk16 = bench_packed(w16, R, steps, dev, log)
     repk = bench_replay(gi.C7, R, steps, warmup, dev, log)
+    pkk = bench_packed(gi.C7, R, steps, dev, log)
+    gts = bench_gates(gi.C7, R, steps, dev, log)
     w_fe = dataclasses.replace(w, qk_raw=True)
     repf = bench_replay(w_fe, R, steps, warmup, dev, log, front_end=True)
     repc = bench_replay(w_fe, R, steps, warmup, dev, log, front_end=True, conv=True)
     cv = bench_conv(w_fe, R, steps, dev, log)
-    pkk = bench_packed(gi.C7, R, steps, dev, log)
-    gts = bench_gates(gi.C7, R, steps, dev, log)
+    # the large pool: 256 rows (8 of them padding) over 512 slots, 4 layer sets
+    rep3 = bench_replay(gi.C3, 4, small, warmup, dev, log)
+    pk3 = bench_packed(gi.C3, 4, small, dev, log)
+    # ring depth
+    depth = {}
+    for L in (1, 4, 32):
+        depth[f"L{L}"] = summary(bench_replay(gi.c4(L), R, small, warmup, dev, log))
+    depth["L16"] = summary(rep)
+    rep_f32r = bench_replay(gi.c4(16, "f32"), R, small, warmup, dev, log)
     wf = bench_window_fold(gi.C5, R, max(4, steps // 8), dev, log)
     ll = bench_lossless(gi.C6, R, max(4, steps // 8), dev, log)
     if args.profile_pass:
         return
     achieved = rep["bytes_per_launch"] / (rep["kernel_ms"] / 1e3) / 1e9
     traffic = load_traffic("replay_decode_c2_hbm_traffic.txt")
+    pk_gbs = pk["bytes_per_launch"] / (pk["kernel_ms"] / 1e3) / 1e9
     out = {
         "metric": METRIC,
         "value": rep["head_steps_per_s"],
@@ -567,54 +759,44 @@ def main():
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
             "kernel": "replay_decode_kernel<128, bf16, f16, f32>",
             "kernel_us": rep["kernel_ms"] * 1e3,
+            "kernel_us_p10": rep["kernel_us_p10"], "kernel_us_p50": rep["kernel_us_p50"],
+            "kernel_us_p90": rep["kernel_us_p90"],
             "algorithmic_bytes_per_launch": rep["bytes_per_launch"],
+            "measured_read_peak_gbs": rp["gbs"],
+            "frac_of_measured_read_peak": achieved / rp["gbs"],
+            "measured_copy_peak_gbs": cp["gbs"],
         },
         "packed_baseline": {
             "head_steps_per_s": pk["head_steps_per_s"], "ms_per_step": pk["ms_per_step"],
-            "kernel_us": pk["kernel_ms"] * 1e3,
-            "achieved_gbs": pk["bytes_per_launch"] / (pk["kernel_ms"] / 1e3) / 1e9,
-            "frac": pk["bytes_per_launch"] / (pk["kernel_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_us": pk["kernel_ms"] * 1e3, "kernel_us_p10": pk["kernel_us_p10"],
+            "kernel_us_p90": pk["kernel_us_p90"],
+            "achieved_gbs": pk_gbs, "frac": pk_gbs / HBM_PEAK_GBS,
+            "frac_of_measured_copy_peak": pk_gbs / cp["gbs"],
             "algorithmic_bytes_per_launch": pk["bytes_per_launch"],
         },
         "replay_vs_packed": rep["head_steps_per_s"] / pk["head_steps_per_s"],
         "replay_vs_packed_kernel": pk["kernel_ms"] / rep["kernel_ms"],
+        "best_mode_c2": rep["best"],
+        "probes": {"read_128MiB": rp, "copy_1GiB": cp,
+                   "note": ("read: the library's gdn_hbm_read_probe over 8 buffers of 128 MiB in "
+                            "the checkpoint's access pattern; copy: a plain 1 GiB device copy")},
         "state_bf16": {
             "note": "the standard workload with a bf16 checkpoint / packed state (fp32 math)",
-            "replay_head_steps_per_s": rep16["head_steps_per_s"],
-            "replay_kernel_us": rep16["kernel_ms"] * 1e3,
-            "replay_gbs": rep16["bytes_per_launch"] / (rep16["kernel_ms"] / 1e3) / 1e9,
-            "replay_frac": rep16["bytes_per_launch"] / (rep16["kernel_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "replay_bytes_per_launch": rep16["bytes_per_launch"],
-            "packed_head_steps_per_s": pk16["head_steps_per_s"],
-            "packed_kernel_us": pk16["kernel_ms"] * 1e3,
-            "packed_gbs": pk16["bytes_per_launch"] / (pk16["kernel_ms"] / 1e3) / 1e9,
-            "packed_bytes_per_launch": pk16["bytes_per_launch"],
-            "replay_vs_packed_kernel": pk16["kernel_ms"] / rep16["kernel_ms"],
+            **summary(rep16, pk16),
+            "best_mode": rep16.get("best"),
             "replay_vs_fp32_replay": rep["kernel_ms"] / rep16["kernel_ms"],
         },
         "kda_c7": {
             "note": ("the standard workload with a per-key gate (KDA): g [B, Hv, dk] and "
                      "ring_g [N, Hv, L, dk]; replay vs the packed decode with the same gate"),
-            "replay_head_steps_per_s": repk["head_steps_per_s"],
-            "replay_kernel_us": repk["kernel_ms"] * 1e3,
-            "replay_gbs": repk["bytes_per_launch"] / (repk["kernel_ms"] / 1e3) / 1e9,
-            "replay_frac": repk["bytes_per_launch"] / (repk["kernel_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "replay_bytes_per_launch": repk["bytes_per_launch"],
-            "packed_head_steps_per_s": pkk["head_steps_per_s"],
-            "packed_kernel_us": pkk["kernel_ms"] * 1e3,
-            "packed_gbs": pkk["bytes_per_launch"] / (pkk["kernel_ms"] / 1e3) / 1e9,
-            "packed_bytes_per_launch": pkk["bytes_per_launch"],
-            "replay_vs_packed_kernel": pkk["kernel_ms"] / repk["kernel_ms"],
-            "replay_vs_packed": repk["head_steps_per_s"] / pkk["head_steps_per_s"],
+            **summary(repk, pkk),
             "gates_kernel_us": gts["kernel_ms"] * 1e3,
             "gates_bytes_per_launch": gts["bytes_per_launch"],
         },
         "front_end_c2": {
             "note": ("the standard workload with q, k, v read from the packed mixed_qkv row "
                      "and q/k L2-normalised (q scaled) in the kernel"),
-            "replay_head_steps_per_s": repf["head_steps_per_s"],
-            "replay_kernel_us": repf["kernel_ms"] * 1e3,
-            "replay_gbs": repf["bytes_per_launch"] / (repf["kernel_ms"] / 1e3) / 1e9,
+            **summary(repf),
             "vs_plain_replay_kernel": rep["kernel_ms"] / repf["kernel_ms"],
         },
         "front_end_conv_c2": {
@@ -629,8 +811,21 @@ def main():
             "conv_gbs": cv["bytes_per_launch"] / (cv["kernel_ms"] / 1e3) / 1e9,
             "vs_plain_replay_step": rep["ms_per_step"] / repc["ms_per_step"],
         },
-        "verify_window_c5": wf,
+        "large_pool_c3": {
+            "note": ("B=256 rows (8 padding) over a pool of N=512 slots, a seeded slot "
+                     "permutation, standard shapes and dtypes; 4 layer sets (4 GiB of checkpoints)"),
+            **summary(rep3, pk3),
+        },
+        "ring_depth_c4": {
+            "note": ("the standard workload at ring depths L = 1, 4, 16, 32 (L16 is the headline "
+                     "run); L = 1 flushes every step, i.e. the packed decode's traffic"),
+            **depth,
+            "L16_fp32_ring": {"note": "fp32 ring (fp32 MFMA reconstruction), fp32 q/k/v/o",
+                              **summary(rep_f32r)},
+        },
+        "verify_window_c5_shapes": wf,
         "lossless_verify_c6": ll,
+        "pages_context": PAGES_CONTEXT,
         "cpu_baseline": None,
         "kernel_sources_sha256_16": kernel_hash(),
     }

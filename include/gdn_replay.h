@@ -108,6 +108,7 @@
 #ifndef GDN_REPLAY_H
 #define GDN_REPLAY_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -397,6 +398,20 @@ typedef struct {
 gdn_status gdn_kda_gates(const gdn_gate_shape *shape, const float *a, const float *b,
                          const float *A, const float *dt_bias, float *g, float *beta,
                          void *stream);
+
+/*
+ * gdn_hbm_read_probe -- a measurement aid, not a step of the method: streams
+ * `nbytes` of device memory at `src` once, in the access pattern of the
+ * decode's checkpoint reads (each wavefront 8 KiB in 16-byte loads, the
+ * non-temporal load policy), and writes nothing (sink is written only in a
+ * case that does not occur). Timed over several launches it gives the read
+ * bandwidth this GPU reaches for that pattern, the measured peak the
+ * decode's bandwidth is compared with beside the 8 TB/s specification.
+ *   src    (device) 16-byte aligned; nbytes a positive multiple of 32 KiB.
+ *   sink   (device) one float.
+ * Returns GDN_ERR_INVALID_ARG for a null pointer, a bad size or alignment.
+ */
+gdn_status gdn_hbm_read_probe(const void *src, size_t nbytes, float *sink, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *gdn_status_string(gdn_status status);

@@ -77,10 +77,12 @@ for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_decode_advance"
            "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_reset", "gdn_conv_update",
            "gdn_kda_gates"):
     getattr(_lib, _f).restype = ctypes.c_int
+_lib.gdn_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
+_lib.gdn_hbm_read_probe.restype = ctypes.c_int
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 9
+ABI_VERSION = 10
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -389,6 +391,17 @@ def gdn_replay_reset(slot_idx, write_pos, err_flags=None, stream=None):
     sh = gdn_shape(slot_idx.shape[0], 1, write_pos.shape[0], 1, 1, 32, 16, 1, 0, 0, 0, 0)
     _raise(_lib.gdn_replay_reset(ctypes.byref(sh), _ptr(slot_idx), _ptr(write_pos),
                                  _ptr(err_flags), _stream(stream)), "gdn_replay_reset")
+
+
+def gdn_hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Stream `src` (a device tensor, its byte size a multiple of 32 KiB) once
+    in the decode's checkpoint read pattern; see gdn_hbm_read_probe in
+    gdn_replay.h. A measurement aid (the measured read peak)."""
+    _check(src, "src", None, None)
+    _check(sink, "sink", torch.float32, None, src.device)
+    nbytes = src.numel() * src.element_size()
+    _raise(_lib.gdn_hbm_read_probe(_ptr(src), ctypes.c_size_t(nbytes), _ptr(sink), _stream(stream)),
+           "gdn_hbm_read_probe")
 
 
 # ------------------------------------------------------------------ prepared calls

@@ -5,7 +5,8 @@ CPU-baseline leg import this package. The product library neither imports,
 links nor calls anything here, and nothing here imports the product.
 
 Parts:
-  O1  gdn_step          plain sequential fp64 recurrence (C, liboracle.so)
+  O1  gdn_step          plain sequential fp64 recurrence (C, liboracle.so);
+                        gdn_step_f32, the same in fp32 (the CPU baseline)
   O2  ReplayModel       the checkpoint + ring + cursor state machine, run
                         exactly on the integers and in fp64 on the values,
                         producing outputs through the closed-form replay
@@ -59,25 +60,47 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def _bind(L):
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    L.oracle_gdn_step_f64.argtypes = [i32] * 6 + [P] * 9
+    L.oracle_gdn_step_f64.restype = None
+    L.oracle_gdn_step_f32.argtypes = [i32] * 6 + [P] * 8
+    L.oracle_gdn_step_f32.restype = None
+    L.oracle_threads.argtypes = [i32]
+    L.oracle_threads.restype = i32
+    L.oracle_fold_f32.argtypes = [i32] * 7 + [P] * 6 + [i32]
+    L.oracle_fold_f32.restype = None
+    L.oracle_kda_step_f64.argtypes = [i32] * 6 + [P] * 9
+    L.oracle_kda_step_f64.restype = None
+    L.oracle_fold_kda_f32.argtypes = [i32] * 7 + [P] * 6
+    L.oracle_fold_kda_f32.restype = None
+    L.oracle_version.restype = i32
+    assert L.oracle_version() == 2
+    return L
+
+
+def timing_library(out_dir: str):
+    """A separate build of the same gdn_oracle.c for timing the CPU baseline
+    on the machine that runs it: -O3 for that host's instruction set, with the
+    OpenMP loop over (row, value head) enabled. Never used for parity (the
+    parity build above is -O2 without contraction). Returns (library, flags)."""
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, "liboracle_timing.so")
+    base = ["-std=c11", "-O3", "-fopenmp", "-fPIC", "-shared"]
+    for arch in (["-march=native"], []):
+        r = subprocess.run(["gcc", *base, *arch, "-o", path, _SRC, "-lm"], capture_output=True)
+        if r.returncode == 0:
+            return _bind(ctypes.CDLL(path)), " ".join(base + arch)
+    raise RuntimeError("could not build the oracle's timing library: " + r.stderr.decode())
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build()
-        L = ctypes.CDLL(_LIB_PATH)
-        P = ctypes.c_void_p
-        i32 = ctypes.c_int32
-        L.oracle_gdn_step_f64.argtypes = [i32] * 6 + [P] * 9
-        L.oracle_gdn_step_f64.restype = None
-        L.oracle_fold_f32.argtypes = [i32] * 7 + [P] * 6 + [i32]
-        L.oracle_fold_f32.restype = None
-        L.oracle_kda_step_f64.argtypes = [i32] * 6 + [P] * 9
-        L.oracle_kda_step_f64.restype = None
-        L.oracle_fold_kda_f32.argtypes = [i32] * 7 + [P] * 6
-        L.oracle_fold_kda_f32.restype = None
-        L.oracle_version.restype = i32
-        assert L.oracle_version() == 2
-        _lib = L
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
     return _lib
 
 
@@ -150,6 +173,21 @@ def gdn_step(S: np.ndarray, slot: np.ndarray, q, k, v, g, beta,
             if 0 <= s < N:
                 S[s] = quantize(S[s], state_fmt)
     return (o, u) if want_u else o
+
+
+def gdn_step_f32(S: np.ndarray, slot: np.ndarray, q, k, v, g, beta, library=None):
+    """O1's fp32 instance (the same recurrence in float32), in place on S
+    [N,Hv,dv,dk] float32; the CPU baseline's decode step. Returns o."""
+    assert S.dtype == np.float32 and S.flags.c_contiguous
+    N, Hv, dv, dk = S.shape
+    B = slot.shape[0]
+    Hk = q.shape[1]
+    slot = _c(slot, np.int32)
+    q, k, v, g, beta = (_c(x, np.float32) for x in (q, k, v, g, beta))
+    o = np.empty((B, Hv, dv), np.float32)
+    (library or lib()).oracle_gdn_step_f32(B, N, Hv, Hk, dk, dv, _p(slot), _p(S), _p(q), _p(k),
+                                           _p(v), _p(g), _p(beta), _p(o))
+    return o
 
 
 # ------------------------------------------------------------------ O6

@@ -25,6 +25,9 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /*
  * O1 -- one decode token of the gated delta rule, in float64.
@@ -48,9 +51,12 @@ void oracle_gdn_step_f64(int32_t B, int32_t N, int32_t Hv, int32_t Hk,
                          double *o, double *u_out)
 {
     const int32_t G = Hv / Hk;
+    /* (row, value head) pairs are independent (the slots of one call are
+       distinct); a timing build with OpenMP runs them on several threads */
+#pragma omp parallel for collapse(2) schedule(static)
     for (int32_t b = 0; b < B; ++b) {
-        const int32_t s = slot[b];
         for (int32_t h = 0; h < Hv; ++h) {
+            const int32_t s = slot[b];
             double *ob = o + ((size_t)b * Hv + h) * dv;
             double *ub = u_out ? u_out + ((size_t)b * Hv + h) * dv : NULL;
             if (s < 0 || s >= N) {
@@ -88,6 +94,67 @@ void oracle_gdn_step_f64(int32_t B, int32_t N, int32_t Hv, int32_t Hk,
             }
         }
     }
+}
+
+/*
+ * O1, fp32 instance -- the same recurrence, statement for statement, in
+ * float32 (exp in double, rounded once). Used by the benchmark's CPU baseline
+ * (the plain read-update-write decode a CPU would run) and for the fp32 noise
+ * floor; parity is always judged against the fp64 function above.
+ */
+void oracle_gdn_step_f32(int32_t B, int32_t N, int32_t Hv, int32_t Hk,
+                         int32_t dk, int32_t dv, const int32_t *slot,
+                         float *S, const float *q, const float *k,
+                         const float *v, const float *g, const float *beta,
+                         float *o)
+{
+    const int32_t G = Hv / Hk;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t b = 0; b < B; ++b) {
+        for (int32_t h = 0; h < Hv; ++h) {
+            const int32_t s = slot[b];
+            float *ob = o + ((size_t)b * Hv + h) * dv;
+            if (s < 0 || s >= N) {
+                for (int32_t i = 0; i < dv; ++i) ob[i] = 0.0f;
+                continue;
+            }
+            const int32_t hk = h / G;
+            float *Sh = S + ((size_t)s * Hv + h) * dv * dk;
+            const float *qb = q + ((size_t)b * Hk + hk) * dk;
+            const float *kb = k + ((size_t)b * Hk + hk) * dk;
+            const float *vb = v + ((size_t)b * Hv + h) * dv;
+            const float alpha = (float)exp((double)g[(size_t)b * Hv + h]);
+            const float bt = beta[(size_t)b * Hv + h];
+
+            for (size_t e = 0; e < (size_t)dv * dk; ++e) Sh[e] = alpha * Sh[e];
+            for (int32_t i = 0; i < dv; ++i) {
+                float *row = Sh + (size_t)i * dk;
+                float sk = 0.0f;
+                for (int32_t j = 0; j < dk; ++j) sk += row[j] * kb[j];
+                const float u = bt * (vb[i] - sk);
+                for (int32_t j = 0; j < dk; ++j) row[j] = row[j] + u * kb[j];
+            }
+            for (int32_t i = 0; i < dv; ++i) {
+                const float *row = Sh + (size_t)i * dk;
+                float y = 0.0f;
+                for (int32_t j = 0; j < dk; ++j) y += row[j] * qb[j];
+                ob[i] = y;
+            }
+        }
+    }
+}
+
+/* Threads of a timing build (OpenMP); the parity build has one. Returns the
+   number of threads the steps will use. */
+int32_t oracle_threads(int32_t n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
 }
 
 /*
@@ -179,9 +246,12 @@ void oracle_kda_step_f64(int32_t B, int32_t N, int32_t Hv, int32_t Hk,
                          double *o, double *u_out)
 {
     const int32_t G = Hv / Hk;
+    /* (row, value head) pairs are independent (the slots of one call are
+       distinct); a timing build with OpenMP runs them on several threads */
+#pragma omp parallel for collapse(2) schedule(static)
     for (int32_t b = 0; b < B; ++b) {
-        const int32_t s = slot[b];
         for (int32_t h = 0; h < Hv; ++h) {
+            const int32_t s = slot[b];
             double *ob = o + ((size_t)b * Hv + h) * dv;
             double *ub = u_out ? u_out + ((size_t)b * Hv + h) * dv : NULL;
             if (s < 0 || s >= N) {

@@ -8,7 +8,8 @@ import pytest
 import linear_attention_ssm_amd as gdn
 from linear_attention_ssm_amd import gdn_shape
 
-EXPECTED = ["gdn_abi_version", "gdn_conv_update", "gdn_kda_gates", "gdn_packed_decode",
+EXPECTED = ["gdn_abi_version", "gdn_conv_update", "gdn_hbm_read_probe", "gdn_kda_gates",
+            "gdn_packed_decode",
             "gdn_replay_advance", "gdn_replay_commit",
             "gdn_replay_decode", "gdn_replay_decode_advance",
             "gdn_replay_decode_advance_noalloc", "gdn_replay_fold",
@@ -31,7 +32,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 9
+    assert lib.gdn_abi_version() == 10
     for st in range(5):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -117,6 +118,16 @@ def test_decode_advance_validates():
     assert call(shape(T=2, window=1), FAKE[14]) == gdn.GDN_ERR_INVALID_ARG   # windows: no
     assert call(shape(dk=96), FAKE[14]) == gdn.GDN_ERR_UNSUPPORTED
     assert call(shape(B=0), FAKE[14]) == gdn.GDN_OK
+
+
+def test_read_probe_validates():
+    lib = gdn.lib()
+    probe = lambda src, n, sink: lib.gdn_hbm_read_probe(src, ctypes.c_size_t(n), sink, None)
+    assert probe(None, 32768, FAKE[1]) == gdn.GDN_ERR_INVALID_ARG
+    assert probe(FAKE[0], 32768, None) == gdn.GDN_ERR_INVALID_ARG
+    assert probe(FAKE[0], 0, FAKE[1]) == gdn.GDN_ERR_INVALID_ARG
+    assert probe(FAKE[0], 32768 + 16, FAKE[1]) == gdn.GDN_ERR_INVALID_ARG
+    assert probe(ctypes.c_void_p(FAKE[0].value + 4), 32768, FAKE[1]) == gdn.GDN_ERR_INVALID_ARG
 
 
 def test_decode_advance_noalloc_validates():
