@@ -614,13 +614,26 @@ __device__ __forceinline__ void weight_keys_lds(const DecodeArgs& a, int lp, uns
 // so every S_t q_t and S_t k_t follows from the products S_0 q_m, S_0 k_m of
 // all window tokens m and the window's inner products k_j . q_m, k_j . k_m
 // (the causal mask over the window, vLLM PR #49887, Core concept). Both sets
-// of products are dense contractions and run on the MFMA units
-// (16x16x4 fp32): with the lane's A operand the window vector x_m (m = the
-// lane's column; q_m for m < 8, k_{m-8} else), P = X^T S_0^T takes the slab
-// registers as the B operand, and the Gram matrix X^T X the same operand
-// twice. The per-row recurrence over the T tokens then costs O(T^2) scalar
+// of products are dense contractions and run on the MFMA units: with the
+// lane's A operand the window vector x_m (m = the lane's column; q_m for
+// m < 8, k_{m-8} else), P = X^T S_0^T takes the slab registers as the B
+// operand, and the Gram matrix X^T X the same operand twice. Each fp32
+// operand is split into two bf16 parts, v = hi + lo with hi = RN_bf16(v) and
+// lo = RN_bf16(v - hi) (|v - hi - lo| <= 2^-17 |v|), and a product takes the
+// three terms hi.hi + hi.lo + lo.hi on the 16x16x32 bf16 MFMA (exact products,
+// fp32 accumulation): a tenth of the matrix-unit time of 16x16x4 fp32
+// products. The per-row recurrence over the T tokens then costs O(T^2) scalar
 // operations instead of two passes over the 16 x dk slab per token. The
-// results differ from the token-by-token update only in rounding.
+// results differ from the token-by-token update in rounding only (relative
+// 1e-5 here, against the 2e-2 of a 16-bit ring).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// v = hi + lo, both bf16 (round to nearest even).
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+  hi = static_cast<__bf16>(v);
+  lo = static_cast<__bf16>(v - static_cast<float>(hi));
+}
+
 template <int DK, int QKV, int RING, int SD>
 __device__ __forceinline__ void window_chunked(const DecodeArgs& a, const ItemGeo& g,
                                                const RowState& r, int T, const f4 (&S)[DK / 16],
@@ -634,14 +647,28 @@ __device__ __forceinline__ void window_chunked(const DecodeArgs& a, const ItemGe
   const int tv = col & 7;
   const float* xv = qk + (tv < T ? tv : 0) * 2 * DK + (col >= 8 ? DK : 0);
   f4 P = {0.f, 0.f, 0.f, 0.f}, Gm = {0.f, 0.f, 0.f, 0.f};
+  // k-step u covers keys 32u .. 32u + 31: the lane's eight keys are the four
+  // of tile 2u and the four of tile 2u + 1 it holds (key_base), in the same
+  // order for the A (window vectors) and the B (slab) operand
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const f4 xa = *reinterpret_cast<const f4*>(xv + key_base<SD>(t, grp));
+  for (int u = 0; u < NT / 2; ++u) {
+    const f4 x0 = *reinterpret_cast<const f4*>(xv + key_base<SD>(2 * u, grp));
+    const f4 x1 = *reinterpret_cast<const f4*>(xv + key_base<SD>(2 * u + 1, grp));
+    bf16x8 xh, xl, sh, sl;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      P = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i], S[t][i], P, 0, 0, 0);
-      Gm = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i], xa[i], Gm, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      __bf16 h, l;
+      split_bf16(x0[j], h, l); xh[j] = h; xl[j] = l;
+      split_bf16(x1[j], h, l); xh[4 + j] = h; xl[4 + j] = l;
+      split_bf16(S[2 * u][j], h, l); sh[j] = h; sl[j] = l;
+      split_bf16(S[2 * u + 1][j], h, l); sh[4 + j] = h; sl[4 + j] = l;
     }
+    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, sh, P, 0, 0, 0);
+    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, sl, P, 0, 0, 0);
+    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, sh, P, 0, 0, 0);
+    Gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, xh, Gm, 0, 0, 0);
+    Gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, xl, Gm, 0, 0, 0);
+    Gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, xh, Gm, 0, 0, 0);
   }
   // P: lane (row col, group grp) holds x_m . S_0[row] for m = 4 grp + i in
   // register i. Gather all 16 into every lane of the row: v_permlane16_swap
