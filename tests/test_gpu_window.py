@@ -16,7 +16,7 @@ import torch
 import gdn_inputs as gi
 from gdn_harness import (DEV, TORCH_DT, CanaryTensor, Pool, bits, dev_inputs, log, to_dev,
                          to_f64, tol_o, tol_state)
-from oracle import fold_f32, gdn_step, rel_err, window_ref
+from oracle import fold_f32, gdn_step, rel_err, step, window_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def _advance_true(S, slots, x64, counts):
             continue
         one = np.array([s], np.int32)
         for t in range(int(counts[b])):
-            gdn_step(S, one, q[b:b + 1, t], k[b:b + 1, t], v[b:b + 1, t], g[b:b + 1, t],
+            step(S, one, q[b:b + 1, t], k[b:b + 1, t], v[b:b + 1, t], g[b:b + 1, t],
                      beta[b:b + 1, t])
 
 
@@ -195,7 +195,22 @@ def test_window_length_sweep_verify_commit_verify(gdn, T):
     second window that reads the committed entries; both windows against the
     oracle, the cursors exact."""
     w = gi.scaled(gi.C5, name=f"win_T{T}", B=16, N=16, T=T, steps=2, seed=640 + T)
-    L = w.L
+    _verify_commit_verify(gdn, w)
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_window_wide_group_long_window(gdn, gate):
+    """Eight value heads per key head and a 16-token window: every (head,
+    token) pair of a workgroup needs its own staged decay and beta, more pairs
+    than one wavefront has lanes when the workgroup holds many heads. Both
+    windows against the oracle, the cursors exact."""
+    w = gi.scaled(gi.C5, name=f"win_G8_T16_{gate}", B=6, N=6, Hv=16, Hk=2, dk=64, dv=64,
+                  L=48, T=16, steps=2, gate=gate, seed=652)
+    _verify_commit_verify(gdn, w)
+
+
+def _verify_commit_verify(gdn, w):
+    T, L = w.T, w.L
     S0 = gi.initial_state(w)
     slots = gi.slot_map(w)
     slot_t = to_dev(slots)
@@ -212,7 +227,7 @@ def test_window_length_sweep_verify_commit_verify(gdn, T):
                               err_flags=pool.err)
         gdn.gdn_replay_advance(to_dev(sl), pool.write_pos, L, err_flags=pool.err)
         q, k, v, g, beta = (a[:, 0] for a in x.f64())
-        gdn_step(S_true, sl, q, k, v, g, beta)
+        step(S_true, sl, q, k, v, g, beta)
     wp = hist[slots].astype(np.int64)
     assert np.array_equal(pool.write_pos.cpu().numpy()[slots], wp)
     for r in range(w.steps):
@@ -223,7 +238,7 @@ def test_window_length_sweep_verify_commit_verify(gdn, T):
                                   err_flags=pool.err, window=True)
         x64 = x.f64()
         e = rel_err(to_f64(o), window_ref(S_true, slots, *x64))
-        assert e <= tol_o(w), f"T={T} round {r}: window rel err {e:.3e}"
+        assert e <= tol_o(w), f"{w.name} round {r}: window rel err {e:.3e}"
         acc = gi.accepted_counts(w, r)
         gdn.gdn_replay_commit(slot_t, to_dev(acc), pool.write_pos, L, T, err_flags=pool.err)
         _advance_true(S_true, slots, x64, acc)
