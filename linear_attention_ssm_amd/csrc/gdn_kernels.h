@@ -622,7 +622,9 @@ __device__ __forceinline__ void weight_keys_lds(const DecodeArgs& a, int lp, uns
 // lo = RN_bf16(v - hi) (|v - hi - lo| <= 2^-17 |v|), and a product takes the
 // three terms hi.hi + hi.lo + lo.hi on the 16x16x32 bf16 MFMA (exact products,
 // fp32 accumulation): a tenth of the matrix-unit time of 16x16x4 fp32
-// products. The per-row recurrence over the T tokens then costs O(T^2) scalar
+// products. XEX: the window vectors are bf16 values as given (bf16 q and k,
+// not normalised in the kernel), so their low parts are zero: P takes two
+// terms, the Gram matrix one, and the vectors need no split. The per-row recurrence over the T tokens then costs O(T^2) scalar
 // operations instead of two passes over the 16 x dk slab per token. The
 // results differ from the token-by-token update in rounding only (relative
 // 1e-5 here, against the 2e-2 of a 16-bit ring).
@@ -634,7 +636,7 @@ __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
   lo = static_cast<__bf16>(v - static_cast<float>(hi));
 }
 
-template <int DK, int QKV, int RING, int SD>
+template <int DK, int QKV, int RING, int SD, bool XEX>
 __device__ __forceinline__ void window_chunked(const DecodeArgs& a, const ItemGeo& g,
                                                const RowState& r, int T, const f4 (&S)[DK / 16],
                                                const float* qk, const float* vl, const float* gts,
@@ -658,17 +660,24 @@ __device__ __forceinline__ void window_chunked(const DecodeArgs& a, const ItemGe
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       __bf16 h, l;
-      split_bf16(x0[j], h, l); xh[j] = h; xl[j] = l;
-      split_bf16(x1[j], h, l); xh[4 + j] = h; xl[4 + j] = l;
+      if constexpr (XEX) {
+        xh[j] = static_cast<__bf16>(x0[j]);            // exact
+        xh[4 + j] = static_cast<__bf16>(x1[j]);
+      } else {
+        split_bf16(x0[j], h, l); xh[j] = h; xl[j] = l;
+        split_bf16(x1[j], h, l); xh[4 + j] = h; xl[4 + j] = l;
+      }
       split_bf16(S[2 * u][j], h, l); sh[j] = h; sl[j] = l;
       split_bf16(S[2 * u + 1][j], h, l); sh[4 + j] = h; sl[4 + j] = l;
     }
     P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, sh, P, 0, 0, 0);
     P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, sl, P, 0, 0, 0);
-    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, sh, P, 0, 0, 0);
     Gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, xh, Gm, 0, 0, 0);
-    Gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, xl, Gm, 0, 0, 0);
-    Gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, xh, Gm, 0, 0, 0);
+    if constexpr (!XEX) {
+      P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, sh, P, 0, 0, 0);
+      Gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, xl, Gm, 0, 0, 0);
+      Gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, xh, Gm, 0, 0, 0);
+    }
   }
   // P: lane (row col, group grp) holds x_m . S_0[row] for m = 4 grp + i in
   // register i. Gather all 16 into every lane of the row: v_permlane16_swap
@@ -706,6 +715,31 @@ __device__ __forceinline__ void window_chunked(const DecodeArgs& a, const ItemGe
     pk[m] = pv[8 + m];
   }
   const bool app = r.ok;                       // a window never flushes
+  // Store targets of token 0, stepped once per token: with a 16-bit o the
+  // lane groups write o (group 0), the ring d entry (group 1) and the two
+  // halves of the ring g entry (group 2) in one instruction.
+  using OT = typename Elem<QKV>::T;
+  constexpr bool ONE = sizeof(OT) == 2 && RING != DT_F32;   // 16-bit o and ring
+  uint16_t* sdst = nullptr;
+  size_t sstep = 0;
+  bool son = false;
+  if constexpr (ONE) {
+    if (grp == 0) {
+      sdst = static_cast<uint16_t*>(a.o) + (static_cast<size_t>(g.b) * T * a.Hv + g.h) * a.dv + g.vcol;
+      sstep = static_cast<size_t>(a.Hv) * a.dv;
+      son = true;
+    } else if (grp == 1) {
+      sdst = static_cast<uint16_t*>(const_cast<void*>(a.ring_d)) + (hs * a.L + r.p) * a.dv + g.vcol;
+      sstep = a.dv;
+      son = app;
+    } else if (grp == 2) {
+      sdst = reinterpret_cast<uint16_t*>(a.ring_g + hs * a.L + r.p) + col;
+      sstep = 2;
+      son = app && gwriter_wave && col < 2;
+    }
+  }
+  size_t kidx = (ks * a.L + r.p) * DK + 4 * lane;
+  const bool kon = app && kwriter && lane < C4;
 #pragma unroll
   for (int tau = 0; tau < 8; ++tau) {
     if (tau < T) {
@@ -714,14 +748,25 @@ __device__ __forceinline__ void window_chunked(const DecodeArgs& a, const ItemGe
       const float vv = vl[tau * 16 + col];
       float d, o;
       token_out(pq[tau], pk[tau], gram(8 + tau, tau), alpha, bt, vv, d, o);
-      const size_t ih = (static_cast<size_t>(g.b) * T + tau) * a.Hv + g.h;
-      const int pos = r.p + tau;
-      small_stores<QKV, RING>(a, ih * a.dv + g.vcol, (hs * a.L + pos) * a.dv + g.vcol,
-                              hs * a.L + pos, r.ok ? o : 0.f, d, gv, app, gwriter_wave, grp, col);
-      if (app && kwriter && lane < C4) {
-        const f4 kv = *reinterpret_cast<const f4*>(qk + tau * 2 * DK + DK + 4 * lane);
-        store4<RING>(a.ring_k, (ks * a.L + pos) * DK + 4 * lane, kv);
+      if constexpr (ONE) {
+        const uint32_t gb = __float_as_uint(gv);
+        const uint16_t hv = static_cast<uint16_t>(col ? gb >> 16 : gb & 0xffffu);
+        const uint16_t val = grp == 0 ? __builtin_bit_cast(uint16_t, from_f32<QKV>(r.ok ? o : 0.f))
+                           : grp == 1 ? __builtin_bit_cast(uint16_t, from_f32<RING>(d))
+                                      : hv;
+        if (son) *sdst = val;
+        sdst += sstep;
+      } else {
+        const size_t ih = (static_cast<size_t>(g.b) * T + tau) * a.Hv + g.h;
+        const int pos = r.p + tau;
+        small_stores<QKV, RING>(a, ih * a.dv + g.vcol, (hs * a.L + pos) * a.dv + g.vcol,
+                                hs * a.L + pos, r.ok ? o : 0.f, d, gv, app, gwriter_wave, grp, col);
       }
+      if (kon) {
+        const f4 kv = *reinterpret_cast<const f4*>(qk + tau * 2 * DK + DK + 4 * lane);
+        store4<RING>(a.ring_k, kidx, kv);
+      }
+      kidx += DK;
       // the later tokens' products after this token's update
 #pragma unroll
       for (int m = tau + 1; m < 8; ++m) {
@@ -1010,7 +1055,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   const size_t ks = static_cast<size_t>(r.sc) * a.Hk + g.hk;
   if constexpr (!TT && !KG) {
     if (a.win_mfma) {
-      window_chunked<DK, QKV, RING, SD>(a, g, r, T, S, qk, vl, gates + 3 * wh * T, hs, ks, kwriter,
+      window_chunked<DK, QKV, RING, SD, QKV == DT_BF16 && !NRM>(a, g, r, T, S, qk, vl, gates + 3 * wh * T, hs, ks, kwriter,
                                         gwriter_wave, grp, col, lane);
       return;
     }
