@@ -1179,10 +1179,20 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
 
   using SE = typename Elem<SD>::T;
   SE* xbase = static_cast<SE*>(a.ckpt) + (hs * a.dv + vb * FV) * DK;   // the block's FV rows
+  // the block's checkpoint rows, read with the non-temporal policy (each line
+  // is read once and written back once: 31.4 -> 30.3 us at p = 15, B = 32)
   f4 x[MAXR];
 #pragma unroll
   for (int m = 0; m < MAXR; ++m)
-    if (m < nr) x[m] = load4<SD>(xbase, (row + m) * DK + e4);
+    if (m < nr) {
+      if constexpr (SD == DT_F32) {
+        x[m] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(xbase + (row + m) * DK + e4));
+      } else {
+        const u16x4 r4 = __builtin_nontemporal_load(reinterpret_cast<const u16x4*>(xbase + (row + m) * DK + e4));
+        x[m] = f4{to_f32<SD>(from_bits<SD>(r4[0])), to_f32<SD>(from_bits<SD>(r4[1])),
+                  to_f32<SD>(from_bits<SD>(r4[2])), to_f32<SD>(from_bits<SD>(r4[3]))};
+      }
+    }
 
   if constexpr (KG) {
     for (int c = tid; c < p * C4; c += blockDim.x) {
