@@ -241,9 +241,9 @@ struct RowState {
   bool slot_ok, ok, flush;
 };
 
-__device__ __forceinline__ RowState row_state(const DecodeArgs& a, int b, int T) {
+__device__ __forceinline__ RowState row_state(const DecodeArgs& a, int b, int T, int slot) {
   RowState r;
-  r.s = ld_uniform(a.slot, b);
+  r.s = slot;
   r.slot_ok = r.s >= 0 && r.s < a.N;
   r.sc = r.slot_ok ? r.s : 0;
   const int p_raw = ld_uniform(a.write_pos, r.sc);
@@ -264,13 +264,14 @@ __device__ __forceinline__ RowState row_state(const DecodeArgs& a, int b, int T)
 // zero without a memory access (they are also the MFMA's zero padding). All
 // loads are unconditional (surplus lanes read a clamped address) so that they
 // issue before the slab.
+// Request an item's token operands: they depend on the row and head only,
+// not on the slot or the cursor, so they are issued before the row's slot and
+// cursor are known and their latency overlaps that scalar chain.
 template <int DK, int QKV, int RING, int TT, int KG>
-__device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const DecodeArgs& a,
-                                            const ItemGeo& g, const RowState& r, int T,
-                                            int tid, int lane, int grp, int wave) {
+__device__ __forceinline__ void fetch_tokens(Small<DK, QKV, RING>& f, const DecodeArgs& a,
+                                             const ItemGeo& g, int T, int tid, int lane,
+                                             int grp, int wave) {
   constexpr int C4 = DK / 4;
-  constexpr bool RF32 = (RING == DT_F32);
-  constexpr int RS = RF32 ? 4 : 2;
   // wave 0: the gates of the workgroup's GH heads, lane hh*T + t
   if (wave == 0) {
     const int ng = a.GH * T;
@@ -290,6 +291,27 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
     f.q_raw = load4_raw<QKV>(a.q, qsrc);
     f.k_raw = load4_raw<QKV>(a.k, qsrc);
   }
+  if constexpr (TT) {
+    f.v_raw = load1_raw<QKV>(a.v, static_cast<size_t>(g.b) * a.v_rs + g.h * a.dv + g.vcol);
+  } else {
+    // every window token's v: the token loop then reads them from LDS
+    // instead of waiting for a load per token (tokens past T read the last
+    // one; T <= 16)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = grp + 4 * i < T ? grp + 4 * i : T - 1;
+      f.vt_raw[i] = load1_raw<QKV>(a.v, (static_cast<size_t>(g.b) * T + t) * a.v_rs + g.h * a.dv + g.vcol);
+    }
+  }
+}
+
+template <int DK, int QKV, int RING, int TT, int KG>
+__device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const DecodeArgs& a,
+                                            const ItemGeo& g, const RowState& r, int T,
+                                            int tid, int lane, int grp, int wave) {
+  constexpr int C4 = DK / 4;
+  constexpr bool RF32 = (RING == DT_F32);
+  constexpr int RS = RF32 ? 4 : 2;
   // the key ring of (slot, key head), the valid entries only
   const char* kbase = static_cast<const char*>(a.ring_k) +
                       (static_cast<size_t>(r.sc) * a.Hk + g.hk) * a.L * DK * RS;
@@ -325,18 +347,6 @@ __device__ __forceinline__ void fetch_small(Small<DK, QKV, RING>& f, const Decod
     const int off = (4 * grp * a.dv + g.vcol) * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.d_raw[i] = __builtin_amdgcn_raw_buffer_load_b16(rd, off, 2 * i * a.dv, 0);
-  }
-  if constexpr (TT) {
-    f.v_raw = load1_raw<QKV>(a.v, static_cast<size_t>(g.b) * a.v_rs + g.h * a.dv + g.vcol);
-  } else {
-    // every window token's v, requested with the other small operands: the
-    // token loop then reads them from LDS instead of waiting for a load per
-    // token (tokens past T read the last one; T <= 16)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = grp + 4 * i < T ? grp + 4 * i : T - 1;
-      f.vt_raw[i] = load1_raw<QKV>(a.v, (static_cast<size_t>(g.b) * T + t) * a.v_rs + g.h * a.dv + g.vcol);
-    }
   }
 }
 
@@ -1118,8 +1128,11 @@ __global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
   // chain before the first vector load is arguments -> slot -> cursor.
   asm volatile("" ::"s"(a.slot), "s"(a.write_pos), "s"(a.ff_flags));
   const ItemGeo g = item_geo(a, wave, col);
-  const RowState r = row_state(a, g.b, T);
+  // the slot load first, then the token operands while it is in flight
+  const int slot = ld_uniform(a.slot, g.b);
   Small<DK, QKV, RING> sm;
+  fetch_tokens<DK, QKV, RING, TT, KG>(sm, a, g, T, tid, lane, grp, wave);
+  const RowState r = row_state(a, g.b, T, slot);
   SlabRaw<SD, DK> R;
   fetch_small<DK, QKV, RING, TT, KG>(sm, a, g, r, T, tid, lane, grp, wave);
   if constexpr (KG) {
