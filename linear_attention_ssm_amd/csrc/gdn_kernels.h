@@ -1114,8 +1114,18 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
 }
 
 // NRM = 1: q and k are L2-normalised (q scaled) in the kernel (a.qk_norm).
+// Windows (TT = 0) are bound by vector issue after the checkpoint arrives;
+// held to 80 VGPRs (6 wavefronts per SIMD instead of 5, no spills at dk <= 128
+// without in-kernel normalisation) their launches run in fewer rounds:
+// 20.4 -> 20.0 us (T = 5, B = 32), lossless 21.9 -> 20.8 us.
+constexpr int window_waves_per_eu(int DK, int TT, int NRM) {
+  return (TT || NRM || DK > 128) ? 1 : 6;
+}
+
 template <int DK, int QKV, int RING, int SD, int TT, int KG, int NRM>
-__global__ __launch_bounds__(512) void replay_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(window_waves_per_eu(DK, TT, NRM)))) void replay_decode_kernel(
+    DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* dump = reinterpret_cast<float*>(smem + a.dump_off);    // [64][8] write sink
   const int tid = threadIdx.x;
