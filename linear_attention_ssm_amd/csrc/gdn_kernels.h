@@ -759,11 +759,13 @@ __device__ __forceinline__ void window_chunked(const DecodeArgs& a, const ItemGe
       float d, o;
       token_out(pq[tau], pk[tau], gram(8 + tau, tau), alpha, bt, vv, d, o);
       if constexpr (ONE) {
+        // every candidate formed on every lane, then one select (no branch
+        // per lane group)
         const uint32_t gb = __float_as_uint(gv);
         const uint16_t hv = static_cast<uint16_t>(col ? gb >> 16 : gb & 0xffffu);
-        const uint16_t val = grp == 0 ? __builtin_bit_cast(uint16_t, from_f32<QKV>(r.ok ? o : 0.f))
-                           : grp == 1 ? __builtin_bit_cast(uint16_t, from_f32<RING>(d))
-                                      : hv;
+        const uint16_t ob = __builtin_bit_cast(uint16_t, from_f32<QKV>(r.ok ? o : 0.f));
+        const uint16_t db = __builtin_bit_cast(uint16_t, from_f32<RING>(d));
+        const uint16_t val = grp == 0 ? ob : (grp == 1 ? db : hv);
         if (son) *sdst = val;
         sdst += sstep;
       } else {
