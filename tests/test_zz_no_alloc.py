@@ -58,3 +58,42 @@ def test_noalloc_equals_workspace_variant(gdn, gate):
     live = big[big >= 0]
     assert int(b.write_pos[to_dev(live).long()].abs().sum().item()) > 0   # cursors moved
     log(f"[noalloc/{gate}] {w.steps} calls equal to the workspace variant")
+
+
+def test_noalloc_at_its_row_limit(gdn):
+    """GDN_SCRATCH_MAX_ROWS rows in one call (every arrival counter of the
+    static scratch in use), then a call of 100 rows, then the limit again,
+    each equal to the workspace variant bit for bit. Small heads (Hv = 2,
+    Hk = 1, dk = dv = 32, L = 4, bf16 inputs, fp16 ring) keep the pool at
+    about 34 MB."""
+    B = gdn.SCRATCH_MAX_ROWS
+    w = gi.scaled(gi.C1, name="noalloc_limit", B=B, N=B, Hv=2, Hk=1, qkv="bf16", ring="f16",
+                  stagger=True, steps=3, seed=4343)
+    S0 = gi.initial_state(w)
+    full = gi.slot_map(w)
+    few = np.random.default_rng(w.seed).permutation(w.N)[:100].astype(np.int32)
+    a, b = Pool(w, S0, canary=True), Pool(w, S0, canary=True)
+    for t, slots in enumerate((full, few, full)):
+        n = len(slots)
+        ws = gi.scaled(w, B=n)
+        xi = dev_inputs(gi.step_inputs(ws, t))
+        slot_t = to_dev(slots)
+        ff = to_dev(gi.force_flush_schedule(ws, t, slots))
+        arrive = gdn.arrive_workspace(n, DEV)
+        oa = gdn.gdn_replay_decode_advance(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, a.ckpt,
+                                           a.ring_d, a.ring_k, a.ring_g, a.write_pos, arrive,
+                                           force_flush=ff, err_flags=a.err)
+        ob = torch.empty_like(oa)
+        gdn.gdn_replay_decode_advance_noalloc(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, b.ckpt,
+                                              b.ring_d, b.ring_k, b.ring_g, b.write_pos, ob,
+                                              force_flush=ff, err_flags=b.err)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(oa), bits(ob)), f"call {t} ({n} rows): outputs differ"
+        assert torch.equal(a.write_pos, b.write_pos), f"call {t}: cursors differ"
+        for x, y, name in zip((a.ckpt, a.ring_d, a.ring_k, a.ring_g),
+                              (b.ckpt, b.ring_d, b.ring_k, b.ring_g), ("ckpt", "d", "k", "g")):
+            assert torch.equal(bits(x), bits(y)), f"call {t}: {name} differs"
+        assert int(a.err.item()) == int(b.err.item()) == 0
+        b.check_canaries(f"call {t}")
+    assert int((b.write_pos != 0).sum().item()) > 0                       # cursors moved
+    log(f"[noalloc/limit] {B} rows, 100 rows, {B} rows: equal to the workspace variant")
