@@ -266,3 +266,56 @@ def test_maximum_sizes(gdn, ring, gate):
     live = slots[slots >= 0]
     assert rel_err(to_f64(pool.ckpt[torch.from_numpy(live).to(DEV)]), S_true[live]) <= tol
     assert int(pool.err.item()) == 0
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_batch_of_padding_rows_only(gdn, gate):
+    """A batch whose every row is padding (slot -1): each entry point runs,
+    returns zero outputs, writes no checkpoint, ring or cursor byte (checked
+    bit for bit, with canary guards around the pool) and sets no error bit:
+    the replay decode (step and window), the fused advance, the packed decode,
+    the cursor calls and the fold."""
+    w = gi.scaled(gi.C2, name=f"all_pad_{gate}", B=6, N=8, L=4, steps=1, gate=gate, seed=77)
+    S0 = gi.initial_state(w)
+    pool = Pool(w, S0, garbage=True, canary=True)
+    # a nonzero phase, so that a stray advance or fold would change something
+    pool.write_pos.copy_(to_dev(np.array([1, 2, 3, 0, 1, 2, 3, 0], np.int32)))
+    snap = [bits(t).clone() for t in (pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
+                                      pool.write_pos)]
+    slots = to_dev(np.full(w.B, -1, np.int32))
+    xi = dev_inputs(gi.step_inputs(w, 0))
+    ff = to_dev(np.ones(w.B, np.int32))                 # forced flushes, ignored on padding
+    o = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slots, pool.ckpt, pool.ring_d,
+                              pool.ring_k, pool.ring_g, pool.write_pos, force_flush=ff,
+                              err_flags=pool.err)
+    assert torch.count_nonzero(o).item() == 0
+    arrive = gdn.arrive_workspace(w.B, DEV)
+    o = gdn.gdn_replay_decode_advance(xi.q, xi.k, xi.v, xi.g, xi.beta, slots, pool.ckpt,
+                                      pool.ring_d, pool.ring_k, pool.ring_g, pool.write_pos,
+                                      arrive, force_flush=ff, err_flags=pool.err)
+    assert torch.count_nonzero(o).item() == 0
+    assert torch.count_nonzero(arrive).item() == 0      # the workspace is left zero
+    xw = dev_inputs(gi.step_inputs(gi.scaled(w, T=3), 0))
+    o = gdn.gdn_replay_decode(xw.q, xw.k, xw.v, xw.g, xw.beta, slots, pool.ckpt, pool.ring_d,
+                              pool.ring_k, pool.ring_g, pool.write_pos, err_flags=pool.err,
+                              window=True)
+    assert torch.count_nonzero(o).item() == 0
+    gdn.gdn_replay_advance(slots, pool.write_pos, w.L, force_flush=ff, err_flags=pool.err)
+    gdn.gdn_replay_commit(slots, to_dev(np.full(w.B, 2, np.int32)), pool.write_pos, w.L, 3,
+                          err_flags=pool.err)
+    gdn.gdn_replay_fold(slots, pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
+                        pool.write_pos, err_flags=pool.err)
+    gdn.gdn_replay_reset(slots, pool.write_pos, err_flags=pool.err)
+    torch.cuda.synchronize()
+    for now, before, name in zip((pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
+                                  pool.write_pos), snap, ("ckpt", "ring d", "ring k", "ring g",
+                                                          "cursors")):
+        assert torch.equal(bits(now), before), f"{name} changed"
+    assert int(pool.err.item()) == 0
+    pool.check_canaries("padding-only batch")
+    state = pool.ckpt.clone()
+    o = gdn.gdn_packed_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slots, state, err_flags=pool.err)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0
+    assert torch.equal(bits(state), bits(pool.ckpt)) and int(pool.err.item()) == 0
+    log(f"[padding-only/{gate}] every entry point: zero outputs, nothing written")
