@@ -681,7 +681,7 @@ def main():
     args = ap.parse_args()
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs on a single MI355X and has "
+        print("bench.py measures one GPU only: the library runs on a single MI355X and has "
               "no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     import torch
