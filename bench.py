@@ -559,7 +559,7 @@ def cpu_model() -> str:
 
 def cpu_baseline(w, budget_s, log):
     """The CPU oracle's sequential decode recurrence (O1), fp64 and its fp32
-    instance, on a bounded sample of the standard workload: the c2 batch
+    instance, on a bounded sample of the standard workload: its 64-row batch
     stepped for about budget_s / 4 seconds per configuration, on one thread
     and on all the host cores this process may use (the OpenMP loop over
     (row, value head) of a -O3 build of the same C source for this host)."""
