@@ -188,9 +188,9 @@ def test_fold_bitwise_against_oracle(gdn, ring):
         f"{int(wp[live].sum())} entries folded")
 
 
-@pytest.mark.parametrize("T", [2, 4, 6, 8])
+@pytest.mark.parametrize("T", [1, 2, 4, 6, 8])
 def test_window_length_sweep_verify_commit_verify(gdn, T):
-    """Windows of T in {2, 4, 6, 8} tokens (vLLM PR #49887, Tests) at B = 16:
+    """Windows of T in {1, 2, 4, 6, 8} tokens (vLLM PR #49887, Tests) at B = 16:
     a single-token history, a verify window, a commit of a ~ U{0..T}, then a
     second window that reads the committed entries; both windows against the
     oracle, the cursors exact."""
@@ -245,3 +245,52 @@ def _verify_commit_verify(gdn, w):
         wp += acc
         assert np.array_equal(pool.write_pos.cpu().numpy()[slots], wp)
     assert int(pool.err.item()) == 0
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_one_token_window_at_the_last_ring_entry(gdn, gate):
+    """Every cursor at L - 1: a one-token verify window appends entry L - 1
+    and, unlike a decode step at that cursor, does not flush (checkpoint
+    untouched, cursor unmoved). Committing it fills the ring (p = L); the fold
+    then writes the true state and the reset clears the cursors."""
+    w = gi.scaled(gi.C5, name=f"win1_last_{gate}", B=8, N=8, T=1, L=4, steps=1, gate=gate,
+                  seed=661)
+    L = w.L
+    S0 = gi.initial_state(w)
+    slots = gi.slot_map(w)
+    slot_t = to_dev(slots)
+    pool = Pool(w, S0, garbage=True, canary=True)
+    S_true = S0.astype(np.float64)
+    for i in range(L - 1):                      # history: L - 1 steps, no flush
+        x = gi.step_inputs(w, 300 + i)
+        xi = dev_inputs(x)
+        gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, pool.ckpt, pool.ring_d,
+                              pool.ring_k, pool.ring_g, pool.write_pos, err_flags=pool.err)
+        gdn.gdn_replay_advance(slot_t, pool.write_pos, L, err_flags=pool.err)
+        step(S_true, slots, *(a[:, 0] for a in x.f64()))
+    assert pool.write_pos.cpu().numpy()[slots].tolist() == [L - 1] * w.B
+    ck0 = bits(pool.ckpt).clone()
+    x = gi.step_inputs(w, 400)
+    xi = dev_inputs(x)
+    o = gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, pool.ckpt, pool.ring_d,
+                              pool.ring_k, pool.ring_g, pool.write_pos, err_flags=pool.err,
+                              window=True)
+    x64 = x.f64()
+    e = rel_err(to_f64(o), window_ref(S_true, slots, *x64))
+    assert e <= tol_o(w), f"one-token window rel err {e:.3e}"
+    assert torch.equal(bits(pool.ckpt), ck0), "a window flushed"
+    assert pool.write_pos.cpu().numpy()[slots].tolist() == [L - 1] * w.B
+    gdn.gdn_replay_commit(slot_t, to_dev(np.ones(w.B, np.int32)), pool.write_pos, L, 1,
+                          err_flags=pool.err)
+    _advance_true(S_true, slots, x64, np.ones(w.B, np.int64))
+    assert pool.write_pos.cpu().numpy()[slots].tolist() == [L] * w.B
+    gdn.gdn_replay_fold(slot_t, pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g,
+                        pool.write_pos, err_flags=pool.err)
+    gdn.gdn_replay_reset(slot_t, pool.write_pos, err_flags=pool.err)
+    torch.cuda.synchronize()
+    es = rel_err(to_f64(pool.ckpt)[slots], S_true[slots])
+    assert es <= tol_state(w), f"folded state rel err {es:.3e}"
+    assert pool.write_pos.cpu().numpy()[slots].tolist() == [0] * w.B
+    assert int(pool.err.item()) == 0
+    pool.check_canaries("one-token window")
+    log(f"[win1/{gate}] window at p = L-1: no flush; commit, fold (rel err {es:.2e}), reset")
