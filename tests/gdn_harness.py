@@ -157,7 +157,12 @@ class Report:
     o_err: List[float] = field(default_factory=list)
     state_err: List[float] = field(default_factory=list)
     recon_err: List[float] = field(default_factory=list)
+    state_t: List[int] = field(default_factory=list)   # step of each state_err entry
     flushes: int = 0
+
+    def state_max(self, t0: int, t1: int) -> float:
+        """Largest checkpoint / state error recorded at steps t0 <= t < t1."""
+        return max(e for e, t in zip(self.state_err, self.state_t) if t0 <= t < t1)
 
     def summary(self) -> str:
         f = lambda x: f"{max(x):.2e}" if x else "-"
@@ -250,6 +255,7 @@ def run_decode(w: gi.Workload, kind: str = "replay", steps: Optional[int] = None
                 for j, i in enumerate(fl_i):
                     es = rel_err(ck[j], S_true[i])
                     rep.state_err.append(es)
+                    rep.state_t.append(t)
                     assert es <= tol_s_, \
                         f"{w.name} step {t}: row {rows[i]} ckpt rel err {es:.3e}"
             if recon_every and (t % recon_every == recon_every - 1 or t == steps - 1):
@@ -263,6 +269,7 @@ def run_decode(w: gi.Workload, kind: str = "replay", steps: Optional[int] = None
             ck = to_f64(pool.ckpt[torch.from_numpy(slots[rows].astype(np.int64)).to(DEV)])
             es = rel_err(ck, S_true)
             rep.state_err.append(es)
+            rep.state_t.append(t)
             assert es <= tol_s_, f"{w.name} step {t}: packed state rel err {es:.3e}"
     assert int(pool.err.item()) == 0, f"unexpected error flags {int(pool.err.item())}"
     if ring0 is not None and kind == "replay":
