@@ -307,6 +307,17 @@ gdn_status replay_decode(const gdn_shape* s, const void* q, const void* k, const
   // a window's v values, [waves][16 tokens][16 rows] floats
   a.v_off = static_cast<int32_t>(up16(end));
   if (s->T > 1) end = a.v_off + static_cast<size_t>(block.x / 64) * 16 * 16 * sizeof(float);
+  // single-token steps with an fp32 checkpoint at dk = 128 over a 16-bit
+  // ring with a per-head gate: rows that do not flush take the split readout
+  // (the kernel checks the rest: 1..16 valid entries, no flush); it needs the
+  // token's q and k in the ring's format (512 bytes) and reuses the key-ring
+  // area for the ring keys in row order
+  a.split_ro = (s->window == 0 && s->gate == GDN_GATE_HEAD && s->ring_dtype != GDN_F32 &&
+                s->state_dtype == GDN_F32 && s->dk == 128 && block.x == 256) ? 1 : 0;
+  if (a.split_ro) {
+    a.qh_off = static_cast<int32_t>(up16(end));
+    end = a.qh_off + static_cast<size_t>(2) * s->dk * 2;
+  }
   a.dump_off = static_cast<int32_t>(up16(end));
   const size_t smem = a.dump_off + 64 * 8 * sizeof(float);
   if (smem > 160 * 1024) return GDN_ERR_UNSUPPORTED;

@@ -660,6 +660,11 @@ struct DecodeArgs {
   // of the packed mixed_qkv row when q, k, v are views into it)
   int32_t qk_rs, v_rs;
   int32_t qk_norm;         // 1: L2-normalise q and k in the kernel, scale q
+  // split readout of a single-token step with an fp32 checkpoint (process(),
+  // "split readout"): enabled for workgroups of 4 wavefronts at dk = 128;
+  // qh_off is the LDS byte offset of the token's q and k in the ring's
+  // 16-bit format ([2][dk])
+  int32_t split_ro, qh_off;
 };
 
 struct CursorArgs {

@@ -813,6 +813,12 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   const int nch = (p + CH - 1) / CH;   // MFMA k-steps over the valid entries
   const int lp = nch * CH;             // entries covered, zero-padded beyond p
   const int nqk = T * C4;
+  // the split readout (a single-token row with 1..16 valid entries that
+  // does not flush): see below
+  constexpr bool SPLIT = TT && !KG && RING != DT_F32 && SD == DT_F32 && DK == 128;
+  constexpr int KNS = DK + 4;          // LDS row stride (elements) of the ring keys in row order
+  bool split = false;
+  if constexpr (SPLIT) split = a.split_ro && !r.flush && p > 0 && p <= 16;
 
   // ---- LDS staging. Every thread writes (threads past the last piece into a
   // per-lane dump area) so the early loads have unconditional uses.
@@ -824,6 +830,21 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
     float* kdst = tid < nqk ? qdst + DK : dump + lane * 8 + 4;
     *reinterpret_cast<f4*>(qdst) = qv;
     *reinterpret_cast<f4*>(kdst) = kv;
+    if constexpr (SPLIT) {
+      // q and k in the ring's 16-bit format: the ring products' operand
+      if (a.split_ro && tid < nqk) {
+        uint16_t* xh = reinterpret_cast<uint16_t*>(buf + a.qh_off) + 4 * tid;
+        u16x4 hq, hk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const typename Elem<RING>::T hqi = from_f32<RING>(qv[i]), hki = from_f32<RING>(kv[i]);
+          hq[i] = __builtin_bit_cast(uint16_t, hqi);
+          hk[i] = __builtin_bit_cast(uint16_t, hki);
+        }
+        *reinterpret_cast<u16x4*>(xh) = hq;
+        *reinterpret_cast<u16x4*>(xh + DK) = hk;
+      }
+    }
     const float kq0 = token_kq<DK>(qv, kv);
     if (tid < nqk && tid - tq * C4 == 0) kq_l[tq] = kq0;
   }
@@ -910,16 +931,26 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
       *reinterpret_cast<uint2*>(in ? kt16 + key * a.kts + 4 * eg : d16) = a0;
       *reinterpret_cast<uint2*>(in ? kt16 + (key + 1) * a.kts + 4 * eg : d16 + 4) = a1;
     };
-    put_kt(tid >> 2, tid & 3, f.kr);
-    const int npr = (lp / 4) * NKG;                    // (entry group, key group) pairs
-    for (int t2 = tid + nthr; t2 < 4 * npr; t2 += nthr) {   // deep rings / small workgroups
-      const int pr = t2 >> 2, sub = t2 & 3;
+    if (split) {
+      // row order [entry][KNS] (4 workgroup wavefronts at dk = 128 hold all
+      // 16 entries): a thread writes its two keys of each of its four entries
+      const int pr = tid >> 2, sub = tid & 3;
       const int eg = pr / NKG, kg = pr % NKG;
-      const int off = (4 * eg * DK + kg * 8 + 2 * sub) * 2;
-      v4u v;
+      uint32_t* kn = reinterpret_cast<uint32_t*>(kt);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + i * DK * 2, 0, 0);
-      put_kt(pr, sub, v);
+      for (int i = 0; i < 4; ++i) kn[((4 * eg + i) * KNS + kg * 8 + 2 * sub) >> 1] = f.kr[i];
+    } else {
+      put_kt(tid >> 2, tid & 3, f.kr);
+      const int npr = (lp / 4) * NKG;                    // (entry group, key group) pairs
+      for (int t2 = tid + nthr; t2 < 4 * npr; t2 += nthr) {   // deep rings / small workgroups
+        const int pr = t2 >> 2, sub = t2 & 3;
+        const int eg = pr / NKG, kg = pr % NKG;
+        const int off = (4 * eg * DK + kg * 8 + 2 * sub) * 2;
+        v4u v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, off + i * DK * 2, 0, 0);
+        put_kt(pr, sub, v);
+      }
     }
   }
 
@@ -929,6 +960,7 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   constexpr int NPRE = RF32 ? 4 : 1;                  // k-steps covered by the fetch
   float A = 1.f, wj = 0.f;
   typename MM::op_t bops[NPRE];
+  float wd[4] = {0.f, 0.f, 0.f, 0.f};   // split rows: w_j d_j of this lane's entries 4 grp + i
   auto bop_of = [&](int c, const float (&dval)[4]) {
     typename MM::op_t bop;
     if constexpr (KG) {
@@ -977,7 +1009,12 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
 #pragma unroll
         for (int i = 0; i < 4; ++i) dv1[i] = dval_of(f.d_raw[i]);
       }
-      bops[c] = bop_of(c, dv1);
+      if (split) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wd[i] = __shfl(wj, (4 * grp + i) & 63, 64) * dv1[i];
+      } else {
+        bops[c] = bop_of(c, dv1);
+      }
     }
   }
   __syncthreads();
@@ -996,6 +1033,84 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
         a.write_pos_w[r.s] = r.flush ? 0 : p + 1;
         __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+    }
+  }
+
+  const int wph = a.VB / 16;
+  const int wh = g.h - (g.hk * a.G + g.hc * a.GH);              // head within the workgroup
+  const bool kwriter = (g.vb == 0) && (g.hc == 0) && (wave == 0);   // one key-ring writer per k-head
+  const bool gwriter_wave = (g.vb == 0) && (wave % wph == 0);     // one g writer per head
+  const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
+  const size_t ks = static_cast<size_t>(r.sc) * a.Hk + g.hk;
+
+  // ---- split readout. A row that does not flush needs its state
+  // S = A S0 + sum_j w_j d_j k_j^T only through S q and S k, and
+  //   S x = A (S0 x) + sum_j (w_j d_j) (k_j . x),
+  // so the state is never formed: S0 x runs over the checkpoint as loaded,
+  // and the ring products k_j . q, k_j . k take one MFMA k-step per 16 keys.
+  // In it lane (col, grp) supplies four keys of ring entry col and of q
+  // (col even) or k (col odd), and receives k_{4 grp + i} . x_col in register
+  // i: the products of exactly the entries whose weights w_j d_j it holds.
+  if constexpr (SPLIT) {
+    if (split) {
+      const uint16_t* kn = reinterpret_cast<const uint16_t*>(kt) + col * KNS + 4 * grp;
+      const uint16_t* xh = reinterpret_cast<const uint16_t*>(buf + a.qh_off) + (col & 1) * DK + 4 * grp;
+      f4 ce = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DK / 16; ++s)
+        ce = MM::mma(*reinterpret_cast<const typename MM::op_t*>(kn + 16 * s),
+                     *reinterpret_cast<const typename MM::op_t*>(xh + 16 * s), ce);
+      float dq = 0.f, dk = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // the neighbour lane (col ^ 1) holds the other vector's product
+        const float nb = __int_as_float(
+            __builtin_amdgcn_mov_dpp(__float_as_int(ce[i]), 0xB1, 0xf, 0xf, false));
+        const float kxq = (col & 1) ? nb : ce[i];
+        const float kxk = (col & 1) ? ce[i] : nb;
+        dq = __builtin_fmaf(wd[i], kxq, dq);
+        dk = __builtin_fmaf(wd[i], kxk, dk);
+      }
+      // S0 q, S0 k over this lane's part of row col. As loaded, lane col
+      // holds rows col & 7 (a) and (col & 7) + 8 (b) of keys
+      // 32u + 16 (col >= 8) + 4 grp .. + 3; lane col ^ 8 holds the other half
+      // of those rows' keys
+      const bool lo = col < 8;
+      const float* ql = qk + (lo ? 0 : 16) + 4 * grp;
+      float qa = 0.f, qb = 0.f, ka = 0.f, kb = 0.f;
+#pragma unroll
+      for (int u = 0; u < DK / 32; ++u) {
+        const f4 qv = *reinterpret_cast<const f4*>(ql + 32 * u);
+        const f4 kv = *reinterpret_cast<const f4*>(ql + DK + 32 * u);
+        const f4 ra = __builtin_bit_cast(f4, R.r[2 * u]);
+        const f4 rb = __builtin_bit_cast(f4, R.r[2 * u + 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          qa = __builtin_fmaf(ra[j], qv[j], qa);
+          qb = __builtin_fmaf(rb[j], qv[j], qb);
+          ka = __builtin_fmaf(ra[j], kv[j], ka);
+          kb = __builtin_fmaf(rb[j], kv[j], kb);
+        }
+      }
+      const float xq = __int_as_float(
+          __builtin_amdgcn_mov_dpp(__float_as_int(lo ? qb : qa), 0x128, 0xf, 0xf, false));
+      const float xk = __int_as_float(
+          __builtin_amdgcn_mov_dpp(__float_as_int(lo ? kb : ka), 0x128, 0xf, 0xf, false));
+      const float mq = (lo ? qa : qb) + xq;
+      const float mk = (lo ? ka : kb) + xk;
+      const float sq = quad_sum(__builtin_fmaf(A, mq, dq));
+      const float sk = quad_sum(__builtin_fmaf(A, mk, dk));
+      const float* gt = gates + 3 * wh;
+      const float alpha = gt[0], bt = gt[1], gv = gt[2];
+      float d, o;
+      token_out(sq, sk, kq_l[0], alpha, bt, to_f32<QKV>(f.v_raw), d, o);
+      const size_t ih = static_cast<size_t>(g.b) * a.Hv + g.h;
+      small_stores<QKV, RING>(a, ih * a.dv + g.vcol, (hs * a.L + p) * a.dv + g.vcol, hs * a.L + p,
+                              o, d, gv, true, gwriter_wave, grp, col);
+      if (kwriter && lane < C4)
+        store4<RING>(a.ring_k, (ks * a.L + p) * DK + 4 * lane,
+                     *reinterpret_cast<const f4*>(qk + DK + 4 * lane));
+      return;
     }
   }
 
@@ -1037,7 +1152,6 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
     for (int c = 0; c < NPRE; ++c)
       if (c < nch) kstep(c, bops[c]);
     if (nch > NPRE) {                                   // rings deeper than 16 entries
-      const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
       const char* dbase = static_cast<const char*>(a.ring_d) + hs * a.L * a.dv * RS;
       const __amdgpu_buffer_rsrc_t rd = brsrc(dbase, static_cast<uint32_t>(p) * a.dv * RS);
       for (int c = NPRE; c < nch; ++c) {
@@ -1059,12 +1173,6 @@ __device__ __forceinline__ void process(const DecodeArgs& a, const ItemGeo& g, c
   }
 
   // ---- tokens
-  const int wph = a.VB / 16;
-  const int wh = g.h - (g.hk * a.G + g.hc * a.GH);              // head within the workgroup
-  const bool kwriter = (g.vb == 0) && (g.hc == 0) && (wave == 0);   // one key-ring writer per k-head
-  const bool gwriter_wave = (g.vb == 0) && (wave % wph == 0);     // one g writer per head
-  const size_t hs = static_cast<size_t>(r.sc) * a.Hv + g.h;
-  const size_t ks = static_cast<size_t>(r.sc) * a.Hk + g.hk;
   if constexpr (!TT && !KG) {
     if (a.win_mfma) {
       window_chunked<DK, QKV, RING, SD, QKV == DT_BF16 && !NRM>(a, g, r, T, S, qk, vl, gates + 3 * wh * T, hs, ks, kwriter,
