@@ -106,6 +106,66 @@ def test_L1_replay_equals_packed_bitwise(gdn):
     assert int(a.err.item()) == 0
 
 
+@pytest.mark.parametrize("p", [1, 7, 16])
+def test_split_readout_matches_reconstruction(gdn, p):
+    """A single-token row that does not flush is read out without forming its
+    state, S x = A (S0 x) + sum_j (w_j d_j)(k_j . x); a forced flush of the
+    same step forms S = A S0 + sum_j w_j d_j k_j^T first (fp32 checkpoint,
+    dk = 128, fp16 ring, 1..16 valid entries). With fp32 q/k/v/o the two
+    outputs differ only by where each rounds to the ring's 16-bit format:
+    the split form rounds q and k (the ring products' operand), the
+    reconstruction rounds w_j d_j (the MFMA's operand), 2^-11 relative
+    each. So per output element
+      |o_split - o_flush| <= alpha (E_q + |k.q| beta E_k) + fp32 slack,
+      E_x = 2^-10 sum_j |w_j d_j| |k_j| |x|,
+    where a dropped or misplaced ring entry would cost |w_j d_j (k_j . q)|,
+    many times that bound."""
+    w = gi.scaled(gi.C2, name=f"split_{p}", B=8, N=8, Hv=4, Hk=2, L=32, steps=p, qkv="f32",
+                  stagger=False, seed=720 + p)
+    S0 = gi.initial_state(w)
+    slots = gi.slot_map(w)
+    pool = Pool(w, S0)
+    slot_t = to_dev(slots)
+    for t in range(p):
+        xi = dev_inputs(gi.step_inputs(w, t))
+        gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, pool.ckpt, pool.ring_d,
+                              pool.ring_k, pool.ring_g, pool.write_pos, err_flags=pool.err)
+        gdn.gdn_replay_advance(slot_t, pool.write_pos, w.L, err_flags=pool.err)
+    assert pool.write_pos.cpu().tolist() == [p] * w.N
+    x = gi.step_inputs(w, p)
+    xi = dev_inputs(x)
+    outs = []
+    for ff in (np.zeros(w.B, np.int32), np.ones(w.B, np.int32)):
+        c = [t.clone() for t in (pool.ckpt, pool.ring_d, pool.ring_k, pool.ring_g)]
+        outs.append(to_f64(gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slot_t, *c,
+                                                 pool.write_pos, force_flush=to_dev(ff),
+                                                 err_flags=pool.err)))
+    assert int(pool.err.item()) == 0
+    o_split, o_flush = (o[:, 0] for o in outs)                 # [B, Hv, dv]
+    q, k, v, g, beta = (a[:, 0] for a in x.f64())
+    G = w.Hv // w.Hk
+    rd, rk, rg = (to_f64(t) for t in (pool.ring_d, pool.ring_k, pool.ring_g))
+    bound = np.zeros_like(o_flush)
+    for b, s in enumerate(slots):
+        for h in range(w.Hv):
+            hk = h // G
+            gs = rg[s, h, :p]
+            wj = np.exp(np.array([gs[j + 1:].sum() for j in range(p)]))
+            wd = np.abs(wj[:, None] * rd[s, h, :p])                       # [p, dv]
+            kn = np.linalg.norm(rk[s, hk, :p], axis=1)                     # [p]
+            qn, knt = np.linalg.norm(q[b, hk]), np.linalg.norm(k[b, hk])
+            alpha, kq = np.exp(g[b, h]), abs(q[b, hk] @ k[b, hk])
+            e_q = 2.0 ** -10 * (wd * kn[:, None]).sum(0) * qn
+            e_k = 2.0 ** -10 * (wd * kn[:, None]).sum(0) * knt
+            bound[b, h] = alpha * (e_q + kq * beta[b, h] * e_k)
+    bound += 1e-5 * np.abs(o_flush).max()
+    diff = np.abs(o_split - o_flush)
+    log(f"[split p={p}] max diff {diff.max():.3e}, max bound {bound.max():.3e}, "
+        f"worst diff/bound {(diff / bound).max():.3f}")
+    assert (diff <= bound).all(), f"split readout off by {(diff / bound).max():.2f}x its bound"
+    assert diff.max() > 0, "the two paths should round differently"
+
+
 def test_corrupted_ring_key_changes_output(gdn):
     """Negative test (vLLM PR #49887, Tests): corrupting one valid cached key
     must change the output of the heads that read it, and only those."""
