@@ -158,7 +158,10 @@ __global__ __launch_bounds__(1024) void packed_decode_kernel(DecodeArgs a) {
 //            the memory unit copies the ring's log-decays and keys into LDS
 //            ahead of the slab (fetch_key_gate, weight_keys_lds). With a
 //            fused cursor advance the row's last workgroup writes the
-//            advanced cursor.
+//            advanced cursor. A single-token row with an fp32 checkpoint
+//            that does not flush skips forming S: its Sq and Sk come from
+//            S0 as loaded and from the ring products k_j . q, k_j . k on the
+//            MFMA units (the split readout in process()).
 // The small operands are requested before the slab: vector loads retire in
 // issue order, so the staging and the MFMA operand build can proceed while
 // the slab is still in flight.

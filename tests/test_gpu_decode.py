@@ -106,8 +106,8 @@ def test_L1_replay_equals_packed_bitwise(gdn):
     assert int(a.err.item()) == 0
 
 
-@pytest.mark.parametrize("p", [1, 7, 16])
-def test_split_readout_matches_reconstruction(gdn, p):
+@pytest.mark.parametrize("p,Hv,Hk", [(1, 4, 2), (7, 4, 2), (16, 4, 2), (9, 2, 2), (12, 8, 2)])
+def test_split_readout_matches_reconstruction(gdn, p, Hv, Hk):
     """A single-token row that does not flush is read out without forming its
     state, S x = A (S0 x) + sum_j (w_j d_j)(k_j . x); a forced flush of the
     same step forms S = A S0 + sum_j w_j d_j k_j^T first (fp32 checkpoint,
@@ -119,9 +119,10 @@ def test_split_readout_matches_reconstruction(gdn, p):
       |o_split - o_flush| <= alpha (E_q + |k.q| beta E_k) + fp32 slack,
       E_x = 2^-10 sum_j |w_j d_j| |k_j| |x|,
     where a dropped or misplaced ring entry would cost |w_j d_j (k_j . q)|,
-    many times that bound."""
-    w = gi.scaled(gi.C2, name=f"split_{p}", B=8, N=8, Hv=4, Hk=2, L=32, steps=p, qkv="f32",
-                  stagger=False, seed=720 + p)
+    many times that bound. Value heads per key head 1, 2 and 4: one head of
+    64 rows, two of 32 or four of 16 per workgroup."""
+    w = gi.scaled(gi.C2, name=f"split_{p}_{Hv}_{Hk}", B=8, N=8, Hv=Hv, Hk=Hk, L=32, steps=p,
+                  qkv="f32", stagger=False, seed=720 + p + 100 * Hv)
     S0 = gi.initial_state(w)
     slots = gi.slot_map(w)
     pool = Pool(w, S0)
@@ -160,7 +161,7 @@ def test_split_readout_matches_reconstruction(gdn, p):
             bound[b, h] = alpha * (e_q + kq * beta[b, h] * e_k)
     bound += 1e-5 * np.abs(o_flush).max()
     diff = np.abs(o_split - o_flush)
-    log(f"[split p={p}] max diff {diff.max():.3e}, max bound {bound.max():.3e}, "
+    log(f"[split p={p} Hv={Hv} Hk={Hk}] max diff {diff.max():.3e}, max bound {bound.max():.3e}, "
         f"worst diff/bound {(diff / bound).max():.3f}")
     assert (diff <= bound).all(), f"split readout off by {(diff / bound).max():.2f}x its bound"
     assert diff.max() > 0, "the two paths should round differently"
