@@ -413,6 +413,23 @@ gdn_status gdn_kda_gates(const gdn_gate_shape *shape, const float *a, const floa
  */
 gdn_status gdn_hbm_read_probe(const void *src, size_t nbytes, float *sink, void *stream);
 
+/*
+ * gdn_hbm_copy_probe -- a measurement aid, not a step of the method: copies
+ * `nbytes` of device memory from `src` to `dst` in the access pattern of a
+ * checkpoint block read and written back (each wavefront 8 KiB in 16-byte
+ * loads with the non-temporal policy, then the same bytes stored with the
+ * policy of the checkpoint write-back). Timed over several launches it gives
+ * the read + write bandwidth this GPU reaches for that pattern, the measured
+ * peak the fold and the packed decode are compared with. `dst` may be `src`
+ * (an exact copy onto itself: each wavefront loads its 8 KiB before storing
+ * them).
+ *   src, dst (device) 16-byte aligned; the same buffer or non-overlapping;
+ *            nbytes a positive multiple of 32 KiB.
+ * Returns GDN_ERR_INVALID_ARG for a null pointer, a bad size or alignment, or
+ * buffers that overlap without being the same.
+ */
+gdn_status gdn_hbm_copy_probe(const void *src, void *dst, size_t nbytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *gdn_status_string(gdn_status status);
 

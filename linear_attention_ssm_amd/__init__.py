@@ -79,10 +79,12 @@ for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_decode_advance"
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.gdn_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
 _lib.gdn_hbm_read_probe.restype = ctypes.c_int
+_lib.gdn_hbm_copy_probe.argtypes = [_P, _P, ctypes.c_size_t, _P]
+_lib.gdn_hbm_copy_probe.restype = ctypes.c_int
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 10
+ABI_VERSION = 11
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -402,6 +404,20 @@ def gdn_hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None):
     nbytes = src.numel() * src.element_size()
     _raise(_lib.gdn_hbm_read_probe(_ptr(src), ctypes.c_size_t(nbytes), _ptr(sink), _stream(stream)),
            "gdn_hbm_read_probe")
+
+
+def gdn_hbm_copy_probe(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Copy `src` into `dst` (device tensors of the same byte size, a multiple
+    of 32 KiB; `dst` may be `src`) in the pattern of a checkpoint read and
+    written back; see gdn_hbm_copy_probe in gdn_replay.h. A measurement aid
+    (the measured read + write peak)."""
+    _check(src, "src", None, None)
+    _check(dst, "dst", None, None, src.device)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    _raise(_lib.gdn_hbm_copy_probe(_ptr(src), _ptr(dst), ctypes.c_size_t(nbytes), _stream(stream)),
+           "gdn_hbm_copy_probe")
 
 
 # ------------------------------------------------------------------ prepared calls

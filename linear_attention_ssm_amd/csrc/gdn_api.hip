@@ -13,7 +13,7 @@ using namespace gdn;
 
 namespace {
 
-constexpr int kAbiVersion = 10;
+constexpr int kAbiVersion = 11;
 static_assert(kArriveStride == GDN_ARRIVE_STRIDE, "arrival counter stride");
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }

@@ -1315,6 +1315,23 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
 
   using SE = typename Elem<SD>::T;
   SE* xbase = static_cast<SE*>(a.ckpt) + (hs * a.dv + vb * FV) * DK;   // the block's FV rows
+  const int F4 = FV >> 2;                             // four d entries per item
+  // This thread's first piece of ring g, d and keys is requested before the
+  // checkpoint rows, so that staging them in LDS waits only for them: vector
+  // loads complete in issue order (30.5 -> 28.6 us at p = 15, B = 32). Only
+  // the wavefronts that hold some of a range request it (a wave-uniform
+  // branch); their surplus lanes read the range's last piece again.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lf4 = FV == 64 ? 4 : (FV == 32 ? 3 : 2);   // F4 = 2^lf4
+  const int cd = tid < p * F4 ? tid : p * F4 - 1, ck = tid < p * C4 ? tid : p * C4 - 1;
+  const int jd = cd >> lf4, jk = ck / C4;
+  float g_raw = 0.f;
+  typename Raw4<RING>::T d_raw{}, k_raw{};
+  if (!KG && wave == 0) g_raw = a.ring_g[hs * a.L + (tid < p ? tid : p - 1)];
+  if (64 * wave < p * F4)
+    d_raw = load4_raw<RING>(a.ring_d, (hs * a.L + jd) * a.dv + vb * FV + (cd - jd * F4) * 4);
+  if (64 * wave < p * C4)
+    k_raw = load4_raw<RING>(a.ring_k, (ks * a.L + jk) * DK + (ck - jk * C4) * 4);
   // the block's checkpoint rows, read with the non-temporal policy (each line
   // is read once and written back once: 31.4 -> 30.3 us at p = 15, B = 32)
   f4 x[MAXR];
@@ -1339,20 +1356,56 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
       *reinterpret_cast<f4*>(al + j * DK + q4) = av;
     }
   } else {
-    if (tid < p) al[tid] = decay_of(a.ring_g[hs * a.L + tid]);
+    if (tid < p) al[tid] = decay_of(g_raw);
   }
-  const int F4 = FV >> 2;                             // four d entries per item
-  for (int c = tid; c < p * F4; c += blockDim.x) {
+  if (tid < p * F4) *reinterpret_cast<f4*>(dl + jd * FV + (cd - jd * F4) * 4) = decode4<RING>(d_raw);
+  if (tid < p * C4) *reinterpret_cast<f4*>(kl + jk * DK + (ck - jk * C4) * 4) = decode4<RING>(k_raw);
+  for (int c = tid + blockDim.x; c < p * F4; c += blockDim.x) {
     const int j = c / F4, r4 = (c - j * F4) * 4;
     *reinterpret_cast<f4*>(dl + j * FV + r4) =
         load4<RING>(a.ring_d, (hs * a.L + j) * a.dv + vb * FV + r4);
   }
-  for (int c = tid; c < p * C4; c += blockDim.x) {
+  for (int c = tid + blockDim.x; c < p * C4; c += blockDim.x) {
     const int j = c / C4, q4 = (c % C4) * 4;
     *reinterpret_cast<f4*>(kl + j * DK + q4) = load4<RING>(a.ring_k, (ks * a.L + j) * DK + q4);
   }
   __syncthreads();
 
+  if (SD == DT_F32 && nr == MAXR) {
+    // fp32 state, four rows per thread, folded two at a time: the first pair
+    // is stored while the second is folded, and the first pair's work starts
+    // once its two rows have arrived (28.2 -> 26.8 us at p = 15, B = 32). One
+    // row at a time reads the staged entries four times (30.0 us); the same
+    // split written for every state format and row count measured 28.5 us.
+    // The same operations in the same order per element as the loop below.
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma clang fp contract(off)
+      for (int j = 0; j < p; ++j) {
+        f4 aj;
+        if constexpr (KG) aj = *reinterpret_cast<const f4*>(al + j * DK + e4);
+        else aj = f4{al[j], al[j], al[j], al[j]};
+        const f4 kv = *reinterpret_cast<const f4*>(kl + j * DK + e4);
+        const float2 d2 = *reinterpret_cast<const float2*>(dl + j * FV + row + 2 * h2);
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const float dj = mm ? d2.y : d2.x;
+          f4& y = x[2 * h2 + mm];
+          const float tx = aj.x * y.x, ty = aj.y * y.y, tz = aj.z * y.z, tw = aj.w * y.w;
+          y.x = __builtin_fmaf(dj, kv.x, tx);
+          y.y = __builtin_fmaf(dj, kv.y, ty);
+          y.z = __builtin_fmaf(dj, kv.z, tz);
+          y.w = __builtin_fmaf(dj, kv.w, tw);
+        }
+      }
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const int off = (row + 2 * h2 + mm) * DK + e4;
+        store16<kFoldStorePolicy>(reinterpret_cast<float*>(xbase), FV * DK * 4, off * 4, x[2 * h2 + mm]);
+      }
+    }
+    return;
+  }
   {
 #pragma clang fp contract(off)
     for (int j = 0; j < p; ++j) {

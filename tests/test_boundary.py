@@ -8,7 +8,8 @@ import pytest
 import linear_attention_ssm_amd as gdn
 from linear_attention_ssm_amd import gdn_shape
 
-EXPECTED = ["gdn_abi_version", "gdn_conv_update", "gdn_hbm_read_probe", "gdn_kda_gates",
+EXPECTED = ["gdn_abi_version", "gdn_conv_update", "gdn_hbm_copy_probe", "gdn_hbm_read_probe",
+            "gdn_kda_gates",
             "gdn_packed_decode",
             "gdn_replay_advance", "gdn_replay_commit",
             "gdn_replay_decode", "gdn_replay_decode_advance",
@@ -32,7 +33,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 10
+    assert lib.gdn_abi_version() == 11
     for st in range(5):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -128,6 +129,25 @@ def test_read_probe_validates():
     assert probe(FAKE[0], 0, FAKE[1]) == gdn.GDN_ERR_INVALID_ARG
     assert probe(FAKE[0], 32768 + 16, FAKE[1]) == gdn.GDN_ERR_INVALID_ARG
     assert probe(ctypes.c_void_p(FAKE[0].value + 4), 32768, FAKE[1]) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_copy_probe_validates():
+    """Null pointers, sizes that are not a positive multiple of 32 KiB,
+    misaligned buffers and buffers that overlap without being the same are
+    rejected before any launch."""
+    lib = gdn.lib()
+    probe = lambda src, dst, n: lib.gdn_hbm_copy_probe(src, dst, ctypes.c_size_t(n), None)
+    a, b = FAKE[0].value, 0x40000000
+    P = ctypes.c_void_p
+    assert probe(None, P(b), 32768) == gdn.GDN_ERR_INVALID_ARG
+    assert probe(P(a), None, 32768) == gdn.GDN_ERR_INVALID_ARG
+    assert probe(P(a), P(b), 0) == gdn.GDN_ERR_INVALID_ARG
+    assert probe(P(a), P(b), 32768 + 16) == gdn.GDN_ERR_INVALID_ARG
+    assert probe(P(a + 4), P(b), 32768) == gdn.GDN_ERR_INVALID_ARG
+    assert probe(P(a), P(b + 8), 32768) == gdn.GDN_ERR_INVALID_ARG
+    # overlapping, not the same: dst starts inside src, or src inside dst
+    assert probe(P(a), P(a + 16384), 32768) == gdn.GDN_ERR_INVALID_ARG
+    assert probe(P(a + 16384), P(a), 32768) == gdn.GDN_ERR_INVALID_ARG
 
 
 def test_decode_advance_noalloc_validates():

@@ -1,5 +1,7 @@
-"""GPU check of the read probe (the measurement aid behind bench.py's measured
-read peak): it must visit every 16-byte piece of the buffer it is given.
+"""GPU checks of the probes (the measurement aids behind bench.py's measured
+peaks). The read probe must visit every 16-byte piece of the buffer it is
+given; the copy probe must copy every byte, onto another buffer and onto
+itself.
 
 The probe sums two words of each of its loads per lane and writes the sum to
 the sink only when it equals 1234.5. A single nonzero float placed in the last
@@ -43,3 +45,19 @@ def test_probe_reads_every_piece(gdn, item, load, lane, word):
     torch.cuda.synchronize()
     log(f"[probe] item {item} load {load} lane {lane} word {word}: sink {sink.item()}")
     assert sink.item() == MAGIC
+
+
+@pytest.mark.parametrize("nbytes", [32768, 5 * 32768])
+def test_copy_probe_copies_every_byte(gdn, nbytes):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(nbytes)
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device=DEV, generator=g)
+    keep = src.clone()
+    dst = torch.zeros_like(src)
+    gdn.gdn_hbm_copy_probe(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, keep), "copy differs"
+    assert torch.equal(src, keep), "source changed"
+    gdn.gdn_hbm_copy_probe(dst, dst)          # onto itself
+    torch.cuda.synchronize()
+    assert torch.equal(dst, keep), "in-place copy changed the buffer"
