@@ -153,6 +153,35 @@ def test_window_equals_token_by_token_windows(gdn):
     assert rel_err(to_f64(oa), to_f64(ob)) <= tol_o(w)
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 96), (64, 48), (128, 16)])
+def test_fold_bitwise_smaller_row_blocks(gdn, dk, dv):
+    """The fold's workgroups cover 32 or 16 value rows when dv is not a
+    multiple of 64 (two rows or one per thread): bit-identical to the
+    oracle's pinned-rounding fold there too, with full, empty and partial
+    rings."""
+    w = dataclasses.replace(gi.C5, dk=dk, dv=dv, Hv=8, Hk=2, N=20, B=16, n_pad=2, permute=True,
+                            seed=830 + dv)
+    rc = gi.random_ring(w, seed_tag=7)
+    slots = gi.slot_map(w)
+    wp = rc.write_pos.copy()
+    live = slots[slots >= 0]
+    wp[live[0]] = w.L
+    wp[live[1]] = 0
+    ckpt = to_dev(rc.ckpt)
+    rd, rk = to_dev(rc.d, w.ring), to_dev(rc.k, w.ring)
+    rg = to_dev(rc.g)
+    wpt = to_dev(wp.astype(np.int32))
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gdn.gdn_replay_fold(to_dev(slots), ckpt, rd, rk, rg, wpt, err_flags=err)
+    assert int(err.item()) == 0
+    ref = rc.ckpt.copy()
+    fold_f32(ref, slots, wp.astype(np.int32).copy(), gi.as_f64(rc.d, w.ring).astype(np.float32),
+             gi.as_f64(rc.k, w.ring).astype(np.float32), rc.g)
+    got = ckpt.cpu().numpy()
+    mism = np.count_nonzero(got.view(np.uint32) != ref.view(np.uint32))
+    assert mism == 0, f"{mism} elements differ from the oracle's fold"
+
+
 @pytest.mark.parametrize("ring", ["f16", "bf16", "f32"])
 def test_fold_bitwise_against_oracle(gdn, ring):
     """gdn_replay_fold is bit-identical to the oracle's pinned-rounding fold
