@@ -153,14 +153,15 @@ def test_window_equals_token_by_token_windows(gdn):
     assert rel_err(to_f64(oa), to_f64(ob)) <= tol_o(w)
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 96), (64, 48), (128, 16)])
-def test_fold_bitwise_smaller_row_blocks(gdn, dk, dv):
+@pytest.mark.parametrize("dk,dv,L", [(128, 96, 16), (64, 48, 16), (128, 16, 16), (128, 128, 64)])
+def test_fold_bitwise_smaller_row_blocks(gdn, dk, dv, L):
     """The fold's workgroups cover 32 or 16 value rows when dv is not a
-    multiple of 64 (two rows or one per thread): bit-identical to the
-    oracle's pinned-rounding fold there too, with full, empty and partial
-    rings."""
-    w = dataclasses.replace(gi.C5, dk=dk, dv=dv, Hv=8, Hk=2, N=20, B=16, n_pad=2, permute=True,
-                            seed=830 + dv)
+    multiple of 64 (two rows or one per thread), and a ring of 64 entries
+    holds more d and key pieces than the workgroup has threads (staged in
+    more than one pass): bit-identical to the oracle's pinned-rounding fold
+    there too, with full, empty and partial rings."""
+    w = dataclasses.replace(gi.C5, dk=dk, dv=dv, L=L, Hv=8, Hk=2, N=20, B=16, n_pad=2,
+                            permute=True, seed=830 + dv + L)
     rc = gi.random_ring(w, seed_tag=7)
     slots = gi.slot_map(w)
     wp = rc.write_pos.copy()
