@@ -16,7 +16,8 @@ with the library's read probe; the read + write kernels against its copy
 probe), the packed read-update-write decode built
 alongside it, the no-flush ("best") mode, the large-pool and ring-depth
 workloads, the 16-bit-state, per-key-gate and front-end variants, the verify
-window + fold of the speculative workload, lossless verify, the pages' own
+window + fold of the speculative workload (the fold one layer per launch and
+all layers in one gdn_replay_fold_layers launch), lossless verify, the pages' own
 context figures, and the CPU oracle baseline on the host's cores.
 
 Modes for profiling runs (same kernels, fewer steps, no CPU baseline):
@@ -437,8 +438,14 @@ def bench_window_fold(w, R, steps, dev, log):
             gdn.gdn_replay_fold(slot_t, ls.state, ls.ring_d, ls.ring_k, ls.ring_g, wpf,
                                 err_flags=err)
 
+    def fold_all():
+        gdn.gdn_replay_fold_layers(slot_t, [ls.state for ls in layers],
+                                   [ls.ring_d for ls in layers], [ls.ring_k for ls in layers],
+                                   [ls.ring_g for ls in layers], wpf, err_flags=err)
+
     mv = time_graph(graph_of(verify), steps) / R
     mf = time_graph(graph_of(fold), steps) / R
+    mfl = time_graph(graph_of(fold_all), steps) / R
     assert int(err.item()) == 0
     G = w.Hv // w.Hk
     live = int(np.count_nonzero(slots >= 0))
@@ -448,10 +455,13 @@ def bench_window_fold(w, R, steps, dev, log):
                         + w.T * (2 * es * w.dk / G + 2 * es * w.dv + 8))
     fb = live * w.Hv * (8 * w.dv * w.dk + pf * ent)
     log(f"verify T={w.T}: {mv * 1e3:.2f} us/launch ({vb / mv / 1e6:.0f} GB/s); "
-        f"fold p={pf}: {mf * 1e3:.2f} us/launch ({fb / mf / 1e6:.0f} GB/s)")
+        f"fold p={pf}: {mf * 1e3:.2f} us/launch ({fb / mf / 1e6:.0f} GB/s); "
+        f"{R} layers in one fold call: {mfl * 1e3:.2f} us per layer ({fb / mfl / 1e6:.0f} GB/s)")
     return dict(verify_kernel_us=mv * 1e3, verify_gbs=vb / mv / 1e6,
                 verify_head_tokens_per_s=live * w.Hv * w.T / (mv / 1e3),
-                fold_kernel_us=mf * 1e3, fold_gbs=fb / mf / 1e6, window_p=p0, fold_p=pf)
+                fold_kernel_us=mf * 1e3, fold_gbs=fb / mf / 1e6, window_p=p0, fold_p=pf,
+                fold_layers_us_per_layer=mfl * 1e3, fold_layers_gbs=fb / mfl / 1e6,
+                fold_layers_n=R)
 
 
 def bench_lossless(w, R, steps, dev, log):
@@ -482,18 +492,31 @@ def bench_lossless(w, R, steps, dev, log):
             gdn.gdn_replay_fold(slot_t, ls.state, ls.ring_d, ls.ring_k, ls.ring_g, wp,
                                 err_flags=err)
 
+    def fold_all():
+        gdn.gdn_replay_fold_layers(slot_t, [ls.state for ls in layers],
+                                   [ls.ring_d for ls in layers], [ls.ring_k for ls in layers],
+                                   [ls.ring_g for ls in layers], wp, err_flags=err)
+
     def round_():
         verify()
         gdn.gdn_replay_commit(slot_t, acc, wp, w.L, w.T, err_flags=err)
         fold()
         gdn.gdn_replay_reset(slot_t, wp, err_flags=err)
 
+    def round_layers():
+        verify()
+        gdn.gdn_replay_commit(slot_t, acc, wp, w.L, w.T, err_flags=err)
+        fold_all()
+        gdn.gdn_replay_reset(slot_t, wp, err_flags=err)
+
     m_round = time_graph(graph_of(round_), steps)
+    m_round_l = time_graph(graph_of(round_layers), steps)
     m_verify = time_graph(graph_of(verify), steps) / R
     wpn = np.zeros(w.N, np.int32)                    # the cursors a commit leaves
     wpn[slots[slots >= 0]] = acc_np[slots >= 0]
     wp.copy_(dev_tensor(wpn, None, dev))
     m_fold = time_graph(graph_of(fold), steps) / R
+    m_fold_l = time_graph(graph_of(fold_all), steps) / R
     assert int(err.item()) == 0
     G = w.Hv // w.Hk
     live = slots >= 0
@@ -506,12 +529,17 @@ def bench_lossless(w, R, steps, dev, log):
     fb = n_fold * 8 * w.dv * w.dk + a_sum * ent
     log(f"lossless verify T={w.T}: round {m_round * 1e3:.1f} us ({R} layers: verify, commit, "
         f"fold, reset); verify {m_verify * 1e3:.2f} us/launch ({vb / m_verify / 1e6:.0f} GB/s), "
-        f"fold {m_fold * 1e3:.2f} us/launch ({fb / m_fold / 1e6:.0f} GB/s)")
+        f"fold {m_fold * 1e3:.2f} us/launch ({fb / m_fold / 1e6:.0f} GB/s); with the {R} "
+        f"layers folded in one call: round {m_round_l * 1e3:.1f} us, fold "
+        f"{m_fold_l * 1e3:.2f} us per layer ({fb / m_fold_l / 1e6:.0f} GB/s)")
     return dict(round_us=m_round * 1e3, layers=R,
                 accepted_tokens_per_s=float(acc_np[live].sum()) / (m_round / 1e3),
                 verify_kernel_us=m_verify * 1e3, verify_gbs=vb / m_verify / 1e6,
                 fold_kernel_us=m_fold * 1e3, fold_gbs=fb / m_fold / 1e6,
-                mean_accepted=float(acc_np[live].mean()))
+                mean_accepted=float(acc_np[live].mean()),
+                round_us_fold_layers=m_round_l * 1e3,
+                accepted_tokens_per_s_fold_layers=float(acc_np[live].sum()) / (m_round_l / 1e3),
+                fold_layers_us_per_layer=m_fold_l * 1e3, fold_layers_gbs=fb / m_fold_l / 1e6)
 
 
 def read_probe(R, reps, dev, log):
@@ -849,10 +877,15 @@ def main():
             "L16_fp32_ring": {"note": "fp32 ring (fp32 MFMA reconstruction), fp32 q/k/v/o",
                               **summary(rep_f32r)},
         },
-        "verify_window_c5_shapes": {**wf,
-                                    "fold_frac_of_measured_copy_peak": wf["fold_gbs"] / rw["gbs"]},
-        "lossless_verify_c6": {**ll,
-                               "fold_frac_of_measured_copy_peak": ll["fold_gbs"] / rw["gbs"]},
+        "verify_window_c5_shapes": {
+            **wf, "fold_frac_of_measured_copy_peak": wf["fold_gbs"] / rw["gbs"],
+            "fold_layers_frac": wf["fold_layers_gbs"] / 8000.0,
+            "fold_layers_frac_of_measured_copy_peak": wf["fold_layers_gbs"] / rw["gbs"],
+            "fold_layers_note": ("fold_layers_*: the same folds with every layer set in one "
+                                 "gdn_replay_fold_layers call (one launch), per layer")},
+        "lossless_verify_c6": {
+            **ll, "fold_frac_of_measured_copy_peak": ll["fold_gbs"] / rw["gbs"],
+            "fold_layers_frac_of_measured_copy_peak": ll["fold_layers_gbs"] / rw["gbs"]},
         "pages_context": PAGES_CONTEXT,
         "cpu_baseline": None,
         "kernel_sources_sha256_16": kernel_hash(),

@@ -326,6 +326,32 @@ gdn_status gdn_replay_fold(const gdn_shape *shape, const int32_t *slot_idx,
                            int32_t *err_flags, void *stream);
 
 /*
+ * gdn_replay_fold_layers -- gdn_replay_fold of n_layers layers in one go:
+ * layer l folds ring_d[l], ring_k[l], ring_g[l] into ckpt[l], with the same
+ * slots, cursors, shapes and dtypes for every layer (SGLang PR #36821,
+ * Technical principle: the fold runs at commit, once the verify pass has
+ * gone through every layer, so all layers' entries are known together).
+ * Each layer's result is bit-identical to gdn_replay_fold on that layer.
+ * The layers run in launches of up to 16 layers each, so the fixed start
+ * and tail cost of a launch is paid once per 16 layers instead of per layer.
+ *   n_layers      1..GDN_FOLD_MAX_LAYERS;
+ *   ckpt, ring_d, ring_k, ring_g
+ *                 host arrays of n_layers device pointers (each with the
+ *                 layout and alignment of gdn_replay_fold). The checkpoints
+ *                 must not overlap one another (checked: GDN_ERR_INVALID_ARG)
+ *                 nor any ring; rings may be shared between layers.
+ * The host arrays are read during the call only. Errors and error bits are
+ * those of gdn_replay_fold; an argument error is returned before anything is
+ * launched.
+ */
+#define GDN_FOLD_MAX_LAYERS 1024
+gdn_status gdn_replay_fold_layers(const gdn_shape *shape, int32_t n_layers,
+                                  const int32_t *slot_idx, void *const *ckpt,
+                                  const void *const *ring_d, const void *const *ring_k,
+                                  const float *const *ring_g, const int32_t *write_pos,
+                                  int32_t *err_flags, void *stream);
+
+/*
  * gdn_replay_reset -- write_pos[s] <- 0 for each row with slot s >= 0: the
  * ring is empty again once every layer has folded it (SGLang PR #36821: after
  * the fold the checkpoint holds the committed state). A slot >= N sets

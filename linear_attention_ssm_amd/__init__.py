@@ -69,12 +69,14 @@ _lib.gdn_replay_decode_advance_noalloc.argtypes = [_S] + [_P] * 15
 _lib.gdn_replay_advance.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_commit.argtypes = [_S] + [_P] * 5
 _lib.gdn_replay_fold.argtypes = [_S] + [_P] * 8
+_lib.gdn_replay_fold_layers.argtypes = [_S, ctypes.c_int32] + [_P] * 8
 _lib.gdn_replay_reset.argtypes = [_S] + [_P] * 4
 _lib.gdn_conv_update.argtypes = [ctypes.POINTER(gdn_conv_shape)] + [_P] * 7
 _lib.gdn_kda_gates.argtypes = [ctypes.POINTER(gdn_gate_shape)] + [_P] * 7
 for _f in ("gdn_packed_decode", "gdn_replay_decode", "gdn_replay_decode_advance",
            "gdn_replay_decode_advance_noalloc", "gdn_replay_advance",
-           "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_reset", "gdn_conv_update",
+           "gdn_replay_commit", "gdn_replay_fold", "gdn_replay_fold_layers",
+           "gdn_replay_reset", "gdn_conv_update",
            "gdn_kda_gates"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.gdn_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
@@ -84,7 +86,7 @@ _lib.gdn_hbm_copy_probe.restype = ctypes.c_int
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_abi_version.restype = ctypes.c_int32
-ABI_VERSION = 11
+ABI_VERSION = 12
 if _lib.gdn_abi_version() != ABI_VERSION:
     raise ImportError("libgdn_replay.so ABI version mismatch; rebuild it")
 
@@ -382,6 +384,40 @@ def gdn_replay_fold(slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags
     _raise(_lib.gdn_replay_fold(ctypes.byref(sh), _ptr(slot_idx), _ptr(ckpt), _ptr(ring_d),
                                 _ptr(ring_k), _ptr(ring_g), _ptr(write_pos), _ptr(err_flags),
                                 _stream(stream)), "gdn_replay_fold")
+
+
+def gdn_replay_fold_layers(slot_idx, ckpts, ring_ds, ring_ks, ring_gs, write_pos,
+                           err_flags=None, stream=None, step_rounding=False):
+    """gdn_replay_fold of several layers of equal shapes and dtypes in as few
+    launches as possible (ckpts[l] folds ring_ds[l], ring_ks[l], ring_gs[l]);
+    see gdn_replay_fold_layers in gdn_replay.h."""
+    n = len(ckpts)
+    if n < 1 or not (len(ring_ds) == len(ring_ks) == len(ring_gs) == n):
+        raise ValueError("one checkpoint, ring_d, ring_k and ring_g per layer")
+    _check(slot_idx, "slot_idx", torch.int32, 1)
+    dev = slot_idx.device
+    _check(ckpts[0], "ckpt", STATE_DTYPES, 4, dev)
+    N, Hv, dv, dk = ckpts[0].shape
+    Hk = ring_ks[0].shape[1]
+    gate = GDN_GATE_KEY if ring_gs[0].dim() == 4 else GDN_GATE_HEAD
+    L = None
+    for c, rd, rk, rg in zip(ckpts, ring_ds, ring_ks, ring_gs):
+        if c.dtype != ckpts[0].dtype or rd.dtype != ring_ds[0].dtype or rg.dim() != ring_gs[0].dim():
+            raise ValueError("every layer needs the dtypes of layer 0")
+        if c.shape != ckpts[0].shape:
+            raise ValueError("every layer needs the checkpoint shape of layer 0")
+        _, Ll = _ring_shape(c, rd, rk, rg, write_pos, Hv, Hk, dk, dv, dev, gate)
+        if L is not None and Ll != L:
+            raise ValueError("every layer needs the ring depth of layer 0")
+        L = Ll
+    _err_word(err_flags, dev)
+    sh = gdn_shape(slot_idx.shape[0], 1, N, Hv, Hk, dk, dv, L, GDN_F32, _DT[ring_ds[0].dtype], 0,
+                   _DT[ckpts[0].dtype], int(bool(step_rounding)), gate)
+    arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])
+    _raise(_lib.gdn_replay_fold_layers(ctypes.byref(sh), n, _ptr(slot_idx), arr(ckpts),
+                                       arr(ring_ds), arr(ring_ks), arr(ring_gs), _ptr(write_pos),
+                                       _ptr(err_flags), _stream(stream)),
+           "gdn_replay_fold_layers")
 
 
 def gdn_replay_reset(slot_idx, write_pos, err_flags=None, stream=None):

@@ -2,6 +2,7 @@
 // launch geometry and dispatch to the typed kernel instances. No call here
 // synchronises, allocates or frees.
 #include <algorithm>
+#include <cstdint>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -13,7 +14,7 @@ using namespace gdn;
 
 namespace {
 
-constexpr int kAbiVersion = 11;
+constexpr int kAbiVersion = 12;
 static_assert(kArriveStride == GDN_ARRIVE_STRIDE, "arrival counter stride");
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -435,23 +436,41 @@ gdn_status gdn_replay_commit(const gdn_shape* s, const int32_t* slot_idx, const 
   return from_hip(launch_commit(a, static_cast<hipStream_t>(stream)));
 }
 
-gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, void* ckpt,
-                           const void* ring_d, const void* ring_k, const float* ring_g,
-                           const int32_t* write_pos, int32_t* err_flags, void* stream) {
+namespace {
+
+// The fold of n layers of equal shapes, kFoldMaxLayers per launch (the layer
+// in blockIdx.y). Every pointer array holds n device pointers.
+gdn_status fold_layers(const gdn_shape* s, int n, const int32_t* slot_idx, void* const* ckpt,
+                       const void* const* ring_d, const void* const* ring_k,
+                       const float* const* ring_g, const int32_t* write_pos, int32_t* err_flags,
+                       void* stream) {
   const gdn_status st = check_shape(s, true);
   if (st != GDN_OK) return st;
-  if (!slot_idx || !ckpt || !ring_d || !ring_k || !ring_g || !write_pos)
-    return GDN_ERR_INVALID_ARG;
+  if (!slot_idx || !write_pos) return GDN_ERR_INVALID_ARG;
   if (s->step_rounding != 0 && s->step_rounding != 1) return GDN_ERR_INVALID_ARG;
-  const size_t rs = elem_size(s->ring_dtype);
   const size_t ga = s->gate == GDN_GATE_KEY ? 16 : 4;
-  if (!aligned(ckpt, 16) || !aligned(ring_d, 16) || !aligned(ring_k, 16) ||
-      !aligned(ring_g, ga) || !aligned(write_pos, 4) || !aligned(slot_idx, 4) ||
-      (err_flags && !aligned(err_flags, 4)))
+  if (!aligned(write_pos, 4) || !aligned(slot_idx, 4) || (err_flags && !aligned(err_flags, 4)))
     return GDN_ERR_INVALID_ARG;
+  for (int l = 0; l < n; ++l) {
+    if (!ckpt[l] || !ring_d[l] || !ring_k[l] || !ring_g[l]) return GDN_ERR_INVALID_ARG;
+    if (!aligned(ckpt[l], 16) || !aligned(ring_d[l], 16) || !aligned(ring_k[l], 16) ||
+        !aligned(ring_g[l], ga))
+      return GDN_ERR_INVALID_ARG;
+  }
+  if (n > 1) {
+    // the launch writes every layer's checkpoint at once: they must not overlap
+    const size_t bytes = static_cast<size_t>(s->N) * s->Hv * s->dv * s->dk *
+                         elem_size(s->state_dtype);
+    for (int l = 0; l < n; ++l)
+      for (int m = l + 1; m < n; ++m) {
+        const uintptr_t x = reinterpret_cast<uintptr_t>(ckpt[l]);
+        const uintptr_t y = reinterpret_cast<uintptr_t>(ckpt[m]);
+        if ((x < y ? y - x : x - y) < bytes) return GDN_ERR_INVALID_ARG;
+      }
+  }
   if (s->B == 0) return GDN_OK;
   FoldArgs a{};
-  a.slot = slot_idx; a.ckpt = ckpt; a.ring_d = ring_d; a.ring_k = ring_k; a.ring_g = ring_g;
+  a.slot = slot_idx;
   a.write_pos = write_pos; a.err = err_flags;
   a.B = s->B; a.N = s->N; a.Hv = s->Hv; a.Hk = s->Hk; a.dv = s->dv; a.L = s->L;
   a.G = s->Hv / s->Hk;
@@ -459,14 +478,43 @@ gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, void* ck
   // value rows per workgroup: 64 (or the largest of 32, 16 dividing dv), so
   // that the ring entries staged in LDS serve several rows per thread
   a.fv = s->dv % 64 == 0 ? 64 : (s->dv % 32 == 0 ? 32 : 16);
-  const dim3 grid(static_cast<unsigned>(s->B) * s->Hv * (s->dv / a.fv));
   const dim3 block(static_cast<unsigned>(16 * s->dk / 4));
   // LDS: the ring's keys [L][dk], d [L][fv] and decays ([L], or [L][dk] per key)
   const size_t n_al = s->gate == GDN_GATE_KEY ? static_cast<size_t>(s->dk) : 1;
   const size_t smem = static_cast<size_t>(s->L) * (n_al + a.fv + s->dk) * sizeof(float);
   if (smem > 160 * 1024) return GDN_ERR_UNSUPPORTED;
-  return from_hip(dispatch_fold(s->dk, a, s->ring_dtype, s->state_dtype, s->gate, grid, block,
-                                smem, static_cast<hipStream_t>(stream)));
+  for (int l0 = 0; l0 < n; l0 += kFoldMaxLayers) {
+    const int nl = std::min(n - l0, kFoldMaxLayers);
+    for (int i = 0; i < kFoldMaxLayers; ++i) {
+      const int l = l0 + (i < nl ? i : 0);
+      a.ckpt[i] = ckpt[l]; a.ring_d[i] = ring_d[l]; a.ring_k[i] = ring_k[l]; a.ring_g[i] = ring_g[l];
+    }
+    const dim3 grid(static_cast<unsigned>(s->B) * s->Hv * (s->dv / a.fv), static_cast<unsigned>(nl));
+    const gdn_status r = from_hip(dispatch_fold(s->dk, a, s->ring_dtype, s->state_dtype, s->gate,
+                                                grid, block, smem,
+                                                static_cast<hipStream_t>(stream)));
+    if (r != GDN_OK) return r;
+  }
+  return GDN_OK;
+}
+
+}  // namespace
+
+gdn_status gdn_replay_fold(const gdn_shape* s, const int32_t* slot_idx, void* ckpt,
+                           const void* ring_d, const void* ring_k, const float* ring_g,
+                           const int32_t* write_pos, int32_t* err_flags, void* stream) {
+  return fold_layers(s, 1, slot_idx, &ckpt, &ring_d, &ring_k, &ring_g, write_pos, err_flags,
+                     stream);
+}
+
+gdn_status gdn_replay_fold_layers(const gdn_shape* s, int32_t n_layers, const int32_t* slot_idx,
+                                  void* const* ckpt, const void* const* ring_d,
+                                  const void* const* ring_k, const float* const* ring_g,
+                                  const int32_t* write_pos, int32_t* err_flags, void* stream) {
+  if (n_layers < 1 || n_layers > GDN_FOLD_MAX_LAYERS || !ckpt || !ring_d || !ring_k || !ring_g)
+    return GDN_ERR_INVALID_ARG;
+  return fold_layers(s, n_layers, slot_idx, ckpt, ring_d, ring_k, ring_g, write_pos, err_flags,
+                     stream);
 }
 
 gdn_status gdn_replay_reset(const gdn_shape* s, const int32_t* slot_idx, int32_t* write_pos,

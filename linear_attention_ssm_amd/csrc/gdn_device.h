@@ -676,17 +676,22 @@ struct CursorArgs {
   int32_t B, N, L, T;
 };
 
+// Layers one fold launch covers at most (grid.y; their buffers travel in the
+// kernel arguments).
+constexpr int kFoldMaxLayers = 16;
+
 struct FoldArgs {
   const int32_t* slot;
-  void* ckpt;
-  const void* ring_d;
-  const void* ring_k;
-  const float* ring_g;
   const int32_t* write_pos;
   int32_t* err;
   int32_t B, N, Hv, Hk, dv, L, G;
   int32_t step_round;      // round a 16-bit state after each folded entry
   int32_t fv;              // value rows per workgroup (16, 32 or 64, divides dv)
+  // layer blockIdx.y: its checkpoint and ring (same shapes for every layer)
+  void* ckpt[kFoldMaxLayers];
+  const void* ring_d[kFoldMaxLayers];
+  const void* ring_k[kFoldMaxLayers];
+  const float* ring_g[kFoldMaxLayers];
 };
 
 }  // namespace gdn

@@ -1270,8 +1270,12 @@ __attribute__((amdgpu_waves_per_eu(window_waves_per_eu(DK, TT, NRM)))) void repl
 //
 // Fold the valid ring entries into the checkpoint with the pinned two-step
 // rounding (SGLang PR #42388 "The idea"; SGLang PR #36821 fold). Workgroup =
-// (row, value head, FV value rows); thread = one 16-byte group of 4 keys in
-// FV/16 consecutive rows (the ring entries staged in LDS serve all of them).
+// (layer, row, value head, FV value rows), the layer in blockIdx.y; thread =
+// one 16-byte group of 4 keys in FV/16 consecutive rows (the ring entries
+// staged in LDS serve all of them). One launch may fold the same rows of
+// several layers: a single layer's launch at 32 rows has a fixed cost of
+// about 5 us (its first workgroups' start and its last ones' tail) in 27 us,
+// and the layers of a verify round are folded together anyway.
 // KG = 1: per-key gate (ring_g [N, Hv, L, dk]), each channel decays by its
 // own a_j[c].
 // The fold reads each checkpoint line and writes it back: its stores go on
@@ -1289,6 +1293,12 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   float* dl = kl + a.L * DK;                          // [L][FV]  d entries
   float* al = dl + a.L * FV;                          // [L] decays ([L][DK] for KG)
 
+  // this workgroup's layer: the launch folds gridDim.y layers of equal shapes
+  const int layer = blockIdx.y;
+  void* const ckpt = a.ckpt[layer];
+  const void* const ring_d = a.ring_d[layer];
+  const void* const ring_k = a.ring_k[layer];
+  const float* const ring_g = a.ring_g[layer];
   const int nvb = a.dv / FV;
   int blk = item_of_block(blockIdx.x, gridDim.x, nvb * a.G);
   const int vb = blk % nvb;
@@ -1314,7 +1324,7 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   const int row = (tid / C4) * nr, e4 = (tid % C4) * 4;   // rows row .. row + nr - 1
 
   using SE = typename Elem<SD>::T;
-  SE* xbase = static_cast<SE*>(a.ckpt) + (hs * a.dv + vb * FV) * DK;   // the block's FV rows
+  SE* xbase = static_cast<SE*>(ckpt) + (hs * a.dv + vb * FV) * DK;   // the block's FV rows
   const int F4 = FV >> 2;                             // four d entries per item
   // This thread's first piece of ring g, d and keys is requested before the
   // checkpoint rows, so that staging them in LDS waits only for them: vector
@@ -1327,11 +1337,11 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   const int jd = cd >> lf4, jk = ck / C4;
   float g_raw = 0.f;
   typename Raw4<RING>::T d_raw{}, k_raw{};
-  if (!KG && wave == 0) g_raw = a.ring_g[hs * a.L + (tid < p ? tid : p - 1)];
+  if (!KG && wave == 0) g_raw = ring_g[hs * a.L + (tid < p ? tid : p - 1)];
   if (64 * wave < p * F4)
-    d_raw = load4_raw<RING>(a.ring_d, (hs * a.L + jd) * a.dv + vb * FV + (cd - jd * F4) * 4);
+    d_raw = load4_raw<RING>(ring_d, (hs * a.L + jd) * a.dv + vb * FV + (cd - jd * F4) * 4);
   if (64 * wave < p * C4)
-    k_raw = load4_raw<RING>(a.ring_k, (ks * a.L + jk) * DK + (ck - jk * C4) * 4);
+    k_raw = load4_raw<RING>(ring_k, (ks * a.L + jk) * DK + (ck - jk * C4) * 4);
   // the block's checkpoint rows, read with the non-temporal policy (each line
   // is read once and written back once: 31.4 -> 30.3 us at p = 15, B = 32)
   f4 x[MAXR];
@@ -1350,7 +1360,7 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   if constexpr (KG) {
     for (int c = tid; c < p * C4; c += blockDim.x) {
       const int j = c / C4, q4 = (c % C4) * 4;
-      const f4 g4 = *reinterpret_cast<const f4*>(a.ring_g + (hs * a.L + j) * DK + q4);
+      const f4 g4 = *reinterpret_cast<const f4*>(ring_g + (hs * a.L + j) * DK + q4);
       f4 av;
       av.x = decay_of(g4.x); av.y = decay_of(g4.y); av.z = decay_of(g4.z); av.w = decay_of(g4.w);
       *reinterpret_cast<f4*>(al + j * DK + q4) = av;
@@ -1363,11 +1373,11 @@ __global__ __launch_bounds__(1024) void fold_kernel(FoldArgs a) {
   for (int c = tid + blockDim.x; c < p * F4; c += blockDim.x) {
     const int j = c / F4, r4 = (c - j * F4) * 4;
     *reinterpret_cast<f4*>(dl + j * FV + r4) =
-        load4<RING>(a.ring_d, (hs * a.L + j) * a.dv + vb * FV + r4);
+        load4<RING>(ring_d, (hs * a.L + j) * a.dv + vb * FV + r4);
   }
   for (int c = tid + blockDim.x; c < p * C4; c += blockDim.x) {
     const int j = c / C4, q4 = (c % C4) * 4;
-    *reinterpret_cast<f4*>(kl + j * DK + q4) = load4<RING>(a.ring_k, (ks * a.L + j) * DK + q4);
+    *reinterpret_cast<f4*>(kl + j * DK + q4) = load4<RING>(ring_k, (ks * a.L + j) * DK + q4);
   }
   __syncthreads();
 

@@ -13,7 +13,7 @@ EXPECTED = ["gdn_abi_version", "gdn_conv_update", "gdn_hbm_copy_probe", "gdn_hbm
             "gdn_packed_decode",
             "gdn_replay_advance", "gdn_replay_commit",
             "gdn_replay_decode", "gdn_replay_decode_advance",
-            "gdn_replay_decode_advance_noalloc", "gdn_replay_fold",
+            "gdn_replay_decode_advance_noalloc", "gdn_replay_fold", "gdn_replay_fold_layers",
             "gdn_replay_reset", "gdn_status_string"]
 
 # Fake, 256-byte aligned, non-null device addresses: never dereferenced, since
@@ -33,7 +33,7 @@ def test_header_declares_exactly_the_exported_symbols():
     lib = gdn.lib()
     for name in EXPECTED:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 11
+    assert lib.gdn_abi_version() == 12
     for st in range(5):
         assert lib.gdn_status_string(st)
     assert lib.gdn_status_string(99) == b"unknown status"
@@ -148,6 +148,42 @@ def test_copy_probe_validates():
     # overlapping, not the same: dst starts inside src, or src inside dst
     assert probe(P(a), P(a + 16384), 32768) == gdn.GDN_ERR_INVALID_ARG
     assert probe(P(a + 16384), P(a), 32768) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_fold_layers_validates():
+    """The multi-layer fold checks its layer count, every layer's pointers and
+    alignment, and that no two checkpoints overlap, before any launch; with
+    valid arguments and B = 0 it returns at once."""
+    lib = gdn.lib()
+    P = ctypes.c_void_p
+    mib = 1 << 20            # one checkpoint of shape(): 4 x 4 x 128 x 128 fp32
+    base = 0x10000000
+
+    def arr(xs):
+        return (P * len(xs))(*[P(x) if x is not None else None for x in xs])
+
+    def call(n, ck, rd=None, rk=None, rg=None, B=2):
+        rd = rd if rd is not None else [0x40000000 + 0x10000 * i for i in range(len(ck))]
+        rk = rk if rk is not None else [0x50000000 + 0x10000 * i for i in range(len(ck))]
+        rg = rg if rg is not None else [0x60000000 + 0x10000 * i for i in range(len(ck))]
+        sh = shape(B=B)
+        return lib.gdn_replay_fold_layers(ctypes.byref(sh), n, FAKE[0], arr(ck), arr(rd), arr(rk),
+                                          arr(rg), FAKE[1], None, None)
+    ok = [base + i * mib for i in range(3)]
+    assert call(3, ok, B=0) == gdn.GDN_OK
+    assert call(0, ok) == gdn.GDN_ERR_INVALID_ARG
+    assert call(1025, ok) == gdn.GDN_ERR_INVALID_ARG
+    sh = shape()
+    assert lib.gdn_replay_fold_layers(ctypes.byref(sh), 1, FAKE[0], None, arr(ok), arr(ok),
+                                      arr(ok), FAKE[1], None, None) == gdn.GDN_ERR_INVALID_ARG
+    assert call(3, [ok[0], None, ok[2]]) == gdn.GDN_ERR_INVALID_ARG
+    assert call(3, [ok[0], ok[1] + 8, ok[2]]) == gdn.GDN_ERR_INVALID_ARG          # misaligned
+    assert call(2, ok[:2], rk=[0x50000000, 0x50000004]) == gdn.GDN_ERR_INVALID_ARG
+    assert call(3, [ok[0], ok[1], ok[0]]) == gdn.GDN_ERR_INVALID_ARG              # same twice
+    assert call(2, [ok[1], ok[0] + mib // 2]) == gdn.GDN_ERR_INVALID_ARG         # overlapping
+    # shared rings are allowed (they are only read)
+    assert call(2, ok[:2], rd=[0x40000000] * 2, rk=[0x50000000] * 2, rg=[0x60000000] * 2,
+                B=0) == gdn.GDN_OK
 
 
 def test_decode_advance_noalloc_validates():

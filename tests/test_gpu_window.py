@@ -218,6 +218,54 @@ def test_fold_bitwise_against_oracle(gdn, ring):
         f"{int(wp[live].sum())} entries folded")
 
 
+@pytest.mark.parametrize("n_layers,ring,state,gate", [
+    (3, "f16", "f32", "head"), (17, "bf16", "f32", "head"), (2, "f32", "bf16", "head"),
+    (2, "f16", "f32", "key")])
+def test_fold_layers_bitwise(gdn, n_layers, ring, state, gate):
+    """gdn_replay_fold_layers folds each layer's own ring into its own
+    checkpoint under one cursor array, bit-identical to gdn_replay_fold on
+    that layer and, with an fp32 state and the per-head gate, to the oracle's
+    pinned-rounding fold; 17 layers take two launches (16 + 1). Canaries
+    around every checkpoint stay untouched."""
+    w = dataclasses.replace(gi.C5, ring=ring, state=state, gate=gate, Hv=4, Hk=2, N=10, B=8,
+                            n_pad=1, permute=True, seed=870 + n_layers)
+    rcs = [gi.random_ring(w, seed_tag=20 + i) for i in range(n_layers)]
+    slots = gi.slot_map(w)
+    slot_t = to_dev(slots)
+    wp = rcs[0].write_pos.copy()
+    live = slots[slots >= 0]
+    wp[live[0]] = w.L
+    wp[live[1]] = 0
+    wpt = to_dev(wp.astype(np.int32))
+    sdt = TORCH_DT[state]
+    guards, ones, rings = [], [], []
+    for rc in rcs:
+        init = to_dev(rc.ckpt).to(sdt)
+        guards.append(CanaryTensor(rc.ckpt.shape, state, init=init))
+        ones.append(init.clone())
+        rings.append((to_dev(rc.d, ring), to_dev(rc.k, ring), to_dev(rc.g)))
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gdn.gdn_replay_fold_layers(slot_t, [g.t for g in guards], [r[0] for r in rings],
+                               [r[1] for r in rings], [r[2] for r in rings], wpt, err_flags=err)
+    for ck, r in zip(ones, rings):
+        gdn.gdn_replay_fold(slot_t, ck, r[0], r[1], r[2], wpt, err_flags=err)
+    assert int(err.item()) == 0
+    assert np.array_equal(wpt.cpu().numpy(), wp.astype(np.int32))
+    for i, (g, ck, rc) in enumerate(zip(guards, ones, rcs)):
+        g.check(f"fold_layers: layer {i}")
+        assert torch.equal(bits(g.t), bits(ck)), f"layer {i} differs from its own fold"
+        if state == "f32" and gate == "head":
+            ref = rc.ckpt.copy()
+            fold_f32(ref, slots, wp.astype(np.int32).copy(),
+                     gi.as_f64(rc.d, ring).astype(np.float32),
+                     gi.as_f64(rc.k, ring).astype(np.float32), rc.g)
+            got = g.t.cpu().numpy()
+            mism = np.count_nonzero(got.view(np.uint32) != ref.view(np.uint32))
+            assert mism == 0, f"layer {i}: {mism} elements differ from the oracle's fold"
+    log(f"[fold_layers/{n_layers}/{ring}/{state}/{gate}] every layer bit-identical, "
+        f"{int(wp[live].sum())} entries per layer")
+
+
 @pytest.mark.parametrize("T", [1, 2, 4, 6, 8])
 def test_window_length_sweep_verify_commit_verify(gdn, T):
     """Windows of T in {1, 2, 4, 6, 8} tokens (vLLM PR #49887, Tests) at B = 16:
