@@ -77,6 +77,55 @@ def test_graph_replays_match_eager(gdn, fused, gate):
     assert int(wp_e.max().item()) < w.L
 
 
+def test_graph_verify_round_matches_eager(gdn):
+    """A speculative round captured once and replayed: two layers' verify
+    windows from their checkpoints, the commit of the accepted prefix, both
+    layers' folds in one gdn_replay_fold_layers call and the cursor reset.
+    After every replay (eager work and a synchronisation in between) the
+    outputs, checkpoints, rings and cursors equal, bit for bit, those of the
+    same round run eagerly on a twin pool."""
+    w = gi.scaled(gi.C5, name="graph_round", B=8, N=12, T=3, steps=1, permute=True, n_pad=1,
+                  seed=73)
+    S0 = gi.initial_state(w)
+    slots = to_dev(gi.slot_map(w))
+    eager = [Pool(w, S0), Pool(w, S0)]
+    graphd = [Pool(w, S0), Pool(w, S0)]
+    wp_e = torch.zeros(w.N, dtype=torch.int32, device=DEV)
+    wp_g = torch.zeros(w.N, dtype=torch.int32, device=DEV)
+    xi = dev_inputs(gi.step_inputs(w, 0))
+    acc = to_dev(gi.accepted_counts(w, 0))
+    assert int(acc.max().item()) > 0
+    o_e = torch.empty((w.B, w.T, w.Hv, w.dv), dtype=torch.bfloat16, device=DEV)
+    o_g = torch.empty_like(o_e)
+
+    def round_(pools, wp, o):
+        for p in pools:
+            gdn.gdn_replay_decode(xi.q, xi.k, xi.v, xi.g, xi.beta, slots, p.ckpt, p.ring_d,
+                                  p.ring_k, p.ring_g, wp, o=o, window=True)
+        gdn.gdn_replay_commit(slots, acc, wp, w.L, w.T)
+        gdn.gdn_replay_fold_layers(slots, [p.ckpt for p in pools], [p.ring_d for p in pools],
+                                   [p.ring_k for p in pools], [p.ring_g for p in pools], wp)
+        gdn.gdn_replay_reset(slots, wp)
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        round_(graphd, wp_g, o_g)
+    torch.cuda.synchronize()
+    for step in range(4):
+        round_(eager, wp_e, o_e)
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (o_e.float() * 2).sum().item()         # unrelated eager work between replays
+        assert torch.equal(bits(o_e), bits(o_g)), f"replay {step}: outputs differ"
+        for a, b in zip(_state(eager[0]) + _state(eager[1]), _state(graphd[0]) + _state(graphd[1])):
+            assert torch.equal(a, b), f"replay {step}: state differs"
+        assert torch.equal(wp_e, wp_g)
+        assert int(wp_e.abs().sum().item()) == 0
+
+
 def test_prepared_call_matches_plain_call(gdn):
     w = gi.scaled(gi.C2, name="prepared", B=6, N=6, L=8, steps=1, stagger=False, seed=72)
     S0 = gi.initial_state(w)
