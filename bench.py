@@ -649,7 +649,8 @@ def cpu_baseline(w, budget_s, log):
                 kind="oracle",
                 sample=(f"{top['steps']} decode steps of the B={live} x Hv={w.Hv} (dk=dv={w.dk}) "
                         f"batch through the fp64 sequential recurrence on {top['threads']} threads, "
-                        f"{top['seconds']:.1f} s"),
+                        f"{top['seconds']:.1f} s (the whole CPU leg, fp64 and fp32 on 1 and "
+                        f"{top['threads']} threads: {sum(v['seconds'] for v in res.values()):.1f} s)"),
                 cpu_model=cpu_model(), host_cpus_available=avail, build_flags=flags,
                 fp64_1_thread=res[("f64", 1)]["head_steps_per_s"],
                 fp32_1_thread=res[("f32", 1)]["head_steps_per_s"],
