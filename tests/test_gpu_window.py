@@ -266,6 +266,32 @@ def test_fold_layers_bitwise(gdn, n_layers, ring, state, gate):
         f"{int(wp[live].sum())} entries per layer")
 
 
+def test_fold_layers_rejects_mismatched_layers(gdn):
+    """The binding refuses layers whose counts, dtypes, shapes or ring depths
+    differ from layer 0's, and the library refuses a checkpoint passed twice;
+    all before any launch, so the checkpoints stay as they were."""
+    w = dataclasses.replace(gi.C5, Hv=4, Hk=2, N=6, B=4, seed=880)
+    rc = gi.random_ring(w, seed_tag=1)
+    slot_t = to_dev(gi.slot_map(w))
+    wpt = to_dev(rc.write_pos.astype(np.int32))
+    mk = lambda: (to_dev(rc.ckpt), to_dev(rc.d, w.ring), to_dev(rc.k, w.ring), to_dev(rc.g))
+    (c0, d0, k0, g0), (c1, d1, k1, g1) = mk(), mk()
+    before = [bits(c0).clone(), bits(c1).clone()]
+    with pytest.raises(ValueError):       # one ring_d short
+        gdn.gdn_replay_fold_layers(slot_t, [c0, c1], [d0], [k0, k1], [g0, g1], wpt)
+    with pytest.raises(ValueError):       # layer 1's checkpoint in another dtype
+        gdn.gdn_replay_fold_layers(slot_t, [c0, c1.to(torch.bfloat16)], [d0, d1], [k0, k1],
+                                   [g0, g1], wpt)
+    with pytest.raises(ValueError):       # layer 1's ring one entry shorter
+        gdn.gdn_replay_fold_layers(slot_t, [c0, c1], [d0, d1[:, :, :-1].contiguous()],
+                                   [k0, k1[:, :, :-1].contiguous()], [g0, g1[:, :, :-1].contiguous()],
+                                   wpt)
+    with pytest.raises(gdn.GdnError):     # the same checkpoint twice
+        gdn.gdn_replay_fold_layers(slot_t, [c0, c0], [d0, d1], [k0, k1], [g0, g1], wpt)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(c0), before[0]) and torch.equal(bits(c1), before[1])
+
+
 @pytest.mark.parametrize("T", [1, 2, 4, 6, 8])
 def test_window_length_sweep_verify_commit_verify(gdn, T):
     """Windows of T in {1, 2, 4, 6, 8} tokens (vLLM PR #49887, Tests) at B = 16:
