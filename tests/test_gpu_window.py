@@ -266,6 +266,42 @@ def test_fold_layers_bitwise(gdn, n_layers, ring, state, gate):
         f"{int(wp[live].sum())} entries per layer")
 
 
+def test_fold_layers_full_size_eight_layers(gdn):
+    """The launch the benchmark times: the speculative workload's 8 layers
+    (B = 32, Hv = 32, dk = dv = 128, fp16 ring) in one gdn_replay_fold_layers
+    call, with cursors from 0 to L over the slots. Every layer's checkpoint is
+    bit-identical to gdn_replay_fold on that layer, whose own parity with the
+    oracle's fold at these shapes test_fold_bitwise_against_oracle checks;
+    layer 0 is also checked against the oracle's fold directly."""
+    w = dataclasses.replace(gi.C5, seed=890)
+    n = 8
+    rcs = [gi.random_ring(w, seed_tag=40 + i) for i in range(n)]
+    slots = gi.slot_map(w)
+    slot_t = to_dev(slots)
+    wp = rcs[0].write_pos.copy()
+    wp[slots[0]] = w.L
+    wp[slots[1]] = 0
+    wpt = to_dev(wp.astype(np.int32))
+    many = [to_dev(rc.ckpt) for rc in rcs]
+    one = [c.clone() for c in many]
+    rings = [(to_dev(rc.d, w.ring), to_dev(rc.k, w.ring), to_dev(rc.g)) for rc in rcs]
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gdn.gdn_replay_fold_layers(slot_t, many, [r[0] for r in rings], [r[1] for r in rings],
+                               [r[2] for r in rings], wpt, err_flags=err)
+    for c, r in zip(one, rings):
+        gdn.gdn_replay_fold(slot_t, c, r[0], r[1], r[2], wpt, err_flags=err)
+    assert int(err.item()) == 0
+    for i in range(n):
+        assert torch.equal(bits(many[i]), bits(one[i])), f"layer {i} differs from its own fold"
+    ref = rcs[0].ckpt.copy()
+    fold_f32(ref, slots, wp.astype(np.int32).copy(), gi.as_f64(rcs[0].d, w.ring).astype(np.float32),
+             gi.as_f64(rcs[0].k, w.ring).astype(np.float32), rcs[0].g)
+    got = many[0].cpu().numpy()
+    mism = np.count_nonzero(got.view(np.uint32) != ref.view(np.uint32))
+    assert mism == 0, f"layer 0: {mism} elements differ from the oracle's fold"
+    log(f"[fold_layers/full] 8 layers bit-identical, {int(wp[slots].sum())} entries per layer")
+
+
 def test_fold_layers_rejects_mismatched_layers(gdn):
     """The binding refuses layers whose counts, dtypes, shapes or ring depths
     differ from layer 0's, and the library refuses a checkpoint passed twice;
