@@ -11,10 +11,12 @@
  *
  * Conventions for every entry point
  *   - Pointers marked (device) are device (HBM) pointers; the `shape` struct
- *     is a host pointer read during the call only. `stream` is a hipStream_t
- *     (NULL = the null stream).
+ *     (and the per-layer pointer arrays of gdn_replay_fold_layers) are host
+ *     memory read during the call only. `stream` is a hipStream_t (NULL =
+ *     the null stream).
  *   - Every call is asynchronous on `stream`: it validates its host-side
- *     arguments, enqueues one or two kernels, and returns. It never
+ *     arguments, enqueues one or two kernels (gdn_replay_fold_layers: one
+ *     per 16 layers), and returns. It never
  *     synchronises, never allocates and never frees. The caller owns every
  *     buffer and must keep it alive until the stream has passed the call.
  *   - On a host-side validation failure the call returns a non-zero status
